@@ -1,0 +1,149 @@
+"""Plain fp64 CPU oracle for paged KV-cache decode (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. It shares no code with the GPU library
+and imports nothing from it.
+
+Parts:
+  * ``oracle.c`` (built to ``liboracle.so`` by :func:`build`): closed-form KV
+    size, append, gather and fp64 softmax attention, plus a partitioned
+    (per-partition max/sum, then merge) form of the same attention.
+  * :mod:`oracle.brute`: the same attention in pure-Python loops, for tiny
+    inputs.
+  * :mod:`oracle.block_model`: a plain model of on-demand block allocation,
+    refcounted sharing and copy-on-write.
+
+The wrappers below take numpy arrays and only marshal arguments.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+_SRC = os.path.join(_HERE, "oracle.c")
+
+F32, F16, BF16 = 0, 1, 2
+_NP_STORAGE = {F32: np.float32, F16: np.uint16, BF16: np.uint16}
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (-O3 -fopenmp, no fast-math)."""
+    if force or not os.path.exists(_SO):
+        tmp = _SO + ".tmp"
+        subprocess.run(
+            ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
+             "-o", tmp, _SRC, "-lm"],
+            check=True,
+        )
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        L = ctypes.CDLL(_SO)
+        P = ctypes.c_void_p
+        i32 = ctypes.c_int
+        i64 = ctypes.c_int64
+        L.orc_kv_bytes_per_token.restype = i64
+        L.orc_kv_bytes_per_token.argtypes = [i64, i64, i64, i64]
+        L.orc_elem_to_double.restype = ctypes.c_double
+        L.orc_elem_to_double.argtypes = [P, i64, i32]
+        L.orc_append.restype = None
+        L.orc_append.argtypes = [i32, i32, i32, i32, i32, P, P, P, i32, P, P, P]
+        L.orc_gather.restype = None
+        L.orc_gather.argtypes = [i32, i32, i32, i32, P, P, P, i32, i32, P, P]
+        L.orc_decode.restype = None
+        L.orc_decode.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, i32, P, P,
+                                 ctypes.c_double, P]
+        L.orc_decode_partitioned.restype = None
+        L.orc_decode_partitioned.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, i32, P,
+                                             P, ctypes.c_double, i32, P]
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _storage(a: np.ndarray, dtype: int) -> np.ndarray:
+    want = _NP_STORAGE[dtype]
+    if a.dtype != want:
+        raise TypeError(f"expected storage dtype {np.dtype(want)} for code {dtype}, got {a.dtype}")
+    return np.ascontiguousarray(a)
+
+
+def kv_bytes_per_token(layers: int, kv_heads: int, head_dim: int, bytes_per_elem: int) -> int:
+    return int(lib().orc_kv_bytes_per_token(layers, kv_heads, head_dim, bytes_per_elem))
+
+
+def elem_to_double(storage: np.ndarray, dtype: int) -> np.ndarray:
+    s = _storage(storage.reshape(-1), dtype)
+    L = lib()
+    return np.array([L.orc_elem_to_double(_ptr(s), i, dtype) for i in range(s.size)])
+
+
+def append(k_pool, v_pool, block_table, ctx_lens, k_new, v_new, *, dtype, block_size=16):
+    """In-place append into one layer's K/V pool arrays [NB][Hkv][bs][D]."""
+    k_pool = _storage(k_pool, dtype)
+    v_pool = _storage(v_pool, dtype)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    kn = _storage(k_new, dtype)
+    vn = _storage(v_new, dtype)
+    B, Hkv, D = kn.shape
+    assert k_pool.shape[1] == Hkv and k_pool.shape[2] == block_size and k_pool.shape[3] == D
+    lib().orc_append(B, Hkv, D, block_size, dtype, _ptr(k_pool), _ptr(v_pool), _ptr(bt),
+                     bt.shape[1], _ptr(ctx), _ptr(kn), _ptr(vn))
+    return k_pool, v_pool
+
+
+def gather(k_pool, v_pool, bt_row, n_tokens, g, *, dtype, block_size=16):
+    """Contiguous fp64 K and V rows [n_tokens][D] of kv head g for one sequence."""
+    k_pool = _storage(k_pool, dtype)
+    v_pool = _storage(v_pool, dtype)
+    row = np.ascontiguousarray(bt_row, dtype=np.int32)
+    NB, Hkv, bs, D = k_pool.shape
+    ok = np.zeros((max(n_tokens, 1), D))
+    ov = np.zeros((max(n_tokens, 1), D))
+    lib().orc_gather(Hkv, D, block_size, dtype, _ptr(k_pool), _ptr(v_pool), _ptr(row),
+                     n_tokens, g, _ptr(ok), _ptr(ov))
+    return ok[:n_tokens], ov[:n_tokens]
+
+
+def decode(k_pool, v_pool, block_table, ctx_lens, q, scale, *, dtype, block_size=16,
+           partition_tokens: int = 0):
+    """fp64 attention output [B][Hq][D] for one layer read through the block table.
+
+    ``partition_tokens`` > 0 computes the partitioned form (per-partition
+    max/sum/output, then merged); 0 computes the plain definition.
+    """
+    k_pool = _storage(k_pool, dtype)
+    v_pool = _storage(v_pool, dtype)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    qq = _storage(q, dtype)
+    B, Hq, D = qq.shape
+    NB, Hkv, bs, D2 = k_pool.shape
+    assert D2 == D and bs == block_size and Hq % Hkv == 0
+    out = np.zeros((B, Hq, D))
+    L = lib()
+    if partition_tokens > 0:
+        L.orc_decode_partitioned(B, Hq, Hkv, D, block_size, dtype, _ptr(k_pool), _ptr(v_pool),
+                                 _ptr(bt), bt.shape[1], _ptr(ctx), _ptr(qq), float(scale),
+                                 int(partition_tokens), _ptr(out))
+    else:
+        L.orc_decode(B, Hq, Hkv, D, block_size, dtype, _ptr(k_pool), _ptr(v_pool), _ptr(bt),
+                     bt.shape[1], _ptr(ctx), _ptr(qq), float(scale), _ptr(out))
+    return out

@@ -1,0 +1,287 @@
+/*
+ * Plain fp64 CPU oracle for paged KV-cache decode.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library. It shares no code,
+ * header, table or helper with the GPU library: every layout formula below
+ * is written out again from its definition.
+ *
+ * What it computes, and where the pages define it:
+ *  - KV bytes per token = 2 * layers * kv_heads * head_dim * bytes_per_element
+ *    (ssdnodes.com, "KV cache vs prompt cache", section "How much memory does
+ *    the KV cache use?", the bytes-per-token formula; the 2 counts K and V).
+ *  - Each sequence's cache is cut into fixed blocks (default 16 tokens) that
+ *    need not be adjacent; a per-sequence block table maps logical block ->
+ *    physical block (ahmedhaies.com, "PagedAttention: why LLM serving wastes
+ *    most GPU memory", section "The solution: borrow virtual memory from the
+ *    OS"; thienlv.com, "PagedAttention là gì?", section "How does
+ *    PagedAttention work?").
+ *  - A decode step appends the new token's key/value to the cache and reads
+ *    the whole cache to attend (news.hamidun.com glossary "KV-Cache", the
+ *    prefill/decode paragraph); the new query attends to all previous keys and
+ *    values (same page, the mechanism paragraph).
+ *  - With grouped-query attention several query heads share one stored K/V
+ *    head (ssdnodes.com, same section, the GQA paragraph); query head h reads
+ *    kv head h / (q_heads / kv_heads).
+ *
+ * Physical layout of one layer of the pool (our choice; the pages fix only
+ * "blocks of block_size tokens" and "a block table"): K and V are separate
+ * arrays, each indexed [block][kv_head][row][d] in row-major order, where row
+ * is the token's position inside its block.
+ *
+ * Numbers are read exactly from their stored type (fp32, fp16 or bf16) into
+ * double; all arithmetic is double. No blocking, no online softmax, no split:
+ * gather to a contiguous array, then softmax(q.K^T * scale) . V.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
+
+static size_t orc_elem_bytes(int dtype) { return dtype == ORC_F32 ? 4u : 2u; }
+
+/* IEEE-754 binary16 -> double, from the format's definition:
+ * 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+static double orc_half_bits_to_double(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int ex = (h >> 10) & 0x1f;
+  int fr = h & 0x3ff;
+  double v;
+  if (ex == 0) {
+    v = ldexp((double)fr, -24); /* subnormal: fr * 2^-14 * 2^-10 */
+  } else if (ex == 31) {
+    v = fr ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(1024 + fr), ex - 25); /* (1 + fr/1024) * 2^(ex-15) */
+  }
+  return sign ? -v : v;
+}
+
+/* bfloat16 is the upper half of an IEEE binary32. */
+static double orc_bf16_bits_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static double orc_load(const void* base, size_t idx, int dtype) {
+  if (dtype == ORC_F32) {
+    float f;
+    memcpy(&f, (const char*)base + idx * 4u, 4);
+    return (double)f;
+  }
+  uint16_t b;
+  memcpy(&b, (const char*)base + idx * 2u, 2);
+  return dtype == ORC_F16 ? orc_half_bits_to_double(b) : orc_bf16_bits_to_double(b);
+}
+
+/* Exposed so the tests can check the conversions against library routines. */
+double orc_elem_to_double(const void* base, int64_t idx, int dtype) {
+  return orc_load(base, (size_t)idx, dtype);
+}
+
+/* ssdnodes.com, "KV cache vs prompt cache", "How much memory does the KV cache
+ * use?": bytes per token = 2 * layers * kv_heads * head_dim * bytes/element. */
+int64_t orc_kv_bytes_per_token(int64_t layers, int64_t kv_heads, int64_t head_dim,
+                               int64_t bytes_per_elem) {
+  return 2 * layers * kv_heads * head_dim * bytes_per_elem;
+}
+
+/* Element index of (block, kv_head, row, d) in one layer's K (or V) array. */
+static size_t orc_pool_index(int64_t block, int64_t head, int64_t row, int64_t d,
+                             int kv_heads, int block_size, int head_dim) {
+  return (size_t)((((block * kv_heads) + head) * block_size + row) * head_dim + d);
+}
+
+/*
+ * Append (news.hamidun.com "KV-Cache", prefill/decode paragraph: each decode
+ * step appends the new token's key/value entry to the cache).
+ * For sequence s with context length L (the new token included), the new
+ * token is logical position p = L - 1; it lives in physical block
+ * block_table[s][p / block_size] at row p % block_size. Writes k_new[s][g][:]
+ * and v_new[s][g][:] there for every kv head g. Bytes are copied unchanged.
+ * Sequences with L <= 0 are skipped.
+ */
+void orc_append(int batch, int kv_heads, int head_dim, int block_size, int dtype,
+                void* k_pool, void* v_pool, const int32_t* block_table, int max_blocks,
+                const int32_t* ctx_lens, const void* k_new, const void* v_new) {
+  size_t eb = orc_elem_bytes(dtype);
+  for (int s = 0; s < batch; ++s) {
+    int L = ctx_lens[s];
+    if (L <= 0) continue;
+    int p = L - 1;
+    int32_t blk = block_table[(size_t)s * max_blocks + p / block_size];
+    int row = p % block_size;
+    for (int g = 0; g < kv_heads; ++g) {
+      size_t dst = orc_pool_index(blk, g, row, 0, kv_heads, block_size, head_dim) * eb;
+      size_t src = ((size_t)s * kv_heads + g) * head_dim * eb;
+      memcpy((char*)k_pool + dst, (const char*)k_new + src, head_dim * eb);
+      memcpy((char*)v_pool + dst, (const char*)v_new + src, head_dim * eb);
+    }
+  }
+}
+
+/*
+ * Gather one sequence's first n_tokens K and V rows of kv head g into
+ * contiguous double arrays out_k[t][d], out_v[t][d]: logical token t sits in
+ * physical block block_table[s][t / block_size], row t % block_size.
+ */
+void orc_gather(int kv_heads, int head_dim, int block_size, int dtype, const void* k_pool,
+                const void* v_pool, const int32_t* bt_row, int n_tokens, int g, double* out_k,
+                double* out_v) {
+  for (int t = 0; t < n_tokens; ++t) {
+    int32_t blk = bt_row[t / block_size];
+    int row = t % block_size;
+    for (int d = 0; d < head_dim; ++d) {
+      size_t i = orc_pool_index(blk, g, row, d, kv_heads, block_size, head_dim);
+      out_k[(size_t)t * head_dim + d] = orc_load(k_pool, i, dtype);
+      out_v[(size_t)t * head_dim + d] = orc_load(v_pool, i, dtype);
+    }
+  }
+}
+
+/*
+ * Softmax attention of one query vector over n contiguous K/V rows, in fp64:
+ *   z_t = scale * sum_d q[d] * K[t][d]
+ *   p_t = exp(z_t - max z) / sum_u exp(z_u - max z)
+ *   out[d] = sum_t p_t * V[t][d]
+ */
+void orc_attend(int n, int head_dim, const double* q, const double* kc, const double* vc,
+                double scale, double* out) {
+  double* z = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  double mx = -INFINITY;
+  for (int t = 0; t < n; ++t) {
+    double acc = 0.0;
+    for (int d = 0; d < head_dim; ++d) acc += q[d] * kc[(size_t)t * head_dim + d];
+    z[t] = scale * acc;
+    if (z[t] > mx) mx = z[t];
+  }
+  double den = 0.0;
+  for (int t = 0; t < n; ++t) {
+    z[t] = exp(z[t] - mx);
+    den += z[t];
+  }
+  for (int d = 0; d < head_dim; ++d) out[d] = 0.0;
+  for (int t = 0; t < n; ++t) {
+    double p = z[t] / den;
+    for (int d = 0; d < head_dim; ++d) out[d] += p * vc[(size_t)t * head_dim + d];
+  }
+  free(z);
+}
+
+/*
+ * Decode attention for a batch, reading the cache through the block tables:
+ * for every sequence s and query head h, gather the first ctx_lens[s] rows of
+ * kv head h / (q_heads / kv_heads) and attend with q[s][h].
+ * q is stored in the cache dtype, [batch][q_heads][head_dim]; out is double
+ * [batch][q_heads][head_dim]. Parallel over (sequence, kv head) with OpenMP.
+ */
+void orc_decode(int batch, int q_heads, int kv_heads, int head_dim, int block_size, int dtype,
+                const void* k_pool, const void* v_pool, const int32_t* block_table,
+                int max_blocks, const int32_t* ctx_lens, const void* q, double scale,
+                double* out) {
+  int group = q_heads / kv_heads;
+  int npairs = batch * kv_heads;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int pi = 0; pi < npairs; ++pi) {
+    int s = pi / kv_heads;
+    int g = pi % kv_heads;
+    int L = ctx_lens[s];
+    size_t n = (size_t)(L > 0 ? L : 1) * head_dim;
+    double* kc = (double*)malloc(sizeof(double) * n);
+    double* vc = (double*)malloc(sizeof(double) * n);
+    double* qd = (double*)malloc(sizeof(double) * head_dim);
+    orc_gather(kv_heads, head_dim, block_size, dtype, k_pool, v_pool,
+               block_table + (size_t)s * max_blocks, L, g, kc, vc);
+    for (int h = g * group; h < (g + 1) * group; ++h) {
+      for (int d = 0; d < head_dim; ++d)
+        qd[d] = orc_load(q, ((size_t)s * q_heads + h) * head_dim + d, dtype);
+      orc_attend(L, head_dim, qd, kc, vc, scale, out + ((size_t)s * q_heads + h) * head_dim);
+    }
+    free(kc);
+    free(vc);
+    free(qd);
+  }
+}
+
+/*
+ * The same decode computed as independent partitions of part_tokens tokens
+ * (partition i covers tokens [i*part_tokens, min(L, (i+1)*part_tokens))),
+ * each reduced to (m_i = max logit, l_i = sum exp(z - m_i),
+ * o_i = sum exp(z - m_i) * V), then merged with M = max_i m_i:
+ *   out = sum_i exp(m_i - M) o_i / sum_i exp(m_i - M) l_i.
+ * The merge is an exact identity of softmax, so in exact arithmetic this
+ * equals orc_decode; the tests hold the two together to ~1e-12.
+ */
+void orc_decode_partitioned(int batch, int q_heads, int kv_heads, int head_dim, int block_size,
+                            int dtype, const void* k_pool, const void* v_pool,
+                            const int32_t* block_table, int max_blocks, const int32_t* ctx_lens,
+                            const void* q, double scale, int part_tokens, double* out) {
+  int group = q_heads / kv_heads;
+  int npairs = batch * q_heads;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int pi = 0; pi < npairs; ++pi) {
+    int s = pi / q_heads;
+    int h = pi % q_heads;
+    int g = h / group;
+    int L = ctx_lens[s];
+    size_t n = (size_t)(L > 0 ? L : 1) * head_dim;
+    double* kc = (double*)malloc(sizeof(double) * n);
+    double* vc = (double*)malloc(sizeof(double) * n);
+    double* qd = (double*)malloc(sizeof(double) * head_dim);
+    double* oi = (double*)malloc(sizeof(double) * head_dim);
+    double* acc = out + ((size_t)s * q_heads + h) * head_dim;
+    orc_gather(kv_heads, head_dim, block_size, dtype, k_pool, v_pool,
+               block_table + (size_t)s * max_blocks, L, g, kc, vc);
+    for (int d = 0; d < head_dim; ++d)
+      qd[d] = orc_load(q, ((size_t)s * q_heads + h) * head_dim + d, dtype);
+    int nparts = (L + part_tokens - 1) / part_tokens;
+    double* m = (double*)malloc(sizeof(double) * (size_t)(nparts > 0 ? nparts : 1));
+    double* l = (double*)malloc(sizeof(double) * (size_t)(nparts > 0 ? nparts : 1));
+    double* o = (double*)malloc(sizeof(double) * (size_t)(nparts > 0 ? nparts : 1) * head_dim);
+    for (int i = 0; i < nparts; ++i) {
+      int t0 = i * part_tokens;
+      int t1 = t0 + part_tokens < L ? t0 + part_tokens : L;
+      double mi = -INFINITY;
+      for (int t = t0; t < t1; ++t) {
+        double z = 0.0;
+        for (int d = 0; d < head_dim; ++d) z += qd[d] * kc[(size_t)t * head_dim + d];
+        z *= scale;
+        if (z > mi) mi = z;
+      }
+      double li = 0.0;
+      for (int d = 0; d < head_dim; ++d) oi[d] = 0.0;
+      for (int t = t0; t < t1; ++t) {
+        double z = 0.0;
+        for (int d = 0; d < head_dim; ++d) z += qd[d] * kc[(size_t)t * head_dim + d];
+        double e = exp(z * scale - mi);
+        li += e;
+        for (int d = 0; d < head_dim; ++d) oi[d] += e * vc[(size_t)t * head_dim + d];
+      }
+      m[i] = mi;
+      l[i] = li;
+      memcpy(o + (size_t)i * head_dim, oi, sizeof(double) * head_dim);
+    }
+    double M = -INFINITY;
+    for (int i = 0; i < nparts; ++i)
+      if (m[i] > M) M = m[i];
+    double den = 0.0;
+    for (int d = 0; d < head_dim; ++d) acc[d] = 0.0;
+    for (int i = 0; i < nparts; ++i) {
+      double w = exp(m[i] - M);
+      den += w * l[i];
+      for (int d = 0; d < head_dim; ++d) acc[d] += w * o[(size_t)i * head_dim + d];
+    }
+    for (int d = 0; d < head_dim; ++d) acc[d] /= den;
+    free(m);
+    free(l);
+    free(o);
+    free(kc);
+    free(vc);
+    free(qd);
+    free(oi);
+  }
+}
