@@ -1,0 +1,220 @@
+"""Benchmark: PagedAttention decode steps on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config llama8b_bf16]
+
+A step is one pass of the whole decode hot path over the batch: host slot
+assignment (block allocation / copy-on-write), block-table upload, copy-on-
+write copies, then for every layer the K/V append and the paged attention
+(with its split merge). The default workload is the Llama-3.1-8B-shaped
+layer stack: 32 layers, batch 64, 32 q / 8 kv heads, head_dim 128, bf16 KV,
+context lengths uniform in [128, 2048], blocks scattered through a 17 GiB
+pool (far larger than the last-level cache, so every layer's reads come
+from HBM). Every step grows each sequence by one token, as decode does.
+
+Prints one JSON line. `value` = KV bytes read by all layers of all timed
+steps / wall time between synchronisations (GB/s). The `roofline` object is
+for the decode kernel alone, timed with HIP events around back-to-back
+decode launches on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+
+
+def kv_bytes(cfg, ctx) -> int:
+    """KV bytes one layer's decode reads: every cached row of K and V once."""
+    import numpy as np
+    from paged_kv_cache_09_amd import workloads as W
+    return int(np.asarray(ctx, dtype=np.int64).sum()) * 2 * cfg.kv_heads * cfg.head_dim * \
+        W.ELEM_BYTES[cfg.dtype]
+
+
+def decode_algorithmic_bytes(cfg, ctx) -> int:
+    """Bytes one decode launch must move: KV rows, q, fp32 output, block-table entries, lengths."""
+    import numpy as np
+    from paged_kv_cache_09_amd import workloads as W
+    e = W.ELEM_BYTES[cfg.dtype]
+    B = len(ctx)
+    nblk = int(((np.asarray(ctx, dtype=np.int64) + 15) // 16).sum())
+    return (kv_bytes(cfg, ctx) + B * cfg.q_heads * cfg.head_dim * e +
+            B * cfg.q_heads * cfg.head_dim * 4 + nblk * 4 * cfg.kv_heads + B * 4)
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The fp64 oracle on the host cores, on a bounded sample of the same workload (one layer)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    cfg = w.cfg
+
+    def storage(t):
+        t = t.detach().contiguous().cpu()
+        if t.dtype == torch.float32:
+            return t.numpy().copy()
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+    def run(seqs):
+        used = sorted({b for s in seqs for b in w.pre_tables[s]} |
+                      {int(w.new_blocks[s]) for s in seqs if w.new_blocks[s] >= 0})
+        remap = {b: i for i, b in enumerate(used)}
+        idx = torch.tensor(used, dtype=torch.long, device=w.pool.device)
+        kl, vl = w.layer_views(0)
+        kc, vc = storage(kl.index_select(0, idx)), storage(vl.index_select(0, idx))
+        bt = np.full((len(seqs), w.max_blocks), -1, dtype=np.int32)
+        for i, s in enumerate(seqs):
+            row = [remap[b] for b in w.pre_tables[s]]
+            if w.new_blocks[s] >= 0:
+                row.append(remap[int(w.new_blocks[s])])
+            bt[i, :len(row)] = row
+        ctx = np.ascontiguousarray(w.ctx[seqs], dtype=np.int32)
+        sel = torch.tensor(seqs, dtype=torch.long, device=w.pool.device)
+        q = storage(w.q.index_select(0, sel))
+        t0 = time.perf_counter()
+        oracle.decode(kc, vc, bt, ctx, q, 1.0 / math.sqrt(cfg.head_dim), dtype=cfg.dtype)
+        return time.perf_counter() - t0, ctx
+
+    oracle.build(force=False)
+    probe = list(range(min(2, w.B)))
+    t, _ = run(probe)
+    n = max(1, min(w.B, int(len(probe) * budget_s / max(t, 1e-3))))
+    seqs = list(range(n))
+    t, ctx = run(seqs)
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(kv_bytes(cfg, ctx) / t / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"one layer, first {n} of {w.B} sequences ({int(ctx.sum())} context tokens), "
+                      f"{t:.1f} s",
+            "seq_tokens_per_s": round(float(ctx.sum()) / t, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="llama8b_bf16")
+    ap.add_argument("--partition", type=int, default=None,
+                    help="decode partition tokens (default: the workload's own; 0 = balanced)")
+    ap.add_argument("--decode-reps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
+              "multi-GPU path; see DESIGN.md for how the decode path would shard.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_09_amd import workloads as W
+    from paged_kv_cache_09_amd.session import DecodeSession
+
+    cfg = W.CONFIGS[args.config]
+    part = cfg.partition_tokens if args.partition is None else args.partition
+    growth = args.warmup + args.steps + 1
+    w = W.make(cfg, device="cuda", layers=cfg.layers, form="step", fill="random",
+               extra_blocks=(growth + 15) // 16 + 1)
+    sess = DecodeSession(w)
+    out = sess.new_out()
+    stream = torch.cuda.current_stream()
+    layers = list(range(cfg.layers))
+
+    def one_step():
+        sess.step(out, layers=layers, partition_tokens=part)
+
+    total_kv = 0
+    for _ in range(args.warmup):
+        one_step()
+        sess.ctx += 1
+    torch.cuda.synchronize()
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        total_kv += kv_bytes(cfg, sess.ctx) * cfg.layers
+        one_step()
+        sess.ctx += 1
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1)
+    elapsed = max(wall, ev_ms / 1e3)
+
+    # decode kernel alone: back-to-back launches over all layers, same upload
+    sess.ctx -= 1  # the uploaded table matches the last step's lengths
+    ctx_now = sess.ctx.copy()
+    reps = args.decode_reps
+    for layer in layers[:4]:
+        sess.decode(layer, out, part)
+    torch.cuda.synchronize()
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
+    for _ in range(reps):
+        for layer in layers:
+            sess.decode(layer, out, part)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    per_launch_s = d0.elapsed_time(d1) / 1e3 / (reps * len(layers))
+    alg = decode_algorithmic_bytes(cfg, ctx_now)
+    achieved = alg / per_launch_s / 1e9
+
+    res = {
+        "metric": "paged decode KV-read GB/s (% of HBM peak) + seq-tokens/s, 8B-shaped layer",
+        "value": round(total_kv / elapsed / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": W.DTYPE_NAME[cfg.dtype],
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.layers} layers x batch {cfg.batch}, "
+                        f"{cfg.q_heads} q / {cfg.kv_heads} kv heads, head_dim {cfg.head_dim}, "
+                        f"block 16, context {int(w.ctx.min())}..{int(w.ctx.max())} growing 1/step",
+            "layers": cfg.layers, "batch": cfg.batch, "q_heads": cfg.q_heads,
+            "kv_heads": cfg.kv_heads, "head_dim": cfg.head_dim, "block_size": 16,
+            "partition_tokens": part, "pool_gib": round(w.pool.numel() / 2**30, 2),
+        },
+        "pct_of_hbm_peak": round(100 * total_kv / elapsed / 1e9 / HBM_PEAK_GBS, 2),
+        "seq_tokens_per_s": round(float(sum(int(c) for c in ctx_now)) * cfg.layers *
+                                  args.steps / elapsed, 1),
+        "decode_tokens_per_s": round(cfg.batch * args.steps / elapsed, 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "decode_kernel (+ split merge) per layer launch",
+            "avg_launch_us": round(per_launch_s * 1e6, 3),
+            "algorithmic_bytes_per_launch": alg,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w)
+    sess.close()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,223 @@
+/*
+ * pkv.h — C ABI of libpkv: PagedAttention decode on AMD MI355X (gfx950).
+ *
+ * The KV cache of every sequence is cut into fixed blocks of block_size
+ * tokens (16) that sit anywhere in one shared pool; a per-sequence block
+ * table maps logical block -> physical block, the way an OS page table maps
+ * pages (ahmedhaies.com, "PagedAttention: why LLM serving wastes most GPU
+ * memory", section "The solution: borrow virtual memory from the OS";
+ * thienlv.com, "PagedAttention là gì?", section "How does PagedAttention
+ * work?"). One decode step appends each sequence's new key/value and attends
+ * its new query over the whole cache (news.hamidun.com glossary "KV-Cache",
+ * prefill/decode paragraph).
+ *
+ * Conventions for every call:
+ *  - Return value: PKV_OK (0) or a negative PKV_E* code. No exception or
+ *    abort crosses the ABI. pkv_last_error() gives a message for the last
+ *    failing call on this host thread.
+ *  - Device memory (the pool, q, out, k_new, v_new, slots, workspace) is
+ *    owned by the caller (e.g. torch tensors) and must outlive the calls
+ *    that use it. Host metadata (free list, reference counts, the device
+ *    copies of tables, lengths and schedules, pinned staging) is owned by the
+ *    library and released by pkv_kv_pool_free.
+ *  - Streams are passed as uintptr_t (a hipStream_t; 0 = null stream). All
+ *    device work is asynchronous on that stream; no call synchronises the
+ *    device except pkv_kv_pool_free.
+ *  - A pool handle must not be used from two host threads at once.
+ *
+ * Pool layout in device memory (dev_base, dev_bytes >= pkv_pool_bytes):
+ *   K region: [layers][num_blocks][kv_heads][block_size][head_dim] elements,
+ *   V region: the same shape, starting right after the K region.
+ * A physical block id names the same block in every layer. One
+ * (block, kv_head) tile of K (or V) is block_size * head_dim contiguous
+ * elements: 4 KiB for bf16/fp16 x 128 or fp32 x 64.
+ *
+ * Supported: block_size 16, head_dim 64 or 128, dtype fp32/fp16/bf16,
+ * q_heads / kv_heads (the GQA group) from 1 to 8. Other shapes return
+ * PKV_EUNSUPPORTED.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct pkv_pool pkv_pool; /* opaque */
+
+enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 };
+
+enum {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,          /* bad argument or inconsistent table              */
+  PKV_ECAPACITY = -2,       /* pool cannot hold max_seq_len tokens             */
+  PKV_EOUT_OF_BLOCKS = -3,  /* free list exhausted: the caller should queue    */
+  PKV_EUNSUPPORTED = -4,    /* shape outside the supported set                 */
+  PKV_EHIP = -5             /* HIP runtime error (allocation, copy, launch)    */
+};
+
+typedef struct {
+  int32_t layers;      /* layers sharing one block id space                      */
+  int32_t num_blocks;  /* physical blocks per layer                              */
+  int32_t block_size;  /* tokens per block; must be 16                           */
+  int32_t kv_heads;    /* stored K/V heads                                       */
+  int32_t head_dim;    /* 64 or 128                                              */
+  int32_t dtype;       /* PKV_F32 | PKV_F16 | PKV_BF16                           */
+  int32_t max_seq_len; /* longest context any sequence may reach                 */
+  int32_t max_seqs;    /* largest batch passed to upload/prepare                 */
+} pkv_shape;
+
+/*
+ * Bytes of device memory the pool needs:
+ *   layers * num_blocks * block_size * 2 * kv_heads * head_dim * elem_bytes,
+ * i.e. num_blocks * block_size tokens at the per-token size
+ * 2 * layers * kv_heads * head_dim * elem_bytes (ssdnodes.com, "KV cache vs
+ * prompt cache", section "How much memory does the KV cache use?").
+ * Returns 0 for an invalid shape.
+ */
+size_t pkv_pool_bytes(const pkv_shape* shape);
+
+/*
+ * Create a pool over caller-owned device memory dev_base[0, dev_bytes).
+ * Startup capacity check: if max_seq_len > num_blocks * block_size the call
+ * fails with PKV_ECAPACITY and a message naming both numbers (the check
+ * described on ssdnodes.com, "KV cache vs prompt cache", section "Why a model
+ * that works at 2k refuses to load at 32k").
+ * dev_base == NULL creates a host-only pool: the block manager works, every
+ * device call returns PKV_EINVAL. Otherwise the library allocates its device
+ * metadata (tables, lengths, slots, schedules) and pinned staging here.
+ * On success *out receives the handle; on failure *out is untouched.
+ */
+int pkv_kv_pool_alloc(const pkv_shape* shape, void* dev_base, size_t dev_bytes, pkv_pool** out);
+
+/* Synchronise the device, release library-owned memory and the handle. NULL is a no-op. */
+int pkv_kv_pool_free(pkv_pool* pool);
+
+/* ---- host block manager: ids are physical block ids shared by all layers ---- */
+
+/*
+ * Take n free blocks (refcount 1 each) into ids_out[n]. Blocks are handed out
+ * only on demand (thienlv.com, "PagedAttention là gì?", "How does
+ * PagedAttention work?"). If fewer than n are free nothing is taken and
+ * PKV_EOUT_OF_BLOCKS is returned: the caller queues the request (ssdnodes.com,
+ * "KV cache vs prompt cache", section "What concurrency does").
+ */
+int pkv_block_alloc(pkv_pool* pool, int n, int32_t* ids_out);
+
+/* Take the given free blocks (refcount 1): restores a known placement. All-or-nothing. */
+int pkv_block_claim(pkv_pool* pool, const int32_t* ids, int n);
+
+/*
+ * Add one reference to each allocated block: a sequence starts sharing it
+ * (shared prompt, parallel sampling; ahmedhaies.com, "PagedAttention: why LLM
+ * serving wastes most GPU memory", the copy-on-write paragraph). All-or-nothing.
+ */
+int pkv_block_ref(pkv_pool* pool, const int32_t* ids, int n);
+
+/*
+ * Drop one reference from each block; a block returns to the free list at
+ * zero (a request's cache is released when it ends: ssdnodes.com, "KV cache
+ * vs prompt cache", FAQ). All-or-nothing.
+ */
+int pkv_block_free(pkv_pool* pool, const int32_t* ids, int n);
+
+/* Reference count of one block (>= 0), or PKV_EINVAL for an out-of-range id. */
+int pkv_block_refcount(const pkv_pool* pool, int32_t id);
+
+/*
+ * Slot assignment for one decode step. host_bt is the caller's block table,
+ * int32 [batch][max_blocks] row-major, -1 for absent entries; ctx_lens[s] is
+ * the context length with the new token included (>= 1). For each sequence in
+ * batch order, with p = ctx_lens[s] - 1 and j = p / 16:
+ *   - host_bt[s][j] == -1: a free block is taken and written there;
+ *   - host_bt[s][j] shared (refcount > 1): copy-on-write — a free block is
+ *     taken, the pair (old, new) is appended to cow_pairs_out, the old block
+ *     loses one reference and host_bt[s][j] becomes the new block;
+ *   - otherwise the block is written in place.
+ * slot_out[s] = host_bt[s][j] * 16 + p % 16 (int64).
+ * cow_pairs_out receives n_cow (old, new) int32 pairs; cow_capacity is its
+ * capacity in pairs (batch always suffices). On any failure (including
+ * PKV_EOUT_OF_BLOCKS) every change made by this call is undone.
+ */
+int pkv_prepare_append(pkv_pool* pool, int32_t* host_bt, int batch, int max_blocks,
+                       const int32_t* ctx_lens, int64_t* slot_out, int32_t* cow_pairs_out,
+                       int cow_capacity, int* n_cow);
+
+/*
+ * Upload the block table int32 [batch][max_blocks] (-1 padded), the context
+ * lengths int32 [batch] and optionally the slots int64 [batch] (NULL: keep
+ * none) to the library's device copies, asynchronously on `stream` from
+ * pinned staging. Checked on the host first: 1 <= batch <= max_seqs,
+ * max_blocks * 16 <= the pool's table width, 1 <= ctx <= max_seq_len, every
+ * entry j < ceil(ctx/16) in [0, num_blocks), non-negative slots in range and
+ * pairwise distinct (two equal slots would race in kv_append).
+ * Later kv_append / decode calls use this upload.
+ */
+int pkv_block_table_upload(pkv_pool* pool, const int32_t* host_bt, int batch, int max_blocks,
+                           const int32_t* ctx_lens, const int64_t* host_slots, uintptr_t stream);
+
+/*
+ * Copy-on-write copies: for each host pair (src, dst) int32 [n][2], copy the
+ * whole K and V block src -> dst in every layer (ahmedhaies.com,
+ * "PagedAttention: why LLM serving wastes most GPU memory", copy-on-write
+ * paragraph). Pairs are uploaded through pinned staging. Must run before the
+ * kv_append that writes into dst. n == 0 is a no-op.
+ */
+int pkv_copy_blocks(pkv_pool* pool, const int32_t* host_pairs, int n, uintptr_t stream);
+
+/*
+ * Append: for s < batch and every kv head g, write k_new[s][g][:] and
+ * v_new[s][g][:] (cache dtype, [batch][kv_heads][head_dim]) into the pool row
+ * of layer `layer` at slot[s] (block slot/16, row slot%16); slot < 0 skips.
+ * dev_slots: device int64 [batch], or NULL for the slots of the last upload
+ * (batch must then equal the uploaded batch). Bytes are copied unchanged.
+ */
+int pkv_kv_append(pkv_pool* pool, int layer, const void* k_new, const void* v_new,
+                  const int64_t* dev_slots, int batch, uintptr_t stream);
+
+/*
+ * Decode attention of layer `layer` for the uploaded batch:
+ *   out[s][h][:] = sum_t softmax_t(scale * q[s][h] . K_s[t][g]) * V_s[t][g],
+ *   g = h / (q_heads / kv_heads), t < ctx[s],
+ * where K_s[t] is row t % 16 of block bt[s][t / 16] (news.hamidun.com
+ * "KV-Cache", mechanism and prefill/decode paragraphs; the GQA head sharing of
+ * ssdnodes.com, "KV cache vs prompt cache").
+ * q: device [batch][q_heads][head_dim] in the cache dtype. out: device fp32
+ * [batch][q_heads][head_dim]. Softmax and accumulation are fp32.
+ * partition_tokens: 0 = balanced split — every wavefront of a full-chip launch
+ * takes an equal share of all (sequence, kv head, block) tiles and partial
+ * results are merged by a reduce kernel; > 0 (multiple of 16) = fixed split-K
+ * partitions of that many tokens per sequence, each keeping its own max/sum,
+ * merged by the same reduce (a partition >= the longest context is the
+ * single-pass form, no reduce).
+ * workspace / ws_bytes: device scratch of at least
+ * pkv_decode_workspace_bytes(...) bytes (may be NULL when that is 0).
+ */
+int pkv_paged_attn_decode(pkv_pool* pool, int layer, const void* q, int q_heads, float scale,
+                          float* out, int partition_tokens, void* workspace, size_t ws_bytes,
+                          uintptr_t stream);
+
+/* Workspace bytes a decode of `batch` sequences with these settings may need (upper bound). */
+size_t pkv_decode_workspace_bytes(const pkv_pool* pool, int batch, int q_heads,
+                                  int partition_tokens);
+
+/*
+ * stats_out[0] free blocks, [1] allocated blocks, [2] blocks with refcount > 1,
+ * [3] internal waste in tokens of the last upload: sum over sequences of
+ * 16 * ceil(ctx/16) - ctx (only the last block of a sequence is partly empty;
+ * ahmedhaies.com, "PagedAttention: why LLM serving wastes most GPU memory",
+ * "The solution: borrow virtual memory from the OS").
+ */
+int pkv_pool_stats(const pkv_pool* pool, int64_t stats_out[4]);
+
+/* Message for the last failing call on this host thread ("" if none). */
+const char* pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,63 @@
+"""One decode step on host copies of the pool, in the oracle's own terms (test infrastructure).
+
+The block bookkeeping follows :mod:`oracle.block_model` (on-demand blocks,
+refcounted sharing, copy-on-write); the byte writes follow ``orc_append``.
+The oracle picks its own fresh block ids (any id free before the step), so
+its physical placement generally differs from the library's; what must agree
+is the logical content of every sequence and the attention output, neither
+of which depends on placement.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from oracle.block_model import BlockModel
+
+BLOCK = 16
+
+
+def run_step(k_layers, v_layers, pre_tables, shared, ctx, k_new_layers, v_new_layers, *,
+             dtype, num_blocks, max_blocks):
+    """Apply one decode step to host pools.
+
+    k_layers / v_layers: lists (one per layer) of storage arrays [NB][Hkv][16][D],
+    updated in place. k_new_layers / v_new_layers: per-layer [B][Hkv][D] rows.
+    Returns (post_table int32 [B][max_blocks], kinds).
+    """
+    model = BlockModel(num_blocks)
+    used = sorted({b for row in pre_tables for b in row})
+    model.claim(used)
+    for b, rc in shared:
+        model.ref([b] * (rc - 1))
+    kinds = model.plan_append(pre_tables, ctx)
+    free_ids = iter(sorted(set(range(num_blocks)) - set(used)))
+    B = len(pre_tables)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    for s, row in enumerate(pre_tables):
+        table[s, :len(row)] = row
+    for s, kind in enumerate(kinds):
+        j = (int(ctx[s]) - 1) // BLOCK
+        if kind == "new":
+            table[s, j] = next(free_ids)
+        elif kind == "cow":
+            src = int(table[s, j])
+            dst = next(free_ids)
+            for kl, vl in zip(k_layers, v_layers):
+                kl[dst] = kl[src]
+                vl[dst] = vl[src]
+            table[s, j] = dst
+    for kl, vl, kn, vn in zip(k_layers, v_layers, k_new_layers, v_new_layers):
+        oracle.append(kl, vl, table, ctx, kn, vn, dtype=dtype)
+    return table, kinds
+
+
+def logical_rows(k_pool, v_pool, table, ctx):
+    """Raw bytes of every sequence's K and V rows in logical order: list of (K, V) arrays [L][Hkv][D]."""
+    out = []
+    for s, L in enumerate(ctx):
+        t = np.arange(int(L))
+        blocks = table[s][t // BLOCK]
+        rows = t % BLOCK
+        out.append((k_pool[blocks, :, rows, :], v_pool[blocks, :, rows, :]))
+    return out

@@ -1,0 +1,701 @@
+// Host side of libpkv: pool descriptor, block manager (free list, reference
+// counts, copy-on-write planning), uploads through pinned staging, decode
+// scheduling, argument checks and kernel launches. See include/pkv.h for the
+// contract of every entry point.
+#include "pkv.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int elem_bytes(int dtype) {
+  return dtype == PKV_F32 ? 4 : (dtype == PKV_F16 || dtype == PKV_BF16) ? 2 : 0;
+}
+
+// Shape checks shared by pkv_pool_bytes and pkv_kv_pool_alloc.
+int check_shape(const pkv_shape* sh) {
+  if (!sh) return fail(PKV_EINVAL, "shape is NULL");
+  if (sh->layers < 1 || sh->num_blocks < 1 || sh->kv_heads < 1 || sh->max_seqs < 1 ||
+      sh->max_seq_len < 1)
+    return fail(PKV_EINVAL, "layers, num_blocks, kv_heads, max_seqs and max_seq_len must be >= 1");
+  if (elem_bytes(sh->dtype) == 0) return fail(PKV_EINVAL, "unknown dtype %d", sh->dtype);
+  if (sh->block_size != pkv::kBlock)
+    return fail(PKV_EUNSUPPORTED, "block_size %d is not supported (16 only)", sh->block_size);
+  if (sh->head_dim != 64 && sh->head_dim != 128)
+    return fail(PKV_EUNSUPPORTED, "head_dim %d is not supported (64 or 128)", sh->head_dim);
+  if ((int64_t)sh->num_blocks * sh->block_size > INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "num_blocks * block_size must fit in int32");
+  return PKV_OK;
+}
+
+struct Staging {
+  char* host = nullptr;
+  size_t bytes = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+
+}  // namespace
+
+struct pkv_pool {
+  pkv_shape shape{};
+  bool device = false;
+  int dev_id = 0;
+  int num_cus = 0;
+  char* k_base = nullptr;
+  char* v_base = nullptr;
+  int64_t row_bytes = 0;    // head_dim * elem
+  int64_t tile_bytes = 0;   // 16 rows
+  int64_t block_bytes = 0;  // kv_heads tiles: one block of one layer, K or V
+  int64_t layer_bytes = 0;  // num_blocks blocks
+  int32_t max_blocks_per_seq = 0;
+
+  // block manager
+  std::vector<int32_t> free_list;  // stack of free ids
+  std::vector<int32_t> free_pos;   // index of an id in free_list, -1 when allocated
+  std::vector<int32_t> refcount;
+
+  // device metadata (library owned). One buffer so that an upload is one copy:
+  // [slots int64 max_seqs | ctx int32 max_seqs | cum int32 max_seqs+1 | pad | table]
+  char* d_meta = nullptr;
+  size_t off_ctx = 0, off_cum = 0, off_bt = 0, meta_bytes = 0;
+  int32_t* d_bt = nullptr;
+  int32_t* d_ctx = nullptr;
+  int32_t* d_cum = nullptr;
+  int64_t* d_slots = nullptr;
+  std::vector<char> h_stage;  // packed image of one upload
+  int32_t* d_sched = nullptr;
+  size_t sched_cap = 0;  // ints
+  int32_t* d_pairs = nullptr;
+  int32_t pairs_cap = 0;  // pairs
+
+  // last upload (host copies)
+  bool uploaded = false;
+  bool has_slots = false;
+  int up_batch = 0;
+  int up_stride = 0;
+  uint64_t up_gen = 0;
+  std::vector<int32_t> h_ctx;
+  std::vector<int32_t> h_cum;
+
+  // decode schedule built for (up_gen, partition, gp)
+  uint64_t sched_gen = 0;
+  int sched_part = -1;
+  int sched_gp = 0;
+  int sched_nwaves = 0;
+  bool sched_needs_reduce = false;
+  std::vector<int32_t> h_sched;
+
+  Staging ring[4];
+  int ring_next = 0;
+};
+
+namespace {
+
+void free_push(pkv_pool* p, int32_t id) {
+  p->free_pos[id] = (int32_t)p->free_list.size();
+  p->free_list.push_back(id);
+}
+
+void free_remove(pkv_pool* p, int32_t id) {
+  const int32_t i = p->free_pos[id];
+  const int32_t last = p->free_list.back();
+  p->free_list[i] = last;
+  p->free_pos[last] = i;
+  p->free_list.pop_back();
+  p->free_pos[id] = -1;
+}
+
+int32_t free_pop(pkv_pool* p) {
+  const int32_t id = p->free_list.back();
+  p->free_list.pop_back();
+  p->free_pos[id] = -1;
+  return id;
+}
+
+// Copy `bytes` from `src` into the next pinned staging buffer and enqueue the
+// host-to-device copy on `stream`. The buffer is reused only after the copy
+// that last read it has finished.
+int stage_copy(pkv_pool* p, void* dst, const void* src, size_t bytes, hipStream_t stream,
+               Staging** used) {
+  Staging& st = p->ring[p->ring_next];
+  p->ring_next = (p->ring_next + 1) % 4;
+  hipError_t e;
+  if (st.pending) {
+    if ((e = hipEventSynchronize(st.ev)) != hipSuccess) return hip_fail(e, "staging wait");
+    st.pending = false;
+  }
+  if (st.bytes < bytes) {
+    if (st.host) hipHostFree(st.host);
+    st.host = nullptr;
+    st.bytes = 0;
+    size_t want = std::max(bytes, (size_t)1 << 16);
+    if ((e = hipHostMalloc((void**)&st.host, want, hipHostMallocDefault)) != hipSuccess)
+      return hip_fail(e, "pinned staging allocation");
+    st.bytes = want;
+  }
+  if (!st.ev && (e = hipEventCreateWithFlags(&st.ev, hipEventDisableTiming)) != hipSuccess)
+    return hip_fail(e, "event create");
+  std::memcpy(st.host, src, bytes);
+  if ((e = hipMemcpyAsync(dst, st.host, bytes, hipMemcpyHostToDevice, stream)) != hipSuccess)
+    return hip_fail(e, "host-to-device copy");
+  if (used) *used = &st;
+  if ((e = hipEventRecord(st.ev, stream)) != hipSuccess) return hip_fail(e, "event record");
+  st.pending = true;
+  return PKV_OK;
+}
+
+int need_device(const pkv_pool* p) {
+  if (!p) return fail(PKV_EINVAL, "pool is NULL");
+  if (!p->device) return fail(PKV_EINVAL, "host-only pool (created without device memory)");
+  return PKV_OK;
+}
+
+int64_t nblk(int32_t tokens) { return (tokens + pkv::kBlock - 1) / pkv::kBlock; }
+
+// Build the decode schedule for the current upload.
+//   part > 0: one wave per (kv head, sequence, part/16-block partition).
+//   part == 0: `target` waves, each an equal share of all tiles.
+// Layout of h_sched: wave_start[nwaves + 1], seg_w0[nseg], seg_w1[nseg].
+void build_schedule(pkv_pool* p, int part, int target) {
+  const int B = p->up_batch;
+  const int H = p->shape.kv_heads;
+  const int64_t tseq = p->h_cum[B];
+  const int64_t T = tseq * H;
+  std::vector<int32_t> ws;
+  if (part > 0) {
+    const int64_t pb = part / pkv::kBlock;
+    for (int g = 0; g < H; ++g)
+      for (int s = 0; s < B; ++s) {
+        const int64_t n = nblk(p->h_ctx[s]);
+        for (int64_t j = 0; j < n; j += pb) ws.push_back((int32_t)(g * tseq + p->h_cum[s] + j));
+      }
+  } else {
+    const int64_t W = std::max<int64_t>(1, std::min<int64_t>(target, T));
+    ws.resize(W);
+    for (int64_t w = 0; w < W; ++w) ws[w] = (int32_t)(w * T / W);
+  }
+  const int W = (int)ws.size();
+  ws.push_back((int32_t)T);
+  const int nseg = B * H;
+  std::vector<int32_t> w0(nseg), w1(nseg);
+  bool multi = false;
+  int w = 0;
+  for (int g = 0; g < H; ++g)
+    for (int s = 0; s < B; ++s) {
+      const int seg = g * B + s;
+      const int64_t first = g * tseq + p->h_cum[s];
+      const int64_t last = first + nblk(p->h_ctx[s]) - 1;
+      while (ws[w + 1] <= first) ++w;
+      w0[seg] = w;
+      int v = w;
+      while (ws[v + 1] <= last) ++v;
+      w1[seg] = v;
+      multi |= v != w;
+    }
+  p->h_sched.clear();
+  p->h_sched.insert(p->h_sched.end(), ws.begin(), ws.end());
+  p->h_sched.insert(p->h_sched.end(), w0.begin(), w0.end());
+  p->h_sched.insert(p->h_sched.end(), w1.begin(), w1.end());
+  p->sched_nwaves = W;
+  p->sched_needs_reduce = multi;
+}
+
+int waves_target(const pkv_pool* p, int gp) {
+  int per_cu = pkv::decode_blocks_per_cu(p->shape.dtype, p->shape.head_dim, gp);
+  if (const char* env = std::getenv("PKV_WAVES_PER_CU")) {
+    const int v = std::atoi(env);
+    if (v > 0) per_cu = v;
+  }
+  per_cu = std::max(1, std::min(per_cu, 32));
+  return std::max(1, p->num_cus) * per_cu;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_err.c_str(); }
+
+size_t pkv_pool_bytes(const pkv_shape* sh) {
+  if (check_shape(sh) != PKV_OK) return 0;
+  return (size_t)sh->layers * sh->num_blocks * sh->block_size * 2 * sh->kv_heads * sh->head_dim *
+         elem_bytes(sh->dtype);
+}
+
+int pkv_kv_pool_alloc(const pkv_shape* sh, void* dev_base, size_t dev_bytes, pkv_pool** out) {
+  int rc = check_shape(sh);
+  if (rc != PKV_OK) return rc;
+  if (!out) return fail(PKV_EINVAL, "out is NULL");
+  const int64_t storable = (int64_t)sh->num_blocks * sh->block_size;
+  if (sh->max_seq_len > storable)
+    return fail(PKV_ECAPACITY,
+                "max seq len (%d) is larger than the maximum number of tokens that can be stored "
+                "in KV cache (%lld)",
+                sh->max_seq_len, (long long)storable);
+  const size_t need = pkv_pool_bytes(sh);
+  if (dev_base && dev_bytes < need)
+    return fail(PKV_EINVAL, "device buffer holds %zu bytes, the pool needs %zu", dev_bytes, need);
+  if (dev_base && (reinterpret_cast<uintptr_t>(dev_base) & 15))
+    return fail(PKV_EINVAL, "device buffer must be 16-byte aligned");
+
+  pkv_pool* p = new pkv_pool();
+  p->shape = *sh;
+  p->row_bytes = (int64_t)sh->head_dim * elem_bytes(sh->dtype);
+  p->tile_bytes = p->row_bytes * sh->block_size;
+  p->block_bytes = p->tile_bytes * sh->kv_heads;
+  p->layer_bytes = p->block_bytes * sh->num_blocks;
+  p->max_blocks_per_seq = (int32_t)nblk(sh->max_seq_len);
+  p->refcount.assign(sh->num_blocks, 0);
+  p->free_pos.assign(sh->num_blocks, -1);
+  p->free_list.reserve(sh->num_blocks);
+  for (int32_t id = sh->num_blocks - 1; id >= 0; --id) free_push(p, id);  // pops 0, 1, 2, ...
+
+  if (dev_base) {
+    p->device = true;
+    p->k_base = static_cast<char*>(dev_base);
+    p->v_base = p->k_base + (size_t)sh->layers * p->layer_bytes;
+    hipError_t e;
+    hipDeviceProp_t prop;
+    if ((e = hipGetDevice(&p->dev_id)) != hipSuccess ||
+        (e = hipGetDeviceProperties(&prop, p->dev_id)) != hipSuccess) {
+      delete p;
+      return hip_fail(e, "device query");
+    }
+    p->num_cus = prop.multiProcessorCount;
+    const size_t max_tiles =
+        (size_t)sh->max_seqs * p->max_blocks_per_seq * sh->kv_heads;
+    p->sched_cap = max_tiles + 1 + 2 * (size_t)sh->max_seqs * sh->kv_heads;
+    p->pairs_cap = sh->max_seqs;
+    const size_t bt_bytes = (size_t)sh->max_seqs * p->max_blocks_per_seq * 4;
+    p->off_ctx = (size_t)sh->max_seqs * 8;
+    p->off_cum = p->off_ctx + (size_t)sh->max_seqs * 4;
+    p->off_bt = (p->off_cum + ((size_t)sh->max_seqs + 1) * 4 + 15) & ~(size_t)15;
+    p->meta_bytes = p->off_bt + bt_bytes;
+    if ((e = hipMalloc((void**)&p->d_meta, p->meta_bytes)) != hipSuccess ||
+        (e = hipMalloc((void**)&p->d_sched, p->sched_cap * 4)) != hipSuccess ||
+        (e = hipMalloc((void**)&p->d_pairs, (size_t)p->pairs_cap * 8)) != hipSuccess) {
+      pkv_kv_pool_free(p);
+      return hip_fail(e, "device metadata allocation");
+    }
+    p->d_slots = reinterpret_cast<int64_t*>(p->d_meta);
+    p->d_ctx = reinterpret_cast<int32_t*>(p->d_meta + p->off_ctx);
+    p->d_cum = reinterpret_cast<int32_t*>(p->d_meta + p->off_cum);
+    p->d_bt = reinterpret_cast<int32_t*>(p->d_meta + p->off_bt);
+  }
+  *out = p;
+  return PKV_OK;
+}
+
+int pkv_kv_pool_free(pkv_pool* p) {
+  if (!p) return PKV_OK;
+  if (p->device) hipDeviceSynchronize();
+  for (Staging& st : p->ring) {
+    if (st.ev) hipEventDestroy(st.ev);
+    if (st.host) hipHostFree(st.host);
+  }
+  hipFree(p->d_meta);
+  hipFree(p->d_sched);
+  hipFree(p->d_pairs);
+  delete p;
+  return PKV_OK;
+}
+
+int pkv_block_alloc(pkv_pool* p, int n, int32_t* ids_out) {
+  if (!p || n < 0 || (n > 0 && !ids_out)) return fail(PKV_EINVAL, "bad arguments");
+  if ((size_t)n > p->free_list.size())
+    return fail(PKV_EOUT_OF_BLOCKS, "asked for %d blocks, %zu free", n, p->free_list.size());
+  for (int i = 0; i < n; ++i) {
+    const int32_t id = free_pop(p);
+    p->refcount[id] = 1;
+    ids_out[i] = id;
+  }
+  return PKV_OK;
+}
+
+int pkv_block_claim(pkv_pool* p, const int32_t* ids, int n) {
+  if (!p || n < 0 || (n > 0 && !ids)) return fail(PKV_EINVAL, "bad arguments");
+  for (int i = 0; i < n; ++i) {
+    if (ids[i] < 0 || ids[i] >= p->shape.num_blocks)
+      return fail(PKV_EINVAL, "block id %d out of range", ids[i]);
+    if (p->refcount[ids[i]] != 0) return fail(PKV_EINVAL, "block %d is not free", ids[i]);
+  }
+  std::vector<int32_t> sorted(ids, ids + n);
+  std::sort(sorted.begin(), sorted.end());
+  auto dup = std::adjacent_find(sorted.begin(), sorted.end());
+  if (dup != sorted.end()) return fail(PKV_EINVAL, "block %d listed twice", *dup);
+  for (int i = 0; i < n; ++i) {
+    free_remove(p, ids[i]);
+    p->refcount[ids[i]] = 1;
+  }
+  return PKV_OK;
+}
+
+int pkv_block_ref(pkv_pool* p, const int32_t* ids, int n) {
+  if (!p || n < 0 || (n > 0 && !ids)) return fail(PKV_EINVAL, "bad arguments");
+  for (int i = 0; i < n; ++i) {
+    if (ids[i] < 0 || ids[i] >= p->shape.num_blocks)
+      return fail(PKV_EINVAL, "block id %d out of range", ids[i]);
+    if (p->refcount[ids[i]] <= 0) return fail(PKV_EINVAL, "block %d is not allocated", ids[i]);
+  }
+  for (int i = 0; i < n; ++i) ++p->refcount[ids[i]];
+  return PKV_OK;
+}
+
+int pkv_block_free(pkv_pool* p, const int32_t* ids, int n) {
+  if (!p || n < 0 || (n > 0 && !ids)) return fail(PKV_EINVAL, "bad arguments");
+  // all-or-nothing: count how many references each listed block loses
+  std::vector<std::pair<int32_t, int>> drops;
+  drops.reserve(n);
+  for (int i = 0; i < n; ++i) {
+    if (ids[i] < 0 || ids[i] >= p->shape.num_blocks)
+      return fail(PKV_EINVAL, "block id %d out of range", ids[i]);
+    drops.push_back({ids[i], 1});
+  }
+  std::sort(drops.begin(), drops.end());
+  for (size_t i = 0; i < drops.size();) {
+    size_t k = i;
+    int cnt = 0;
+    while (k < drops.size() && drops[k].first == drops[i].first) cnt += drops[k++].second;
+    if (p->refcount[drops[i].first] < cnt)
+      return fail(PKV_EINVAL, "block %d has %d references, %d released", drops[i].first,
+                  p->refcount[drops[i].first], cnt);
+    i = k;
+  }
+  for (int i = 0; i < n; ++i)
+    if (--p->refcount[ids[i]] == 0) free_push(p, ids[i]);
+  return PKV_OK;
+}
+
+int pkv_block_refcount(const pkv_pool* p, int32_t id) {
+  if (!p || id < 0 || id >= p->shape.num_blocks) return fail(PKV_EINVAL, "bad block id");
+  return p->refcount[id];
+}
+
+int pkv_prepare_append(pkv_pool* p, int32_t* bt, int batch, int max_blocks,
+                       const int32_t* ctx, int64_t* slot_out, int32_t* cow_out,
+                       int cow_capacity, int* n_cow) {
+  if (!p || !bt || !ctx || !slot_out || !n_cow || batch < 1 || max_blocks < 1)
+    return fail(PKV_EINVAL, "bad arguments");
+  if (batch > p->shape.max_seqs)
+    return fail(PKV_EINVAL, "batch %d exceeds max_seqs %d", batch, p->shape.max_seqs);
+  struct Undo {
+    int64_t entry;
+    int32_t old;
+  };
+  std::vector<Undo> undo;
+  std::vector<int32_t> taken, unref;
+  int ncow = 0;
+  auto rollback = [&]() {
+    for (auto it = undo.rbegin(); it != undo.rend(); ++it) bt[it->entry] = it->old;
+    for (int32_t id : taken) {
+      p->refcount[id] = 0;
+      free_push(p, id);
+    }
+    for (int32_t id : unref) ++p->refcount[id];
+  };
+  for (int s = 0; s < batch; ++s) {
+    const int32_t L = ctx[s];
+    if (L < 1 || L > p->shape.max_seq_len || nblk(L) > max_blocks) {
+      rollback();
+      return fail(PKV_EINVAL, "sequence %d: context length %d outside [1, %d]", s, L,
+                  std::min<int64_t>(p->shape.max_seq_len, (int64_t)max_blocks * pkv::kBlock));
+    }
+    const int32_t pos = L - 1;
+    const int64_t e = (int64_t)s * max_blocks + pos / pkv::kBlock;
+    int32_t b = bt[e];
+    if (b < 0) {
+      if (p->free_list.empty()) {
+        rollback();
+        return fail(PKV_EOUT_OF_BLOCKS, "no free block for sequence %d", s);
+      }
+      const int32_t nb = free_pop(p);
+      p->refcount[nb] = 1;
+      taken.push_back(nb);
+      undo.push_back({e, b});
+      bt[e] = nb;
+      b = nb;
+    } else {
+      if (b >= p->shape.num_blocks || p->refcount[b] < 1) {
+        rollback();
+        return fail(PKV_EINVAL, "sequence %d: table entry %d is not an allocated block", s, b);
+      }
+      if (p->refcount[b] > 1) {
+        if (!cow_out || ncow >= cow_capacity) {
+          rollback();
+          return fail(PKV_EINVAL, "copy-on-write pair buffer too small (%d)", cow_capacity);
+        }
+        if (p->free_list.empty()) {
+          rollback();
+          return fail(PKV_EOUT_OF_BLOCKS, "no free block for copy-on-write of sequence %d", s);
+        }
+        const int32_t nb = free_pop(p);
+        p->refcount[nb] = 1;
+        taken.push_back(nb);
+        --p->refcount[b];
+        unref.push_back(b);
+        undo.push_back({e, b});
+        cow_out[2 * ncow] = b;
+        cow_out[2 * ncow + 1] = nb;
+        ++ncow;
+        bt[e] = nb;
+        b = nb;
+      }
+    }
+    slot_out[s] = (int64_t)b * pkv::kBlock + pos % pkv::kBlock;
+  }
+  *n_cow = ncow;
+  return PKV_OK;
+}
+
+int pkv_block_table_upload(pkv_pool* p, const int32_t* bt, int batch, int max_blocks,
+                           const int32_t* ctx, const int64_t* slots, uintptr_t stream_u) {
+  int rc = need_device(p);
+  if (rc != PKV_OK) return rc;
+  if (!bt || !ctx || batch < 1 || max_blocks < 1) return fail(PKV_EINVAL, "bad arguments");
+  if (batch > p->shape.max_seqs)
+    return fail(PKV_EINVAL, "batch %d exceeds max_seqs %d", batch, p->shape.max_seqs);
+  if (max_blocks > p->max_blocks_per_seq)
+    return fail(PKV_EINVAL, "table width %d exceeds %d blocks (max_seq_len %d)", max_blocks,
+                p->max_blocks_per_seq, p->shape.max_seq_len);
+  std::vector<int32_t> cum(batch + 1);
+  cum[0] = 0;
+  for (int s = 0; s < batch; ++s) {
+    const int32_t L = ctx[s];
+    if (L < 1 || L > p->shape.max_seq_len || nblk(L) > max_blocks)
+      return fail(PKV_EINVAL, "sequence %d: context length %d outside [1, %d]", s, L,
+                  std::min<int64_t>(p->shape.max_seq_len, (int64_t)max_blocks * pkv::kBlock));
+    const int64_t n = nblk(L);
+    for (int64_t j = 0; j < n; ++j) {
+      const int32_t b = bt[(int64_t)s * max_blocks + j];
+      if (b < 0 || b >= p->shape.num_blocks)
+        return fail(PKV_EINVAL, "sequence %d: block table entry %lld = %d out of range", s,
+                    (long long)j, b);
+    }
+    if ((int64_t)cum[s] + n > INT32_MAX / p->shape.kv_heads)
+      return fail(PKV_EUNSUPPORTED, "too many tiles in one batch");
+    cum[s + 1] = cum[s] + (int32_t)n;
+  }
+  if (slots) {
+    const int64_t lim = (int64_t)p->shape.num_blocks * pkv::kBlock;
+    std::vector<int64_t> seen;
+    seen.reserve(batch);
+    for (int s = 0; s < batch; ++s) {
+      if (slots[s] >= lim) return fail(PKV_EINVAL, "slot %lld out of range", (long long)slots[s]);
+      if (slots[s] >= 0) seen.push_back(slots[s]);
+    }
+    std::sort(seen.begin(), seen.end());
+    for (size_t i = 1; i < seen.size(); ++i)
+      if (seen[i] == seen[i - 1])
+        return fail(PKV_EINVAL, "slot %lld appears twice (the appends would race)",
+                    (long long)seen[i]);
+  }
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_u);
+  // pack slots, lengths, prefix sums and the table into one image: one copy
+  const size_t bytes = p->off_bt + (size_t)batch * max_blocks * 4;
+  p->h_stage.assign(bytes, 0);
+  char* img = p->h_stage.data();
+  if (slots) std::memcpy(img, slots, (size_t)batch * 8);
+  std::memcpy(img + p->off_ctx, ctx, (size_t)batch * 4);
+  std::memcpy(img + p->off_cum, cum.data(), (size_t)(batch + 1) * 4);
+  std::memcpy(img + p->off_bt, bt, (size_t)batch * max_blocks * 4);
+  if ((rc = stage_copy(p, p->d_meta, img, bytes, stream, nullptr))) return rc;
+  p->uploaded = true;
+  p->has_slots = slots != nullptr;
+  p->up_batch = batch;
+  p->up_stride = max_blocks;
+  p->h_ctx.assign(ctx, ctx + batch);
+  p->h_cum = std::move(cum);
+  ++p->up_gen;
+  return PKV_OK;
+}
+
+int pkv_copy_blocks(pkv_pool* p, const int32_t* pairs, int n, uintptr_t stream_u) {
+  int rc = need_device(p);
+  if (rc != PKV_OK) return rc;
+  if (n == 0) return PKV_OK;
+  if (n < 0 || !pairs) return fail(PKV_EINVAL, "bad arguments");
+  if (n > p->pairs_cap) return fail(PKV_EINVAL, "%d pairs exceed capacity %d", n, p->pairs_cap);
+  std::vector<int32_t> dsts;
+  for (int i = 0; i < n; ++i) {
+    for (int k = 0; k < 2; ++k)
+      if (pairs[2 * i + k] < 0 || pairs[2 * i + k] >= p->shape.num_blocks)
+        return fail(PKV_EINVAL, "pair %d: block id %d out of range", i, pairs[2 * i + k]);
+    if (pairs[2 * i] == pairs[2 * i + 1]) return fail(PKV_EINVAL, "pair %d copies onto itself", i);
+    dsts.push_back(pairs[2 * i + 1]);
+  }
+  std::sort(dsts.begin(), dsts.end());
+  if (std::adjacent_find(dsts.begin(), dsts.end()) != dsts.end())
+    return fail(PKV_EINVAL, "two pairs copy into the same block");
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_u);
+  if ((rc = stage_copy(p, p->d_pairs, pairs, (size_t)n * 8, stream, nullptr))) return rc;
+  hipError_t e = pkv::launch_copy_blocks(p->d_pairs, n, p->k_base, p->v_base, p->shape.layers,
+                                         p->layer_bytes, p->block_bytes, stream);
+  if (e != hipSuccess) return hip_fail(e, "copy_blocks launch");
+  return PKV_OK;
+}
+
+int pkv_kv_append(pkv_pool* p, int layer, const void* k_new, const void* v_new,
+                  const int64_t* dev_slots, int batch, uintptr_t stream_u) {
+  int rc = need_device(p);
+  if (rc != PKV_OK) return rc;
+  if (layer < 0 || layer >= p->shape.layers) return fail(PKV_EINVAL, "layer %d out of range", layer);
+  if (!k_new || !v_new || batch < 1) return fail(PKV_EINVAL, "bad arguments");
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
+    return fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");
+  const int64_t* slots = dev_slots;
+  if (!slots) {
+    if (!p->uploaded || !p->has_slots)
+      return fail(PKV_EINVAL, "no slots given and none uploaded");
+    if (batch != p->up_batch)
+      return fail(PKV_EINVAL, "batch %d differs from the uploaded batch %d", batch, p->up_batch);
+    slots = p->d_slots;
+  }
+  char* kl = p->k_base + (size_t)layer * p->layer_bytes;
+  char* vl = p->v_base + (size_t)layer * p->layer_bytes;
+  hipError_t e = pkv::launch_append(k_new, v_new, slots, batch, kl, vl, p->shape.kv_heads,
+                                    (int)p->row_bytes, reinterpret_cast<hipStream_t>(stream_u));
+  if (e != hipSuccess) return hip_fail(e, "kv_append launch");
+  return PKV_OK;
+}
+
+size_t pkv_decode_workspace_bytes(const pkv_pool* p, int batch, int q_heads,
+                                  int partition_tokens) {
+  if (!p || batch < 1 || q_heads < 1 || q_heads % p->shape.kv_heads) return 0;
+  const int group = q_heads / p->shape.kv_heads;
+  if (group > pkv::kMaxGroup) return 0;
+  const int gp = pkv::padded_group(group);
+  const int64_t nseg = (int64_t)batch * p->shape.kv_heads;
+  int64_t waves;
+  if (partition_tokens > 0) {
+    const int64_t pb = std::max(1, partition_tokens / pkv::kBlock);
+    waves = nseg * ((p->max_blocks_per_seq + pb - 1) / pb);
+  } else {
+    waves = std::max<int64_t>(1, std::max(p->num_cus, 1) * 32);
+  }
+  return (size_t)(nseg + waves) * gp * (p->shape.head_dim + 2) * sizeof(float);
+}
+
+int pkv_paged_attn_decode(pkv_pool* p, int layer, const void* q, int q_heads, float scale,
+                          float* out, int partition_tokens, void* ws, size_t ws_bytes,
+                          uintptr_t stream_u) {
+  int rc = need_device(p);
+  if (rc != PKV_OK) return rc;
+  if (!p->uploaded) return fail(PKV_EINVAL, "no block table uploaded");
+  if (layer < 0 || layer >= p->shape.layers) return fail(PKV_EINVAL, "layer %d out of range", layer);
+  if (!q || !out) return fail(PKV_EINVAL, "q and out must be device pointers");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return fail(PKV_EINVAL, "q and out must be 16-byte aligned");
+  if (q_heads < 1 || q_heads % p->shape.kv_heads)
+    return fail(PKV_EINVAL, "q_heads %d is not a multiple of kv_heads %d", q_heads,
+                p->shape.kv_heads);
+  const int group = q_heads / p->shape.kv_heads;
+  if (group > pkv::kMaxGroup)
+    return fail(PKV_EUNSUPPORTED, "GQA group %d exceeds %d", group, pkv::kMaxGroup);
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "scale must be finite");
+  if (partition_tokens < 0 || partition_tokens % pkv::kBlock)
+    return fail(PKV_EINVAL, "partition_tokens %d must be 0 or a positive multiple of 16",
+                partition_tokens);
+  const int gp = pkv::padded_group(group);
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_u);
+
+  if (p->sched_gen != p->up_gen || p->sched_part != partition_tokens || p->sched_gp != gp) {
+    build_schedule(p, partition_tokens, waves_target(p, gp));
+    if (p->h_sched.size() > p->sched_cap)
+      return fail(PKV_EUNSUPPORTED, "decode schedule of %zu entries exceeds %zu",
+                  p->h_sched.size(), p->sched_cap);
+    if ((rc = stage_copy(p, p->d_sched, p->h_sched.data(), p->h_sched.size() * 4, stream,
+                         nullptr)))
+      return rc;
+    p->sched_gen = p->up_gen;
+    p->sched_part = partition_tokens;
+    p->sched_gp = gp;
+  }
+  const int B = p->up_batch;
+  const int W = p->sched_nwaves;
+  const int64_t nseg = (int64_t)B * p->shape.kv_heads;
+  const int64_t nparts = nseg + W;
+  const size_t need = (size_t)nparts * gp * (p->shape.head_dim + 2) * sizeof(float);
+  if (ws_bytes < need || (!ws && need > 0))
+    return fail(PKV_EINVAL, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
+                need);
+  if (reinterpret_cast<uintptr_t>(ws) & 15) return fail(PKV_EINVAL, "workspace must be 16-byte aligned");
+
+  pkv::DecodeParams dp{};
+  dp.k = p->k_base + (size_t)layer * p->layer_bytes;
+  dp.v = p->v_base + (size_t)layer * p->layer_bytes;
+  dp.bt = p->d_bt;
+  dp.ctx = p->d_ctx;
+  dp.cum = p->d_cum;
+  dp.wave_start = p->d_sched;
+  dp.q = q;
+  dp.out = out;
+  dp.part_o = static_cast<float*>(ws);
+  dp.part_ml = static_cast<float*>(ws) + (size_t)nparts * gp * p->shape.head_dim;
+  dp.scale_log2 = scale * 1.4426950408889634f;
+  dp.bt_stride = p->up_stride;
+  dp.batch = B;
+  dp.kv_heads = p->shape.kv_heads;
+  dp.q_heads = q_heads;
+  dp.group = group;
+  dp.tseq = p->h_cum[B];
+  dp.nwaves = W;
+  dp.waves_per_xcd = (W + pkv::kNumXcd - 1) / pkv::kNumXcd;
+  hipError_t e = pkv::launch_decode(p->shape.dtype, p->shape.head_dim, gp, dp, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (p->sched_needs_reduce) {
+    pkv::ReduceParams rp{};
+    rp.part_o = dp.part_o;
+    rp.part_ml = dp.part_ml;
+    rp.seg_w0 = p->d_sched + W + 1;
+    rp.seg_w1 = p->d_sched + W + 1 + nseg;
+    rp.out = out;
+    rp.batch = B;
+    rp.kv_heads = p->shape.kv_heads;
+    rp.q_heads = q_heads;
+    rp.group = group;
+    e = pkv::launch_reduce(p->shape.head_dim, gp, rp, stream);
+    if (e != hipSuccess) return hip_fail(e, "reduce launch");
+  }
+  return PKV_OK;
+}
+
+int pkv_pool_stats(const pkv_pool* p, int64_t stats[4]) {
+  if (!p || !stats) return fail(PKV_EINVAL, "bad arguments");
+  int64_t shared = 0;
+  for (int32_t r : p->refcount) shared += r > 1;
+  int64_t waste = 0;
+  for (int32_t L : p->h_ctx) waste += nblk(L) * pkv::kBlock - L;
+  stats[0] = (int64_t)p->free_list.size();
+  stats[1] = p->shape.num_blocks - stats[0];
+  stats[2] = shared;
+  stats[3] = waste;
+  return PKV_OK;
+}
+
+}  // extern "C"

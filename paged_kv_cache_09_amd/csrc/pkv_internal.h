@@ -1,0 +1,64 @@
+// Internal interface between the host library (pkv_host.cpp) and the HIP
+// kernels (pkv_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kBlock = 16;       // tokens per block
+constexpr int kMaxGroup = 8;     // largest GQA group (q heads per kv head)
+constexpr int kNumXcd = 8;       // MI355X: workgroups are dealt round-robin to 8 XCDs
+
+struct DecodeParams {
+  const void* k;               // layer base of K: [num_blocks][kv_heads][16][head_dim]
+  const void* v;               // layer base of V, same shape
+  const int32_t* bt;           // block table [batch][bt_stride]
+  const int32_t* ctx;          // context lengths [batch]
+  const int32_t* cum;          // blocks before each sequence [batch + 1]
+  const int32_t* wave_start;   // first tile of each wave [nwaves + 1]
+  const void* q;               // [batch][q_heads][head_dim], cache dtype
+  float* out;                  // [batch][q_heads][head_dim]
+  float* part_o;               // [(nseg + nwaves) * gp][head_dim] unnormalised partial outputs
+  float* part_ml;              // [(nseg + nwaves) * gp][2] partial (max, sum), log2 domain
+  float scale_log2;            // softmax scale * log2(e)
+  int32_t bt_stride;
+  int32_t batch;
+  int32_t kv_heads;
+  int32_t q_heads;
+  int32_t group;               // q_heads / kv_heads
+  int32_t tseq;                // tiles per kv head = cum[batch]
+  int32_t nwaves;
+  int32_t waves_per_xcd;       // ceil(nwaves / 8)
+};
+
+struct ReduceParams {
+  const float* part_o;
+  const float* part_ml;
+  const int32_t* seg_w0;       // first wave touching each (kv head, sequence) segment
+  const int32_t* seg_w1;       // last wave touching it
+  float* out;
+  int32_t batch;
+  int32_t kv_heads;
+  int32_t q_heads;
+  int32_t group;
+};
+
+// Padded group size used by the kernels: 1, 2, 4 or 8.
+inline int padded_group(int g) { return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : 8; }
+
+hipError_t launch_decode(int dtype, int head_dim, int gp, const DecodeParams& p,
+                         hipStream_t stream);
+hipError_t launch_reduce(int head_dim, int gp, const ReduceParams& p, hipStream_t stream);
+// Workgroups of the decode kernel one CU can hold at once (occupancy), 0 on error.
+int decode_blocks_per_cu(int dtype, int head_dim, int gp);
+
+hipError_t launch_append(const void* k_new, const void* v_new, const int64_t* slots, int batch,
+                         void* k_layer, void* v_layer, int kv_heads, int row_bytes,
+                         hipStream_t stream);
+hipError_t launch_copy_blocks(const int32_t* pairs, int n, void* k_base, void* v_base,
+                              int layers, int64_t layer_bytes, int64_t block_bytes,
+                              hipStream_t stream);
+
+}  // namespace pkv

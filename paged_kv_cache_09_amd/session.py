@@ -1,0 +1,113 @@
+"""A decode step driven through the C ABI for one workload (used by tests, smoke and bench).
+
+This is plumbing over :mod:`paged_kv_cache_09_amd.pkv`: it owns the pool
+handle, the host block table and the device workspace, and calls the ABI in
+the order of one decode step:
+
+  a1 ``prepare``      host slot assignment (allocation, copy-on-write)
+  a2 ``upload``       block table, lengths and slots to the device
+  a3 ``copy_blocks``  copy-on-write copies (all layers)
+  a4 ``append``       new K/V rows of one layer
+  a5-a9 ``decode``    paged attention of one layer (+ reduce when split)
+
+No arithmetic of the method happens here.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import pkv
+from .workloads import Workload
+
+
+class DecodeSession:
+    def __init__(self, w: Workload, *, max_seq_len: int | None = None, placement: str = "pre"):
+        cfg = w.cfg
+        self.w = w
+        self.cfg = cfg
+        msl = max_seq_len if max_seq_len is not None else w.max_blocks * 16
+        self.shape = pkv.make_shape(w.layers, cfg.num_blocks, cfg.kv_heads, cfg.head_dim,
+                                    cfg.dtype, msl, cfg.batch)
+        need = pkv.pool_bytes(self.shape)
+        if w.pool.numel() < need:
+            raise ValueError(f"pool tensor holds {w.pool.numel()} bytes, need {need}")
+        self.pool = pkv.kv_pool_alloc(self.shape, w.pool, w.pool.numel())
+        # restore the workload's placement in the block manager
+        pkv.block_claim(self.pool, w.allocated_ids(placement))
+        for b, rc in w.shared:
+            if rc > 1:
+                pkv.block_ref(self.pool, [b] * (rc - 1))
+        self.table = np.ascontiguousarray(w.table(placement))
+        self.ctx = np.ascontiguousarray(w.ctx, dtype=np.int32)
+        self.slots = None
+        self.pairs = np.zeros((0, 2), dtype=np.int32)
+        self._ws = None
+        self._ws_key = None
+
+    @property
+    def stream(self) -> int:
+        return torch.cuda.current_stream().cuda_stream
+
+    def prepare(self):
+        self.slots, self.pairs = pkv.prepare_append(self.pool, self.table, self.ctx)
+        return self.slots, self.pairs
+
+    def upload(self, with_slots: bool = True):
+        pkv.block_table_upload(self.pool, self.table, self.ctx,
+                               self.slots if with_slots else None, self.stream)
+
+    def copy_blocks(self):
+        if len(self.pairs):
+            pkv.copy_blocks(self.pool, self.pairs, self.stream)
+
+    def append(self, layer: int, k_new=None, v_new=None):
+        k_new = self.w.k_new if k_new is None else k_new
+        v_new = self.w.v_new if v_new is None else v_new
+        pkv.kv_append(self.pool, layer, k_new, v_new, None, self.cfg.batch, self.stream)
+
+    def workspace(self, partition_tokens: int) -> torch.Tensor:
+        key = partition_tokens
+        if self._ws_key != key:
+            nbytes = pkv.decode_workspace_bytes(self.pool, self.cfg.batch, self.cfg.q_heads,
+                                                partition_tokens)
+            self._ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.w.pool.device)
+            self._ws_key = key
+        return self._ws
+
+    def decode(self, layer: int, out: torch.Tensor, partition_tokens: int = 0, q=None,
+               scale: float | None = None):
+        from .workloads import attn_scale
+        q = self.w.q if q is None else q
+        ws = self.workspace(partition_tokens)
+        pkv.paged_attn_decode(self.pool, layer, q, self.cfg.q_heads,
+                              attn_scale(self.cfg) if scale is None else scale, out,
+                              partition_tokens, ws, ws.numel(), self.stream)
+
+    def new_out(self) -> torch.Tensor:
+        c = self.cfg
+        return torch.empty((c.batch, c.q_heads, c.head_dim), dtype=torch.float32,
+                           device=self.w.pool.device)
+
+    def step(self, out: torch.Tensor, layers=None, partition_tokens: int = 0):
+        """One full decode step: a1-a3 once, then append + decode per layer."""
+        self.prepare()
+        self.upload()
+        self.copy_blocks()
+        for layer in (range(self.w.layers) if layers is None else layers):
+            self.append(layer)
+            self.decode(layer, out, partition_tokens)
+
+    def stats(self) -> dict:
+        return pkv.pool_stats(self.pool)
+
+    def close(self):
+        if self.pool is not None:
+            pkv.kv_pool_free(self.pool)
+            self.pool = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

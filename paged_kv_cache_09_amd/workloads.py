@@ -198,7 +198,7 @@ def _fill_normal(t: torch.Tensor, sigma: float, gen: torch.Generator, chunk: int
 
 
 def make(cfg: Config, *, device="cpu", layers: int | None = None, form: str = "step",
-         fill: str = "nan", extra_blocks: int = 0) -> Workload:
+         fill: str = "nan", extra_blocks: int = 0, tensors: bool = True) -> Workload:
     """Build one workload.
 
     form   "step": the pool holds ctx-1 cached tokens per sequence and the step
@@ -207,6 +207,7 @@ def make(cfg: Config, *, device="cpu", layers: int | None = None, form: str = "s
     fill   "nan": rows holding no token are NaN; "random": every pool row is
            a random draw (benchmark).
     extra_blocks  table columns beyond the longest sequence (room to grow).
+    tensors  False: lengths and placement only (pool, q, k_new, v_new are None).
     """
     layers = cfg.layers if layers is None else layers
     r_len, r_perm, r_vals = _children(cfg.seed, 3)
@@ -234,6 +235,9 @@ def make(cfg: Config, *, device="cpu", layers: int | None = None, form: str = "s
         if _nblk(int(ctx[s])) > len(pre_tables[s]):
             new_blocks[s] = next(take)
     max_blocks = max(_nblk(int(c)) for c in ctx) + extra_blocks
+    if not tensors:
+        return Workload(cfg, layers, ctx, pre_tables, new_blocks, shared, max_blocks, None, None,
+                        None, None, form)
 
     seed_vals = int(r_vals.integers(0, 2**62))
     gen = torch.Generator(device=device)
