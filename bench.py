@@ -100,6 +100,10 @@ def cpu_baseline(w, budget_s: float = 12.0):
             "seq_tokens_per_s": round(float(ctx.sum()) / t, 1)}
 
 
+def log(msg: str):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,9 +130,11 @@ def main():
     cfg = W.CONFIGS[args.config]
     part = cfg.partition_tokens if args.partition is None else args.partition
     growth = args.warmup + args.steps + 1
+    log(f"building {cfg.name}: {cfg.layers} layers")
     w = W.make(cfg, device="cuda", layers=cfg.layers, form="step", fill="random",
                extra_blocks=(growth + 15) // 16 + 1)
     sess = DecodeSession(w)
+    log("pool ready; warm-up")
     out = sess.new_out()
     stream = torch.cuda.current_stream()
     layers = list(range(cfg.layers))
@@ -141,6 +147,7 @@ def main():
         one_step()
         sess.ctx += 1
     torch.cuda.synchronize()
+    log("timed steps")
 
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -155,6 +162,7 @@ def main():
     ev_ms = ev0.elapsed_time(ev1)
     elapsed = max(wall, ev_ms / 1e3)
 
+    log("decode-only launches")
     # decode kernel alone: back-to-back launches over all layers, same upload
     sess.ctx -= 1  # the uploaded table matches the last step's lengths
     ctx_now = sess.ctx.copy()
@@ -211,6 +219,7 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
+        log("cpu baseline")
         res["cpu_baseline"] = cpu_baseline(w)
     sess.close()
     print(json.dumps(res), flush=True)

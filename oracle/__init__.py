@@ -104,6 +104,7 @@ def append(k_pool, v_pool, block_table, ctx_lens, k_new, v_new, *, dtype, block_
     vn = _storage(v_new, dtype)
     B, Hkv, D = kn.shape
     assert k_pool.shape[1] == Hkv and k_pool.shape[2] == block_size and k_pool.shape[3] == D
+    _check_tables(bt, ctx, k_pool.shape[0], block_size)
     lib().orc_append(B, Hkv, D, block_size, dtype, _ptr(k_pool), _ptr(v_pool), _ptr(bt),
                      bt.shape[1], _ptr(ctx), _ptr(kn), _ptr(vn))
     return k_pool, v_pool
@@ -115,11 +116,25 @@ def gather(k_pool, v_pool, bt_row, n_tokens, g, *, dtype, block_size=16):
     v_pool = _storage(v_pool, dtype)
     row = np.ascontiguousarray(bt_row, dtype=np.int32)
     NB, Hkv, bs, D = k_pool.shape
+    _check_tables(row[None, :], np.array([n_tokens]), NB, block_size)
     ok = np.zeros((max(n_tokens, 1), D))
     ov = np.zeros((max(n_tokens, 1), D))
     lib().orc_gather(Hkv, D, block_size, dtype, _ptr(k_pool), _ptr(v_pool), _ptr(row),
                      n_tokens, g, _ptr(ok), _ptr(ov))
     return ok[:n_tokens], ov[:n_tokens]
+
+
+def _check_tables(bt, ctx, num_blocks, block_size):
+    """Every table entry a sequence reads must name a block of the pool."""
+    if bt.shape[0] != ctx.shape[0]:
+        raise ValueError("block table and context lengths disagree on the batch")
+    for s, L in enumerate(ctx):
+        n = (int(L) + block_size - 1) // block_size
+        if L < 0 or n > bt.shape[1]:
+            raise ValueError(f"sequence {s}: length {L} does not fit the table")
+        row = bt[s, :n]
+        if n and (row.min() < 0 or row.max() >= num_blocks):
+            raise ValueError(f"sequence {s}: table entry outside [0, {num_blocks})")
 
 
 def decode(k_pool, v_pool, block_table, ctx_lens, q, scale, *, dtype, block_size=16,
@@ -137,6 +152,7 @@ def decode(k_pool, v_pool, block_table, ctx_lens, q, scale, *, dtype, block_size
     B, Hq, D = qq.shape
     NB, Hkv, bs, D2 = k_pool.shape
     assert D2 == D and bs == block_size and Hq % Hkv == 0
+    _check_tables(bt, ctx, NB, block_size)
     out = np.zeros((B, Hq, D))
     L = lib()
     if partition_tokens > 0:

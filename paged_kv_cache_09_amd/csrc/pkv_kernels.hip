@@ -41,6 +41,15 @@ __device__ __forceinline__ u32x4 ld16(const char* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Bit casts from one 32-bit lane of a u32x4. The element is copied to a
+// scalar first: __builtin_bit_cast applied directly to a vector element
+// expression reads element 0 whatever the index.
+template <typename T>
+__device__ __forceinline__ T lane_as(u32x4 v, int i) {
+  const unsigned u = v[i];
+  return __builtin_bit_cast(T, u);
+}
+
 // Dot product of one 16-byte piece of q with the matching piece of a K row,
 // accumulated in fp32. bf16/fp16 products are exact in fp32; the dot2
 // instructions add two of them per step.
@@ -49,17 +58,16 @@ __device__ __forceinline__ float dot_piece(u32x4 q, u32x4 k, float acc) {
   if constexpr (DT == DT_BF16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[i]),
-                                            __builtin_bit_cast(bf16x2, k[i]), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(lane_as<bf16x2>(q, i), lane_as<bf16x2>(k, i), acc,
+                                            false);
   } else if constexpr (DT == DT_F16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, q[i]),
-                                   __builtin_bit_cast(f16x2, k[i]), acc, false);
+      acc = __builtin_amdgcn_fdot2(lane_as<f16x2>(q, i), lane_as<f16x2>(k, i), acc, false);
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      acc = __builtin_fmaf(__builtin_bit_cast(float, q[i]), __builtin_bit_cast(float, k[i]), acc);
+      acc = __builtin_fmaf(lane_as<float>(q, i), lane_as<float>(k, i), acc);
   }
   return acc;
 }
@@ -70,19 +78,20 @@ __device__ __forceinline__ void to_f32(u32x4 w, float* out) {
   if constexpr (DT == DT_BF16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      out[2 * i] = __builtin_bit_cast(float, w[i] << 16);
-      out[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+      const unsigned u = w[i];
+      out[2 * i] = __builtin_bit_cast(float, u << 16);
+      out[2 * i + 1] = __builtin_bit_cast(float, u & 0xffff0000u);
     }
   } else if constexpr (DT == DT_F16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f16x2 h = __builtin_bit_cast(f16x2, w[i]);
+      const f16x2 h = lane_as<f16x2>(w, i);
       out[2 * i] = (float)h[0];
       out[2 * i + 1] = (float)h[1];
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = __builtin_bit_cast(float, w[i]);
+    for (int i = 0; i < 4; ++i) out[i] = lane_as<float>(w, i);
   }
 }
 

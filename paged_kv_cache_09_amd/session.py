@@ -38,8 +38,8 @@ class DecodeSession:
         for b, rc in w.shared:
             if rc > 1:
                 pkv.block_ref(self.pool, [b] * (rc - 1))
-        self.table = np.ascontiguousarray(w.table(placement))
-        self.ctx = np.ascontiguousarray(w.ctx, dtype=np.int32)
+        self.table = np.array(w.table(placement), dtype=np.int32, copy=True)
+        self.ctx = np.array(w.ctx, dtype=np.int32, copy=True)  # grows per step; never alias w.ctx
         self.slots = None
         self.pairs = np.zeros((0, 2), dtype=np.int32)
         self._ws = None
