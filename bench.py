@@ -66,7 +66,15 @@ def cpu_baseline(w, budget_s: float = 12.0):
             return t.numpy().copy()
         return t.view(torch.int16).numpy().view(np.uint16).copy()
 
+    cache = {}
+
     def run(seqs):
+        key = tuple(seqs)
+        if key in cache:
+            kc, vc, bt, ctx, q = cache[key]
+            t0 = time.perf_counter()
+            oracle.decode(kc, vc, bt, ctx, q, 1.0 / math.sqrt(cfg.head_dim), dtype=cfg.dtype)
+            return time.perf_counter() - t0, ctx
         used = sorted({b for s in seqs for b in w.pre_tables[s]} |
                       {int(w.new_blocks[s]) for s in seqs if w.new_blocks[s] >= 0})
         remap = {b: i for i, b in enumerate(used)}
@@ -82,22 +90,28 @@ def cpu_baseline(w, budget_s: float = 12.0):
         ctx = np.ascontiguousarray(w.ctx[seqs], dtype=np.int32)
         sel = torch.tensor(seqs, dtype=torch.long, device=w.pool.device)
         q = storage(w.q.index_select(0, sel))
+        cache[key] = (kc, vc, bt, ctx, q)
         t0 = time.perf_counter()
         oracle.decode(kc, vc, bt, ctx, q, 1.0 / math.sqrt(cfg.head_dim), dtype=cfg.dtype)
         return time.perf_counter() - t0, ctx
 
     oracle.build(force=False)
-    probe = list(range(min(2, w.B)))
-    t, _ = run(probe)
-    n = max(1, min(w.B, int(len(probe) * budget_s / max(t, 1e-3))))
-    seqs = list(range(n))
+    # The oracle decodes one layer of the whole batch in well under a second on
+    # many cores, so the sample is that layer decoded repeatedly until about
+    # budget_s of CPU work has accumulated.
+    seqs = list(range(w.B))
     t, ctx = run(seqs)
+    reps, total = 1, t
+    while total < budget_s and reps < 10000:
+        dt, _ = run(seqs)
+        total += dt
+        reps += 1
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(kv_bytes(cfg, ctx) / t / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"one layer, first {n} of {w.B} sequences ({int(ctx.sum())} context tokens), "
-                      f"{t:.1f} s",
-            "seq_tokens_per_s": round(float(ctx.sum()) / t, 1)}
+    return {"value": round(kv_bytes(cfg, ctx) * reps / total / 1e9, 4), "unit": "GB/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"one layer of all {w.B} sequences ({int(ctx.sum())} context tokens) "
+                      f"decoded {reps} times, {total:.1f} s of oracle time",
+            "seq_tokens_per_s": round(float(ctx.sum()) * reps / total, 1)}
 
 
 def log(msg: str):
