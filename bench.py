@@ -41,13 +41,16 @@ def kv_bytes(cfg, ctx) -> int:
 
 
 def decode_algorithmic_bytes(cfg, ctx) -> int:
-    """Bytes one decode launch must move: KV rows, q, fp32 output, block-table entries, lengths."""
+    """Bytes one fused append + decode launch must move: every KV row once (the new
+    row comes from k_new/v_new), the new rows written to the pool, q, the fp32
+    output, the block-table entries and the lengths."""
     import numpy as np
     from paged_kv_cache_09_amd import workloads as W
     e = W.ELEM_BYTES[cfg.dtype]
     B = len(ctx)
     nblk = int(((np.asarray(ctx, dtype=np.int64) + 15) // 16).sum())
-    return (kv_bytes(cfg, ctx) + B * cfg.q_heads * cfg.head_dim * e +
+    new_rows = B * 2 * cfg.kv_heads * cfg.head_dim * e
+    return (kv_bytes(cfg, ctx) + new_rows + B * cfg.q_heads * cfg.head_dim * e +
             B * cfg.q_heads * cfg.head_dim * 4 + nblk * 4 * cfg.kv_heads + B * 4)
 
 
@@ -128,6 +131,11 @@ def main():
                     help="decode partition tokens (default: the workload's own; 0 = balanced)")
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes (3 times) and "
+                         "exit: reference for calibrating HBM byte counters")
+    ap.add_argument("--unfused", action="store_true",
+                    help="kv_append and paged_attn_decode as two launches per layer")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
@@ -137,6 +145,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_probe:
+        src = torch.empty(args.copy_probe, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe}), flush=True)
+        return
 
     from paged_kv_cache_09_amd import workloads as W
     from paged_kv_cache_09_amd.session import DecodeSession
@@ -154,7 +172,7 @@ def main():
     layers = list(range(cfg.layers))
 
     def one_step():
-        sess.step(out, layers=layers, partition_tokens=part)
+        sess.step(out, layers=layers, partition_tokens=part, fused=not args.unfused)
 
     total_kv = 0
     for _ in range(args.warmup):
@@ -177,18 +195,24 @@ def main():
     elapsed = max(wall, ev_ms / 1e3)
 
     log("decode-only launches")
-    # decode kernel alone: back-to-back launches over all layers, same upload
+    # the per-layer kernel alone: back-to-back launches over all layers, same upload
     sess.ctx -= 1  # the uploaded table matches the last step's lengths
     ctx_now = sess.ctx.copy()
     reps = args.decode_reps
+    def layer_call(layer):
+        if args.unfused:
+            sess.decode(layer, out, part)
+        else:
+            sess.append_decode(layer, out, part)
+
     for layer in layers[:4]:
-        sess.decode(layer, out, part)
+        layer_call(layer)
     torch.cuda.synchronize()
     d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     d0.record(stream)
     for _ in range(reps):
-        for layer in layers:
-            sess.decode(layer, out, part)
+        for layer in layers:  # re-appending the same rows is idempotent
+            layer_call(layer)
     d1.record(stream)
     torch.cuda.synchronize()
     per_launch_s = d0.elapsed_time(d1) / 1e3 / (reps * len(layers))
@@ -227,7 +251,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "kernel": "decode_kernel (+ split merge) per layer launch",
+            "kernel": "decode_kernel (fused append + paged attention + split merge), one launch per layer",
             "avg_launch_us": round(per_launch_s * 1e6, 3),
             "algorithmic_bytes_per_launch": alg,
         },

@@ -152,8 +152,9 @@ int pkv_prepare_append(pkv_pool* pool, int32_t* host_bt, int batch, int max_bloc
  * none) to the library's device copies, asynchronously on `stream` from
  * pinned staging. Checked on the host first: 1 <= batch <= max_seqs,
  * max_blocks * 16 <= the pool's table width, 1 <= ctx <= max_seq_len, every
- * entry j < ceil(ctx/16) in [0, num_blocks), non-negative slots in range and
- * pairwise distinct (two equal slots would race in kv_append).
+ * entry j < ceil(ctx/16) in [0, num_blocks); a non-negative slot must be the
+ * table position of the sequence's new token (row ctx-1), as
+ * pkv_prepare_append produces; negative slots skip the append.
  * Later kv_append / decode calls use this upload.
  */
 int pkv_block_table_upload(pkv_pool* pool, const int32_t* host_bt, int batch, int max_blocks,
@@ -194,11 +195,25 @@ int pkv_kv_append(pkv_pool* pool, int layer, const void* k_new, const void* v_ne
  * merged by the same reduce (a partition >= the longest context is the
  * single-pass form, no reduce).
  * workspace / ws_bytes: device scratch of at least
- * pkv_decode_workspace_bytes(...) bytes (may be NULL when that is 0).
+ * pkv_decode_workspace_bytes(...) bytes, 16-byte aligned, for the split
+ * partials (unused, may be NULL, when no sequence is split). Calls sharing
+ * one workspace must not overlap.
  */
 int pkv_paged_attn_decode(pkv_pool* pool, int layer, const void* q, int q_heads, float scale,
                           float* out, int partition_tokens, void* workspace, size_t ws_bytes,
                           uintptr_t stream);
+
+/*
+ * kv_append followed by paged_attn_decode of the same layer, in one launch:
+ * the wavefront that reads a sequence's last block takes the new token's row
+ * from k_new / v_new ([batch][kv_heads][head_dim], cache dtype), writes it to
+ * the pool at the uploaded slot and attends over it. The last upload must
+ * carry slots. Same results, bit for bit in the pool, as the two calls.
+ */
+int pkv_append_paged_attn_decode(pkv_pool* pool, int layer, const void* k_new, const void* v_new,
+                                 const void* q, int q_heads, float scale, float* out,
+                                 int partition_tokens, void* workspace, size_t ws_bytes,
+                                 uintptr_t stream);
 
 /* Workspace bytes a decode of `batch` sequences with these settings may need (upper bound). */
 size_t pkv_decode_workspace_bytes(const pkv_pool* pool, int batch, int q_heads,

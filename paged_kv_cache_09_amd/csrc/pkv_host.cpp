@@ -102,14 +102,15 @@ struct pkv_pool {
   uint64_t up_gen = 0;
   std::vector<int32_t> h_ctx;
   std::vector<int32_t> h_cum;
+  std::vector<int32_t> h_bt;  // uploaded table (for per-wave descriptors)
 
   // decode schedule built for (up_gen, partition, gp)
   uint64_t sched_gen = 0;
   int sched_part = -1;
   int sched_gp = 0;
   int sched_nwaves = 0;
-  bool sched_needs_reduce = false;
-  std::vector<int32_t> h_sched;
+  bool sched_needs_merge = false;   // some segment spans several waves
+  std::vector<int32_t> h_sched;     // wdesc[8 * nwaves] | seg_w0[nseg] | seg_w1[nseg]
 
   Staging ring[4];
   int ring_next = 0;
@@ -178,39 +179,88 @@ int need_device(const pkv_pool* p) {
 
 int64_t nblk(int32_t tokens) { return (tokens + pkv::kBlock - 1) / pkv::kBlock; }
 
+// Cost, in tiles, of starting a segment inside a wave (balanced schedule).
+#ifndef PKV_SEG_START_COST
+#define PKV_SEG_START_COST 4
+#endif
+constexpr int64_t kSegStartCost = PKV_SEG_START_COST;
+
 // Build the decode schedule for the current upload.
 //   part > 0: one wave per (kv head, sequence, part/16-block partition).
 //   part == 0: `target` waves, each an equal share of all tiles.
-// Layout of h_sched: wave_start[nwaves + 1], seg_w0[nseg], seg_w1[nseg].
+// Tiles are numbered kv-head-major: x = g * tseq + cum[s] + j.
+// h_sched = wdesc[8 * nwaves] | seg_w0[nseg] | seg_w1[nseg]; a wave's
+// descriptor holds its first and end tile, the sequence, kv head and block
+// index of its first tile, that sequence's length and the first block's id.
 void build_schedule(pkv_pool* p, int part, int target) {
   const int B = p->up_batch;
   const int H = p->shape.kv_heads;
   const int64_t tseq = p->h_cum[B];
   const int64_t T = tseq * H;
-  std::vector<int32_t> ws;
+  std::vector<int64_t> ws;
   if (part > 0) {
     const int64_t pb = part / pkv::kBlock;
     for (int g = 0; g < H; ++g)
       for (int s = 0; s < B; ++s) {
         const int64_t n = nblk(p->h_ctx[s]);
-        for (int64_t j = 0; j < n; j += pb) ws.push_back((int32_t)(g * tseq + p->h_cum[s] + j));
+        for (int64_t j = 0; j < n; j += pb) ws.push_back(g * tseq + p->h_cum[s] + j);
       }
   } else {
+    // Equal cost per wave, where starting a (kv head, sequence) segment costs
+    // kSegStartCost tiles on top of its tiles (q, lengths and the first block
+    // id are fetched before the first tile can be requested). Cuts fall where
+    // the running cost crosses multiples of total / W.
     const int64_t W = std::max<int64_t>(1, std::min<int64_t>(target, T));
-    ws.resize(W);
-    for (int64_t w = 0; w < W; ++w) ws[w] = (int32_t)(w * T / W);
+    const int64_t total = T + kSegStartCost * (int64_t)B * H;
+    ws.assign(1, 0);
+    int64_t cost = 0, x = 0;
+    for (int g = 0; g < H && (int64_t)ws.size() < W; ++g)
+      for (int s = 0; s < B && (int64_t)ws.size() < W; ++s) {
+        cost += kSegStartCost;
+        const int64_t n = nblk(p->h_ctx[s]);
+        for (int64_t j = 0; j < n; ++j, ++x) {
+          // open a new wave at tile x when the cost before it passes the next cut
+          while ((int64_t)ws.size() < W && cost * W >= (int64_t)ws.size() * total && x > ws.back())
+            ws.push_back(x);
+          ++cost;
+        }
+      }
   }
   const int W = (int)ws.size();
-  ws.push_back((int32_t)T);
+  ws.push_back(T);
   const int nseg = B * H;
-  std::vector<int32_t> w0(nseg), w1(nseg);
+  p->h_sched.assign((size_t)8 * W + 2 * (size_t)nseg, 0);
+  int32_t* desc = p->h_sched.data();
+  int32_t* w0 = desc + (size_t)8 * W;
+  int32_t* w1 = w0 + nseg;
+  // descriptors: walk waves and segments together
+  int g = 0, s = 0;
+  for (int w = 0; w < W; ++w) {
+    const int64_t x0 = ws[w];
+    while (g * tseq + p->h_cum[s + 1] <= x0) {
+      if (++s == B) {
+        s = 0;
+        ++g;
+      }
+    }
+    const int64_t j0 = x0 - g * tseq - p->h_cum[s];
+    int32_t* d = desc + (size_t)8 * w;
+    d[0] = (int32_t)x0;
+    d[1] = (int32_t)ws[w + 1];
+    d[2] = s;
+    d[3] = g;
+    d[4] = (int32_t)j0;
+    d[5] = p->h_ctx[s];
+    d[6] = p->h_bt[(size_t)s * p->up_stride + j0];
+    d[7] = 0;
+  }
   bool multi = false;
   int w = 0;
-  for (int g = 0; g < H; ++g)
-    for (int s = 0; s < B; ++s) {
-      const int seg = g * B + s;
-      const int64_t first = g * tseq + p->h_cum[s];
-      const int64_t last = first + nblk(p->h_ctx[s]) - 1;
+  for (int gg = 0; gg < H; ++gg)
+    for (int ss = 0; ss < B; ++ss) {
+      const int seg = gg * B + ss;
+      const int64_t first = gg * tseq + p->h_cum[ss];
+      const int64_t last = first + nblk(p->h_ctx[ss]) - 1;
       while (ws[w + 1] <= first) ++w;
       w0[seg] = w;
       int v = w;
@@ -218,12 +268,8 @@ void build_schedule(pkv_pool* p, int part, int target) {
       w1[seg] = v;
       multi |= v != w;
     }
-  p->h_sched.clear();
-  p->h_sched.insert(p->h_sched.end(), ws.begin(), ws.end());
-  p->h_sched.insert(p->h_sched.end(), w0.begin(), w0.end());
-  p->h_sched.insert(p->h_sched.end(), w1.begin(), w1.end());
   p->sched_nwaves = W;
-  p->sched_needs_reduce = multi;
+  p->sched_needs_merge = multi;
 }
 
 int waves_target(const pkv_pool* p, int gp) {
@@ -288,9 +334,9 @@ int pkv_kv_pool_alloc(const pkv_shape* sh, void* dev_base, size_t dev_bytes, pkv
       return hip_fail(e, "device query");
     }
     p->num_cus = prop.multiProcessorCount;
-    const size_t max_tiles =
-        (size_t)sh->max_seqs * p->max_blocks_per_seq * sh->kv_heads;
-    p->sched_cap = max_tiles + 1 + 2 * (size_t)sh->max_seqs * sh->kv_heads;
+    // balanced schedules need 8 ints per wave (at most 32 waves per CU); very
+    // small fixed partitions may grow this buffer on first use
+    p->sched_cap = (size_t)8 * std::max(p->num_cus, 1) * 32 + 2 * (size_t)sh->max_seqs * sh->kv_heads;
     p->pairs_cap = sh->max_seqs;
     const size_t bt_bytes = (size_t)sh->max_seqs * p->max_blocks_per_seq * 4;
     p->off_ctx = (size_t)sh->max_seqs * 8;
@@ -509,6 +555,15 @@ int pkv_block_table_upload(pkv_pool* p, const int32_t* bt, int batch, int max_bl
       if (slots[s] >= lim) return fail(PKV_EINVAL, "slot %lld out of range", (long long)slots[s]);
       if (slots[s] >= 0) seen.push_back(slots[s]);
     }
+    for (int s = 0; s < batch; ++s) {
+      if (slots[s] < 0) continue;
+      const int32_t pos = ctx[s] - 1;
+      const int64_t want =
+          (int64_t)bt[(int64_t)s * max_blocks + pos / pkv::kBlock] * pkv::kBlock + pos % pkv::kBlock;
+      if (slots[s] != want)
+        return fail(PKV_EINVAL, "sequence %d: slot %lld is not the table position %lld of its "
+                    "new token", s, (long long)slots[s], (long long)want);
+    }
     std::sort(seen.begin(), seen.end());
     for (size_t i = 1; i < seen.size(); ++i)
       if (seen[i] == seen[i - 1])
@@ -531,6 +586,7 @@ int pkv_block_table_upload(pkv_pool* p, const int32_t* bt, int batch, int max_bl
   p->up_stride = max_blocks;
   p->h_ctx.assign(ctx, ctx + batch);
   p->h_cum = std::move(cum);
+  p->h_bt.assign(bt, bt + (size_t)batch * max_blocks);
   ++p->up_gen;
   return PKV_OK;
 }
@@ -601,9 +657,11 @@ size_t pkv_decode_workspace_bytes(const pkv_pool* p, int batch, int q_heads,
   return (size_t)(nseg + waves) * gp * (p->shape.head_dim + 2) * sizeof(float);
 }
 
-int pkv_paged_attn_decode(pkv_pool* p, int layer, const void* q, int q_heads, float scale,
-                          float* out, int partition_tokens, void* ws, size_t ws_bytes,
-                          uintptr_t stream_u) {
+namespace {
+
+int decode_impl(pkv_pool* p, int layer, const void* k_new, const void* v_new, const void* q,
+                int q_heads, float scale, float* out, int partition_tokens, void* ws,
+                size_t ws_bytes, uintptr_t stream_u) {
   int rc = need_device(p);
   if (rc != PKV_OK) return rc;
   if (!p->uploaded) return fail(PKV_EINVAL, "no block table uploaded");
@@ -611,6 +669,12 @@ int pkv_paged_attn_decode(pkv_pool* p, int layer, const void* q, int q_heads, fl
   if (!q || !out) return fail(PKV_EINVAL, "q and out must be device pointers");
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
     return fail(PKV_EINVAL, "q and out must be 16-byte aligned");
+  if (k_new) {
+    if (!v_new) return fail(PKV_EINVAL, "k_new without v_new");
+    if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
+      return fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");
+    if (!p->has_slots) return fail(PKV_EINVAL, "append needs slots in the last upload");
+  }
   if (q_heads < 1 || q_heads % p->shape.kv_heads)
     return fail(PKV_EINVAL, "q_heads %d is not a multiple of kv_heads %d", q_heads,
                 p->shape.kv_heads);
@@ -623,12 +687,21 @@ int pkv_paged_attn_decode(pkv_pool* p, int layer, const void* q, int q_heads, fl
                 partition_tokens);
   const int gp = pkv::padded_group(group);
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_u);
+  hipError_t e;
 
   if (p->sched_gen != p->up_gen || p->sched_part != partition_tokens || p->sched_gp != gp) {
     build_schedule(p, partition_tokens, waves_target(p, gp));
-    if (p->h_sched.size() > p->sched_cap)
-      return fail(PKV_EUNSUPPORTED, "decode schedule of %zu entries exceeds %zu",
-                  p->h_sched.size(), p->sched_cap);
+    if (p->h_sched.size() > p->sched_cap) {  // grow (rare: very small fixed partitions)
+      if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "sync");
+      hipFree(p->d_sched);
+      p->d_sched = nullptr;
+      p->sched_cap = p->h_sched.size() + p->h_sched.size() / 2;
+      if ((e = hipMalloc((void**)&p->d_sched, p->sched_cap * 4)) != hipSuccess) {
+        p->sched_cap = 0;
+        p->sched_gen = 0;
+        return hip_fail(e, "schedule allocation");
+      }
+    }
     if ((rc = stage_copy(p, p->d_sched, p->h_sched.data(), p->h_sched.size() * 4, stream,
                          nullptr)))
       return rc;
@@ -641,39 +714,44 @@ int pkv_paged_attn_decode(pkv_pool* p, int layer, const void* q, int q_heads, fl
   const int64_t nseg = (int64_t)B * p->shape.kv_heads;
   const int64_t nparts = nseg + W;
   const size_t need = (size_t)nparts * gp * (p->shape.head_dim + 2) * sizeof(float);
-  if (ws_bytes < need || (!ws && need > 0))
+  if (p->sched_needs_merge && (ws_bytes < need || !ws))
     return fail(PKV_EINVAL, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
                 need);
-  if (reinterpret_cast<uintptr_t>(ws) & 15) return fail(PKV_EINVAL, "workspace must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(ws) & 15)
+    return fail(PKV_EINVAL, "workspace must be 16-byte aligned");
+  float* part = static_cast<float*>(ws);
 
   pkv::DecodeParams dp{};
   dp.k = p->k_base + (size_t)layer * p->layer_bytes;
   dp.v = p->v_base + (size_t)layer * p->layer_bytes;
   dp.bt = p->d_bt;
   dp.ctx = p->d_ctx;
-  dp.cum = p->d_cum;
-  dp.wave_start = p->d_sched;
+  dp.wdesc = p->d_sched;
+  dp.seg_w0 = p->d_sched + (size_t)8 * W;
+  dp.seg_w1 = dp.seg_w0 + nseg;
   dp.q = q;
+  dp.k_new = k_new;
+  dp.v_new = v_new;
+  dp.slots = p->d_slots;
   dp.out = out;
-  dp.part_o = static_cast<float*>(ws);
-  dp.part_ml = static_cast<float*>(ws) + (size_t)nparts * gp * p->shape.head_dim;
+  dp.part_o = part;
+  dp.part_ml = part + (size_t)nparts * gp * p->shape.head_dim;
   dp.scale_log2 = scale * 1.4426950408889634f;
   dp.bt_stride = p->up_stride;
   dp.batch = B;
   dp.kv_heads = p->shape.kv_heads;
   dp.q_heads = q_heads;
   dp.group = group;
-  dp.tseq = p->h_cum[B];
   dp.nwaves = W;
   dp.waves_per_xcd = (W + pkv::kNumXcd - 1) / pkv::kNumXcd;
-  hipError_t e = pkv::launch_decode(p->shape.dtype, p->shape.head_dim, gp, dp, stream);
+  e = pkv::launch_decode(p->shape.dtype, p->shape.head_dim, gp, dp, stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
-  if (p->sched_needs_reduce) {
+  if (p->sched_needs_merge) {
     pkv::ReduceParams rp{};
     rp.part_o = dp.part_o;
     rp.part_ml = dp.part_ml;
-    rp.seg_w0 = p->d_sched + W + 1;
-    rp.seg_w1 = p->d_sched + W + 1 + nseg;
+    rp.seg_w0 = dp.seg_w0;
+    rp.seg_w1 = dp.seg_w1;
     rp.out = out;
     rp.batch = B;
     rp.kv_heads = p->shape.kv_heads;
@@ -683,6 +761,24 @@ int pkv_paged_attn_decode(pkv_pool* p, int layer, const void* q, int q_heads, fl
     if (e != hipSuccess) return hip_fail(e, "reduce launch");
   }
   return PKV_OK;
+}
+
+}  // namespace
+
+int pkv_paged_attn_decode(pkv_pool* p, int layer, const void* q, int q_heads, float scale,
+                          float* out, int partition_tokens, void* ws, size_t ws_bytes,
+                          uintptr_t stream) {
+  return decode_impl(p, layer, nullptr, nullptr, q, q_heads, scale, out, partition_tokens, ws,
+                     ws_bytes, stream);
+}
+
+int pkv_append_paged_attn_decode(pkv_pool* p, int layer, const void* k_new, const void* v_new,
+                                 const void* q, int q_heads, float scale, float* out,
+                                 int partition_tokens, void* ws, size_t ws_bytes,
+                                 uintptr_t stream) {
+  if (!k_new || !v_new) return fail(PKV_EINVAL, "k_new and v_new are required");
+  return decode_impl(p, layer, k_new, v_new, q, q_heads, scale, out, partition_tokens, ws,
+                     ws_bytes, stream);
 }
 
 int pkv_pool_stats(const pkv_pool* p, int64_t stats[4]) {

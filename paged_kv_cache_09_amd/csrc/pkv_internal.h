@@ -16,9 +16,13 @@ struct DecodeParams {
   const void* v;               // layer base of V, same shape
   const int32_t* bt;           // block table [batch][bt_stride]
   const int32_t* ctx;          // context lengths [batch]
-  const int32_t* cum;          // blocks before each sequence [batch + 1]
-  const int32_t* wave_start;   // first tile of each wave [nwaves + 1]
+  const int32_t* wdesc;        // per wave: x0, x1, seq, kv head, j0, ctx, first block, 0
+  const int32_t* seg_w0;       // first wave touching each (kv head, sequence) segment
+  const int32_t* seg_w1;       // last wave touching it
   const void* q;               // [batch][q_heads][head_dim], cache dtype
+  const void* k_new;           // null, or new K rows [batch][kv_heads][head_dim] to append
+  const void* v_new;           // new V rows (with k_new)
+  const int64_t* slots;        // uploaded slots (with k_new): < 0 skips a sequence
   float* out;                  // [batch][q_heads][head_dim]
   float* part_o;               // [(nseg + nwaves) * gp][head_dim] unnormalised partial outputs
   float* part_ml;              // [(nseg + nwaves) * gp][2] partial (max, sum), log2 domain
@@ -28,7 +32,6 @@ struct DecodeParams {
   int32_t kv_heads;
   int32_t q_heads;
   int32_t group;               // q_heads / kv_heads
-  int32_t tseq;                // tiles per kv head = cum[batch]
   int32_t nwaves;
   int32_t waves_per_xcd;       // ceil(nwaves / 8)
 };

@@ -9,6 +9,10 @@
 //                   otherwise it writes an unnormalised partial (max, sum, o).
 //  reduce_kernel  — merges the partials of one (sequence, q head):
 //                   out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
+//                   (A merge by the last-finishing wavefront would save this
+//                   launch, but publishing partials across XCDs needs an
+//                   agent-scope release, an L2 write-back on this chip, which
+//                   measured ~3x slower than the extra launch.)
 //  append_kernel  — scatters each sequence's new K/V rows into the pool at its slot.
 //  copy_blocks_kernel — copy-on-write: whole K/V blocks src -> dst for every layer.
 //
@@ -50,28 +54,6 @@ __device__ __forceinline__ T lane_as(u32x4 v, int i) {
   return __builtin_bit_cast(T, u);
 }
 
-// Dot product of one 16-byte piece of q with the matching piece of a K row,
-// accumulated in fp32. bf16/fp16 products are exact in fp32; the dot2
-// instructions add two of them per step.
-template <int DT>
-__device__ __forceinline__ float dot_piece(u32x4 q, u32x4 k, float acc) {
-  if constexpr (DT == DT_BF16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc = __builtin_amdgcn_fdot2_f32_bf16(lane_as<bf16x2>(q, i), lane_as<bf16x2>(k, i), acc,
-                                            false);
-  } else if constexpr (DT == DT_F16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc = __builtin_amdgcn_fdot2(lane_as<f16x2>(q, i), lane_as<f16x2>(k, i), acc, false);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc = __builtin_fmaf(lane_as<float>(q, i), lane_as<float>(k, i), acc);
-  }
-  return acc;
-}
-
 // 16 bytes of cache elements -> fp32 values.
 template <int DT>
 __device__ __forceinline__ void to_f32(u32x4 w, float* out) {
@@ -97,38 +79,144 @@ __device__ __forceinline__ void to_f32(u32x4 w, float* out) {
 
 __device__ __forceinline__ float xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
-// Lanes 4r..4r+3 hold partial dot products of one K row for GP heads.
-// Sum them within the quad. With GP >= 4 the sums are scattered so lane
-// (4r + q) keeps heads q, q+4, ...; with GP < 4 every lane keeps all heads.
-template <int GP>
-__device__ __forceinline__ void quad_reduce(const float (&sc)[GP],
-                                            float (&out)[GP >= 4 ? GP / 4 : GP], int lane) {
-  if constexpr (GP >= 4) {
-    const bool b1 = lane & 2;
-    float k1[GP / 2];
+// Merge the n partial results (m_i, l_i, o_i) of one (kv head, sequence)
+// segment for query head slot hh, stored at partial indices first .. first+n-1:
+//   out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i.
+// One wavefront; lane handles head_dim/64 consecutive output elements. Up to
+// 64 partials are merged with all loads issued before any arithmetic (lane i
+// holds partial i's max and sum, the first eight outputs are prefetched);
+// more partials take a strided path.
+template <int D, int GP>
+__device__ __forceinline__ void merge_partials(const float* part_o, const float* part_ml,
+                                               size_t first, int n, int hh, float* dst,
+                                               int lane) {
+  constexpr int PER = D / 64;
+  constexpr int PF = 8;
+  float o[PER];
 #pragma unroll
-    for (int i = 0; i < GP / 2; ++i) {
-      const int h0 = (i / 2) * 4 + (i % 2);  // heads with bit 1 clear
-      const int h1 = h0 + 2;
-      const float keep = b1 ? sc[h1] : sc[h0];
-      const float send = b1 ? sc[h0] : sc[h1];
-      k1[i] = keep + xor_f(send, 2);
+  for (int e = 0; e < PER; ++e) o[e] = 0.f;
+  float den = 0.f;
+  if (n <= 64) {
+    float mi = -__builtin_inff(), li = 0.f;
+    if (lane < n) {
+      mi = part_ml[((first + lane) * GP + hh) * 2];
+      li = part_ml[((first + lane) * GP + hh) * 2 + 1];
     }
-    const bool b0 = lane & 1;
+    float ob[PF][PER];
 #pragma unroll
-    for (int i = 0; i < GP / 4; ++i) {
-      const float keep = b0 ? k1[2 * i + 1] : k1[2 * i];
-      const float send = b0 ? k1[2 * i] : k1[2 * i + 1];
-      out[i] = keep + xor_f(send, 1);
+    for (int u = 0; u < PF; ++u)
+#pragma unroll
+      for (int e = 0; e < PER; ++e)
+        ob[u][e] = u < n ? part_o[((first + u) * GP + hh) * D + lane * PER + e] : 0.f;
+    float M = mi;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, xor_f(M, off));
+    const float wi = lane < n ? __builtin_amdgcn_exp2f(mi - M) : 0.f;
+    den = wi * li;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) den += xor_f(den, off);
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const float wu = __shfl(wi, u, 64);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[e] = __builtin_fmaf(wu, ob[u][e], o[e]);
+    }
+    for (int u = PF; u < n; ++u) {
+      const float wu = __shfl(wi, u, 64);
+#pragma unroll
+      for (int e = 0; e < PER; ++e)
+        o[e] = __builtin_fmaf(wu, part_o[((first + u) * GP + hh) * D + lane * PER + e], o[e]);
     }
   } else {
+    float M = -__builtin_inff();
+    for (int i = lane; i < n; i += 64) M = fmaxf(M, part_ml[((first + i) * GP + hh) * 2]);
 #pragma unroll
-    for (int h = 0; h < GP; ++h) {
-      float v = sc[h];
-      v += xor_f(v, 2);
-      v += xor_f(v, 1);
-      out[h] = v;
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, xor_f(M, off));
+    for (int i = lane; i < n; i += 64) {
+      const float* ml = part_ml + ((first + i) * GP + hh) * 2;
+      den += __builtin_amdgcn_exp2f(ml[0] - M) * ml[1];
     }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) den += xor_f(den, off);
+    int i = 0;
+    for (; i + 4 <= n; i += 4) {  // four independent partials in flight
+      float wgt[4], src[4][PER];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        wgt[u] = part_ml[((first + i + u) * GP + hh) * 2];
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+          src[u][e] = part_o[((first + i + u) * GP + hh) * D + lane * PER + e];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wu = __builtin_amdgcn_exp2f(wgt[u] - M);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) o[e] = __builtin_fmaf(wu, src[u][e], o[e]);
+      }
+    }
+    for (; i < n; ++i) {
+      const float wu = __builtin_amdgcn_exp2f(part_ml[((first + i) * GP + hh) * 2] - M);
+#pragma unroll
+      for (int e = 0; e < PER; ++e)
+        o[e] = __builtin_fmaf(wu, part_o[((first + i) * GP + hh) * D + lane * PER + e], o[e]);
+    }
+  }
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) dst[lane * PER + e] = o[e] * inv;
+}
+
+// Softmax bookkeeping is in the log2 domain. A running maximum is raised
+// (and the accumulators rescaled) only when a score exceeds it by more than
+// this many binary orders; weights stay <= 2^kLazy, far from fp32 overflow,
+// and the result is the same softmax up to rounding.
+constexpr float kLazy = 8.f;
+
+// Row-wide (16-lane DPP row) all-reductions.
+template <int CTRL>
+__device__ __forceinline__ float row_ror(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, row_ror<0x128>(v));  // row_ror:8
+  v = fmaxf(v, row_ror<0x124>(v));  // row_ror:4
+  v = fmaxf(v, row_ror<0x122>(v));  // row_ror:2
+  return fmaxf(v, row_ror<0x121>(v));  // row_ror:1
+}
+__device__ __forceinline__ float row_sum(float v) {
+  v += row_ror<0x128>(v);
+  v += row_ror<0x124>(v);
+  v += row_ror<0x122>(v);
+  return v + row_ror<0x121>(v);
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// One 16-byte piece of the q.K^T contraction on the matrix cores:
+// A = q (16 rows = heads of the group, zero-padded), B = K^T (16 columns =
+// the tile's tokens). Lane l supplies row/column l%16 and the same 16 bytes
+// of head_dim for both operands, so the products pair up correctly whatever
+// order the instruction walks its K dimension in.
+template <int DT>
+__device__ __forceinline__ f32x4 qk_piece(u32x4 q, u32x4 k, f32x4 acc) {
+  if constexpr (DT == DT_BF16) {
+    const u32x4 qq = q, kk = k;
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qq),
+                                                   __builtin_bit_cast(bf16x8, kk), acc, 0, 0, 0);
+  } else if constexpr (DT == DT_F16) {
+    const u32x4 qq = q, kk = k;
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, qq),
+                                                  __builtin_bit_cast(f16x8, kk), acc, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(lane_as<float>(q, i), lane_as<float>(k, i), acc,
+                                                 0, 0, 0);
+    return acc;
   }
 }
 
@@ -136,72 +224,106 @@ template <int DT, int D, int GP>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   constexpr int EB = Elem<DT>::bytes;
   constexpr int RB = D * EB;       // bytes per K/V row
-  constexpr int NP = RB / 64;      // 16-byte K pieces per lane per tile (4 lanes per row)
+  constexpr int NP = RB / 64;      // 16-byte K loads per lane per tile (4 lane groups per row)
   constexpr int CPR = RB / 16;     // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;    // rows covered by one V load instruction
   constexpr int NV = 16 / RPI;     // V loads per lane per tile
   constexpr int EPC = 16 / EB;     // elements per chunk
-  constexpr int HPL = GP >= 4 ? GP / 4 : GP;  // heads whose scores a lane holds
+  constexpr int NG = GP >= 4 ? GP / 4 : 1;  // lane groups (of 16) holding real heads
+  constexpr int HPG = GP >= 4 ? 4 : GP;     // heads per lane group
   constexpr int TILE = 16 * RB;
-  static_assert(RB % 64 == 0 && CPR <= 64, "row size");
+  static_assert(RB % 64 == 0 && CPR <= 64 && GP <= 16, "shape");
 
-  __shared__ float p_lds[16 * GP];  // softmax weights of the current tile, [row][head]
-  __shared__ float a_lds[GP];       // per-head rescale factor of the current tile
-  __shared__ float l_lds[GP];       // per-head sums at the end of a run
-  __shared__ float m_lds[GP];       // per-head maxima at the end of a run
+  __shared__ float p_lds[2][16 * GP];  // softmax weights, [tile parity][row][head]
+  __shared__ float a_lds[GP];          // per-head rescale factors
+  __shared__ float l_lds[GP];          // per-head sums at the end of a run
+  __shared__ float m_lds[GP];          // per-head maxima at the end of a run
 
   const int lane = threadIdx.x;
   // Workgroups are dealt round-robin to the 8 XCDs; give each XCD one
   // contiguous eighth of the tile space so a kv head's tiles share one L2.
   const int w = (blockIdx.x % kNumXcd) * p.waves_per_xcd + blockIdx.x / kNumXcd;
   if (w >= p.nwaves) return;
-  int x = p.wave_start[w];
-  const int xend = p.wave_start[w + 1];
-  if (x >= xend) return;
 
-  const int row = lane >> 2;        // K row this lane's quad reads
-  const int quad = lane & 3;
-  const int vc = lane % CPR;        // V chunk this lane owns
-  const int vr = lane / CPR;        // first V row of this lane
+  // Per-wave descriptor: first tile, end tile, sequence, kv head, first block
+  // of the run inside the sequence, context length, physical id of that block.
+  const int* desc = p.wdesc + 8 * w;
+  int x = desc[0];
+  const int xend = desc[1];
+  int s = desc[2];
+  int g = desc[3];
+  int j0 = desc[4];
+  int L = desc[5];
+  int blk_first = desc[6];
 
-  // Locate the first tile: kv head, then sequence (count of prefix sums <= r).
-  int g = x / p.tseq;
-  int s;
-  {
-    const int r = x - g * p.tseq;
-    int cnt = 0;
-    for (int base = 0; base <= p.batch; base += 64) {
-      const int i = base + lane;
-      const int v = i <= p.batch ? p.cum[i] : 0x7fffffff;
-      cnt += __popcll(__ballot(v <= r));
-    }
-    s = cnt - 1;
-  }
+  const int t16 = lane & 15;  // K row (token) this lane feeds; q row (head) likewise
+  const int kg = lane >> 4;   // which 16-byte piece of each 64 bytes
+  const bool head_lane = kg < NG;  // this lane's score rows are real heads
+  const int vc = lane % CPR;  // V chunk this lane owns
+  const int vr = lane / CPR;  // first V row of this lane
+  const size_t blk_stride = (size_t)p.kv_heads * TILE;
+  int parity = 0;
 
-  while (x < xend) {
-    const int L = p.ctx[s];
+  while (true) {
     const int nblk = (L + 15) >> 4;
-    const int j0 = x - g * p.tseq - p.cum[s];
     const int take = min(xend - x, nblk - j0);
     const int j1 = j0 + take;
+    const int seg = g * p.batch + s;
+    // Prefetch the next segment's length and first block id (scalar loads
+    // in flight while this segment's tiles stream).
+    int next_s = s + 1, next_g = g, next_L = 0, next_blk = 0;
+    if (next_s == p.batch) {
+      next_s = 0;
+      ++next_g;
+    }
+    if (x + take < xend) {
+      next_L = p.ctx[next_s];
+      next_blk = p.bt[(size_t)next_s * p.bt_stride];
+    }
+    const char* kbase = reinterpret_cast<const char*>(p.k) + (size_t)g * TILE;
+    const char* vbase = reinterpret_cast<const char*>(p.v) + (size_t)g * TILE;
+    const int32_t* bt_row = p.bt + (size_t)s * p.bt_stride;
 
-    // q of the GQA group, in this lane's K pieces; padded heads are zero.
-    u32x4 qv[GP][NP];
+    // Append fused into the pass: the cached rows are ctx-1; the run holding
+    // the last block also takes the new token's row from k_new / v_new as a
+    // one-row tile, writes it to the pool where the table puts it and
+    // attends over it.
+    const bool app = p.k_new != nullptr && p.slots[s] >= 0;
+    const char* kn_row =
+        reinterpret_cast<const char*>(p.k_new) + ((size_t)s * p.kv_heads + g) * RB;
+    const char* vn_row =
+        reinterpret_cast<const char*>(p.v_new) + ((size_t)s * p.kv_heads + g) * RB;
+    const int Lc = L - (app ? 1 : 0);         // rows already in the pool
+    const int j1c = min(j1, (Lc + 15) >> 4);  // tiles holding cached rows
+
+    auto load_tile = [&](int blk, u32x4 (&kb)[NP], u32x4 (&vb)[NV]) {
+      const char* kt = kbase + (size_t)blk * blk_stride + t16 * RB + kg * 16;
+#pragma unroll
+      for (int k = 0; k < NP; ++k) kb[k] = ld16(kt + k * 64);
+      const char* vt = vbase + (size_t)blk * blk_stride + vr * RB + vc * 16;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) vb[i] = ld16(vt + i * RPI * RB);
+    };
+
+    // q rows of the GQA group (row = head t16, zero past the group), in the
+    // same pieces as K.
+    u32x4 qv[NP];
     {
-      const char* qb = reinterpret_cast<const char*>(p.q) +
-                       ((size_t)s * p.q_heads + (size_t)g * p.group) * RB;
+      const int hq = min(t16, p.group - 1);
+      const char* qr = reinterpret_cast<const char*>(p.q) +
+                       ((size_t)s * p.q_heads + (size_t)g * p.group + hq) * RB + kg * 16;
 #pragma unroll
-      for (int h = 0; h < GP; ++h)
-#pragma unroll
-        for (int k = 0; k < NP; ++k)
-          qv[h][k] = h < p.group ? ld16(qb + (size_t)h * RB + (quad + 4 * k) * 16)
-                                 : u32x4{0u, 0u, 0u, 0u};
+      for (int k = 0; k < NP; ++k) {
+        const u32x4 v = ld16(qr + k * 64);
+        qv[k] = t16 < p.group ? v : u32x4{0u, 0u, 0u, 0u};
+      }
     }
 
-    float m[HPL], lsum[HPL];
+    // Lane (t16, kg) keeps softmax state for heads 4*kg + i of its row.
+    float m[HPG], lsum[HPG];
     float acc[GP][EPC];
 #pragma unroll
-    for (int i = 0; i < HPL; ++i) {
+    for (int i = 0; i < HPG; ++i) {
       m[i] = -__builtin_inff();
       lsum[i] = 0.f;
     }
@@ -210,71 +332,32 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[h][e] = 0.f;
 
-    const int32_t* bt_row = p.bt + (size_t)s * p.bt_stride;
-    const char* kbase = reinterpret_cast<const char*>(p.k) + (size_t)g * TILE;
-    const char* vbase = reinterpret_cast<const char*>(p.v) + (size_t)g * TILE;
-    const size_t blk_stride = (size_t)p.kv_heads * TILE;
-
-    auto load_tile = [&](int blk, u32x4 (&kb)[NP], u32x4 (&vb)[NV]) {
-      const char* kt = kbase + (size_t)blk * blk_stride + row * RB + quad * 16;
-      const char* vt = vbase + (size_t)blk * blk_stride + vr * RB + vc * 16;
+    auto compute_tile = [&](int valid, const u32x4 (&kb)[NP], const u32x4 (&vb)[NV]) {
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < NP; ++k) kb[k] = ld16(kt + k * 64);
+      for (int k = 0; k < NP; ++k) sacc = qk_piece<DT>(qv[k], kb[k], sacc);
+      // sacc[i] = q(head 4*kg + i) . K(token t16)
+      float s2[HPG];
+      bool over = false;
 #pragma unroll
-      for (int i = 0; i < NV; ++i) vb[i] = ld16(vt + i * RPI * RB);
-    };
-
-    auto compute_tile = [&](int j, const u32x4 (&kb)[NP], const u32x4 (&vb)[NV]) {
-      const int valid = min(16, L - 16 * j);
-      float sc[GP];
-#pragma unroll
-      for (int h = 0; h < GP; ++h) {
-        float a = 0.f;
-#pragma unroll
-        for (int k = 0; k < NP; ++k) a = dot_piece<DT>(qv[h][k], kb[k], a);
-        sc[h] = a;
+      for (int i = 0; i < HPG; ++i) {
+        s2[i] = t16 < valid ? sacc[i] * p.scale_log2 : -__builtin_inff();
+        over |= head_lane && s2[i] > m[i] + kLazy;
       }
-      float s2[HPL];
-      quad_reduce<GP>(sc, s2, lane);
-      float mt[HPL];
+      if (__any(over)) {  // raise the running maxima to this tile's
+        float alpha[HPG];
 #pragma unroll
-      for (int i = 0; i < HPL; ++i) {
-        s2[i] = row < valid ? s2[i] * p.scale_log2 : -__builtin_inff();
-        mt[i] = s2[i];
-      }
-#pragma unroll
-      for (int off = 4; off < 64; off <<= 1)
-#pragma unroll
-        for (int i = 0; i < HPL; ++i) mt[i] = fmaxf(mt[i], xor_f(mt[i], off));
-      bool changed = false;
-      float alpha[HPL], pw[HPL];
-#pragma unroll
-      for (int i = 0; i < HPL; ++i) {
-        const float mn = fmaxf(m[i], mt[i]);
-        changed |= mn != m[i];
-        alpha[i] = __builtin_amdgcn_exp2f(m[i] - mn);
-        pw[i] = __builtin_amdgcn_exp2f(s2[i] - mn);
-        lsum[i] = lsum[i] * alpha[i] + pw[i];
-        m[i] = mn;
-      }
-      __syncthreads();  // previous tile's reads of p_lds/a_lds are done
-      if constexpr (GP >= 4) {
-#pragma unroll
-        for (int i = 0; i < HPL; ++i) {
-          p_lds[row * GP + 4 * i + quad] = pw[i];
-          if (row == 0) a_lds[4 * i + quad] = alpha[i];
+        for (int i = 0; i < HPG; ++i) {
+          const float mn = fmaxf(m[i], row_max(s2[i]));
+          alpha[i] = __builtin_amdgcn_exp2f(m[i] - mn);
+          lsum[i] *= alpha[i];
+          m[i] = mn;
         }
-      } else {
-        if (quad == 0) {
+        if (head_lane && t16 == 0) {
 #pragma unroll
-          for (int i = 0; i < HPL; ++i) {
-            p_lds[row * GP + i] = pw[i];
-            if (row == 0) a_lds[i] = alpha[i];
-          }
+          for (int i = 0; i < HPG; ++i) a_lds[4 * kg + i] = alpha[i];
         }
-      }
-      __syncthreads();
-      if (__any(changed)) {
+        __syncthreads();
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
           const float a = a_lds[h];
@@ -282,6 +365,15 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
           for (int e = 0; e < EPC; ++e) acc[h][e] *= a;
         }
       }
+      float* pl = p_lds[parity];
+      parity ^= 1;
+#pragma unroll
+      for (int i = 0; i < HPG; ++i) {
+        const float pw = __builtin_amdgcn_exp2f(s2[i] - m[i]);
+        lsum[i] += pw;
+        if (head_lane) pl[t16 * GP + 4 * kg + i] = pw;
+      }
+      __syncthreads();
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int t = vr + RPI * i;
@@ -293,7 +385,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
         }
         float pt[GP];
 #pragma unroll
-        for (int h = 0; h < GP; ++h) pt[h] = p_lds[t * GP + h];
+        for (int h = 0; h < GP; ++h) pt[h] = pl[t * GP + h];
 #pragma unroll
         for (int h = 0; h < GP; ++h)
 #pragma unroll
@@ -301,58 +393,62 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
       }
     };
 
-    for (int jb = j0; jb < j1; jb += 64) {
-      const int nb = min(64, j1 - jb);
-      const int my_blk = lane < nb ? bt_row[jb + lane] : 0;
+    for (int jb = j0; jb < j1c; jb += 64) {
+      const int nb = min(64, j1c - jb);
+      const int b0 = jb == j0 ? blk_first : bt_row[jb];
       u32x4 ka[NP], va[NV], kb2[NP], vb2[NV];
-      load_tile(__builtin_amdgcn_readlane(my_blk, 0), ka, va);
+      load_tile(b0, ka, va);
+      const int my_blk = lane < nb ? bt_row[jb + lane] : 0;
       for (int jj = 0; jj < nb; jj += 2) {
         if (jj + 1 < nb) load_tile(__builtin_amdgcn_readlane(my_blk, jj + 1), kb2, vb2);
-        compute_tile(jb + jj, ka, va);
+        compute_tile(min(16, Lc - 16 * (jb + jj)), ka, va);
         if (jj + 1 < nb) {
           if (jj + 2 < nb) load_tile(__builtin_amdgcn_readlane(my_blk, jj + 2), ka, va);
-          compute_tile(jb + jj + 1, kb2, vb2);
+          compute_tile(min(16, Lc - 16 * (jb + jj + 1)), kb2, vb2);
         }
       }
     }
+    if (app && j1 == nblk) {
+      // The new token: every lane loads the k_new / v_new row as row 0 of a
+      // one-row tile; the lanes of row 0 store it into the pool.
+      u32x4 kn[NP], vn[NV];
+#pragma unroll
+      for (int k = 0; k < NP; ++k) kn[k] = ld16(kn_row + kg * 16 + k * 64);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) vn[i] = ld16(vn_row + vc * 16);
+      const int blk_last = bt_row[nblk - 1];
+      const int t_new = (L - 1) & 15;
+      char* kd = const_cast<char*>(kbase) + (size_t)blk_last * blk_stride + t_new * RB;
+      char* vd = const_cast<char*>(vbase) + (size_t)blk_last * blk_stride + t_new * RB;
+      if (t16 == 0) {
+#pragma unroll
+        for (int k = 0; k < NP; ++k) *reinterpret_cast<u32x4*>(kd + kg * 16 + k * 64) = kn[k];
+      }
+      if (vr == 0) *reinterpret_cast<u32x4*>(vd + vc * 16) = vn[0];
+      compute_tile(1, kn, vn);
+    }
 
     // Totals over the 16 rows, and over the lanes sharing a V chunk.
-    float lt[HPL];
+    float lt[HPG];
 #pragma unroll
-    for (int i = 0; i < HPL; ++i) {
-      float v = lsum[i];
-#pragma unroll
-      for (int off = 4; off < 64; off <<= 1) v += xor_f(v, off);
-      lt[i] = v;
-    }
+    for (int i = 0; i < HPG; ++i) lt[i] = row_sum(lsum[i]);
 #pragma unroll
     for (int off = CPR; off < 64; off <<= 1)
 #pragma unroll
       for (int h = 0; h < GP; ++h)
 #pragma unroll
         for (int e = 0; e < EPC; ++e) acc[h][e] += xor_f(acc[h][e], off);
-    __syncthreads();
-    if constexpr (GP >= 4) {
-      if (row == 0) {
+    if (head_lane && t16 == 0) {
 #pragma unroll
-        for (int i = 0; i < HPL; ++i) {
-          l_lds[4 * i + quad] = lt[i];
-          m_lds[4 * i + quad] = m[i];
-        }
-      }
-    } else {
-      if (lane == 0) {
-#pragma unroll
-        for (int i = 0; i < HPL; ++i) {
-          l_lds[i] = lt[i];
-          m_lds[i] = m[i];
-        }
+      for (int i = 0; i < HPG; ++i) {
+        l_lds[4 * kg + i] = lt[i];
+        m_lds[4 * kg + i] = m[i];
       }
     }
     __syncthreads();
-    if (lane < CPR) {
-      const bool whole = j0 == 0 && j1 == nblk;
-      if (whole) {
+    const bool whole = j0 == 0 && j1 == nblk;
+    if (whole) {
+      if (lane < CPR) {
         float* o = p.out + ((size_t)s * p.q_heads + (size_t)g * p.group) * D + lane * EPC;
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
@@ -362,34 +458,38 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
             for (int e = 0; e < EPC; ++e) o[(size_t)h * D + e] = acc[h][e] * inv;
           }
         }
-      } else {
-        const size_t idx = (size_t)g * p.batch + s + w;
+      }
+    } else {
+      const size_t idx = (size_t)seg + w;
+      if (lane < CPR) {
         float* o = p.part_o + idx * GP * D + lane * EPC;
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
           if (h < p.group) {
 #pragma unroll
             for (int e = 0; e < EPC; ++e) o[(size_t)h * D + e] = acc[h][e];
-            if (lane == 0) {
-              p.part_ml[(idx * GP + h) * 2 + 0] = m_lds[h];
-              p.part_ml[(idx * GP + h) * 2 + 1] = l_lds[h];
-            }
           }
         }
       }
+      if (lane < p.group) {
+        p.part_ml[(idx * GP + lane) * 2 + 0] = m_lds[lane];
+        p.part_ml[(idx * GP + lane) * 2 + 1] = l_lds[lane];
+      }
     }
+    __syncthreads();  // l_lds / m_lds / a_lds are reused by the next run
 
     x += take;
-    if (++s == p.batch) {
-      s = 0;
-      ++g;
-    }
+    if (x >= xend) break;
+    s = next_s;
+    g = next_g;
+    j0 = 0;
+    L = next_L;
+    blk_first = next_blk;
   }
 }
 
 template <int D, int GP>
 __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
-  constexpr int PER = D / 64;
   const int lane = threadIdx.x;
   const int s = blockIdx.x / p.q_heads;
   const int h = blockIdx.x % p.q_heads;
@@ -399,34 +499,8 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
   const int w0 = p.seg_w0[seg];
   const int w1 = p.seg_w1[seg];
   if (w0 == w1) return;  // written directly by the decode kernel
-  const int n = w1 - w0 + 1;
-  const size_t base = (size_t)seg + w0;
-
-  float M = -__builtin_inff();
-  for (int i = lane; i < n; i += 64) M = fmaxf(M, p.part_ml[((base + i) * GP + hh) * 2]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, xor_f(M, off));
-  float den = 0.f;
-  for (int i = lane; i < n; i += 64) {
-    const float* ml = p.part_ml + ((base + i) * GP + hh) * 2;
-    den += __builtin_amdgcn_exp2f(ml[0] - M) * ml[1];
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) den += xor_f(den, off);
-
-  float o[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) o[e] = 0.f;
-  for (int i = 0; i < n; ++i) {
-    const float wgt = __builtin_amdgcn_exp2f(p.part_ml[((base + i) * GP + hh) * 2] - M);
-    const float* src = p.part_o + ((base + i) * GP + hh) * D + lane * PER;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] = __builtin_fmaf(wgt, src[e], o[e]);
-  }
-  const float inv = 1.f / den;
-  float* dst = p.out + ((size_t)s * p.q_heads + h) * D + lane * PER;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) dst[e] = o[e] * inv;
+  merge_partials<D, GP>(p.part_o, p.part_ml, (size_t)seg + w0, w1 - w0 + 1, hh,
+                        p.out + ((size_t)s * p.q_heads + h) * D, lane);
 }
 
 __global__ __launch_bounds__(256) void append_kernel(const char* k_new, const char* v_new,

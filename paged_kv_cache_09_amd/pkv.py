@@ -56,6 +56,8 @@ _SIGS = {
     "pkv_copy_blocks": (_I, [_P, _P, _I, _U]),
     "pkv_kv_append": (_I, [_P, _I, _P, _P, _P, _I, _U]),
     "pkv_paged_attn_decode": (_I, [_P, _I, _P, _I, ctypes.c_float, _P, _I, _P, _SZ, _U]),
+    "pkv_append_paged_attn_decode": (_I, [_P, _I, _P, _P, _P, _I, ctypes.c_float, _P, _I, _P,
+                                          _SZ, _U]),
     "pkv_decode_workspace_bytes": (_SZ, [_P, _I, _I, _I]),
     "pkv_pool_stats": (_I, [_P, _P]),
     "pkv_last_error": (ctypes.c_char_p, []),
@@ -181,6 +183,15 @@ def paged_attn_decode(pool, layer: int, q, q_heads: int, scale: float, out,
     _check(_lib.pkv_paged_attn_decode(pool, int(layer), _ptr(q), int(q_heads), float(scale),
                                       _ptr(out), int(partition_tokens), _ptr(workspace),
                                       int(ws_bytes), int(stream)))
+
+
+def append_paged_attn_decode(pool, layer: int, k_new, v_new, q, q_heads: int, scale: float,
+                             out, partition_tokens: int = 0, workspace=None, ws_bytes: int = 0,
+                             stream: int = 0) -> None:
+    _check(_lib.pkv_append_paged_attn_decode(pool, int(layer), _ptr(k_new), _ptr(v_new), _ptr(q),
+                                             int(q_heads), float(scale), _ptr(out),
+                                             int(partition_tokens), _ptr(workspace),
+                                             int(ws_bytes), int(stream)))
 
 
 def decode_workspace_bytes(pool, batch: int, q_heads: int, partition_tokens: int = 0) -> int:

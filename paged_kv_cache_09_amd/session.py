@@ -71,7 +71,7 @@ class DecodeSession:
         if self._ws_key != key:
             nbytes = pkv.decode_workspace_bytes(self.pool, self.cfg.batch, self.cfg.q_heads,
                                                 partition_tokens)
-            self._ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.w.pool.device)
+            self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.w.pool.device)
             self._ws_key = key
         return self._ws
 
@@ -84,19 +84,32 @@ class DecodeSession:
                               attn_scale(self.cfg) if scale is None else scale, out,
                               partition_tokens, ws, ws.numel(), self.stream)
 
+    def append_decode(self, layer: int, out: torch.Tensor, partition_tokens: int = 0):
+        """a4 + a5-a9 of one layer in one launch (fused append)."""
+        from .workloads import attn_scale
+        ws = self.workspace(partition_tokens)
+        pkv.append_paged_attn_decode(self.pool, layer, self.w.k_new, self.w.v_new, self.w.q,
+                                     self.cfg.q_heads, attn_scale(self.cfg), out,
+                                     partition_tokens, ws, ws.numel(), self.stream)
+
     def new_out(self) -> torch.Tensor:
         c = self.cfg
         return torch.empty((c.batch, c.q_heads, c.head_dim), dtype=torch.float32,
                            device=self.w.pool.device)
 
-    def step(self, out: torch.Tensor, layers=None, partition_tokens: int = 0):
-        """One full decode step: a1-a3 once, then append + decode per layer."""
+    def step(self, out: torch.Tensor, layers=None, partition_tokens: int = 0,
+             fused: bool = True):
+        """One full decode step: a1-a3 once, then append + decode per layer
+        (one launch per layer when fused, else kv_append then decode)."""
         self.prepare()
         self.upload()
         self.copy_blocks()
         for layer in (range(self.w.layers) if layers is None else layers):
-            self.append(layer)
-            self.decode(layer, out, partition_tokens)
+            if fused:
+                self.append_decode(layer, out, partition_tokens)
+            else:
+                self.append(layer)
+                self.decode(layer, out, partition_tokens)
 
     def stats(self) -> dict:
         return pkv.pool_stats(self.pool)

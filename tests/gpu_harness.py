@@ -106,7 +106,7 @@ def pick_seqs(w: W.Workload, sample: int | None, seed: int = 0):
 
 
 def run_step_case(cfg, *, layers=1, partitions=(0,), sample=None, check_untouched=True,
-                  label=""):
+                  label="", fused=False):
     """Full step on both sides; returns a dict of max errors per (layer, partition)."""
     say(f"case {label or cfg.name}: build workload B={cfg.batch} layers={layers}")
     w = W.make(cfg, device="cuda", layers=layers, form="step", fill="nan")
@@ -115,18 +115,22 @@ def run_step_case(cfg, *, layers=1, partitions=(0,), sample=None, check_untouche
     ora = OracleSide(w, seqs).run()
     before = w.pool.clone() if check_untouched else None
     sess = DecodeSession(w)
-    say(f"case {label or cfg.name}: GPU step partitions={list(partitions)}")
+    say(f"case {label or cfg.name}: GPU step partitions={list(partitions)} fused={fused}")
     slots, pairs = sess.prepare()
     sess.upload()
     sess.copy_blocks()
     errs = {}
     outs = {}
     for layer in range(layers):
-        sess.append(layer)
-        for part in partitions:
+        if not fused:
+            sess.append(layer)
+        for k, part in enumerate(partitions):
             out = sess.new_out()
             out.fill_(float("nan"))
-            sess.decode(layer, out, part)
+            if fused and k == 0:
+                sess.append_decode(layer, out, part)  # append fused into the first decode
+            else:
+                sess.decode(layer, out, part)
             torch.cuda.synchronize()
             got = out.cpu().numpy()[seqs]
             assert np.isfinite(got).all(), f"non-finite output layer {layer} partition {part}"

@@ -44,15 +44,18 @@ SMALL = {
 }
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["append+decode", "fused"])
 @pytest.mark.parametrize("name", list(SMALL))
-def test_small_step_parity(name):
+def test_small_step_parity(name, fused):
     cfg = SMALL[name]
-    errs, _, _ = run_step_case(cfg, layers=2, partitions=SPLITS, label=name)
+    errs, _, _ = run_step_case(cfg, layers=2, partitions=SPLITS, label=name, fused=fused)
     tol = tolerance(cfg)
     for key, e in errs.items():
         assert e <= tol, f"{name} layer/partition {key}: max abs error {e} > {tol}"
 
 
+# Full-size workloads in the launch configuration bench.py times: the append is
+# fused into the first decode listed (the workload's own partition setting).
 FULL = [
     ("tiny_f32", 1, (0, 512), None),
     ("llama8b_bf16", 2, (0, 512), None),
@@ -67,7 +70,8 @@ FULL = [
 def test_full_size_parity(name, layers, parts, sample):
     cfg = W.CONFIGS[name]
     errs, _, _ = run_step_case(cfg, layers=layers, partitions=parts, sample=sample,
-                               check_untouched=name != "mha13b_f16", label=f"full {name}")
+                               check_untouched=name != "mha13b_f16", label=f"full {name}",
+                               fused=True)
     tol = tolerance(cfg)
     for key, e in errs.items():
         assert e <= tol, f"{name} {key}: max abs error {e} > {tol}"
@@ -151,6 +155,9 @@ def test_bad_arguments_are_rejected_without_launch():
     bad[0, 0] = cfg.num_blocks
     with pytest.raises(pkv.PkvError):
         pkv.block_table_upload(sess.pool, bad, sess.ctx, None, sess.stream)
-    with pytest.raises(pkv.PkvError):  # duplicate slots would race
+    with pytest.raises(pkv.PkvError):  # slots that are not the new tokens' table positions
         pkv.block_table_upload(sess.pool, sess.table, sess.ctx, [5, 5, 6, 7], sess.stream)
+    with pytest.raises(pkv.PkvError):  # fused append needs uploaded slots
+        pkv.append_paged_attn_decode(sess.pool, 0, w.k_new, w.v_new, w.q, 4, 0.125, out, 0, ws,
+                                     ws.numel(), sess.stream)
     sess.close()
