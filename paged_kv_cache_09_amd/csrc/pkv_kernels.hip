@@ -488,11 +488,15 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   }
 }
 
+// Four wavefronts per workgroup, one (sequence, q head) pair each: fewer,
+// larger workgroups keep the dispatch ramp of this short kernel small.
 template <int D, int GP>
-__global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
-  const int lane = threadIdx.x;
-  const int s = blockIdx.x / p.q_heads;
-  const int h = blockIdx.x % p.q_heads;
+__global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= p.batch * p.q_heads) return;
+  const int s = pair / p.q_heads;
+  const int h = pair % p.q_heads;
   const int g = h / p.group;
   const int hh = h - g * p.group;
   const int seg = g * p.batch + s;
@@ -615,7 +619,7 @@ hipError_t launch_reduce(int head_dim, int gp, const ReduceParams& p, hipStream_
   if (!fn) return hipErrorInvalidValue;
   ReduceParams args = p;
   void* argv[] = {&args};
-  dim3 grid((unsigned)(p.batch * p.q_heads)), block(64);
+  dim3 grid((unsigned)((p.batch * p.q_heads + 3) / 4)), block(256);
   return hipLaunchKernel(fn, grid, block, argv, 0, stream);
 }
 
