@@ -30,6 +30,27 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_09_amd", "csrc", "pkv_kernels.hip")
+TRAFFIC = os.path.join(ROOT, "profiles", "decode_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(config: str):
+    """HBM bytes per decode launch from the committed counter run, if it was taken
+    on this workload with the current kernel source (else None)."""
+    try:
+        with open(TRAFFIC) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash() or t.get("config") != config:
+        return None
+    return int(t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"])
 
 
 def kv_bytes(cfg, ctx) -> int:
@@ -162,6 +183,8 @@ def main():
     cfg = W.CONFIGS[args.config]
     part = cfg.partition_tokens if args.partition is None else args.partition
     growth = args.warmup + args.steps + 1
+    # spare blocks so every sequence can grow by `growth` tokens
+    cfg = W.scaled(cfg, num_blocks=cfg.num_blocks + cfg.batch * ((growth + 15) // 16 + 1))
     log(f"building {cfg.name}: {cfg.layers} layers")
     w = W.make(cfg, device="cuda", layers=cfg.layers, form="step", fill="random",
                extra_blocks=(growth + 15) // 16 + 1)
@@ -250,12 +273,17 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(cfg.name),
             "kernel": "decode_kernel (fused append + paged attention + split merge), one launch per layer",
             "avg_launch_us": round(per_launch_s * 1e6, 3),
             "algorithmic_bytes_per_launch": alg,
         },
     }
+    if w.shared:  # shared blocks are read by every sharer but fetched from HBM once
+        shared_rows = cfg.prefix_tokens * (cfg.batch - 1)
+        unique = total_kv - shared_rows * 2 * cfg.kv_heads * cfg.head_dim * \
+            W.ELEM_BYTES[cfg.dtype] * cfg.layers * args.steps
+        res["unique_kv_GBps"] = round(unique / elapsed / 1e9, 2)
     if not args.no_cpu_baseline:
         log("cpu baseline")
         res["cpu_baseline"] = cpu_baseline(w)

@@ -152,7 +152,7 @@ int stage_copy(pkv_pool* p, void* dst, const void* src, size_t bytes, hipStream_
     st.pending = false;
   }
   if (st.bytes < bytes) {
-    if (st.host) hipHostFree(st.host);
+    if (st.host) (void)hipHostFree(st.host);
     st.host = nullptr;
     st.bytes = 0;
     size_t want = std::max(bytes, (size_t)1 << 16);
@@ -301,8 +301,8 @@ int pkv_kv_pool_alloc(const pkv_shape* sh, void* dev_base, size_t dev_bytes, pkv
   const int64_t storable = (int64_t)sh->num_blocks * sh->block_size;
   if (sh->max_seq_len > storable)
     return fail(PKV_ECAPACITY,
-                "max seq len (%d) is larger than the maximum number of tokens that can be stored "
-                "in KV cache (%lld)",
+                "max_seq_len %d exceeds the pool's capacity of %lld tokens "
+                "(num_blocks x block_size)",
                 sh->max_seq_len, (long long)storable);
   const size_t need = pkv_pool_bytes(sh);
   if (dev_base && dev_bytes < need)
@@ -360,14 +360,14 @@ int pkv_kv_pool_alloc(const pkv_shape* sh, void* dev_base, size_t dev_bytes, pkv
 
 int pkv_kv_pool_free(pkv_pool* p) {
   if (!p) return PKV_OK;
-  if (p->device) hipDeviceSynchronize();
+  if (p->device) (void)hipDeviceSynchronize();
   for (Staging& st : p->ring) {
-    if (st.ev) hipEventDestroy(st.ev);
-    if (st.host) hipHostFree(st.host);
+    if (st.ev) (void)hipEventDestroy(st.ev);
+    if (st.host) (void)hipHostFree(st.host);
   }
-  hipFree(p->d_meta);
-  hipFree(p->d_sched);
-  hipFree(p->d_pairs);
+  (void)hipFree(p->d_meta);
+  (void)hipFree(p->d_sched);
+  (void)hipFree(p->d_pairs);
   delete p;
   return PKV_OK;
 }
@@ -693,7 +693,7 @@ int decode_impl(pkv_pool* p, int layer, const void* k_new, const void* v_new, co
     build_schedule(p, partition_tokens, waves_target(p, gp));
     if (p->h_sched.size() > p->sched_cap) {  // grow (rare: very small fixed partitions)
       if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "sync");
-      hipFree(p->d_sched);
+      (void)hipFree(p->d_sched);
       p->d_sched = nullptr;
       p->sched_cap = p->h_sched.size() + p->h_sched.size() / 2;
       if ((e = hipMalloc((void**)&p->d_sched, p->sched_cap * 4)) != hipSuccess) {
