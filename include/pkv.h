@@ -23,7 +23,9 @@
  *  - Streams are passed as uintptr_t (a hipStream_t; 0 = null stream). All
  *    device work is asynchronous on that stream; no call synchronises the
  *    device except pkv_kv_pool_free.
- *  - A pool handle must not be used from two host threads at once.
+ *  - A pool handle must not be used from two host threads at once, and its
+ *    device work must be ordered: issue it on one stream, or order the
+ *    streams, since an upload rewrites device copies that earlier launches read.
  *
  * Pool layout in device memory (dev_base, dev_bytes >= pkv_pool_bytes):
  *   K region: [layers][num_blocks][kv_heads][block_size][head_dim] elements,
@@ -149,8 +151,11 @@ int pkv_prepare_append(pkv_pool* pool, int32_t* host_bt, int batch, int max_bloc
 /*
  * Upload the block table int32 [batch][max_blocks] (-1 padded), the context
  * lengths int32 [batch] and optionally the slots int64 [batch] (NULL: keep
- * none) to the library's device copies, asynchronously on `stream` from
- * pinned staging. Checked on the host first: 1 <= batch <= max_seqs,
+ * none) to the library's device copies, asynchronously on `stream`: the
+ * data is packed into coherent pinned staging (a ring of four buffers, each
+ * reused once the copy that last read it has finished) and copied by a small
+ * kernel on `stream`, together with the decode schedule for the partition
+ * setting and group of the previous decode call. Checked on the host first: 1 <= batch <= max_seqs,
  * max_blocks * 16 <= the pool's table width, 1 <= ctx <= max_seq_len, every
  * entry j < ceil(ctx/16) in [0, num_blocks); a non-negative slot must be the
  * table position of the sequence's new token (row ctx-1), as

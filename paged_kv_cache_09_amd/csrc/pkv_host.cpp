@@ -54,7 +54,8 @@ int check_shape(const pkv_shape* sh) {
 }
 
 struct Staging {
-  char* host = nullptr;
+  char* host = nullptr;  // coherent pinned host memory
+  char* dev = nullptr;   // the same memory as the device addresses it
   size_t bytes = 0;
   hipEvent_t ev = nullptr;
   bool pending = false;
@@ -81,16 +82,20 @@ struct pkv_pool {
   std::vector<int32_t> refcount;
 
   // device metadata (library owned). One buffer so that an upload is one copy:
-  // [slots int64 max_seqs | ctx int32 max_seqs | cum int32 max_seqs+1 | pad | table]
+  // [slots int64 max_seqs | ctx int32 max_seqs | cum int32 max_seqs+1 | pad |
+  //  table int32 batch x width | pad | decode schedule (up to sched_cap ints)]
+  // The schedule follows the table of the current upload (offset off_sched).
   char* d_meta = nullptr;
-  size_t off_ctx = 0, off_cum = 0, off_bt = 0, meta_bytes = 0;
+  size_t off_ctx = 0, off_cum = 0, off_bt = 0, meta_bytes = 0, off_sched = 0;
   int32_t* d_bt = nullptr;
   int32_t* d_ctx = nullptr;
   int32_t* d_cum = nullptr;
   int64_t* d_slots = nullptr;
   std::vector<char> h_stage;  // packed image of one upload
-  int32_t* d_sched = nullptr;
-  size_t sched_cap = 0;  // ints
+  size_t sched_cap = 0;       // ints the schedule region after the table holds
+  int32_t* d_sched = nullptr;  // where the current schedule lives
+  int32_t* d_sched_over = nullptr;  // larger schedules (small fixed partitions)
+  size_t over_cap = 0;              // ints
   int32_t* d_pairs = nullptr;
   int32_t pairs_cap = 0;  // pairs
 
@@ -139,11 +144,14 @@ int32_t free_pop(pkv_pool* p) {
   return id;
 }
 
-// Copy `bytes` from `src` into the next pinned staging buffer and enqueue the
-// host-to-device copy on `stream`. The buffer is reused only after the copy
-// that last read it has finished.
-int stage_copy(pkv_pool* p, void* dst, const void* src, size_t bytes, hipStream_t stream,
-               Staging** used) {
+size_t round16(size_t n) { return (n + 15) & ~(size_t)15; }
+
+// Copy `bytes` from `src` into the next pinned staging buffer and enqueue its
+// copy to `dst` (16-byte aligned, room for round16(bytes)) as a kernel on
+// `stream`: the kernel reads the coherent pinned memory over PCIe, which
+// avoids a hand-off to a copy engine and back for these small images. The
+// buffer is reused only after the kernel that last read it has finished.
+int stage_copy(pkv_pool* p, void* dst, const void* src, size_t bytes, hipStream_t stream) {
   Staging& st = p->ring[p->ring_next];
   p->ring_next = (p->ring_next + 1) % 4;
   hipError_t e;
@@ -151,21 +159,28 @@ int stage_copy(pkv_pool* p, void* dst, const void* src, size_t bytes, hipStream_
     if ((e = hipEventSynchronize(st.ev)) != hipSuccess) return hip_fail(e, "staging wait");
     st.pending = false;
   }
-  if (st.bytes < bytes) {
+  const size_t padded = round16(bytes);
+  if (st.bytes < padded) {
     if (st.host) (void)hipHostFree(st.host);
-    st.host = nullptr;
+    st.host = st.dev = nullptr;
     st.bytes = 0;
-    size_t want = std::max(bytes, (size_t)1 << 16);
-    if ((e = hipHostMalloc((void**)&st.host, want, hipHostMallocDefault)) != hipSuccess)
+    size_t want = std::max(padded, (size_t)1 << 16);
+    if ((e = hipHostMalloc((void**)&st.host, want, hipHostMallocCoherent | hipHostMallocMapped)) !=
+        hipSuccess)
       return hip_fail(e, "pinned staging allocation");
+    if ((e = hipHostGetDevicePointer((void**)&st.dev, st.host, 0)) != hipSuccess) {
+      (void)hipHostFree(st.host);
+      st.host = nullptr;
+      return hip_fail(e, "pinned staging device address");
+    }
     st.bytes = want;
   }
   if (!st.ev && (e = hipEventCreateWithFlags(&st.ev, hipEventDisableTiming)) != hipSuccess)
     return hip_fail(e, "event create");
   std::memcpy(st.host, src, bytes);
-  if ((e = hipMemcpyAsync(dst, st.host, bytes, hipMemcpyHostToDevice, stream)) != hipSuccess)
-    return hip_fail(e, "host-to-device copy");
-  if (used) *used = &st;
+  if (padded > bytes) std::memset(st.host + bytes, 0, padded - bytes);
+  if ((e = pkv::launch_upload(st.dev, dst, padded, stream)) != hipSuccess)
+    return hip_fail(e, "upload launch");
   if ((e = hipEventRecord(st.ev, stream)) != hipSuccess) return hip_fail(e, "event record");
   st.pending = true;
   return PKV_OK;
@@ -341,11 +356,10 @@ int pkv_kv_pool_alloc(const pkv_shape* sh, void* dev_base, size_t dev_bytes, pkv
     const size_t bt_bytes = (size_t)sh->max_seqs * p->max_blocks_per_seq * 4;
     p->off_ctx = (size_t)sh->max_seqs * 8;
     p->off_cum = p->off_ctx + (size_t)sh->max_seqs * 4;
-    p->off_bt = (p->off_cum + ((size_t)sh->max_seqs + 1) * 4 + 15) & ~(size_t)15;
-    p->meta_bytes = p->off_bt + bt_bytes;
+    p->off_bt = round16(p->off_cum + ((size_t)sh->max_seqs + 1) * 4);
+    p->meta_bytes = round16(p->off_bt + bt_bytes) + round16(p->sched_cap * 4);
     if ((e = hipMalloc((void**)&p->d_meta, p->meta_bytes)) != hipSuccess ||
-        (e = hipMalloc((void**)&p->d_sched, p->sched_cap * 4)) != hipSuccess ||
-        (e = hipMalloc((void**)&p->d_pairs, (size_t)p->pairs_cap * 8)) != hipSuccess) {
+        (e = hipMalloc((void**)&p->d_pairs, round16((size_t)p->pairs_cap * 8))) != hipSuccess) {
       pkv_kv_pool_free(p);
       return hip_fail(e, "device metadata allocation");
     }
@@ -366,7 +380,7 @@ int pkv_kv_pool_free(pkv_pool* p) {
     if (st.host) (void)hipHostFree(st.host);
   }
   (void)hipFree(p->d_meta);
-  (void)hipFree(p->d_sched);
+  (void)hipFree(p->d_sched_over);
   (void)hipFree(p->d_pairs);
   delete p;
   return PKV_OK;
@@ -571,16 +585,8 @@ int pkv_block_table_upload(pkv_pool* p, const int32_t* bt, int batch, int max_bl
                     (long long)seen[i]);
   }
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_u);
-  // pack slots, lengths, prefix sums and the table into one image: one copy
-  const size_t bytes = p->off_bt + (size_t)batch * max_blocks * 4;
-  p->h_stage.assign(bytes, 0);
-  char* img = p->h_stage.data();
-  if (slots) std::memcpy(img, slots, (size_t)batch * 8);
-  std::memcpy(img + p->off_ctx, ctx, (size_t)batch * 4);
-  std::memcpy(img + p->off_cum, cum.data(), (size_t)(batch + 1) * 4);
-  std::memcpy(img + p->off_bt, bt, (size_t)batch * max_blocks * 4);
-  if ((rc = stage_copy(p, p->d_meta, img, bytes, stream, nullptr))) return rc;
-  p->uploaded = true;
+  // host copies first: the decode schedule is built from them
+  p->uploaded = false;
   p->has_slots = slots != nullptr;
   p->up_batch = batch;
   p->up_stride = max_blocks;
@@ -588,6 +594,34 @@ int pkv_block_table_upload(pkv_pool* p, const int32_t* bt, int batch, int max_bl
   p->h_cum = std::move(cum);
   p->h_bt.assign(bt, bt + (size_t)batch * max_blocks);
   ++p->up_gen;
+  // Pack slots, lengths, prefix sums, the table and — when a decode has run
+  // before — the schedule for that decode's partition setting and group into
+  // one image: one copy per step.
+  const size_t tbl_end = p->off_bt + (size_t)batch * max_blocks * 4;
+  const size_t off_sched = round16(tbl_end);
+  size_t bytes = tbl_end;
+  bool packed = false;
+  if (p->sched_part >= 0) {
+    build_schedule(p, p->sched_part, waves_target(p, p->sched_gp));
+    if (p->h_sched.size() <= p->sched_cap) {
+      packed = true;
+      bytes = off_sched + p->h_sched.size() * 4;
+    }
+  }
+  p->h_stage.assign(bytes, 0);
+  char* img = p->h_stage.data();
+  if (slots) std::memcpy(img, slots, (size_t)batch * 8);
+  std::memcpy(img + p->off_ctx, ctx, (size_t)batch * 4);
+  std::memcpy(img + p->off_cum, p->h_cum.data(), (size_t)(batch + 1) * 4);
+  std::memcpy(img + p->off_bt, bt, (size_t)batch * max_blocks * 4);
+  if (packed) std::memcpy(img + off_sched, p->h_sched.data(), p->h_sched.size() * 4);
+  if ((rc = stage_copy(p, p->d_meta, img, bytes, stream))) return rc;
+  p->off_sched = off_sched;
+  if (packed) {
+    p->d_sched = reinterpret_cast<int32_t*>(p->d_meta + off_sched);
+    p->sched_gen = p->up_gen;
+  }
+  p->uploaded = true;
   return PKV_OK;
 }
 
@@ -609,7 +643,7 @@ int pkv_copy_blocks(pkv_pool* p, const int32_t* pairs, int n, uintptr_t stream_u
   if (std::adjacent_find(dsts.begin(), dsts.end()) != dsts.end())
     return fail(PKV_EINVAL, "two pairs copy into the same block");
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_u);
-  if ((rc = stage_copy(p, p->d_pairs, pairs, (size_t)n * 8, stream, nullptr))) return rc;
+  if ((rc = stage_copy(p, p->d_pairs, pairs, (size_t)n * 8, stream))) return rc;
   hipError_t e = pkv::launch_copy_blocks(p->d_pairs, n, p->k_base, p->v_base, p->shape.layers,
                                          p->layer_bytes, p->block_bytes, stream);
   if (e != hipSuccess) return hip_fail(e, "copy_blocks launch");
@@ -691,20 +725,26 @@ int decode_impl(pkv_pool* p, int layer, const void* k_new, const void* v_new, co
 
   if (p->sched_gen != p->up_gen || p->sched_part != partition_tokens || p->sched_gp != gp) {
     build_schedule(p, partition_tokens, waves_target(p, gp));
-    if (p->h_sched.size() > p->sched_cap) {  // grow (rare: very small fixed partitions)
-      if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "sync");
-      (void)hipFree(p->d_sched);
-      p->d_sched = nullptr;
-      p->sched_cap = p->h_sched.size() + p->h_sched.size() / 2;
-      if ((e = hipMalloc((void**)&p->d_sched, p->sched_cap * 4)) != hipSuccess) {
-        p->sched_cap = 0;
-        p->sched_gen = 0;
-        return hip_fail(e, "schedule allocation");
+    int32_t* dst = reinterpret_cast<int32_t*>(p->d_meta + p->off_sched);
+    if (p->h_sched.size() > p->sched_cap) {  // rare: very small fixed partitions
+      if (p->h_sched.size() > p->over_cap) {
+        if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "sync");
+        (void)hipFree(p->d_sched_over);
+        p->d_sched_over = nullptr;
+        p->over_cap = p->h_sched.size() + p->h_sched.size() / 2;
+        if ((e = hipMalloc((void**)&p->d_sched_over, round16(p->over_cap * 4))) != hipSuccess) {
+          p->over_cap = 0;
+          p->sched_gen = 0;
+          return hip_fail(e, "schedule allocation");
+        }
       }
+      dst = p->d_sched_over;
     }
-    if ((rc = stage_copy(p, p->d_sched, p->h_sched.data(), p->h_sched.size() * 4, stream,
-                         nullptr)))
+    if ((rc = stage_copy(p, dst, p->h_sched.data(), p->h_sched.size() * 4, stream))) {
+      p->sched_gen = 0;
       return rc;
+    }
+    p->d_sched = dst;
     p->sched_gen = p->up_gen;
     p->sched_part = partition_tokens;
     p->sched_gp = gp;

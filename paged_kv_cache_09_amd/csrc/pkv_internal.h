@@ -60,6 +60,9 @@ int decode_blocks_per_cu(int dtype, int head_dim, int gp);
 hipError_t launch_append(const void* k_new, const void* v_new, const int64_t* slots, int batch,
                          void* k_layer, void* v_layer, int kv_heads, int row_bytes,
                          hipStream_t stream);
+// Copy `bytes` (a multiple of 16, both pointers 16-byte aligned) from mapped
+// pinned host memory to device memory with a kernel on `stream`.
+hipError_t launch_upload(const void* host_src, void* dst, size_t bytes, hipStream_t stream);
 hipError_t launch_copy_blocks(const int32_t* pairs, int n, void* k_base, void* v_base,
                               int layers, int64_t layer_bytes, int64_t block_bytes,
                               hipStream_t stream);

@@ -14,6 +14,8 @@
 //                   agent-scope release, an L2 write-back on this chip, which
 //                   measured ~3x slower than the extra launch.)
 //  append_kernel  — scatters each sequence's new K/V rows into the pool at its slot.
+//  upload_kernel  — copies a packed metadata image from pinned host memory to
+//                   the device on the launch stream (no copy-engine hand-off).
 //  copy_blocks_kernel — copy-on-write: whole K/V blocks src -> dst for every layer.
 //
 // What is computed follows the pages: the cache is split into 16-token blocks
@@ -24,7 +26,8 @@
 // heads share one stored K/V head (ssdnodes.com, "KV cache vs prompt cache",
 // GQA paragraph). Decode is bound by memory bandwidth (ssdnodes.com, same
 // page, "What the KV cache holds"), so every tile is read exactly once, with
-// full 16-byte lanes, and all arithmetic is plain fp32 VALU work.
+// full 16-byte lanes; q.K^T of the GQA group runs on 16x16 MFMA tiles, the
+// softmax and P.V on the fp32 VALU.
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -548,6 +551,13 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const int32_t* pairs, 
     *reinterpret_cast<u32x4*>(dp + off) = *reinterpret_cast<const u32x4*>(sp + off);
 }
 
+// Pinned host memory (read over PCIe) -> device, 16 bytes per lane, grid-stride.
+__global__ __launch_bounds__(256) void upload_kernel(const u32x4* __restrict__ src,
+                                                     u32x4* __restrict__ dst, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
 template <int DT, int D, int GP>
 const void* decode_fn() {
   return reinterpret_cast<const void*>(&decode_kernel<DT, D, GP>);
@@ -641,6 +651,15 @@ hipError_t launch_copy_blocks(const int32_t* pairs, int n, void* k_base, void* v
   hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)(n * layers * 2)), dim3(256), 0, stream,
                      pairs, layers, static_cast<char*>(k_base), static_cast<char*>(v_base),
                      layer_bytes, block_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_upload(const void* host_src, void* dst, size_t bytes, hipStream_t stream) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  const int64_t wg = n16 < 256 * 256 ? (n16 + 255) / 256 : 256;
+  hipLaunchKernelGGL(upload_kernel, dim3((unsigned)wg), dim3(256), 0, stream,
+                     static_cast<const u32x4*>(host_src), static_cast<u32x4*>(dst), n16);
   return hipGetLastError();
 }
 
