@@ -46,9 +46,10 @@ def measured_traffic(config: str):
     try:
         with open(TRAFFIC) as f:
             t = json.load(f)
+        current = kernel_source_hash()
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != kernel_source_hash() or t.get("config") != config:
+    if t.get("kernel_source_sha256") != current or t.get("config") != config:
         return None
     return int(t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"])
 
