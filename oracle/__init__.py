@@ -7,7 +7,8 @@ and imports nothing from it.
 Parts:
   * ``oracle.c`` (built to ``liboracle.so`` by :func:`build`): closed-form KV
     size, append, gather and fp64 softmax attention, plus a partitioned
-    (per-partition max/sum, then merge) form of the same attention.
+    (per-partition max/sum, then merge) form of the same attention; the q8_0
+    quantised cache (quantisation of new rows, exact dequantisation).
   * :mod:`oracle.brute`: the same attention in pure-Python loops, for tiny
     inputs.
   * :mod:`oracle.block_model`: a plain model of on-demand block allocation,
@@ -27,8 +28,21 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "liboracle.so")
 _SRC = os.path.join(_HERE, "oracle.c")
 
-F32, F16, BF16 = 0, 1, 2
-_NP_STORAGE = {F32: np.float32, F16: np.uint16, BF16: np.uint16}
+F32, F16, BF16, Q8_0 = 0, 1, 2, 3
+_NP_STORAGE = {F32: np.float32, F16: np.uint16, BF16: np.uint16, Q8_0: np.uint8}
+Q8_GROUP = 32
+
+
+def q8_tile_bytes(head_dim: int, block_size: int = 16) -> int:
+    """Bytes of one q8_0 (block, kv head) tile: int8 codes, then fp16 scales."""
+    return block_size * head_dim + block_size * (head_dim // Q8_GROUP) * 2
+
+
+def input_dtype(dtype: int) -> int:
+    """Storage type of q, k_new and v_new for a cache of `dtype` (bf16 for q8_0)."""
+    return BF16 if dtype == Q8_0 else dtype
+
+
 _lib = None
 
 
@@ -65,6 +79,10 @@ def lib():
         L.orc_decode.restype = None
         L.orc_decode.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, i32, P, P,
                                  ctypes.c_double, P]
+        L.orc_float_to_half.restype = None
+        L.orc_float_to_half.argtypes = [P, i64, P]
+        L.orc_q8_quantize.restype = None
+        L.orc_q8_quantize.argtypes = [P, i64, P, P]
         L.orc_decode_partitioned.restype = None
         L.orc_decode_partitioned.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, i32, P,
                                              P, ctypes.c_double, i32, P]
@@ -94,16 +112,43 @@ def elem_to_double(storage: np.ndarray, dtype: int) -> np.ndarray:
     return np.array([L.orc_elem_to_double(_ptr(s), i, dtype) for i in range(s.size)])
 
 
+def float_to_half_bits(x) -> np.ndarray:
+    """fp32 values -> IEEE binary16 bit patterns (round to nearest even)."""
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    out = np.zeros(x.size, dtype=np.uint16)
+    lib().orc_float_to_half(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def q8_quantize(x):
+    """q8_0 groups of 32 fp32 values -> (int8 codes [n][32], fp16 scale bits [n])."""
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1, Q8_GROUP)
+    codes = np.zeros(x.shape, dtype=np.int8)
+    d = np.zeros(x.shape[0], dtype=np.uint16)
+    lib().orc_q8_quantize(_ptr(x), x.shape[0], _ptr(codes), _ptr(d))
+    return codes, d
+
+
+def _pool_shape(pool, dtype, block_size, head_dim):
+    """(NB, Hkv) of a layer array: [NB][Hkv][bs][D], or [NB][Hkv][tile bytes] for q8_0."""
+    if dtype == Q8_0:
+        assert pool.ndim == 3 and pool.shape[2] == q8_tile_bytes(head_dim, block_size)
+    else:
+        assert pool.ndim == 4 and pool.shape[2] == block_size and pool.shape[3] == head_dim
+    return pool.shape[0], pool.shape[1]
+
+
 def append(k_pool, v_pool, block_table, ctx_lens, k_new, v_new, *, dtype, block_size=16):
-    """In-place append into one layer's K/V pool arrays [NB][Hkv][bs][D]."""
+    """In-place append into one layer's K/V pool arrays ([NB][Hkv][bs][D], or
+    [NB][Hkv][tile bytes] uint8 for q8_0, whose new rows come in bf16)."""
     k_pool = _storage(k_pool, dtype)
     v_pool = _storage(v_pool, dtype)
     bt = np.ascontiguousarray(block_table, dtype=np.int32)
     ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
-    kn = _storage(k_new, dtype)
-    vn = _storage(v_new, dtype)
+    kn = _storage(k_new, input_dtype(dtype))
+    vn = _storage(v_new, input_dtype(dtype))
     B, Hkv, D = kn.shape
-    assert k_pool.shape[1] == Hkv and k_pool.shape[2] == block_size and k_pool.shape[3] == D
+    assert _pool_shape(k_pool, dtype, block_size, D)[1] == Hkv
     _check_tables(bt, ctx, k_pool.shape[0], block_size)
     lib().orc_append(B, Hkv, D, block_size, dtype, _ptr(k_pool), _ptr(v_pool), _ptr(bt),
                      bt.shape[1], _ptr(ctx), _ptr(kn), _ptr(vn))
@@ -115,7 +160,12 @@ def gather(k_pool, v_pool, bt_row, n_tokens, g, *, dtype, block_size=16):
     k_pool = _storage(k_pool, dtype)
     v_pool = _storage(v_pool, dtype)
     row = np.ascontiguousarray(bt_row, dtype=np.int32)
-    NB, Hkv, bs, D = k_pool.shape
+    if dtype == Q8_0:
+        NB, Hkv, tb = k_pool.shape
+        D = (tb // block_size) * Q8_GROUP // (Q8_GROUP + 2)
+        assert q8_tile_bytes(D, block_size) == tb
+    else:
+        NB, Hkv, bs, D = k_pool.shape
     _check_tables(row[None, :], np.array([n_tokens]), NB, block_size)
     ok = np.zeros((max(n_tokens, 1), D))
     ov = np.zeros((max(n_tokens, 1), D))
@@ -148,10 +198,10 @@ def decode(k_pool, v_pool, block_table, ctx_lens, q, scale, *, dtype, block_size
     v_pool = _storage(v_pool, dtype)
     bt = np.ascontiguousarray(block_table, dtype=np.int32)
     ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
-    qq = _storage(q, dtype)
+    qq = _storage(q, input_dtype(dtype))
     B, Hq, D = qq.shape
-    NB, Hkv, bs, D2 = k_pool.shape
-    assert D2 == D and bs == block_size and Hq % Hkv == 0
+    NB, Hkv = _pool_shape(k_pool, dtype, block_size, D)
+    assert Hq % Hkv == 0
     _check_tables(bt, ctx, NB, block_size)
     out = np.zeros((B, Hq, D))
     L = lib()

@@ -24,13 +24,19 @@
  *    head (ssdnodes.com, same section, the GQA paragraph); query head h reads
  *    kv head h / (q_heads / kv_heads).
  *
+ *  - A quantised cache: q8_0 (ssdnodes.com, same page, "Four ways to make the
+ *    KV cache smaller", item 2), read as llama.cpp's Q8_0 block format: per
+ *    32 consecutive head_dim elements one fp16 scale and 32 int8 codes.
+ *
  * Physical layout of one layer of the pool (our choice; the pages fix only
  * "blocks of block_size tokens" and "a block table"): K and V are separate
  * arrays, each indexed [block][kv_head][row][d] in row-major order, where row
  * is the token's position inside its block.
  *
- * Numbers are read exactly from their stored type (fp32, fp16 or bf16) into
- * double; all arithmetic is double. No blocking, no online softmax, no split:
+ * Numbers are read exactly from their stored type (fp32, fp16, bf16, or a
+ * q8_0 code times its fp16 scale) into double; all attention arithmetic is
+ * double. (Quantising a new q8_0 row makes its integer decisions in fp32, as
+ * the format's definition does.) No blocking, no online softmax, no split:
  * gather to a contiguous array, then softmax(q.K^T * scale) . V.
  */
 #include <math.h>
@@ -38,7 +44,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_Q8_0 = 3 };
 
 static size_t orc_elem_bytes(int dtype) { return dtype == ORC_F32 ? 4u : 2u; }
 
@@ -83,6 +89,90 @@ double orc_elem_to_double(const void* base, int64_t idx, int dtype) {
   return orc_load(base, (size_t)idx, dtype);
 }
 
+/*
+ * IEEE-754 binary32 value -> binary16 bits, rounded to nearest with ties to
+ * even, from the format's definition: the value is scaled by a power of two
+ * (exact in double) so that the kept bits are the integer part, and rint()
+ * (default rounding mode) rounds it. Overflow gives infinity.
+ */
+static uint16_t orc_float_to_half_bits(float f) {
+  uint16_t sign = signbit(f) ? 0x8000u : 0u;
+  if (isnan(f)) return sign | 0x7e00u;
+  if (isinf(f)) return sign | 0x7c00u;
+  double a = fabs((double)f);
+  if (a < ldexp(1.0, -14)) {
+    /* subnormal range: a multiple of 2^-24; 1024 units is the smallest normal */
+    return sign | (uint16_t)rint(ldexp(a, 24));
+  }
+  int E;
+  frexp(a, &E); /* a = m * 2^E, m in [0.5, 1): a = 1.f * 2^(E-1) */
+  int ex = E - 1;
+  int units = (int)rint(ldexp(a, 10 - ex)); /* 1.f in units of 2^-10: [1024, 2048] */
+  int field = ex + 15;
+  if (units == 2048) {
+    units = 1024;
+    ++field;
+  }
+  if (field >= 31) return sign | 0x7c00u;
+  return sign | (uint16_t)(field << 10) | (uint16_t)(units - 1024);
+}
+
+void orc_float_to_half(const float* x, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_float_to_half_bits(x[i]);
+}
+
+/*
+ * q8_0 quantisation of one group of 32 consecutive values. ssdnodes.com,
+ * "KV cache vs prompt cache", "Four ways to make the KV cache smaller" (item
+ * 2) and its FAQ name q8_0 as the cache type that about halves the memory of
+ * an f16 cache; its definition is llama.cpp's Q8_0 block: one scale
+ * d = max|x| / 127 stored as fp16 and 32 int8 codes round(x / d) (rounding
+ * half away from zero, x / d taken as x * (1 / d)), value = d * code. The
+ * integer decisions are made in fp32, as that definition does; the codes use
+ * the fp32 scale, the stored scale is its fp16 rounding.
+ */
+static void orc_q8_quantize_group(const float* x, int8_t* codes, uint16_t* d_bits) {
+  float amax = 0.0f;
+  for (int i = 0; i < 32; ++i) {
+    float a = fabsf(x[i]);
+    if (a > amax) amax = a;
+  }
+  float d = amax / 127.0f;
+  float id = d != 0.0f ? 1.0f / d : 0.0f;
+  for (int i = 0; i < 32; ++i) codes[i] = (int8_t)roundf(x[i] * id);
+  *d_bits = orc_float_to_half_bits(d);
+}
+
+void orc_q8_quantize(const float* x, int64_t n_groups, int8_t* codes, uint16_t* d_bits) {
+  for (int64_t g = 0; g < n_groups; ++g) orc_q8_quantize_group(x + 32 * g, codes + 32 * g, d_bits + g);
+}
+
+/*
+ * q8_0 tile of one (block, kv head) in the pool (our layout; the pages fix
+ * none): block_size rows x head_dim int8 codes, row-major, then
+ * block_size x head_dim/32 fp16 scales, ordered [row][group] in the K region
+ * and [group][row] in the V region.
+ */
+static size_t orc_q8_tile_bytes(int block_size, int head_dim) {
+  return (size_t)block_size * head_dim + (size_t)block_size * (head_dim / 32) * 2;
+}
+
+static size_t orc_q8_scale_offset(int is_v, int row, int grp, int block_size, int head_dim) {
+  size_t codes = (size_t)block_size * head_dim;
+  int ng = head_dim / 32;
+  return codes + 2 * (size_t)(is_v ? grp * block_size + row : row * ng + grp);
+}
+
+/* Value of element d of row `row` in a q8_0 tile: fp16 scale * int8 code, exact in double. */
+static double orc_q8_load(const char* tile, int is_v, int row, int d, int block_size,
+                          int head_dim) {
+  int8_t c;
+  uint16_t h;
+  memcpy(&c, tile + (size_t)row * head_dim + d, 1);
+  memcpy(&h, tile + orc_q8_scale_offset(is_v, row, d / 32, block_size, head_dim), 2);
+  return orc_half_bits_to_double(h) * (double)c;
+}
+
 /* ssdnodes.com, "KV cache vs prompt cache", "How much memory does the KV cache
  * use?": bytes per token = 2 * layers * kv_heads * head_dim * bytes/element. */
 int64_t orc_kv_bytes_per_token(int64_t layers, int64_t kv_heads, int64_t head_dim,
@@ -115,6 +205,28 @@ void orc_append(int batch, int kv_heads, int head_dim, int block_size, int dtype
     int p = L - 1;
     int32_t blk = block_table[(size_t)s * max_blocks + p / block_size];
     int row = p % block_size;
+    if (dtype == ORC_Q8_0) {
+      /* new rows arrive in bf16 and are quantised group by group */
+      size_t tb = orc_q8_tile_bytes(block_size, head_dim);
+      for (int g = 0; g < kv_heads; ++g) {
+        for (int is_v = 0; is_v < 2; ++is_v) {
+          const void* src = is_v ? v_new : k_new;
+          char* tile = (char*)(is_v ? v_pool : k_pool) + ((size_t)blk * kv_heads + g) * tb;
+          for (int grp = 0; grp < head_dim / 32; ++grp) {
+            float x[32];
+            for (int i = 0; i < 32; ++i)
+              x[i] = (float)orc_load(src, ((size_t)s * kv_heads + g) * head_dim + grp * 32 + i,
+                                     ORC_BF16);
+            int8_t codes[32];
+            uint16_t d;
+            orc_q8_quantize_group(x, codes, &d);
+            memcpy(tile + (size_t)row * head_dim + grp * 32, codes, 32);
+            memcpy(tile + orc_q8_scale_offset(is_v, row, grp, block_size, head_dim), &d, 2);
+          }
+        }
+      }
+      continue;
+    }
     for (int g = 0; g < kv_heads; ++g) {
       size_t dst = orc_pool_index(blk, g, row, 0, kv_heads, block_size, head_dim) * eb;
       size_t src = ((size_t)s * kv_heads + g) * head_dim * eb;
@@ -135,6 +247,16 @@ void orc_gather(int kv_heads, int head_dim, int block_size, int dtype, const voi
   for (int t = 0; t < n_tokens; ++t) {
     int32_t blk = bt_row[t / block_size];
     int row = t % block_size;
+    if (dtype == ORC_Q8_0) {
+      size_t off = ((size_t)blk * kv_heads + g) * orc_q8_tile_bytes(block_size, head_dim);
+      for (int d = 0; d < head_dim; ++d) {
+        out_k[(size_t)t * head_dim + d] =
+            orc_q8_load((const char*)k_pool + off, 0, row, d, block_size, head_dim);
+        out_v[(size_t)t * head_dim + d] =
+            orc_q8_load((const char*)v_pool + off, 1, row, d, block_size, head_dim);
+      }
+      continue;
+    }
     for (int d = 0; d < head_dim; ++d) {
       size_t i = orc_pool_index(blk, g, row, d, kv_heads, block_size, head_dim);
       out_k[(size_t)t * head_dim + d] = orc_load(k_pool, i, dtype);
@@ -176,7 +298,8 @@ void orc_attend(int n, int head_dim, const double* q, const double* kc, const do
  * Decode attention for a batch, reading the cache through the block tables:
  * for every sequence s and query head h, gather the first ctx_lens[s] rows of
  * kv head h / (q_heads / kv_heads) and attend with q[s][h].
- * q is stored in the cache dtype, [batch][q_heads][head_dim]; out is double
+ * q is stored in the cache dtype (bf16 for a q8_0 cache),
+ * [batch][q_heads][head_dim]; out is double
  * [batch][q_heads][head_dim]. Parallel over (sequence, kv head) with OpenMP.
  */
 void orc_decode(int batch, int q_heads, int kv_heads, int head_dim, int block_size, int dtype,
@@ -185,6 +308,7 @@ void orc_decode(int batch, int q_heads, int kv_heads, int head_dim, int block_si
                 double* out) {
   int group = q_heads / kv_heads;
   int npairs = batch * kv_heads;
+  int qdt = dtype == ORC_Q8_0 ? ORC_BF16 : dtype; /* q of a q8_0 cache is bf16 */
 #pragma omp parallel for schedule(dynamic, 1)
   for (int pi = 0; pi < npairs; ++pi) {
     int s = pi / kv_heads;
@@ -198,7 +322,7 @@ void orc_decode(int batch, int q_heads, int kv_heads, int head_dim, int block_si
                block_table + (size_t)s * max_blocks, L, g, kc, vc);
     for (int h = g * group; h < (g + 1) * group; ++h) {
       for (int d = 0; d < head_dim; ++d)
-        qd[d] = orc_load(q, ((size_t)s * q_heads + h) * head_dim + d, dtype);
+        qd[d] = orc_load(q, ((size_t)s * q_heads + h) * head_dim + d, qdt);
       orc_attend(L, head_dim, qd, kc, vc, scale, out + ((size_t)s * q_heads + h) * head_dim);
     }
     free(kc);
@@ -237,7 +361,8 @@ void orc_decode_partitioned(int batch, int q_heads, int kv_heads, int head_dim, 
     orc_gather(kv_heads, head_dim, block_size, dtype, k_pool, v_pool,
                block_table + (size_t)s * max_blocks, L, g, kc, vc);
     for (int d = 0; d < head_dim; ++d)
-      qd[d] = orc_load(q, ((size_t)s * q_heads + h) * head_dim + d, dtype);
+      qd[d] = orc_load(q, ((size_t)s * q_heads + h) * head_dim + d,
+                       dtype == ORC_Q8_0 ? ORC_BF16 : dtype);
     int nparts = (L + part_tokens - 1) / part_tokens;
     double* m = (double*)malloc(sizeof(double) * (size_t)(nparts > 0 ? nparts : 1));
     double* l = (double*)malloc(sizeof(double) * (size_t)(nparts > 0 ? nparts : 1));

@@ -21,8 +21,9 @@ def run_step(k_layers, v_layers, pre_tables, shared, ctx, k_new_layers, v_new_la
              dtype, num_blocks, max_blocks):
     """Apply one decode step to host pools.
 
-    k_layers / v_layers: lists (one per layer) of storage arrays [NB][Hkv][16][D],
-    updated in place. k_new_layers / v_new_layers: per-layer [B][Hkv][D] rows.
+    k_layers / v_layers: lists (one per layer) of storage arrays [NB][Hkv][16][D]
+    ([NB][Hkv][tile bytes] for q8_0), updated in place. k_new_layers /
+    v_new_layers: per-layer [B][Hkv][D] rows.
     Returns (post_table int32 [B][max_blocks], kinds).
     """
     model = BlockModel(num_blocks)
@@ -52,12 +53,35 @@ def run_step(k_layers, v_layers, pre_tables, shared, ctx, k_new_layers, v_new_la
     return table, kinds
 
 
+def q8_row_bytes(pool, blocks, rows, is_v):
+    """Bytes of q8_0 rows as [n][Hkv][D codes + 2 * D/32 scale bytes], scales in group
+    order. A tile is 16 x D int8 codes, then fp16 scales ordered [row][group]
+    (K region) or [group][row] (V region)."""
+    tb = pool.shape[2]
+    D = tb * 2 // 34
+    ng = D // 32
+    rows = np.asarray(rows, dtype=np.int64)
+    blocks = np.asarray(blocks, dtype=np.int64)
+    code_idx = rows[:, None] * D + np.arange(D)[None, :]
+    grp = np.arange(ng)[None, :]
+    si = grp * BLOCK + rows[:, None] if is_v else rows[:, None] * ng + grp
+    sb = BLOCK * D + 2 * si
+    scale_idx = np.stack([sb, sb + 1], axis=2).reshape(len(rows), 2 * ng)
+    idx = np.concatenate([code_idx, scale_idx], axis=1)
+    return np.take_along_axis(pool[blocks], idx[:, None, :], axis=2)
+
+
 def logical_rows(k_pool, v_pool, table, ctx):
-    """Raw bytes of every sequence's K and V rows in logical order: list of (K, V) arrays [L][Hkv][D]."""
+    """Raw bytes of every sequence's K and V rows in logical order: list of (K, V)
+    arrays [L][Hkv][D] (q8_0 pools [NB][Hkv][tile bytes]: codes then scale bytes)."""
     out = []
     for s, L in enumerate(ctx):
         t = np.arange(int(L))
         blocks = table[s][t // BLOCK]
         rows = t % BLOCK
-        out.append((k_pool[blocks, :, rows, :], v_pool[blocks, :, rows, :]))
+        if k_pool.ndim == 3:
+            out.append((q8_row_bytes(k_pool, blocks, rows, False),
+                        q8_row_bytes(v_pool, blocks, rows, True)))
+        else:
+            out.append((k_pool[blocks, :, rows, :], v_pool[blocks, :, rows, :]))
     return out

@@ -19,9 +19,10 @@ live in 16-token physical blocks scattered through one pool:
 Physical placement follows a seeded permutation of the pool's block ids,
 taken in (sequence, logical block) order, so logical neighbours are scattered
 through the pool. Cache values, q and the new K/V are N(0, sigma) draws made
-in fp32 and rounded to the cache dtype by torch (round to nearest even).
-Rows of the pool that hold no token are NaN for parity runs, so a kernel that
-reads them poisons its output.
+in fp32 and rounded to the cache dtype by torch (round to nearest even). A
+q8_0 cache holds random int8 codes and random fp16 scales (its q and new rows
+are bf16). Rows of the pool that hold no token are NaN (q8_0: NaN scales) for
+parity runs, so a kernel that reads them poisons its output.
 
 The five shapes follow the pages' statement of the problem (layers, kv heads,
 query heads with grouped-query attention, head_dim, block size 16) at the
@@ -35,11 +36,27 @@ import math
 import numpy as np
 import torch
 
-F32, F16, BF16 = 0, 1, 2
-TORCH_DTYPE = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}
+F32, F16, BF16, Q8_0 = 0, 1, 2, 3
+# element type of q, k_new and v_new (and of the cache itself, except q8_0)
+TORCH_DTYPE = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16,
+               Q8_0: torch.bfloat16}
 ELEM_BYTES = {F32: 4, F16: 2, BF16: 2}
-DTYPE_NAME = {F32: "f32", F16: "f16", BF16: "bf16"}
+DTYPE_NAME = {F32: "f32", F16: "f16", BF16: "bf16", Q8_0: "q8_0"}
 BLOCK = 16
+Q8_GROUP = 32
+
+
+def row_bytes(cfg) -> int:
+    """Pool bytes of one token's K (or V) row of one kv head: head_dim elements,
+    or for q8_0 head_dim int8 codes plus one fp16 scale per 32 of them."""
+    if cfg.dtype == Q8_0:
+        return cfg.head_dim + 2 * (cfg.head_dim // Q8_GROUP)
+    return cfg.head_dim * ELEM_BYTES[cfg.dtype]
+
+
+def tile_bytes(cfg) -> int:
+    """Bytes of one (block, kv head) tile of K (or V)."""
+    return BLOCK * row_bytes(cfg)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -84,6 +101,10 @@ CONFIGS = {
     "shared_prefix_cow_bf16": Config("shared_prefix_cow_bf16", 4, 128, 32, 8, 128, BF16, 1.0,
                                      8192, 8, "shared_prefix", prefix_tokens=1016,
                                      suffix_hi=0),
+    # The Llama-3.1-8B-shaped layer with a q8_0 cache (int8 codes, one fp16
+    # scale per 32 elements); same lengths and placement as the bf16 one.
+    "llama8b_q8": Config("llama8b_q8", 2, 64, 32, 8, 128, Q8_0, 1.0, 64 * 136, 32,
+                         "uniform", ctx_lo=128, ctx_hi=2048),
     # Long context: batch 4 x 131072 tokens (8192 blocks each), GQA 32/8, d 128,
     # bf16, 512-token split-K partitions.
     "long_ctx_bf16": Config("long_ctx_bf16", 5, 4, 32, 8, 128, BF16, 1.0, 32768, 1, "fixed",
@@ -174,17 +195,37 @@ class Workload:
         return pool_layer_views(self.pool, self.cfg, self.layers, layer)
 
 
-def pool_elems(cfg: Config, layers: int) -> int:
-    return layers * cfg.num_blocks * cfg.kv_heads * BLOCK * cfg.head_dim
+def region_bytes(cfg: Config, layers: int) -> int:
+    """Bytes of the K region (the V region is the same size)."""
+    return layers * cfg.num_blocks * cfg.kv_heads * tile_bytes(cfg)
 
 
 def pool_layer_views(pool: torch.Tensor, cfg: Config, layers: int, layer: int):
-    n = pool_elems(cfg, layers)
-    typed = pool.view(TORCH_DTYPE[cfg.dtype])
+    """(K, V) views of one layer: typed [NB][Hkv][16][D], or uint8
+    [NB][Hkv][tile bytes] for q8_0."""
+    n = region_bytes(cfg, layers)
+    if cfg.dtype == Q8_0:
+        shape = (layers, cfg.num_blocks, cfg.kv_heads, tile_bytes(cfg))
+        return pool[:n].view(shape)[layer], pool[n:2 * n].view(shape)[layer]
     shape = (layers, cfg.num_blocks, cfg.kv_heads, BLOCK, cfg.head_dim)
-    k = typed[:n].view(shape)[layer]
-    v = typed[n:2 * n].view(shape)[layer]
-    return k, v
+    tdt = TORCH_DTYPE[cfg.dtype]
+    return pool[:n].view(tdt).view(shape)[layer], pool[n:2 * n].view(tdt).view(shape)[layer]
+
+
+def _fill_q8(pool: torch.Tensor, cfg: Config, layers: int, gen: torch.Generator,
+             chunk: int = 1 << 26):
+    """q8_0 pool contents: int8 codes uniform in [-127, 127] and fp16 scales drawn
+    uniform in [0.005, 0.03] (rounded to fp16 by torch)."""
+    D = cfg.head_dim
+    tiles = pool.view(2 * layers * cfg.num_blocks * cfg.kv_heads, tile_bytes(cfg))
+    for i in range(0, tiles.shape[0], max(1, chunk // tiles.shape[1])):
+        part = tiles[i:i + max(1, chunk // tiles.shape[1])]
+        codes = torch.randint(-127, 128, (part.shape[0], BLOCK * D), generator=gen,
+                              device=pool.device, dtype=torch.int16)
+        part[:, :BLOCK * D].copy_(codes.to(torch.int8).view(torch.uint8))
+        sc = torch.rand((part.shape[0], BLOCK * (D // Q8_GROUP)), generator=gen,
+                        device=pool.device, dtype=torch.float32) * 0.025 + 0.005
+        part[:, BLOCK * D:].copy_(sc.to(torch.float16).view(torch.uint8).view(part.shape[0], -1))
 
 
 def _fill_normal(t: torch.Tensor, sigma: float, gen: torch.Generator, chunk: int = 1 << 26):
@@ -243,10 +284,12 @@ def make(cfg: Config, *, device="cpu", layers: int | None = None, form: str = "s
     gen = torch.Generator(device=device)
     gen.manual_seed(seed_vals)
     tdt = TORCH_DTYPE[cfg.dtype]
-    n = pool_elems(cfg, layers)
-    pool = torch.empty(2 * n * ELEM_BYTES[cfg.dtype], dtype=torch.uint8, device=device)
-    typed = pool.view(tdt)
-    _fill_normal(typed, cfg.sigma, gen)
+    nb = region_bytes(cfg, layers)
+    pool = torch.empty(2 * nb, dtype=torch.uint8, device=device)
+    if cfg.dtype == Q8_0:
+        _fill_q8(pool, cfg, layers, gen)
+    else:
+        _fill_normal(pool.view(tdt), cfg.sigma, gen)
     q = torch.empty((B, cfg.q_heads, cfg.head_dim), dtype=tdt, device=device)
     k_new = torch.empty((B, cfg.kv_heads, cfg.head_dim), dtype=tdt, device=device)
     v_new = torch.empty((B, cfg.kv_heads, cfg.head_dim), dtype=tdt, device=device)
@@ -267,9 +310,25 @@ def make(cfg: Config, *, device="cpu", layers: int | None = None, form: str = "s
                 if rows > 0:
                     valid[b, :rows] = True
         mask = torch.from_numpy(~valid).to(device)
-        shape = (layers, cfg.num_blocks, cfg.kv_heads, BLOCK, cfg.head_dim)
-        for region in (typed[:n], typed[n:2 * n]):
-            region.view(shape).masked_fill_(mask[None, :, None, :, None], float("nan"))
+        if cfg.dtype == Q8_0:
+            # a row without a token gets NaN scales: K scales are [row][group],
+            # V scales [group][row] after the 16 x head_dim codes of a tile
+            ng = cfg.head_dim // Q8_GROUP
+            shape = (layers, cfg.num_blocks, cfg.kv_heads, tile_bytes(cfg))
+            for r, region in enumerate((pool[:nb], pool[nb:2 * nb])):
+                sc = region.view(shape)[..., BLOCK * cfg.head_dim:].view(torch.float16)
+                if r == 0:
+                    sc.view(layers, cfg.num_blocks, cfg.kv_heads, BLOCK, ng).masked_fill_(
+                        mask[None, :, None, :, None], float("nan"))
+                else:
+                    sc.view(layers, cfg.num_blocks, cfg.kv_heads, ng, BLOCK).masked_fill_(
+                        mask[None, :, None, None, :], float("nan"))
+        else:
+            shape = (layers, cfg.num_blocks, cfg.kv_heads, BLOCK, cfg.head_dim)
+            typed = pool.view(tdt)
+            n = nb // ELEM_BYTES[cfg.dtype]
+            for region in (typed[:n], typed[n:2 * n]):
+                region.view(shape).masked_fill_(mask[None, :, None, :, None], float("nan"))
     elif fill != "random":
         raise ValueError(fill)
 
