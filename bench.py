@@ -58,8 +58,7 @@ def kv_bytes(cfg, ctx) -> int:
     """KV bytes one layer's decode reads: every cached row of K and V once."""
     import numpy as np
     from paged_kv_cache_09_amd import workloads as W
-    return int(np.asarray(ctx, dtype=np.int64).sum()) * 2 * cfg.kv_heads * cfg.head_dim * \
-        W.ELEM_BYTES[cfg.dtype]
+    return int(np.asarray(ctx, dtype=np.int64).sum()) * 2 * cfg.kv_heads * W.row_bytes(cfg)
 
 
 def decode_algorithmic_bytes(cfg, ctx) -> int:
@@ -68,11 +67,13 @@ def decode_algorithmic_bytes(cfg, ctx) -> int:
     output, the block-table entries and the lengths."""
     import numpy as np
     from paged_kv_cache_09_amd import workloads as W
-    e = W.ELEM_BYTES[cfg.dtype]
+    e_in = W.TORCH_DTYPE[cfg.dtype].itemsize  # q, k_new, v_new (bf16 for q8_0)
     B = len(ctx)
     nblk = int(((np.asarray(ctx, dtype=np.int64) + 15) // 16).sum())
-    new_rows = B * 2 * cfg.kv_heads * cfg.head_dim * e
-    return (kv_bytes(cfg, ctx) + new_rows + B * cfg.q_heads * cfg.head_dim * e +
+    # kv_bytes counts every row once, the new one included; that one is read
+    # from k_new / v_new (input dtype) rather than the pool, and written to it
+    new_rows = B * 2 * cfg.kv_heads * cfg.head_dim * e_in
+    return (kv_bytes(cfg, ctx) + new_rows + B * cfg.q_heads * cfg.head_dim * e_in +
             B * cfg.q_heads * cfg.head_dim * 4 + nblk * 4 * cfg.kv_heads + B * 4)
 
 
@@ -87,7 +88,7 @@ def cpu_baseline(w, budget_s: float = 12.0):
 
     def storage(t):
         t = t.detach().contiguous().cpu()
-        if t.dtype == torch.float32:
+        if t.dtype in (torch.float32, torch.uint8):
             return t.numpy().copy()
         return t.view(torch.int16).numpy().view(np.uint16).copy()
 
@@ -282,8 +283,8 @@ def main():
     }
     if w.shared:  # shared blocks are read by every sharer but fetched from HBM once
         shared_rows = cfg.prefix_tokens * (cfg.batch - 1)
-        unique = total_kv - shared_rows * 2 * cfg.kv_heads * cfg.head_dim * \
-            W.ELEM_BYTES[cfg.dtype] * cfg.layers * args.steps
+        unique = total_kv - shared_rows * 2 * cfg.kv_heads * W.row_bytes(cfg) * \
+            cfg.layers * args.steps
         res["unique_kv_GBps"] = round(unique / elapsed / 1e9, 2)
     if not args.no_cpu_baseline:
         log("cpu baseline")

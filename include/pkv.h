@@ -34,7 +34,18 @@
  * (block, kv_head) tile of K (or V) is block_size * head_dim contiguous
  * elements: 4 KiB for bf16/fp16 x 128 or fp32 x 64.
  *
- * Supported: block_size 16, head_dim 64 or 128, dtype fp32/fp16/bf16,
+ * q8_0 cache (PKV_Q8_0): the quantised cache type ssdnodes.com ("KV cache vs
+ * prompt cache", "Four ways to make the KV cache smaller", item 2) names as
+ * halving an f16 cache, in llama.cpp's Q8_0 block format: every 32
+ * consecutive head_dim elements of a row are one fp16 scale d and 32 int8
+ * codes c, value d * c. A tile is block_size * head_dim int8 codes (row-major)
+ * followed by block_size * head_dim/32 fp16 scales, ordered [row][group] in
+ * the K region and [group][row] in the V region (2176 bytes for head_dim
+ * 128). q, k_new and v_new are bf16 for a q8_0 cache; appends quantise each
+ * group with d = max|x| / 127 and c = round(x * (1/d)) (halves away from
+ * zero, fp32 arithmetic, d stored rounded to fp16).
+ *
+ * Supported: block_size 16, head_dim 64 or 128, dtype fp32/fp16/bf16/q8_0,
  * q_heads / kv_heads (the GQA group) from 1 to 8. Other shapes return
  * PKV_EUNSUPPORTED.
  */
@@ -50,7 +61,7 @@ extern "C" {
 
 typedef struct pkv_pool pkv_pool; /* opaque */
 
-enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 };
+enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_Q8_0 = 3 };
 
 enum {
   PKV_OK = 0,
@@ -176,10 +187,11 @@ int pkv_copy_blocks(pkv_pool* pool, const int32_t* host_pairs, int n, uintptr_t 
 
 /*
  * Append: for s < batch and every kv head g, write k_new[s][g][:] and
- * v_new[s][g][:] (cache dtype, [batch][kv_heads][head_dim]) into the pool row
- * of layer `layer` at slot[s] (block slot/16, row slot%16); slot < 0 skips.
- * dev_slots: device int64 [batch], or NULL for the slots of the last upload
- * (batch must then equal the uploaded batch). Bytes are copied unchanged.
+ * v_new[s][g][:] (cache dtype, [batch][kv_heads][head_dim]; bf16 for q8_0)
+ * into the pool row of layer `layer` at slot[s] (block slot/16, row
+ * slot%16); slot < 0 skips. dev_slots: device int64 [batch], or NULL for the
+ * slots of the last upload (batch must then equal the uploaded batch). Bytes
+ * are copied unchanged (q8_0: quantised as described above).
  */
 int pkv_kv_append(pkv_pool* pool, int layer, const void* k_new, const void* v_new,
                   const int64_t* dev_slots, int batch, uintptr_t stream);
@@ -191,7 +203,8 @@ int pkv_kv_append(pkv_pool* pool, int layer, const void* k_new, const void* v_ne
  * where K_s[t] is row t % 16 of block bt[s][t / 16] (news.hamidun.com
  * "KV-Cache", mechanism and prefill/decode paragraphs; the GQA head sharing of
  * ssdnodes.com, "KV cache vs prompt cache").
- * q: device [batch][q_heads][head_dim] in the cache dtype. out: device fp32
+ * q: device [batch][q_heads][head_dim] in the cache dtype (bf16 for q8_0,
+ * whose K/V values are scale * code). out: device fp32
  * [batch][q_heads][head_dim]. Softmax and accumulation are fp32.
  * partition_tokens: 0 = balanced split — every wavefront of a full-chip launch
  * takes an equal share of all (sequence, kv head, block) tiles and partial
@@ -211,8 +224,9 @@ int pkv_paged_attn_decode(pkv_pool* pool, int layer, const void* q, int q_heads,
 /*
  * kv_append followed by paged_attn_decode of the same layer, in one launch:
  * the wavefront that reads a sequence's last block takes the new token's row
- * from k_new / v_new ([batch][kv_heads][head_dim], cache dtype), writes it to
- * the pool at the uploaded slot and attends over it. The last upload must
+ * from k_new / v_new ([batch][kv_heads][head_dim], cache dtype; bf16 for
+ * q8_0, quantised as pkv_kv_append does), writes it to the pool at the
+ * uploaded slot and attends over it. The last upload must
  * carry slots. Same results, bit for bit in the pool, as the two calls.
  */
 int pkv_append_paged_attn_decode(pkv_pool* pool, int layer, const void* k_new, const void* v_new,

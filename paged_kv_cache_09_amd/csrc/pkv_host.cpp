@@ -33,8 +33,18 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Bytes of one stored element (a q8_0 code is one byte; its scales are extra).
 int elem_bytes(int dtype) {
-  return dtype == PKV_F32 ? 4 : (dtype == PKV_F16 || dtype == PKV_BF16) ? 2 : 0;
+  return dtype == PKV_F32 ? 4 : (dtype == PKV_F16 || dtype == PKV_BF16) ? 2
+                                : dtype == PKV_Q8_0 ? 1 : 0;
+}
+
+// Bytes of one (block, kv head) tile of K or V: block_size rows of head_dim
+// elements, plus for q8_0 one fp16 scale per 32 elements of each row.
+int64_t tile_bytes_of(const pkv_shape* sh) {
+  const int64_t codes = (int64_t)sh->block_size * sh->head_dim * elem_bytes(sh->dtype);
+  return sh->dtype == PKV_Q8_0 ? codes + (int64_t)sh->block_size * (sh->head_dim / 32) * 2
+                               : codes;
 }
 
 // Shape checks shared by pkv_pool_bytes and pkv_kv_pool_alloc.
@@ -70,8 +80,8 @@ struct pkv_pool {
   int num_cus = 0;
   char* k_base = nullptr;
   char* v_base = nullptr;
-  int64_t row_bytes = 0;    // head_dim * elem
-  int64_t tile_bytes = 0;   // 16 rows
+  int64_t row_bytes = 0;    // head_dim * elem (codes only for q8_0)
+  int64_t tile_bytes = 0;   // 16 rows (+ scales for q8_0)
   int64_t block_bytes = 0;  // kv_heads tiles: one block of one layer, K or V
   int64_t layer_bytes = 0;  // num_blocks blocks
   int32_t max_blocks_per_seq = 0;
@@ -305,8 +315,7 @@ const char* pkv_last_error(void) { return g_err.c_str(); }
 
 size_t pkv_pool_bytes(const pkv_shape* sh) {
   if (check_shape(sh) != PKV_OK) return 0;
-  return (size_t)sh->layers * sh->num_blocks * sh->block_size * 2 * sh->kv_heads * sh->head_dim *
-         elem_bytes(sh->dtype);
+  return (size_t)sh->layers * sh->num_blocks * 2 * sh->kv_heads * tile_bytes_of(sh);
 }
 
 int pkv_kv_pool_alloc(const pkv_shape* sh, void* dev_base, size_t dev_bytes, pkv_pool** out) {
@@ -328,7 +337,7 @@ int pkv_kv_pool_alloc(const pkv_shape* sh, void* dev_base, size_t dev_bytes, pkv
   pkv_pool* p = new pkv_pool();
   p->shape = *sh;
   p->row_bytes = (int64_t)sh->head_dim * elem_bytes(sh->dtype);
-  p->tile_bytes = p->row_bytes * sh->block_size;
+  p->tile_bytes = tile_bytes_of(sh);
   p->block_bytes = p->tile_bytes * sh->kv_heads;
   p->layer_bytes = p->block_bytes * sh->num_blocks;
   p->max_blocks_per_seq = (int32_t)nblk(sh->max_seq_len);
@@ -668,8 +677,13 @@ int pkv_kv_append(pkv_pool* p, int layer, const void* k_new, const void* v_new,
   }
   char* kl = p->k_base + (size_t)layer * p->layer_bytes;
   char* vl = p->v_base + (size_t)layer * p->layer_bytes;
-  hipError_t e = pkv::launch_append(k_new, v_new, slots, batch, kl, vl, p->shape.kv_heads,
-                                    (int)p->row_bytes, reinterpret_cast<hipStream_t>(stream_u));
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_u);
+  hipError_t e =
+      p->shape.dtype == PKV_Q8_0
+          ? pkv::launch_append_q8(k_new, v_new, slots, batch, kl, vl, p->shape.kv_heads,
+                                  p->shape.head_dim, stream)
+          : pkv::launch_append(k_new, v_new, slots, batch, kl, vl, p->shape.kv_heads,
+                               (int)p->row_bytes, stream);
   if (e != hipSuccess) return hip_fail(e, "kv_append launch");
   return PKV_OK;
 }

@@ -14,6 +14,8 @@
 //                   agent-scope release, an L2 write-back on this chip, which
 //                   measured ~3x slower than the extra launch.)
 //  append_kernel  — scatters each sequence's new K/V rows into the pool at its slot.
+//  append_q8_kernel — the same for a q8_0 cache: quantises each 32-value group
+//                   of the bf16 new rows to int8 codes and an fp16 scale.
 //  upload_kernel  — copies a packed metadata image from pinned host memory to
 //                   the device on the launch stream (no copy-engine hand-off).
 //  copy_blocks_kernel — copy-on-write: whole K/V blocks src -> dst for every layer.
@@ -33,19 +35,79 @@
 namespace pkv {
 namespace {
 
-enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_Q8 = 3 };
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+// Bytes of one stored element (q8_0: one int8 code; its scales are extra).
 template <int DT>
 struct Elem {
-  static constexpr int bytes = DT == DT_F32 ? 4 : 2;
+  static constexpr int bytes = DT == DT_F32 ? 4 : DT == DT_Q8 ? 1 : 2;
 };
 
 __device__ __forceinline__ u32x4 ld16(const char* p) {
   return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x2 ld8(const char* p) {
+  return *reinterpret_cast<const u32x2*>(p);
+}
+__device__ __forceinline__ unsigned ld4(const char* p) {
+  return *reinterpret_cast<const unsigned*>(p);
+}
+
+// fp16 halves of a 32-bit word, as fp32.
+__device__ __forceinline__ float half_lo(unsigned u) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(u & 0xffffu));
+}
+__device__ __forceinline__ float half_hi(unsigned u) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(u >> 16));
+}
+__device__ __forceinline__ unsigned half_bits(float f) {
+  return (unsigned)__builtin_bit_cast(unsigned short, (_Float16)f);
+}
+
+// Byte b of w as a signed 8-bit integer, in fp32.
+__device__ __forceinline__ float sbyte(unsigned w, int b) {
+  return (float)(int)(signed char)(w >> (8 * b));
+}
+
+// The upper halves of two fp32 values as one bf16 pair (exact for the small
+// integers this is used on: their fp32 encodings end in 16 zero bits).
+__device__ __forceinline__ unsigned bf16_pair(float lo, float hi) {
+  return __builtin_amdgcn_perm(__builtin_bit_cast(unsigned, hi), __builtin_bit_cast(unsigned, lo),
+                               0x07060302u);
+}
+
+// 8 int8 codes -> 8 bf16 values (exact), an MFMA operand.
+__device__ __forceinline__ u32x4 codes_to_bf16(u32x2 c) {
+  const unsigned w0 = c[0], w1 = c[1];
+  u32x4 r;
+  r[0] = bf16_pair(sbyte(w0, 0), sbyte(w0, 1));
+  r[1] = bf16_pair(sbyte(w0, 2), sbyte(w0, 3));
+  r[2] = bf16_pair(sbyte(w1, 0), sbyte(w1, 1));
+  r[3] = bf16_pair(sbyte(w1, 2), sbyte(w1, 3));
+  return r;
+}
+
+// q8_0 quantisation of 8 values of one 32-value group whose max |x| is amax:
+// scale d = amax / 127 (fp32, stored as fp16), codes round(x * (1 / d)),
+// halves away from zero (llama.cpp's Q8_0 format, the q8_0 cache type of
+// ssdnodes.com, "KV cache vs prompt cache", "Four ways to make the KV cache
+// smaller"). Returns the 8 codes; *d_out gets the fp32 scale.
+__device__ __forceinline__ u32x2 q8_codes(const float (&x)[8], float amax, float* d_out) {
+  const float d = amax / 127.f;
+  const float id = d != 0.f ? 1.f / d : 0.f;
+  unsigned w[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = (int)__builtin_roundf(x[j] * id);
+    w[j >> 2] |= ((unsigned)c & 0xffu) << (8 * (j & 3));
+  }
+  *d_out = d;
+  return u32x2{w[0], w[1]};
 }
 
 // Bit casts from one 32-bit lane of a u32x4. The element is copied to a
@@ -223,19 +285,45 @@ __device__ __forceinline__ f32x4 qk_piece(u32x4 q, u32x4 k, f32x4 acc) {
   }
 }
 
+// One lane's share of a (block, kv head) K and V tile.
+//   fp32 / fp16 / bf16: NP 16-byte K pieces (lane (t16, kg) holds bytes
+//   kg*16 + 64*k of row t16) and NV 16-byte V chunks (chunk vc of rows
+//   vr + RPI*i).
+//   q8_0: NP 8-byte K pieces (codes 32*k + 8*kg .. +8 of row t16, one piece
+//   per 32-code scale group) with that row's NP fp16 scales, and NV 8-byte V
+//   chunks (codes 8*vc .. +8 of rows NV*vr + i) with those rows' scales of
+//   group vc/4.
+template <int DT, int D>
+struct TileRegs {
+  static constexpr int RB = D * Elem<DT>::bytes;
+  static constexpr int NP = RB / 64, CPR = RB / 16, RPI = 64 / CPR, NV = 16 / RPI;
+  u32x4 k[NP];
+  u32x4 v[NV];
+};
+template <int D>
+struct TileRegs<DT_Q8, D> {
+  static constexpr int NP = D / 32, CPR = D / 8, RPI = 64 / CPR, NV = 16 / RPI;
+  u32x2 k[NP];
+  u32x2 v[NV];
+  unsigned ks[NP / 2];  // fp16 pairs: scale of group k in half k % 2 of ks[k / 2]
+  unsigned vs[NV / 2];  // fp16 pairs: scale of row NV*vr + i in half i % 2 of vs[i / 2]
+};
+
 template <int DT, int D, int GP>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
-  constexpr int EB = Elem<DT>::bytes;
-  constexpr int RB = D * EB;       // bytes per K/V row
-  constexpr int NP = RB / 64;      // 16-byte K loads per lane per tile (4 lane groups per row)
-  constexpr int CPR = RB / 16;     // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;    // rows covered by one V load instruction
-  constexpr int NV = 16 / RPI;     // V loads per lane per tile
-  constexpr int EPC = 16 / EB;     // elements per chunk
+  constexpr bool Q8 = DT == DT_Q8;
+  using TR = TileRegs<DT, D>;
+  constexpr int RB = D * Elem<DT>::bytes;  // bytes per K/V row (codes only for q8_0)
+  constexpr int QB = Q8 ? 2 * D : RB;      // bytes per q / new K,V row (bf16 for q8_0)
+  constexpr int NP = TR::NP;               // K pieces per lane per tile (= q pieces)
+  constexpr int CPR = TR::CPR;             // V chunks per row
+  constexpr int RPI = TR::RPI;             // rows covered by one V load instruction
+  constexpr int NV = TR::NV;               // V loads per lane per tile
+  constexpr int EPC = Q8 ? 8 : 16 / Elem<DT>::bytes;  // elements per V chunk
   constexpr int NG = GP >= 4 ? GP / 4 : 1;  // lane groups (of 16) holding real heads
   constexpr int HPG = GP >= 4 ? 4 : GP;     // heads per lane group
-  constexpr int TILE = 16 * RB;
-  static_assert(RB % 64 == 0 && CPR <= 64 && GP <= 16, "shape");
+  constexpr int TILE = Q8 ? 16 * D + 16 * (D / 32) * 2 : 16 * RB;
+  static_assert(RB % 32 == 0 && CPR <= 64 && GP <= 16, "shape");
 
   __shared__ float p_lds[2][16 * GP];  // softmax weights, [tile parity][row][head]
   __shared__ float a_lds[GP];          // per-head rescale factors
@@ -263,7 +351,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   const int kg = lane >> 4;   // which 16-byte piece of each 64 bytes
   const bool head_lane = kg < NG;  // this lane's score rows are real heads
   const int vc = lane % CPR;  // V chunk this lane owns
-  const int vr = lane / CPR;  // first V row of this lane
+  const int vr = lane / CPR;  // V row group of this lane
+  // V row held in the lane's i-th chunk
+  auto vrow = [&](int i) { return Q8 ? NV * vr + i : vr + RPI * i; };
   const size_t blk_stride = (size_t)p.kv_heads * TILE;
   int parity = 0;
 
@@ -293,19 +383,47 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     // attends over it.
     const bool app = p.k_new != nullptr && p.slots[s] >= 0;
     const char* kn_row =
-        reinterpret_cast<const char*>(p.k_new) + ((size_t)s * p.kv_heads + g) * RB;
+        reinterpret_cast<const char*>(p.k_new) + ((size_t)s * p.kv_heads + g) * QB;
     const char* vn_row =
-        reinterpret_cast<const char*>(p.v_new) + ((size_t)s * p.kv_heads + g) * RB;
+        reinterpret_cast<const char*>(p.v_new) + ((size_t)s * p.kv_heads + g) * QB;
     const int Lc = L - (app ? 1 : 0);         // rows already in the pool
     const int j1c = min(j1, (Lc + 15) >> 4);  // tiles holding cached rows
 
-    auto load_tile = [&](int blk, u32x4 (&kb)[NP], u32x4 (&vb)[NV]) {
-      const char* kt = kbase + (size_t)blk * blk_stride + t16 * RB + kg * 16;
+    auto load_tile = [&](int blk, TR& t) {
+      const char* ktile = kbase + (size_t)blk * blk_stride;
+      const char* vtile = vbase + (size_t)blk * blk_stride;
+      if constexpr (Q8) {
+        const char* kt = ktile + t16 * D + kg * 8;
 #pragma unroll
-      for (int k = 0; k < NP; ++k) kb[k] = ld16(kt + k * 64);
-      const char* vt = vbase + (size_t)blk * blk_stride + vr * RB + vc * 16;
+        for (int k = 0; k < NP; ++k) t.k[k] = ld8(kt + k * 32);
+        const char* vt = vtile + NV * vr * D + vc * 8;
 #pragma unroll
-      for (int i = 0; i < NV; ++i) vb[i] = ld16(vt + i * RPI * RB);
+        for (int i = 0; i < NV; ++i) t.v[i] = ld8(vt + i * D);
+        // scales after the 16 x D codes: K [row][group], V [group][row]
+        const char* ksp = ktile + 16 * D + t16 * NP * 2;
+        const char* vsp = vtile + 16 * D + ((vc >> 2) * 16 + NV * vr) * 2;
+        if constexpr (NP == 4) {
+          const u32x2 a = ld8(ksp);
+          t.ks[0] = a[0];
+          t.ks[1] = a[1];
+        } else {
+          t.ks[0] = ld4(ksp);
+        }
+        if constexpr (NV == 4) {
+          const u32x2 a = ld8(vsp);
+          t.vs[0] = a[0];
+          t.vs[1] = a[1];
+        } else {
+          t.vs[0] = ld4(vsp);
+        }
+      } else {
+        const char* kt = ktile + t16 * RB + kg * 16;
+#pragma unroll
+        for (int k = 0; k < NP; ++k) t.k[k] = ld16(kt + k * 64);
+        const char* vt = vtile + vr * RB + vc * 16;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) t.v[i] = ld16(vt + i * RPI * RB);
+      }
     };
 
     // q rows of the GQA group (row = head t16, zero past the group), in the
@@ -314,7 +432,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     {
       const int hq = min(t16, p.group - 1);
       const char* qr = reinterpret_cast<const char*>(p.q) +
-                       ((size_t)s * p.q_heads + (size_t)g * p.group + hq) * RB + kg * 16;
+                       ((size_t)s * p.q_heads + (size_t)g * p.group + hq) * QB + kg * 16;
 #pragma unroll
       for (int k = 0; k < NP; ++k) {
         const u32x4 v = ld16(qr + k * 64);
@@ -335,10 +453,22 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[h][e] = 0.f;
 
-    auto compute_tile = [&](int valid, const u32x4 (&kb)[NP], const u32x4 (&vb)[NV]) {
+    auto compute_tile = [&](int valid, const TR& t) {
       f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (Q8) {
+        // one MFMA per 32-code group, then that group's scale for this
+        // lane's token: sum_k d_k * (q_k . c_k)
 #pragma unroll
-      for (int k = 0; k < NP; ++k) sacc = qk_piece<DT>(qv[k], kb[k], sacc);
+        for (int k = 0; k < NP; ++k) {
+          const f32x4 r = qk_piece<DT_BF16>(qv[k], codes_to_bf16(t.k[k]), f32x4{0.f, 0.f, 0.f, 0.f});
+          const float dk = (k & 1) ? half_hi(t.ks[k >> 1]) : half_lo(t.ks[k >> 1]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sacc[i] = __builtin_fmaf(dk, r[i], sacc[i]);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < NP; ++k) sacc = qk_piece<DT>(qv[k], t.k[k], sacc);
+      }
       // sacc[i] = q(head 4*kg + i) . K(token t16)
       float s2[HPG];
       bool over = false;
@@ -379,16 +509,28 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
-        const int t = vr + RPI * i;
+        const int tr = vrow(i);
         float vals[EPC];
-        to_f32<DT>(vb[i], vals);
-        if (t >= valid) {  // rows past the context may hold anything (NaN)
+        float dv = 1.f;  // q8_0: the row's scale for this lane's group
+        if constexpr (Q8) {
+          const unsigned w0 = t.v[i][0], w1 = t.v[i][1];
 #pragma unroll
-          for (int e = 0; e < EPC; ++e) vals[e] = 0.f;
+          for (int b = 0; b < 4; ++b) {
+            vals[b] = sbyte(w0, b);
+            vals[4 + b] = sbyte(w1, b);
+          }
+          dv = (i & 1) ? half_hi(t.vs[i >> 1]) : half_lo(t.vs[i >> 1]);
+          if (tr >= valid) dv = 0.f;  // rows past the context may hold anything (NaN scales)
+        } else {
+          to_f32<DT>(t.v[i], vals);
+          if (tr >= valid) {  // rows past the context may hold anything (NaN)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) vals[e] = 0.f;
+          }
         }
         float pt[GP];
 #pragma unroll
-        for (int h = 0; h < GP; ++h) pt[h] = pl[t * GP + h];
+        for (int h = 0; h < GP; ++h) pt[h] = Q8 ? pl[tr * GP + h] * dv : pl[tr * GP + h];
 #pragma unroll
         for (int h = 0; h < GP; ++h)
 #pragma unroll
@@ -399,36 +541,90 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     for (int jb = j0; jb < j1c; jb += 64) {
       const int nb = min(64, j1c - jb);
       const int b0 = jb == j0 ? blk_first : bt_row[jb];
-      u32x4 ka[NP], va[NV], kb2[NP], vb2[NV];
-      load_tile(b0, ka, va);
+      TR ta, tb;
+      load_tile(b0, ta);
       const int my_blk = lane < nb ? bt_row[jb + lane] : 0;
       for (int jj = 0; jj < nb; jj += 2) {
-        if (jj + 1 < nb) load_tile(__builtin_amdgcn_readlane(my_blk, jj + 1), kb2, vb2);
-        compute_tile(min(16, Lc - 16 * (jb + jj)), ka, va);
+        if (jj + 1 < nb) load_tile(__builtin_amdgcn_readlane(my_blk, jj + 1), tb);
+        compute_tile(min(16, Lc - 16 * (jb + jj)), ta);
         if (jj + 1 < nb) {
-          if (jj + 2 < nb) load_tile(__builtin_amdgcn_readlane(my_blk, jj + 2), ka, va);
-          compute_tile(min(16, Lc - 16 * (jb + jj + 1)), kb2, vb2);
+          if (jj + 2 < nb) load_tile(__builtin_amdgcn_readlane(my_blk, jj + 2), ta);
+          compute_tile(min(16, Lc - 16 * (jb + jj + 1)), tb);
         }
       }
     }
     if (app && j1 == nblk) {
       // The new token: every lane loads the k_new / v_new row as row 0 of a
       // one-row tile; the lanes of row 0 store it into the pool.
-      u32x4 kn[NP], vn[NV];
-#pragma unroll
-      for (int k = 0; k < NP; ++k) kn[k] = ld16(kn_row + kg * 16 + k * 64);
-#pragma unroll
-      for (int i = 0; i < NV; ++i) vn[i] = ld16(vn_row + vc * 16);
       const int blk_last = bt_row[nblk - 1];
       const int t_new = (L - 1) & 15;
-      char* kd = const_cast<char*>(kbase) + (size_t)blk_last * blk_stride + t_new * RB;
-      char* vd = const_cast<char*>(vbase) + (size_t)blk_last * blk_stride + t_new * RB;
-      if (t16 == 0) {
+      char* ktile = const_cast<char*>(kbase) + (size_t)blk_last * blk_stride;
+      char* vtile = const_cast<char*>(vbase) + (size_t)blk_last * blk_stride;
+      TR tn;
+      if constexpr (Q8) {
+        // Quantise the bf16 row group by group (as the append kernel does):
+        // K group k is spread over the four lanes kg of a token column, a V
+        // group over four neighbouring chunks of one row.
 #pragma unroll
-        for (int k = 0; k < NP; ++k) *reinterpret_cast<u32x4*>(kd + kg * 16 + k * 64) = kn[k];
+        for (int k = 0; k < NP; ++k) {
+          float x[8];
+          to_f32<DT_BF16>(ld16(kn_row + kg * 16 + k * 64), x);
+          float a = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) a = fmaxf(a, __builtin_fabsf(x[j]));
+          a = fmaxf(a, xor_f(a, 16));
+          a = fmaxf(a, xor_f(a, 32));
+          float d;
+          tn.k[k] = q8_codes(x, a, &d);
+          const unsigned hb = half_bits(d);
+          if (k & 1) tn.ks[k >> 1] |= hb << 16;
+          else tn.ks[k >> 1] = hb;
+        }
+        {
+          float x[8];
+          to_f32<DT_BF16>(ld16(vn_row + vc * 16), x);
+          float a = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) a = fmaxf(a, __builtin_fabsf(x[j]));
+          a = fmaxf(a, xor_f(a, 1));
+          a = fmaxf(a, xor_f(a, 2));
+          float d;
+          const u32x2 c = q8_codes(x, a, &d);
+#pragma unroll
+          for (int i = 0; i < NV; ++i) tn.v[i] = c;  // only row 0 is attended
+#pragma unroll
+          for (int i = 0; i < NV / 2; ++i) tn.vs[i] = 0u;
+          tn.vs[0] = half_bits(d);
+          if (vr == 0) {
+            *reinterpret_cast<u32x2*>(vtile + t_new * D + vc * 8) = c;
+            if ((vc & 3) == 0)
+              *reinterpret_cast<unsigned short*>(vtile + 16 * D + ((vc >> 2) * 16 + t_new) * 2) =
+                  (unsigned short)tn.vs[0];
+          }
+        }
+        if (t16 == 0) {
+#pragma unroll
+          for (int k = 0; k < NP; ++k)
+            *reinterpret_cast<u32x2*>(ktile + t_new * D + kg * 8 + k * 32) = tn.k[k];
+          if (kg == 0) {
+            char* ksp = ktile + 16 * D + t_new * NP * 2;
+            if constexpr (NP == 4) *reinterpret_cast<u32x2*>(ksp) = u32x2{tn.ks[0], tn.ks[1]};
+            else *reinterpret_cast<unsigned*>(ksp) = tn.ks[0];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < NP; ++k) tn.k[k] = ld16(kn_row + kg * 16 + k * 64);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) tn.v[i] = ld16(vn_row + vc * 16);
+        if (t16 == 0) {
+#pragma unroll
+          for (int k = 0; k < NP; ++k)
+            *reinterpret_cast<u32x4*>(ktile + t_new * RB + kg * 16 + k * 64) = tn.k[k];
+        }
+        if (vr == 0) *reinterpret_cast<u32x4*>(vtile + t_new * RB + vc * 16) = tn.v[0];
       }
-      if (vr == 0) *reinterpret_cast<u32x4*>(vd + vc * 16) = vn[0];
-      compute_tile(1, kn, vn);
+      compute_tile(1, tn);
     }
 
     // Totals over the 16 rows, and over the lanes sharing a V chunk.
@@ -533,6 +729,50 @@ __global__ __launch_bounds__(256) void append_kernel(const char* k_new, const ch
   *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
 }
 
+// q8_0 append: one thread per (sequence, kv head, K|V, 32-value group) of
+// the bf16 new rows; writes 32 codes into the row and the group's fp16 scale
+// (K scales [row][group], V scales [group][row] after the tile's codes).
+template <int D>
+__global__ __launch_bounds__(256) void append_q8_kernel(const char* k_new, const char* v_new,
+                                                        const int64_t* slots, int batch,
+                                                        char* k_layer, char* v_layer,
+                                                        int kv_heads) {
+  constexpr int NGR = D / 32;
+  constexpr int TILE = 16 * D + 16 * NGR * 2;
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const int grp = (int)(idx % NGR);
+  long r = idx / NGR;
+  const int kv = (int)(r & 1);
+  r >>= 1;
+  const int g = (int)(r % kv_heads);
+  const long s = r / kv_heads;
+  if (s >= batch) return;
+  const int64_t slot = slots[s];
+  if (slot < 0) return;
+  const int64_t blk = slot >> 4;
+  const int pos = (int)(slot & 15);
+  const char* src = (kv ? v_new : k_new) + (((size_t)s * kv_heads + g) * D + grp * 32) * 2;
+  float x[4][8];
+  float a = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    to_f32<DT_BF16>(ld16(src + c * 16), x[c]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a = fmaxf(a, __builtin_fabsf(x[c][j]));
+  }
+  char* tile = (kv ? v_layer : k_layer) + ((size_t)blk * kv_heads + g) * TILE;
+  char* dst = tile + pos * D + grp * 32;
+  float d = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; c += 2) {
+    const u32x2 lo = q8_codes(x[c], a, &d);
+    const u32x2 hi = q8_codes(x[c + 1], a, &d);
+    *reinterpret_cast<u32x4*>(dst + c * 8) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+  const int si = kv ? grp * 16 + pos : pos * NGR + grp;
+  *reinterpret_cast<unsigned short*>(tile + 16 * D + si * 2) = (unsigned short)half_bits(d);
+}
+
 __global__ __launch_bounds__(256) void copy_blocks_kernel(const int32_t* pairs, int layers,
                                                           char* k_base, char* v_base,
                                                           int64_t layer_bytes,
@@ -588,6 +828,7 @@ const void* decode_kernel_for(int dtype, int d, int gp) {
     case DT_F32: return pick_d<DT_F32>(d, gp);
     case DT_F16: return pick_d<DT_F16>(d, gp);
     case DT_BF16: return pick_d<DT_BF16>(d, gp);
+    case DT_Q8: return pick_d<DT_Q8>(d, gp);
   }
   return nullptr;
 }
@@ -642,6 +883,26 @@ hipError_t launch_append(const void* k_new, const void* v_new, const int64_t* sl
                      static_cast<const char*>(k_new), static_cast<const char*>(v_new), slots,
                      batch, static_cast<char*>(k_layer), static_cast<char*>(v_layer), kv_heads,
                      row_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_q8(const void* k_new, const void* v_new, const int64_t* slots,
+                            int batch, void* k_layer, void* v_layer, int kv_heads, int head_dim,
+                            hipStream_t stream) {
+  const long threads = (long)batch * kv_heads * 2 * (head_dim / 32);
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  const char* kn = static_cast<const char*>(k_new);
+  const char* vn = static_cast<const char*>(v_new);
+  char* kl = static_cast<char*>(k_layer);
+  char* vl = static_cast<char*>(v_layer);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(append_q8_kernel<128>, grid, block, 0, stream, kn, vn, slots, batch, kl, vl,
+                       kv_heads);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL(append_q8_kernel<64>, grid, block, 0, stream, kn, vn, slots, batch, kl, vl,
+                       kv_heads);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

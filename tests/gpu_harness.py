@@ -45,8 +45,10 @@ class OracleSide:
         for layer in range(w.layers):
             kl, vl = w.layer_views(layer)
             shape = (self.nb,) + tuple(kl.shape[1:])
-            kc = torch.full(shape, float("nan"), dtype=kl.dtype)
-            vc = torch.full(shape, float("nan"), dtype=vl.dtype)
+            # unused blocks: NaN (q8_0 tiles: 0xff bytes, i.e. NaN scales)
+            fillv = 255 if kl.dtype == torch.uint8 else float("nan")
+            kc = torch.full(shape, fillv, dtype=kl.dtype)
+            vc = torch.full(shape, fillv, dtype=vl.dtype)
             if used:
                 kc[:len(used)] = kl.index_select(0, idx).cpu()
                 vc[:len(used)] = vl.index_select(0, idx).cpu()
@@ -82,7 +84,8 @@ class OracleSide:
 
 
 def gpu_logical(sess: DecodeSession, layer: int, seqs):
-    """Bytes of the sampled sequences' rows read back through the library's table."""
+    """Bytes of the sampled sequences' rows read back through the library's table
+    (q8_0: each row's codes then its scale bytes in group order)."""
     k, v = sess.w.layer_views(layer)
     res = []
     for s in seqs:
@@ -90,7 +93,13 @@ def gpu_logical(sess: DecodeSession, layer: int, seqs):
         t = torch.arange(L, device=k.device)
         blocks = torch.from_numpy(sess.table[s].astype(np.int64)).to(k.device)[t // 16]
         rows = t % 16
-        res.append((to_storage(k[blocks, :, rows, :]), to_storage(v[blocks, :, rows, :])))
+        if k.dtype == torch.uint8:
+            kt, vt = to_storage(k[blocks]), to_storage(v[blocks])
+            idx = np.arange(L)
+            res.append((ostep.q8_row_bytes(kt, idx, rows.cpu().numpy(), False),
+                        ostep.q8_row_bytes(vt, idx, rows.cpu().numpy(), True)))
+        else:
+            res.append((to_storage(k[blocks, :, rows, :]), to_storage(v[blocks, :, rows, :])))
     return res
 
 
@@ -153,6 +162,8 @@ def run_step_case(cfg, *, layers=1, partitions=(0,), sample=None, check_untouche
 def _check_untouched(w, before, slots, pairs, layers):
     """Only the appended rows and copy-on-write destination blocks may change."""
     cfg = w.cfg
+    if cfg.dtype == W.Q8_0:
+        return _check_untouched_q8(w, before, slots, pairs, layers)
     shape = (2, layers, cfg.num_blocks, cfg.kv_heads, 16, cfg.head_dim * W.ELEM_BYTES[cfg.dtype])
     a = w.pool.view(shape)
     b = before.view(shape)
@@ -165,3 +176,30 @@ def _check_untouched(w, before, slots, pairs, layers):
             allowed[:, :, int(sl) // 16, :, int(sl) % 16] = True
     bad = changed & ~allowed
     assert not bool(bad.any()), f"{int(bad.sum())} rows changed outside the written slots"
+
+
+def _check_untouched_q8(w, before, slots, pairs, layers):
+    """q8_0 form: byte by byte, only each new row's codes and scales (K scales
+    [row][group], V scales [group][row] after a tile's codes) and whole
+    copy-on-write destination tiles may change."""
+    cfg = w.cfg
+    D = cfg.head_dim
+    ng = D // 32
+    tb = W.tile_bytes(cfg)
+    shape = (2, layers, cfg.num_blocks, cfg.kv_heads, tb)
+    changed = (w.pool.view(shape) != before.view(shape))
+    allowed = torch.zeros_like(changed)
+    for dst in (int(p[1]) for p in pairs):
+        allowed[:, :, dst] = True
+    for sl in slots:
+        if sl < 0:
+            continue
+        b, r = int(sl) // 16, int(sl) % 16
+        allowed[:, :, b, :, r * D:(r + 1) * D] = True
+        for grp in range(ng):
+            ik = 16 * D + 2 * (r * ng + grp)
+            iv = 16 * D + 2 * (grp * 16 + r)
+            allowed[0, :, b, :, ik:ik + 2] = True
+            allowed[1, :, b, :, iv:iv + 2] = True
+    bad = changed & ~allowed
+    assert not bool(bad.any()), f"{int(bad.sum())} bytes changed outside the written rows"

@@ -4,9 +4,10 @@ import torch
 
 
 def to_storage(t: torch.Tensor) -> np.ndarray:
-    """Raw element storage on the host: float32 as np.float32, 16-bit types as np.uint16."""
+    """Raw element storage on the host: float32 as np.float32, 16-bit types as
+    np.uint16, bytes (q8_0 tiles) as np.uint8."""
     t = t.detach().contiguous().cpu()
-    if t.dtype == torch.float32:
+    if t.dtype in (torch.float32, torch.uint8):
         return t.numpy().copy()
     return t.view(torch.int16).numpy().view(np.uint16).copy()
 

@@ -41,6 +41,22 @@ SMALL = {
                              head_dim=128, ctx_fixed=(70, 5, 300), num_blocks=40),
     "gqa2_d64_f16": W.scaled(W.CONFIGS["mha13b_f16"], batch=4, q_heads=4, kv_heads=2,
                              head_dim=64, num_blocks=200, ctx_lo=1, ctx_hi=700),
+    # q8_0 cache: GQA 4 / 1 / 8 and 2 (head_dim 64), shared prefix with
+    # copy-on-write, long split
+    "q8_llama_small": W.scaled(W.CONFIGS["llama8b_q8"], batch=6, num_blocks=6 * 50,
+                               ctx_lo=1, ctx_hi=700),
+    "q8_mha_small": W.scaled(W.CONFIGS["llama8b_q8"], batch=5, q_heads=6, kv_heads=6,
+                             num_blocks=5 * 40, ctx_lo=16, ctx_hi=600),
+    "q8_gqa8": W.scaled(W.CONFIGS["llama8b_q8"], batch=3, q_heads=16, kv_heads=2,
+                        num_blocks=150, ctx_lo=1, ctx_hi=600),
+    "q8_gqa2_d64": W.scaled(W.CONFIGS["llama8b_q8"], batch=4, q_heads=4, kv_heads=2,
+                            head_dim=64, num_blocks=200, ctx_lo=1, ctx_hi=700),
+    "q8_len1": W.scaled(W.CONFIGS["llama8b_q8"], batch=4, q_heads=4, kv_heads=2,
+                        ctx_kind="fixed", ctx_fixed=(1, 16, 17, 33), num_blocks=40),
+    "q8_shared_cow": W.scaled(W.CONFIGS["shared_prefix_cow_bf16"], dtype=W.Q8_0, batch=5,
+                              num_blocks=200),
+    "q8_long_small": W.scaled(W.CONFIGS["long_ctx_bf16"], dtype=W.Q8_0, batch=2,
+                              ctx_fixed=(4097, 3001), num_blocks=500),
 }
 
 
@@ -63,6 +79,7 @@ FULL = [
     ("shared_prefix_bf16", 2, (0,), 24),
     ("shared_prefix_cow_bf16", 2, (0,), None),
     ("long_ctx_bf16", 1, (512, 0), None),
+    ("llama8b_q8", 2, (0, 512), None),
 ]
 
 
