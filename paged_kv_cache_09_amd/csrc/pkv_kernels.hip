@@ -323,6 +323,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   constexpr int NG = GP >= 4 ? GP / 4 : 1;  // lane groups (of 16) holding real heads
   constexpr int HPG = GP >= 4 ? 4 : GP;     // heads per lane group
   constexpr int TILE = Q8 ? 16 * D + 16 * (D / 32) * 2 : 16 * RB;
+  // Tile buffers per wave. Three or four (more bytes in flight per wave) ran
+  // slower than two on MI355X for both bf16 and q8_0 tiles.
+  constexpr int NBUF = 2;
   static_assert(RB % 32 == 0 && CPR <= 64 && GP <= 16, "shape");
 
   __shared__ float p_lds[2][16 * GP];  // softmax weights, [tile parity][row][head]
@@ -538,18 +541,26 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
       }
     };
 
+    // Tiles stream through NBUF register buffers: NBUF - 1 tiles are in
+    // flight while one is computed. Block ids come 64 at a time, one per lane.
     for (int jb = j0; jb < j1c; jb += 64) {
       const int nb = min(64, j1c - jb);
       const int b0 = jb == j0 ? blk_first : bt_row[jb];
-      TR ta, tb;
-      load_tile(b0, ta);
+      TR t[NBUF];
+      load_tile(b0, t[0]);
       const int my_blk = lane < nb ? bt_row[jb + lane] : 0;
-      for (int jj = 0; jj < nb; jj += 2) {
-        if (jj + 1 < nb) load_tile(__builtin_amdgcn_readlane(my_blk, jj + 1), tb);
-        compute_tile(min(16, Lc - 16 * (jb + jj)), ta);
-        if (jj + 1 < nb) {
-          if (jj + 2 < nb) load_tile(__builtin_amdgcn_readlane(my_blk, jj + 2), ta);
-          compute_tile(min(16, Lc - 16 * (jb + jj + 1)), tb);
+#pragma unroll
+      for (int u = 1; u < NBUF - 1; ++u)
+        if (u < nb) load_tile(__builtin_amdgcn_readlane(my_blk, u), t[u]);
+      for (int jj = 0; jj < nb; jj += NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+          const int j = jj + u;
+          if (j < nb) {
+            if (j + NBUF - 1 < nb)
+              load_tile(__builtin_amdgcn_readlane(my_blk, j + NBUF - 1), t[(u + NBUF - 1) % NBUF]);
+            compute_tile(min(16, Lc - 16 * (jb + j)), t[u]);
+          }
         }
       }
     }
