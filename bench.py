@@ -159,6 +159,9 @@ def main():
                          "exit: reference for calibrating HBM byte counters")
     ap.add_argument("--unfused", action="store_true",
                     help="kv_append and paged_attn_decode as two launches per layer")
+    ap.add_argument("--write-chunk", type=int, default=0, metavar="TOKENS",
+                    help="instead of the decode step, time the multi-token paged write of a "
+                         "prompt chunk of TOKENS tokens per sequence (prefill side)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
@@ -182,6 +185,8 @@ def main():
     from paged_kv_cache_09_amd import workloads as W
     from paged_kv_cache_09_amd.session import DecodeSession
 
+    if args.write_chunk:
+        return main_write(args)
     cfg = W.CONFIGS[args.config]
     part = cfg.partition_tokens if args.partition is None else args.partition
     growth = args.warmup + args.steps + 1
@@ -289,6 +294,70 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline")
         res["cpu_baseline"] = cpu_baseline(w)
+    sess.close()
+    print(json.dumps(res), flush=True)
+
+
+def main_write(args):
+    """Multi-token paged write (a prompt chunk per sequence, every layer): one
+    kv_append launch per layer scatters all the chunk's rows through per-token
+    slots. Bytes moved = rows read from the inputs + rows written to the pool."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_09_amd import workloads as W
+    from paged_kv_cache_09_amd.session import DecodeSession
+
+    cfg = W.CONFIGS[args.config]
+    chunk = args.write_chunk
+    cfg = W.scaled(cfg, num_blocks=cfg.num_blocks + cfg.batch * ((chunk + 15) // 16 + 1))
+    log(f"building {cfg.name}: {cfg.layers} layers, write chunk {chunk}")
+    w = W.make(cfg, device="cuda", layers=cfg.layers, form="step", fill="random",
+               extra_blocks=(chunk + 15) // 16 + 1)
+    before_ctx, _, k_rows, v_rows = W.write_rows(w, chunk, chunk)
+    n_new = np.full(w.B, chunk, dtype=np.int32)
+    sess = DecodeSession(w)
+    slots, pairs = sess.prepare_write(before_ctx, n_new)
+    t_host = sess.last_prepare_s
+    sess.copy_blocks()
+    rows = int(n_new.sum())
+    in_bytes = rows * 2 * cfg.kv_heads * cfg.head_dim * W.TORCH_DTYPE[cfg.dtype].itemsize
+    out_bytes = rows * 2 * cfg.kv_heads * W.row_bytes(cfg)
+    layers = list(range(cfg.layers))
+    stream = torch.cuda.current_stream()
+    for _ in range(max(1, args.warmup)):
+        for layer in layers:
+            sess.write(layer, k_rows, v_rows)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        for layer in layers:  # rewriting the same rows is idempotent
+            sess.write(layer, k_rows, v_rows)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch = e0.elapsed_time(e1) / 1e3 / (args.steps * len(layers))
+    achieved = (in_bytes + out_bytes) / per_launch / 1e9
+    res = {
+        "metric": "paged KV multi-token write GB/s (prefill chunk)",
+        "value": round((in_bytes + out_bytes) * len(layers) * args.steps / wall / 1e9, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": W.DTYPE_NAME[cfg.dtype],
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.layers} layers x batch {cfg.batch}, "
+                               f"{chunk} new tokens per sequence behind "
+                               f"{int(before_ctx.min())}..{int(before_ctx.max())} cached",
+                   "rows_per_layer": rows, "block_size": 16},
+        "host_prepare_write_ms": round(t_host * 1e3, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "append kernel, one launch per layer",
+                     "avg_launch_us": round(per_launch * 1e6, 3),
+                     "algorithmic_bytes_per_launch": in_bytes + out_bytes},
+    }
     sess.close()
     print(json.dumps(res), flush=True)
 

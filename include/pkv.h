@@ -160,6 +160,26 @@ int pkv_prepare_append(pkv_pool* pool, int32_t* host_bt, int batch, int max_bloc
                        int cow_capacity, int* n_cow);
 
 /*
+ * Slot assignment for writing several tokens per sequence, e.g. a prompt or a
+ * chunk of one in prefill, whose K/V rows are all written to the cache
+ * (news.hamidun.com "KV-Cache", prefill/decode paragraph). Sequence s writes
+ * n_new[s] >= 0 tokens at logical positions ctx_before[s] ..
+ * ctx_before[s] + n_new[s] - 1. In batch order, every block index j those
+ * positions touch is handled once as pkv_prepare_append handles its one
+ * block: absent -> a free block is taken; shared -> copy-on-write pair;
+ * otherwise in place. slot_out (capacity slot_capacity) receives
+ * sum(n_new) int64 slots, sequence by sequence in position order:
+ * host_bt[s][p / block_size] * block_size + p % block_size. The slots are
+ * distinct and can be passed (on the device) to pkv_kv_append as its
+ * per-row slots. pkv_prepare_append is the case n_new = 1,
+ * ctx_before = ctx_lens - 1. All-or-nothing, as pkv_prepare_append.
+ */
+int pkv_prepare_write(pkv_pool* pool, int32_t* host_bt, int batch, int max_blocks,
+                      const int32_t* ctx_before, const int32_t* n_new, int64_t* slot_out,
+                      int64_t slot_capacity, int32_t* cow_pairs_out, int cow_capacity,
+                      int* n_cow);
+
+/*
  * Upload the block table int32 [batch][max_blocks] (-1 padded), the context
  * lengths int32 [batch] and optionally the slots int64 [batch] (NULL: keep
  * none) to the library's device copies, asynchronously on `stream`: the
@@ -191,7 +211,10 @@ int pkv_copy_blocks(pkv_pool* pool, const int32_t* host_pairs, int n, uintptr_t 
  * into the pool row of layer `layer` at slot[s] (block slot/16, row
  * slot%16); slot < 0 skips. dev_slots: device int64 [batch], or NULL for the
  * slots of the last upload (batch must then equal the uploaded batch). Bytes
- * are copied unchanged (q8_0: quantised as described above).
+ * are copied unchanged (q8_0: quantised as described above). With device
+ * slots, "batch" is any number of rows: the multi-token write of a prefill
+ * passes one row and one slot (from pkv_prepare_write) per token; the slots
+ * must be distinct.
  */
 int pkv_kv_append(pkv_pool* pool, int layer, const void* k_new, const void* v_new,
                   const int64_t* dev_slots, int batch, uintptr_t stream);

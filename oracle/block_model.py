@@ -21,9 +21,14 @@ new token at logical position p = L_s - 1, logical block j = p // block_size:
               copy the old one into it, drop one reference to the old one;
   - "inplace" the block is referenced exactly once: write it in place.
 
+A multi-token write (a prompt, or a chunk of one, whose K/V rows are all
+written to the cache: news.hamidun.com "KV-Cache", prefill/decode paragraph)
+applies the same three rules to every logical block its positions touch,
+block by block, sequences in batch order.
+
 Which free block is taken is not unique, so the model tracks only what is:
-the kind per sequence, the reference count of every pre-existing block after
-the step, and how many blocks are free afterwards.
+the kind per sequence (or per touched block), the reference count of every
+pre-existing block after the step, and how many blocks are free afterwards.
 """
 
 
@@ -77,3 +82,27 @@ class BlockModel:
             else:
                 kinds.append("inplace")
         return kinds
+
+    def plan_write(self, tables, ctx_before, n_new, block_size: int = 16):
+        """Kinds per touched block for writing n_new[s] tokens after ctx_before[s]:
+        a list of (sequence, logical block, kind); updates the model in place."""
+        plan = []
+        for s, (l0, n) in enumerate(zip(ctx_before, n_new)):
+            if n <= 0:
+                continue
+            first = l0 // block_size
+            last = (l0 + n - 1) // block_size
+            row_blocks = tables[s]
+            for j in range(first, last + 1):
+                if j >= len(row_blocks) or row_blocks[j] < 0:
+                    plan.append((s, j, "new"))
+                    self.anonymous += 1
+                    continue
+                b = row_blocks[j]
+                if self.refcount[b] > 1:
+                    plan.append((s, j, "cow"))
+                    self.refcount[b] -= 1
+                    self.anonymous += 1
+                else:
+                    plan.append((s, j, "inplace"))
+        return plan

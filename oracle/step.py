@@ -53,6 +53,47 @@ def run_step(k_layers, v_layers, pre_tables, shared, ctx, k_new_layers, v_new_la
     return table, kinds
 
 
+def run_write(k_layers, v_layers, pre_tables, shared, ctx_before, n_new, k_rows_layers,
+              v_rows_layers, *, dtype, num_blocks, max_blocks):
+    """Write n_new[s] tokens per sequence after ctx_before[s] cached ones into host
+    pools (every layer), the oracle's own block placement.
+
+    k_rows_layers / v_rows_layers: per-layer rows [sum n_new][Hkv][D], sequence by
+    sequence in position order. Returns (post_table int32 [B][max_blocks], plan).
+    """
+    model = BlockModel(num_blocks)
+    used = sorted({b for row in pre_tables for b in row})
+    model.claim(used)
+    for b, rc in shared:
+        model.ref([b] * (rc - 1))
+    plan = model.plan_write(pre_tables, ctx_before, n_new)
+    free_ids = iter(sorted(set(range(num_blocks)) - set(used)))
+    B = len(pre_tables)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    for s, row in enumerate(pre_tables):
+        table[s, :len(row)] = row
+    for s, j, kind in plan:
+        if kind == "new":
+            table[s, j] = next(free_ids)
+        elif kind == "cow":
+            src = int(table[s, j])
+            dst = next(free_ids)
+            for kl, vl in zip(k_layers, v_layers):
+                kl[dst] = kl[src]
+                vl[dst] = vl[src]
+            table[s, j] = dst
+    # token t of every sequence that has one, written as a one-token append
+    offsets = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int64)
+    for t in range(int(max(n_new)) if len(n_new) else 0):
+        has = np.array([t < n for n in n_new])
+        ctx = np.where(has, np.asarray(ctx_before) + t + 1, 0).astype(np.int32)
+        rows = np.where(has, offsets[:-1] + t, 0)
+        for kl, vl, kr, vr in zip(k_layers, v_layers, k_rows_layers, v_rows_layers):
+            oracle.append(kl, vl, table, ctx, np.ascontiguousarray(kr[rows]),
+                          np.ascontiguousarray(vr[rows]), dtype=dtype)
+    return table, plan
+
+
 def q8_row_bytes(pool, blocks, rows, is_v):
     """Bytes of q8_0 rows as [n][Hkv][D codes + 2 * D/32 scale bytes], scales in group
     order. A tile is 16 x D int8 codes, then fp16 scales ordered [row][group]

@@ -466,13 +466,19 @@ int pkv_block_refcount(const pkv_pool* p, int32_t id) {
   return p->refcount[id];
 }
 
-int pkv_prepare_append(pkv_pool* p, int32_t* bt, int batch, int max_blocks,
-                       const int32_t* ctx, int64_t* slot_out, int32_t* cow_out,
-                       int cow_capacity, int* n_cow) {
-  if (!p || !bt || !ctx || !slot_out || !n_cow || batch < 1 || max_blocks < 1)
-    return fail(PKV_EINVAL, "bad arguments");
-  if (batch > p->shape.max_seqs)
-    return fail(PKV_EINVAL, "batch %d exceeds max_seqs %d", batch, p->shape.max_seqs);
+namespace {
+
+// Slot assignment for n_new[s] consecutive tokens of each sequence s at
+// logical positions ctx_before[s] .. ctx_before[s] + n_new[s] - 1, in batch
+// order. Each block index the tokens touch is taken on demand when absent,
+// copied first when shared (refcount > 1), else written in place
+// (thienlv.com, "PagedAttention là gì?", "How does PagedAttention work?";
+// ahmedhaies.com, "PagedAttention: why LLM serving wastes most GPU memory",
+// copy-on-write paragraph). All-or-nothing: a failure undoes every change.
+int prepare_core(pkv_pool* p, int32_t* bt, int batch, int max_blocks, const int32_t* ctx_before,
+                 const int32_t* n_new, int64_t* slot_out, int64_t slot_capacity,
+                 int32_t* cow_out, int cow_capacity, int* n_cow) {
+  const int BS = p->shape.block_size;
   struct Undo {
     int64_t entry;
     int32_t old;
@@ -480,6 +486,7 @@ int pkv_prepare_append(pkv_pool* p, int32_t* bt, int batch, int max_blocks,
   std::vector<Undo> undo;
   std::vector<int32_t> taken, unref;
   int ncow = 0;
+  int64_t nslot = 0;
   auto rollback = [&]() {
     for (auto it = undo.rbegin(); it != undo.rend(); ++it) bt[it->entry] = it->old;
     for (int32_t id : taken) {
@@ -489,57 +496,99 @@ int pkv_prepare_append(pkv_pool* p, int32_t* bt, int batch, int max_blocks,
     for (int32_t id : unref) ++p->refcount[id];
   };
   for (int s = 0; s < batch; ++s) {
-    const int32_t L = ctx[s];
-    if (L < 1 || L > p->shape.max_seq_len || nblk(L) > max_blocks) {
+    const int64_t L0 = ctx_before[s], n = n_new[s], L1 = L0 + n;
+    if (L0 < 0 || n < 0 || L1 > p->shape.max_seq_len || (L1 + BS - 1) / BS > max_blocks) {
       rollback();
-      return fail(PKV_EINVAL, "sequence %d: context length %d outside [1, %d]", s, L,
-                  std::min<int64_t>(p->shape.max_seq_len, (int64_t)max_blocks * pkv::kBlock));
+      return fail(PKV_EINVAL, "sequence %d: tokens [%lld, %lld) outside [0, %lld)", s,
+                  (long long)L0, (long long)L1,
+                  (long long)std::min<int64_t>(p->shape.max_seq_len, (int64_t)max_blocks * BS));
     }
-    const int32_t pos = L - 1;
-    const int64_t e = (int64_t)s * max_blocks + pos / pkv::kBlock;
-    int32_t b = bt[e];
-    if (b < 0) {
-      if (p->free_list.empty()) {
-        rollback();
-        return fail(PKV_EOUT_OF_BLOCKS, "no free block for sequence %d", s);
-      }
-      const int32_t nb = free_pop(p);
-      p->refcount[nb] = 1;
-      taken.push_back(nb);
-      undo.push_back({e, b});
-      bt[e] = nb;
-      b = nb;
-    } else {
-      if (b >= p->shape.num_blocks || p->refcount[b] < 1) {
-        rollback();
-        return fail(PKV_EINVAL, "sequence %d: table entry %d is not an allocated block", s, b);
-      }
-      if (p->refcount[b] > 1) {
-        if (!cow_out || ncow >= cow_capacity) {
-          rollback();
-          return fail(PKV_EINVAL, "copy-on-write pair buffer too small (%d)", cow_capacity);
-        }
+    if (nslot + n > slot_capacity) {
+      rollback();
+      return fail(PKV_EINVAL, "slot buffer too small (%lld)", (long long)slot_capacity);
+    }
+    if (n == 0) continue;
+    for (int64_t jb = L0 / BS; jb <= (L1 - 1) / BS; ++jb) {
+      const int64_t e = (int64_t)s * max_blocks + jb;
+      int32_t b = bt[e];
+      if (b < 0) {
         if (p->free_list.empty()) {
           rollback();
-          return fail(PKV_EOUT_OF_BLOCKS, "no free block for copy-on-write of sequence %d", s);
+          return fail(PKV_EOUT_OF_BLOCKS, "no free block for sequence %d", s);
         }
         const int32_t nb = free_pop(p);
         p->refcount[nb] = 1;
         taken.push_back(nb);
-        --p->refcount[b];
-        unref.push_back(b);
         undo.push_back({e, b});
-        cow_out[2 * ncow] = b;
-        cow_out[2 * ncow + 1] = nb;
-        ++ncow;
         bt[e] = nb;
         b = nb;
+      } else {
+        if (b >= p->shape.num_blocks || p->refcount[b] < 1) {
+          rollback();
+          return fail(PKV_EINVAL, "sequence %d: table entry %d is not an allocated block", s, b);
+        }
+        if (p->refcount[b] > 1) {
+          if (!cow_out || ncow >= cow_capacity) {
+            rollback();
+            return fail(PKV_EINVAL, "copy-on-write pair buffer too small (%d)", cow_capacity);
+          }
+          if (p->free_list.empty()) {
+            rollback();
+            return fail(PKV_EOUT_OF_BLOCKS, "no free block for copy-on-write of sequence %d", s);
+          }
+          const int32_t nb = free_pop(p);
+          p->refcount[nb] = 1;
+          taken.push_back(nb);
+          --p->refcount[b];
+          unref.push_back(b);
+          undo.push_back({e, b});
+          cow_out[2 * ncow] = b;
+          cow_out[2 * ncow + 1] = nb;
+          ++ncow;
+          bt[e] = nb;
+        }
       }
     }
-    slot_out[s] = (int64_t)b * pkv::kBlock + pos % pkv::kBlock;
+    for (int64_t pos = L0; pos < L1; ++pos)
+      slot_out[nslot++] = (int64_t)bt[(int64_t)s * max_blocks + pos / BS] * BS + pos % BS;
   }
   *n_cow = ncow;
   return PKV_OK;
+}
+
+}  // namespace
+
+int pkv_prepare_write(pkv_pool* p, int32_t* bt, int batch, int max_blocks,
+                      const int32_t* ctx_before, const int32_t* n_new, int64_t* slot_out,
+                      int64_t slot_capacity, int32_t* cow_out, int cow_capacity, int* n_cow) {
+  if (!p || !bt || !ctx_before || !n_new || !n_cow || batch < 1 || max_blocks < 1 ||
+      slot_capacity < 0 || (slot_capacity > 0 && !slot_out))
+    return fail(PKV_EINVAL, "bad arguments");
+  if (max_blocks > p->max_blocks_per_seq)
+    return fail(PKV_EINVAL, "table width %d exceeds %d blocks (max_seq_len %d)", max_blocks,
+                p->max_blocks_per_seq, p->shape.max_seq_len);
+  return prepare_core(p, bt, batch, max_blocks, ctx_before, n_new, slot_out, slot_capacity,
+                      cow_out, cow_capacity, n_cow);
+}
+
+int pkv_prepare_append(pkv_pool* p, int32_t* bt, int batch, int max_blocks,
+                       const int32_t* ctx, int64_t* slot_out, int32_t* cow_out,
+                       int cow_capacity, int* n_cow) {
+  if (!p || !bt || !ctx || !slot_out || !n_cow || batch < 1 || max_blocks < 1)
+    return fail(PKV_EINVAL, "bad arguments");
+  if (batch > p->shape.max_seqs)
+    return fail(PKV_EINVAL, "batch %d exceeds max_seqs %d", batch, p->shape.max_seqs);
+  std::vector<int32_t> before(batch), one(batch, 1);
+  for (int s = 0; s < batch; ++s) {
+    if (ctx[s] < 1 || ctx[s] > p->shape.max_seq_len ||
+        nblk(ctx[s]) > max_blocks)
+      return fail(PKV_EINVAL, "sequence %d: context length %d outside [1, %d]", s, ctx[s],
+                  std::min<int64_t>(p->shape.max_seq_len,
+                                    (int64_t)max_blocks * p->shape.block_size));
+    before[s] = ctx[s] - 1;
+  }
+  return prepare_core(p, bt, batch, max_blocks, before.data(), one.data(), slot_out, batch,
+                      cow_out, cow_capacity, n_cow);
 }
 
 int pkv_block_table_upload(pkv_pool* p, const int32_t* bt, int batch, int max_blocks,

@@ -52,6 +52,8 @@ _SIGS = {
     "pkv_block_free": (_I, [_P, _P, _I]),
     "pkv_block_refcount": (_I, [_P, ctypes.c_int32]),
     "pkv_prepare_append": (_I, [_P, _P, _I, _I, _P, _P, _P, _I, ctypes.POINTER(_I)]),
+    "pkv_prepare_write": (_I, [_P, _P, _I, _I, _P, _P, _P, ctypes.c_int64, _P, _I,
+                               ctypes.POINTER(_I)]),
     "pkv_block_table_upload": (_I, [_P, _P, _I, _I, _P, _P, _U]),
     "pkv_copy_blocks": (_I, [_P, _P, _I, _U]),
     "pkv_kv_append": (_I, [_P, _I, _P, _P, _P, _I, _U]),
@@ -157,6 +159,26 @@ def prepare_append(pool, block_table: np.ndarray, ctx_lens):
     _check(_lib.pkv_prepare_append(pool, _addr(block_table), B, mb, _addr(ctx), _addr(slots),
                                    _addr(pairs), B, ctypes.byref(n)))
     return slots, pairs[:n.value].copy()
+
+
+def prepare_write(pool, block_table: np.ndarray, ctx_before, n_new):
+    """Slots for n_new[s] tokens per sequence after ctx_before[s] cached ones;
+    ``block_table`` (int32 [B][max_blocks]) is updated in place.
+
+    Returns (slots int64 [sum n_new], cow_pairs int32 [n][2]).
+    """
+    if block_table.dtype != np.int32 or not block_table.flags["C_CONTIGUOUS"]:
+        raise TypeError("block_table must be a C-contiguous int32 array (updated in place)")
+    before = _np(ctx_before, np.int32)
+    nn = _np(n_new, np.int32)
+    B, mb = block_table.shape
+    total = int(nn.astype(np.int64).sum())
+    slots = np.zeros(max(total, 1), dtype=np.int64)
+    pairs = np.zeros((B, 2), dtype=np.int32)
+    n = _I(0)
+    _check(_lib.pkv_prepare_write(pool, _addr(block_table), B, mb, _addr(before), _addr(nn),
+                                  _addr(slots), total, _addr(pairs), B, ctypes.byref(n)))
+    return slots[:total].copy(), pairs[:n.value].copy()
 
 
 def block_table_upload(pool, block_table, ctx_lens, slots=None, stream: int = 0) -> None:

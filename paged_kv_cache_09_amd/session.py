@@ -10,9 +10,14 @@ the order of one decode step:
   a4 ``append``       new K/V rows of one layer
   a5-a9 ``decode``    paged attention of one layer (+ reduce when split)
 
+and, for a multi-token write (a prompt chunk), ``prepare_write`` then ``write``
+per layer.
+
 No arithmetic of the method happens here.
 """
 from __future__ import annotations
+
+import time
 
 import numpy as np
 import torch
@@ -52,6 +57,22 @@ class DecodeSession:
     def prepare(self):
         self.slots, self.pairs = pkv.prepare_append(self.pool, self.table, self.ctx)
         return self.slots, self.pairs
+
+    def prepare_write(self, ctx_before, n_new):
+        """Slots for a multi-token write (prefill chunk) of n_new[s] tokens after
+        ctx_before[s]; afterwards the session's lengths are ctx_before + n_new."""
+        t0 = time.perf_counter()
+        slots, self.pairs = pkv.prepare_write(self.pool, self.table, ctx_before, n_new)
+        self.last_prepare_s = time.perf_counter() - t0  # host slot assignment alone
+        self.ctx = np.array(np.asarray(ctx_before) + np.asarray(n_new), dtype=np.int32)
+        self.slots = None
+        self.write_slots = torch.from_numpy(slots).to(self.w.pool.device)
+        return slots, self.pairs
+
+    def write(self, layer: int, k_rows: torch.Tensor, v_rows: torch.Tensor):
+        """The rows of the last prepare_write into one layer (one row per slot)."""
+        pkv.kv_append(self.pool, layer, k_rows, v_rows, self.write_slots,
+                      int(self.write_slots.numel()), self.stream)
 
     def upload(self, with_slots: bool = True):
         pkv.block_table_upload(self.pool, self.table, self.ctx,

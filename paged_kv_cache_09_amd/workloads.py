@@ -336,6 +336,29 @@ def make(cfg: Config, *, device="cpu", layers: int | None = None, form: str = "s
                     k_new, v_new, form)
 
 
+def write_rows(w: Workload, n_lo: int, n_hi: int, device=None):
+    """Rows for a multi-token write after a step-form workload's cached tokens:
+    n_new[s] uniform in [n_lo, n_hi] tokens per sequence (a prompt chunk), and
+    their K/V rows [sum n_new][Hkv][D] (input dtype, N(0, sigma)).
+
+    Returns (ctx_before int32 [B] = ctx - 1, n_new int32 [B], k_rows, v_rows).
+    """
+    cfg = w.cfg
+    rng = _children(cfg.seed, 4)[3]
+    n_new = rng.integers(n_lo, n_hi + 1, size=w.B).astype(np.int32)
+    total = int(n_new.sum())
+    dev = device if device is not None else (w.pool.device if w.pool is not None else "cpu")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(int(rng.integers(0, 2**62)))
+    shape = (max(total, 1), cfg.kv_heads, cfg.head_dim)
+    k_rows = torch.empty(shape, dtype=TORCH_DTYPE[cfg.dtype], device=dev)
+    v_rows = torch.empty(shape, dtype=TORCH_DTYPE[cfg.dtype], device=dev)
+    _fill_normal(k_rows, cfg.sigma, gen)
+    _fill_normal(v_rows, cfg.sigma, gen)
+    return (np.ascontiguousarray(w.ctx - 1, dtype=np.int32), n_new, k_rows[:total],
+            v_rows[:total])
+
+
 def attn_scale(cfg: Config) -> float:
     """Softmax scale passed to both sides: 1/sqrt(head_dim) for every shape."""
     return 1.0 / math.sqrt(cfg.head_dim)

@@ -203,3 +203,54 @@ def _check_untouched_q8(w, before, slots, pairs, layers):
             allowed[1, :, b, :, iv:iv + 2] = True
     bad = changed & ~allowed
     assert not bool(bad.any()), f"{int(bad.sum())} bytes changed outside the written rows"
+
+
+def run_write_case(cfg, n_lo, n_hi, *, layers=2, partitions=(0, 48, 1 << 20), label=""):
+    """Multi-token write (prefill chunk) of every layer, then decode; against the oracle."""
+    say(f"write case {label}: build workload B={cfg.batch} layers={layers}")
+    w = W.make(cfg, device="cuda", layers=layers, form="step", fill="nan",
+               extra_blocks=(n_hi + 15) // 16 + 1)
+    before_ctx, n_new, k_rows, v_rows = W.write_rows(w, n_lo, n_hi)
+    after_ctx = before_ctx + n_new
+    ks, vs = [], []
+    for layer in range(layers):
+        kl, vl = w.layer_views(layer)
+        ks.append(to_storage(kl))
+        vs.append(to_storage(vl))
+    kr, vr = to_storage(k_rows), to_storage(v_rows)
+    say(f"write case {label}: oracle, {int(n_new.sum())} rows")
+    table_o, _ = ostep.run_write(ks, vs, w.pre_tables, w.shared, before_ctx, n_new,
+                                 [kr] * layers, [vr] * layers, dtype=cfg.dtype,
+                                 num_blocks=cfg.num_blocks, max_blocks=w.max_blocks)
+    q = to_storage(w.q)
+    ora_out = [oracle.decode(ks[l], vs[l], table_o, after_ctx, q, W.attn_scale(cfg),
+                             dtype=cfg.dtype) for l in range(layers)]
+    before = w.pool.clone()
+    sess = DecodeSession(w)
+    say(f"write case {label}: GPU write + decode partitions={list(partitions)}")
+    slots, pairs = sess.prepare_write(before_ctx, n_new)
+    sess.copy_blocks()
+    for layer in range(layers):
+        sess.write(layer, k_rows, v_rows)
+    sess.upload(with_slots=False)
+    errs = {}
+    for layer in range(layers):
+        for part in partitions:
+            out = sess.new_out()
+            out.fill_(float("nan"))
+            sess.decode(layer, out, part)
+            torch.cuda.synchronize()
+            got = out.cpu().numpy()
+            assert np.isfinite(got).all(), f"non-finite output layer {layer} partition {part}"
+            errs[(layer, part)] = float(np.max(np.abs(got - ora_out[layer])))
+    say(f"write case {label}: max errors {errs}")
+    seqs = list(range(w.B))
+    for layer in range(layers):
+        mine = gpu_logical(sess, layer, seqs)
+        theirs = ostep.logical_rows(ks[layer], vs[layer], table_o, after_ctx)
+        for s in seqs:
+            assert mine[s][0].tobytes() == theirs[s][0].tobytes(), f"K rows of seq {s} layer {layer}"
+            assert mine[s][1].tobytes() == theirs[s][1].tobytes(), f"V rows of seq {s} layer {layer}"
+    _check_untouched(w, before, slots, pairs, layers)
+    sess.close()
+    return errs

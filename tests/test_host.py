@@ -248,3 +248,87 @@ def test_workspace_size_positive():
     assert pkv.decode_workspace_bytes(h, 4, 4, 512) > 0
     assert pkv.decode_workspace_bytes(h, 4, 3, 0) == 0  # 3 q heads over 2 kv heads
     pkv.kv_pool_free(h)
+
+
+# --------------------------------------------------------------- multi-token writes
+
+@pytest.mark.parametrize("name,changes,n_lo,n_hi", [
+    ("llama8b_bf16", dict(batch=16, num_blocks=16 * 190), 0, 700),
+    ("mha13b_f16", dict(batch=24, num_blocks=24 * 150), 1, 40),
+    ("shared_prefix_cow_bf16", dict(batch=16, num_blocks=64 + 16 * 30), 1, 300),
+    ("shared_prefix_bf16", dict(batch=16, num_blocks=64 + 16 * 50), 0, 33),
+    ("tiny_f32", dict(num_blocks=64), 1, 17),
+])
+def test_prepare_write_agrees_with_block_model(name, changes, n_lo, n_hi):
+    cfg = W.scaled(W.CONFIGS[name], **changes)
+    w = W.make(cfg, layers=1, form="step", tensors=False, extra_blocks=50)
+    before_ctx, n_new, _, _ = W.write_rows(w, n_lo, n_hi)
+    h = _session_state(w)
+    free0 = pkv.pool_stats(h)["free"]
+    table = np.ascontiguousarray(w.table("pre"))
+    before = table.copy()
+    slots, pairs = pkv.prepare_write(h, table, before_ctx, n_new)
+
+    model = BlockModel(cfg.num_blocks)
+    model.claim(w.allocated_ids("pre"))
+    for b, rc in w.shared:
+        model.ref([b] * (rc - 1))
+    plan = model.plan_write(w.pre_tables, before_ctx, n_new)
+
+    # slots: sequence by sequence, each position at its table block and row
+    assert len(slots) == int(n_new.sum())
+    k = 0
+    for s in range(w.B):
+        for pos in range(int(before_ctx[s]), int(before_ctx[s] + n_new[s])):
+            assert slots[k] // 16 == table[s, pos // 16] and slots[k] % 16 == pos % 16
+            k += 1
+    assert len(set(slots.tolist())) == len(slots)
+    touched = {(s, j) for s, j, _ in plan}
+    new_ids, cow_map = [], {}
+    for s, j, kind in plan:
+        if kind == "inplace":
+            assert table[s, j] == before[s, j]
+        else:
+            assert table[s, j] != before[s, j]
+            new_ids.append(int(table[s, j]))
+            if kind == "cow":
+                cow_map[int(table[s, j])] = int(before[s, j])
+    for s in range(w.B):
+        for j in range(table.shape[1]):
+            if (s, j) not in touched:
+                assert table[s, j] == before[s, j]
+    assert len(set(new_ids)) == len(new_ids)
+    assert not set(new_ids) & set(w.allocated_ids("pre"))
+    assert {(int(a), int(b)) for a, b in pairs} == {(src, dst) for dst, src in cow_map.items()}
+    assert pkv.pool_stats(h)["free"] == free0 - len(new_ids) == model.free_count()
+    for b in w.allocated_ids("pre"):
+        assert pkv.block_refcount(h, b) == model.refcount[b]
+    pkv.kv_pool_free(h)
+
+
+def test_prepare_write_of_one_token_is_prepare_append():
+    cfg = W.scaled(W.CONFIGS["shared_prefix_cow_bf16"], batch=16, num_blocks=64 + 40)
+    w = W.make(cfg, layers=1, form="step", tensors=False)
+    h1, h2 = _session_state(w), _session_state(w)
+    t1 = np.ascontiguousarray(w.table("pre"))
+    t2 = t1.copy()
+    s1, p1 = pkv.prepare_append(h1, t1, w.ctx)
+    s2, p2 = pkv.prepare_write(h2, t2, w.ctx - 1, np.ones(w.B, np.int32))
+    assert np.array_equal(s1, s2) and np.array_equal(p1, p2) and np.array_equal(t1, t2)
+    pkv.kv_pool_free(h1)
+    pkv.kv_pool_free(h2)
+
+
+def test_prepare_write_rolls_back_and_checks_capacity():
+    h = host_pool(num_blocks=6, max_seq_len=64, max_seqs=2)
+    table = np.full((2, 4), -1, np.int32)
+    with pytest.raises(pkv.PkvError) as e:  # 4 + 3 blocks > 6
+        pkv.prepare_write(h, table, [0, 0], [64, 40])
+    assert e.value.code == pkv.EOUT_OF_BLOCKS
+    assert (table == -1).all() and pkv.pool_stats(h)["free"] == 6
+    with pytest.raises(pkv.PkvError):  # past max_seq_len
+        pkv.prepare_write(h, table, [60, 0], [5, 1])
+    slots, pairs = pkv.prepare_write(h, table, [0, 0], [20, 0])
+    assert slots.tolist() == [table[0, 0] * 16 + i for i in range(16)] + \
+        [table[0, 1] * 16 + i for i in range(4)] and len(pairs) == 0
+    pkv.kv_pool_free(h)
