@@ -159,6 +159,10 @@ def main():
                          "exit: reference for calibrating HBM byte counters")
     ap.add_argument("--unfused", action="store_true",
                     help="kv_append and paged_attn_decode as two launches per layer")
+    ap.add_argument("--request-stream", type=int, default=0, metavar="STEPS",
+                    help="instead of the decode step, run the block manager under a synthetic "
+                         "request stream of STEPS scheduler steps (host only) and report "
+                         "paged vs contiguous waste")
     ap.add_argument("--write-chunk", type=int, default=0, metavar="TOKENS",
                     help="instead of the decode step, time the multi-token paged write of a "
                          "prompt chunk of TOKENS tokens per sequence (prefill side)")
@@ -168,6 +172,25 @@ def main():
               "multi-GPU path; see DESIGN.md for how the decode path would shard.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.request_stream:
+        from paged_kv_cache_09_amd import stream as S
+        cfg = S.StreamConfig(steps=args.request_stream)
+        sim = S.PagedStream(cfg)
+        t0 = time.perf_counter()
+        summary = sim.run(S.draw_requests(cfg))
+        wall = time.perf_counter() - t0
+        sim.close()
+        print(json.dumps({"metric": "KV waste under a request stream (host block manager)",
+                          "value": summary["paged_waste_pct"], "unit": "% of allocated slots",
+                          "higher_is_better": False, "data": "synthetic",
+                          "config": {"workload": f"Poisson arrivals {cfg.arrival_rate}/step, "
+                                                 f"prompt U[{cfg.prompt_lo},{cfg.prompt_hi}], "
+                                                 f"output U[{cfg.output_lo},{cfg.output_hi}], "
+                                                 f"{cfg.num_blocks} blocks of {cfg.block_size}, "
+                                                 f"max_seq_len {cfg.max_seq_len}"},
+                          "wall_s": round(wall, 3), **summary}), flush=True)
+        return
 
     import numpy as np
     import torch
