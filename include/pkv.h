@@ -262,7 +262,39 @@ size_t pkv_decode_workspace_bytes(const pkv_pool* pool, int batch, int q_heads,
                                   int partition_tokens);
 
 /*
- * stats_out[0] free blocks, [1] allocated blocks, [2] blocks with refcount > 1,
+ * Automatic prefix caching (ahmedhaies.com, "PagedAttention: why LLM serving
+ * wastes most GPU memory", the enable-prefix-caching flag and the prefix
+ * caching trade-off; thienlv.com, "PagedAttention là gì?", "Sharing";
+ * ssdnodes.com, "KV cache vs prompt cache", "When local and remote caching
+ * intersect"): a full block's K/V depend on every token up to its end, so a
+ * block is keyed by its token ids together with the key of the block before
+ * it (a chained FNV-1a 64-bit hash, confirmed by comparing the stored token
+ * ids). Cached blocks whose last reference is released stay reusable
+ * ("evictable") instead of returning to the free list; when the free list is
+ * empty, allocation takes the least recently released evictable block and
+ * drops its cache entry. Writing into a cached block held by one sequence
+ * drops its entry (its content changes).
+ *
+ * pkv_prefix_match: walk the full blocks of tokens[0 .. n_tokens) from the
+ * start and return how many leading blocks (at most max_ids) are cached;
+ * their ids go to ids_out and each gains one reference (the caller puts them
+ * at the front of the sequence's table and writes only the remaining tokens).
+ * pkv_prefix_insert: register the full blocks of a sequence whose first
+ * n_tokens tokens are written, bt_row[0 .. n_entries) being its table row;
+ * blocks already cached, or whose content is already cached in another
+ * block, are skipped. Returns the number of blocks added.
+ * pkv_prefix_stats: stats_out[0] cached blocks, [1] of them evictable,
+ * [2] blocks matched so far, [3] evictions so far.
+ */
+int pkv_prefix_match(pkv_pool* pool, const int32_t* tokens, int n_tokens, int32_t* ids_out,
+                     int max_ids);
+int pkv_prefix_insert(pkv_pool* pool, const int32_t* tokens, int n_tokens,
+                      const int32_t* bt_row, int n_entries);
+int pkv_prefix_stats(const pkv_pool* pool, int64_t stats_out[4]);
+
+/*
+ * stats_out[0] free blocks (including evictable cached ones), [1] blocks in
+ * use, [2] blocks with refcount > 1,
  * [3] internal waste in tokens of the last upload: sum over sequences of
  * 16 * ceil(ctx/16) - ctx (only the last block of a sequence is partly empty;
  * ahmedhaies.com, "PagedAttention: why LLM serving wastes most GPU memory",

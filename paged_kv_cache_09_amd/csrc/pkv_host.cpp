@@ -10,7 +10,9 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <list>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "pkv_internal.h"
@@ -91,6 +93,20 @@ struct pkv_pool {
   std::vector<int32_t> free_pos;   // index of an id in free_list, -1 when allocated
   std::vector<int32_t> refcount;
 
+  // prefix cache: full blocks registered under a chained hash of the token
+  // content from the sequence start. A cached block whose last reference is
+  // released stays reusable (evictable, least recently used first) instead of
+  // returning to the free list; allocation evicts only when the free list is
+  // empty.
+  std::unordered_multimap<uint64_t, int32_t> by_hash;
+  std::vector<char> cached;
+  std::vector<uint64_t> blk_hash, blk_parent;
+  std::vector<int32_t> blk_tokens;  // block_size token ids per cached block
+  std::list<int32_t> lru;           // evictable blocks, oldest first
+  std::vector<std::list<int32_t>::iterator> lru_pos;
+  std::vector<char> in_lru;
+  int64_t prefix_hits = 0, prefix_evictions = 0;
+
   // device metadata (library owned). One buffer so that an upload is one copy:
   // [slots int64 max_seqs | ctx int32 max_seqs | cum int32 max_seqs+1 | pad |
   //  table int32 batch x width | pad | decode schedule (up to sched_cap ints)]
@@ -133,12 +149,50 @@ struct pkv_pool {
 
 namespace {
 
+void uncache(pkv_pool* p, int32_t id) {
+  if (!p->cached[id]) return;
+  auto range = p->by_hash.equal_range(p->blk_hash[id]);
+  for (auto it = range.first; it != range.second; ++it)
+    if (it->second == id) {
+      p->by_hash.erase(it);
+      break;
+    }
+  p->cached[id] = 0;
+}
+
+void lru_remove(pkv_pool* p, int32_t id) {
+  p->lru.erase(p->lru_pos[id]);
+  p->in_lru[id] = 0;
+}
+
+// A block whose last reference is gone: cached blocks stay reusable
+// (evictable), others return to the free list.
 void free_push(pkv_pool* p, int32_t id) {
+  if (p->cached[id]) {
+    p->lru_pos[id] = p->lru.insert(p->lru.end(), id);
+    p->in_lru[id] = 1;
+    return;
+  }
   p->free_pos[id] = (int32_t)p->free_list.size();
   p->free_list.push_back(id);
 }
 
+// Blocks that can be handed out: free ones plus evictable cached ones.
+size_t avail(const pkv_pool* p) { return p->free_list.size() + p->lru.size(); }
+
+void free_remove_list(pkv_pool* p, int32_t id);
+
+// Take a specific unreferenced block out of the free list or the evictable set.
 void free_remove(pkv_pool* p, int32_t id) {
+  if (p->in_lru[id]) {
+    lru_remove(p, id);
+    uncache(p, id);
+    return;
+  }
+  free_remove_list(p, id);
+}
+
+void free_remove_list(pkv_pool* p, int32_t id) {
   const int32_t i = p->free_pos[id];
   const int32_t last = p->free_list.back();
   p->free_list[i] = last;
@@ -147,7 +201,16 @@ void free_remove(pkv_pool* p, int32_t id) {
   p->free_pos[id] = -1;
 }
 
+// Next block to hand out (avail(p) > 0): a free one, else the least recently
+// used evictable cached block, whose cache entry is dropped.
 int32_t free_pop(pkv_pool* p) {
+  if (p->free_list.empty()) {
+    const int32_t id = p->lru.front();
+    lru_remove(p, id);
+    uncache(p, id);
+    ++p->prefix_evictions;
+    return id;
+  }
   const int32_t id = p->free_list.back();
   p->free_list.pop_back();
   p->free_pos[id] = -1;
@@ -344,6 +407,11 @@ int pkv_kv_pool_alloc(const pkv_shape* sh, void* dev_base, size_t dev_bytes, pkv
   p->refcount.assign(sh->num_blocks, 0);
   p->free_pos.assign(sh->num_blocks, -1);
   p->free_list.reserve(sh->num_blocks);
+  p->cached.assign(sh->num_blocks, 0);
+  p->in_lru.assign(sh->num_blocks, 0);
+  p->lru_pos.resize(sh->num_blocks);
+  p->blk_hash.assign(sh->num_blocks, 0);
+  p->blk_parent.assign(sh->num_blocks, 0);
   for (int32_t id = sh->num_blocks - 1; id >= 0; --id) free_push(p, id);  // pops 0, 1, 2, ...
 
   if (dev_base) {
@@ -397,8 +465,8 @@ int pkv_kv_pool_free(pkv_pool* p) {
 
 int pkv_block_alloc(pkv_pool* p, int n, int32_t* ids_out) {
   if (!p || n < 0 || (n > 0 && !ids_out)) return fail(PKV_EINVAL, "bad arguments");
-  if ((size_t)n > p->free_list.size())
-    return fail(PKV_EOUT_OF_BLOCKS, "asked for %d blocks, %zu free", n, p->free_list.size());
+  if ((size_t)n > avail(p))
+    return fail(PKV_EOUT_OF_BLOCKS, "asked for %d blocks, %zu free", n, avail(p));
   for (int i = 0; i < n; ++i) {
     const int32_t id = free_pop(p);
     p->refcount[id] = 1;
@@ -512,7 +580,7 @@ int prepare_core(pkv_pool* p, int32_t* bt, int batch, int max_blocks, const int3
       const int64_t e = (int64_t)s * max_blocks + jb;
       int32_t b = bt[e];
       if (b < 0) {
-        if (p->free_list.empty()) {
+        if (avail(p) == 0) {
           rollback();
           return fail(PKV_EOUT_OF_BLOCKS, "no free block for sequence %d", s);
         }
@@ -527,12 +595,13 @@ int prepare_core(pkv_pool* p, int32_t* bt, int batch, int max_blocks, const int3
           rollback();
           return fail(PKV_EINVAL, "sequence %d: table entry %d is not an allocated block", s, b);
         }
+        if (p->refcount[b] == 1 && p->cached[b]) uncache(p, b);  // its content changes
         if (p->refcount[b] > 1) {
           if (!cow_out || ncow >= cow_capacity) {
             rollback();
             return fail(PKV_EINVAL, "copy-on-write pair buffer too small (%d)", cow_capacity);
           }
-          if (p->free_list.empty()) {
+          if (avail(p) == 0) {
             rollback();
             return fail(PKV_EOUT_OF_BLOCKS, "no free block for copy-on-write of sequence %d", s);
           }
@@ -884,13 +953,113 @@ int pkv_append_paged_attn_decode(pkv_pool* p, int layer, const void* k_new, cons
                      ws_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// FNV-1a, 64-bit (Fowler, Noll, Vo): offset basis 14695981039346656037,
+// prime 1099511628211, over the little-endian bytes of the parent block's
+// hash followed by the block's token ids.
+uint64_t block_hash(uint64_t parent, const int32_t* tokens, int n) {
+  uint64_t h = 14695981039346656037ull;
+  auto mix = [&h](uint64_t v, int bytes) {
+    for (int i = 0; i < bytes; ++i) {
+      h ^= (v >> (8 * i)) & 0xffu;
+      h *= 1099511628211ull;
+    }
+  };
+  mix(parent, 8);
+  for (int i = 0; i < n; ++i) mix((uint32_t)tokens[i], 4);
+  return h;
+}
+
+int32_t cache_find(const pkv_pool* p, uint64_t h, uint64_t parent, const int32_t* tokens) {
+  const int BS = p->shape.block_size;
+  auto range = p->by_hash.equal_range(h);
+  for (auto it = range.first; it != range.second; ++it) {
+    const int32_t id = it->second;
+    if (p->blk_parent[id] == parent &&
+        std::memcmp(&p->blk_tokens[(size_t)id * BS], tokens, (size_t)BS * 4) == 0)
+      return id;
+  }
+  return -1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_prefix_match(pkv_pool* p, const int32_t* tokens, int n_tokens, int32_t* ids_out,
+                     int max_ids) {
+  if (!p || n_tokens < 0 || (n_tokens > 0 && !tokens) || max_ids < 0 ||
+      (max_ids > 0 && !ids_out))
+    return fail(PKV_EINVAL, "bad arguments");
+  const int BS = p->shape.block_size;
+  uint64_t parent = 0;
+  int k = 0;
+  for (; k < max_ids && (int64_t)(k + 1) * BS <= n_tokens; ++k) {
+    const int32_t* t = tokens + (size_t)k * BS;
+    const uint64_t h = block_hash(parent, t, BS);
+    const int32_t id = cache_find(p, h, parent, t);
+    if (id < 0) break;
+    if (p->refcount[id] == 0) lru_remove(p, id);
+    ++p->refcount[id];
+    ids_out[k] = id;
+    parent = h;
+  }
+  p->prefix_hits += k;
+  return k;
+}
+
+int pkv_prefix_insert(pkv_pool* p, const int32_t* tokens, int n_tokens, const int32_t* bt_row,
+                      int n_entries) {
+  if (!p || n_tokens < 0 || (n_tokens > 0 && (!tokens || !bt_row)) || n_entries < 0)
+    return fail(PKV_EINVAL, "bad arguments");
+  const int BS = p->shape.block_size;
+  const int full = std::min<int64_t>(n_tokens / BS, n_entries);
+  for (int j = 0; j < full; ++j) {
+    const int32_t id = bt_row[j];
+    if (id < 0 || id >= p->shape.num_blocks || p->refcount[id] < 1)
+      return fail(PKV_EINVAL, "entry %d = %d is not an allocated block", j, id);
+  }
+  uint64_t parent = 0;
+  int added = 0;
+  for (int j = 0; j < full; ++j) {
+    const int32_t id = bt_row[j];
+    const int32_t* t = tokens + (size_t)j * BS;
+    const uint64_t h = block_hash(parent, t, BS);
+    if (!p->cached[id] && cache_find(p, h, parent, t) < 0) {
+      p->cached[id] = 1;
+      p->blk_hash[id] = h;
+      p->blk_parent[id] = parent;
+      if (p->blk_tokens.empty()) p->blk_tokens.assign((size_t)p->shape.num_blocks * BS, 0);
+      std::memcpy(&p->blk_tokens[(size_t)id * BS], t, (size_t)BS * 4);
+      p->by_hash.emplace(h, id);
+      ++added;
+    }
+    parent = h;
+  }
+  return added;
+}
+
+int pkv_prefix_stats(const pkv_pool* p, int64_t stats[4]) {
+  if (!p || !stats) return fail(PKV_EINVAL, "bad arguments");
+  int64_t n = 0;
+  for (char c : p->cached) n += c;
+  stats[0] = n;
+  stats[1] = (int64_t)p->lru.size();
+  stats[2] = p->prefix_hits;
+  stats[3] = p->prefix_evictions;
+  return PKV_OK;
+}
+
 int pkv_pool_stats(const pkv_pool* p, int64_t stats[4]) {
   if (!p || !stats) return fail(PKV_EINVAL, "bad arguments");
   int64_t shared = 0;
   for (int32_t r : p->refcount) shared += r > 1;
   int64_t waste = 0;
   for (int32_t L : p->h_ctx) waste += nblk(L) * pkv::kBlock - L;
-  stats[0] = (int64_t)p->free_list.size();
+  stats[0] = (int64_t)avail(p);
   stats[1] = p->shape.num_blocks - stats[0];
   stats[2] = shared;
   stats[3] = waste;

@@ -62,6 +62,9 @@ _SIGS = {
                                           _SZ, _U]),
     "pkv_decode_workspace_bytes": (_SZ, [_P, _I, _I, _I]),
     "pkv_pool_stats": (_I, [_P, _P]),
+    "pkv_prefix_match": (_I, [_P, _P, _I, _P, _I]),
+    "pkv_prefix_insert": (_I, [_P, _P, _I, _P, _I]),
+    "pkv_prefix_stats": (_I, [_P, _P]),
     "pkv_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -226,3 +229,28 @@ def pool_stats(pool) -> dict:
     _check(_lib.pkv_pool_stats(pool, _addr(out)))
     return {"free": int(out[0]), "used": int(out[1]), "shared": int(out[2]),
             "waste_tokens": int(out[3])}
+
+
+def prefix_match(pool, tokens, max_ids: int | None = None) -> np.ndarray:
+    """Ids of the cached leading full blocks of ``tokens`` (each gains a reference)."""
+    t = _np(tokens, np.int32)
+    cap = t.size if max_ids is None else int(max_ids)
+    ids = np.zeros(max(cap, 1), dtype=np.int32)
+    k = _lib.pkv_prefix_match(pool, _addr(t), t.size, _addr(ids), cap)
+    _check(min(k, 0))
+    return ids[:k].copy()
+
+
+def prefix_insert(pool, tokens, bt_row) -> int:
+    t = _np(tokens, np.int32)
+    row = _np(bt_row, np.int32)
+    k = _lib.pkv_prefix_insert(pool, _addr(t), t.size, _addr(row), row.size)
+    _check(min(k, 0))
+    return int(k)
+
+
+def prefix_stats(pool) -> dict:
+    out = np.zeros(4, dtype=np.int64)
+    _check(_lib.pkv_prefix_stats(pool, _addr(out)))
+    return {"cached": int(out[0]), "evictable": int(out[1]), "hits": int(out[2]),
+            "evictions": int(out[3])}

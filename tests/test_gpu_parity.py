@@ -12,7 +12,8 @@ import torch
 
 from paged_kv_cache_09_amd import workloads as W
 from paged_kv_cache_09_amd.session import DecodeSession
-from tests.gpu_harness import run_step_case, run_write_case, say, tolerance
+from tests.gpu_harness import (run_prefix_case, run_step_case, run_write_case, say,
+                               tolerance)
 
 pytestmark = pytest.mark.gpu
 
@@ -116,6 +117,30 @@ def test_multi_token_write_then_decode(name):
     tol = tolerance(cfg)
     for key, e in errs.items():
         assert e <= tol, f"{name} layer/partition {key}: max abs error {e} > {tol}"
+
+
+# Prefix caching: prompts sharing system prompts reuse cached blocks written
+# by earlier requests (evictions in the tight pool).
+PREFIX = {
+    "prefix_bf16": (W.CONFIGS["llama8b_bf16"], dict(num_blocks=600, n_prefixes=3,
+                                                     prefix_len=300, suffix_hi=200, na=8,
+                                                     nb=8, seed=1)),
+    "prefix_q8_tight": (W.CONFIGS["llama8b_q8"], dict(num_blocks=160, n_prefixes=4,
+                                                       prefix_len=200, suffix_hi=150, na=10,
+                                                       nb=6, seed=2)),
+    "prefix_f16_mha": (W.scaled(W.CONFIGS["mha13b_f16"], q_heads=4, kv_heads=4),
+                       dict(num_blocks=400, n_prefixes=2, prefix_len=500, suffix_hi=100,
+                            na=4, nb=6, seed=3)),
+}
+
+
+@pytest.mark.parametrize("name", list(PREFIX))
+def test_prefix_cached_blocks_decode_like_written_ones(name):
+    cfg, kw = PREFIX[name]
+    errs = run_prefix_case(cfg, label=name, **kw)
+    tol = tolerance(cfg)
+    for key, e in errs.items():
+        assert e <= tol, f"{name} partition {key}: max abs error {e} > {tol}"
 
 
 def _decode_form(cfg, device="cuda"):
