@@ -141,6 +141,8 @@ struct pkv_pool {
   int sched_gp = 0;
   int sched_nwaves = 0;
   bool sched_needs_merge = false;   // some segment spans several waves
+  bool sched_bins = false;          // eight-wave bins form (merges in LDS)
+  int sched_gp_building = 1;        // padded group of the schedule being built
   std::vector<int32_t> h_sched;     // wdesc[8 * nwaves] | seg_w0[nseg] | seg_w1[nseg]
 
   Staging ring[4];
@@ -280,7 +282,14 @@ constexpr int64_t kSegStartCost = PKV_SEG_START_COST;
 // h_sched = wdesc[8 * nwaves] | seg_w0[nseg] | seg_w1[nseg]; a wave's
 // descriptor holds its first and end tile, the sequence, kv head and block
 // index of its first tile, that sequence's length and the first block's id.
+bool build_bins(pkv_pool* p, int nbins);
+
 void build_schedule(pkv_pool* p, int part, int target) {
+  if (part == 0 && p->shape.dtype != PKV_F32) {  // fp32 tiles spill in the eight-wave form
+    const int per_cu = pkv::decode_blocks_per_cu(p->shape.dtype, p->shape.head_dim,
+                                                  p->sched_gp_building, true);
+    if (per_cu > 0 && build_bins(p, std::max(1, p->num_cus) * per_cu)) return;
+  }
   const int B = p->up_batch;
   const int H = p->shape.kv_heads;
   const int64_t tseq = p->h_cum[B];
@@ -358,16 +367,158 @@ void build_schedule(pkv_pool* p, int part, int target) {
     }
   p->sched_nwaves = W;
   p->sched_needs_merge = multi;
+  p->sched_bins = false;
 }
 
 int waves_target(const pkv_pool* p, int gp) {
-  int per_cu = pkv::decode_blocks_per_cu(p->shape.dtype, p->shape.head_dim, gp);
-  if (const char* env = std::getenv("PKV_WAVES_PER_CU")) {
-    const int v = std::atoi(env);
-    if (v > 0) per_cu = v;
-  }
+  int per_cu = pkv::decode_blocks_per_cu(p->shape.dtype, p->shape.head_dim, gp, false);
   per_cu = std::max(1, std::min(per_cu, 32));
   return std::max(1, p->num_cus) * per_cu;
+}
+
+// Bins packed no more unevenly than this (max bin / mean bin) are used;
+// otherwise the split form with its reduce launch is cheaper.
+constexpr double kBinSlack = 1.06;
+constexpr int kBinWaves = 8;
+
+// Bins form of the balanced schedule: whole (kv head, sequence) segments are
+// packed into nbins bins, longest processing time first (each segment to the
+// least loaded bin; cost = tiles + kSegStartCost), and each bin's tiles are
+// cut into kBinWaves equal-cost runs. Returns false (schedule untouched) when
+// the packing is too uneven, e.g. a few very long sequences.
+//   wdesc per wave: [0] index of its first segment in the bin lists, [1] tile
+//   count, [2] sequence, [3] kv head, [4] first block index in that segment,
+//   [5] its length, [6] that block's id, [7] merge it owns: bit 16 set when
+//   its first segment started in an earlier wave wa of the bin and ends in
+//   this one; bits 0-7 wa, bit 8 the LDS slot of wa's piece.
+//   seglist per listed segment: sequence, kv head, length, first block id.
+bool build_bins(pkv_pool* p, int nbins) {
+  const int B = p->up_batch;
+  const int H = p->shape.kv_heads;
+  const int nseg = B * H;
+  if (nbins < 1 || nseg < 1) return false;
+  struct Seg {
+    int64_t cost;
+    int g, s;
+  };
+  std::vector<Seg> segs;
+  segs.reserve(nseg);
+  int64_t total = 0;
+  for (int g = 0; g < H; ++g)
+    for (int s = 0; s < B; ++s) {
+      const int64_t c = nblk(p->h_ctx[s]) + kSegStartCost;
+      segs.push_back({c, g, s});
+      total += c;
+    }
+  std::stable_sort(segs.begin(), segs.end(),
+                   [](const Seg& a, const Seg& b) { return a.cost > b.cost; });
+  std::vector<int64_t> load(nbins, 0);
+  std::vector<std::vector<int>> members(nbins);
+  // min-heap of (load, bin)
+  std::vector<std::pair<int64_t, int>> heap;
+  for (int b = 0; b < nbins; ++b) heap.push_back({0, b});
+  auto cmp = [](const std::pair<int64_t, int>& a, const std::pair<int64_t, int>& b) {
+    return a.first != b.first ? a.first > b.first : a.second > b.second;
+  };
+  std::make_heap(heap.begin(), heap.end(), cmp);
+  for (int i = 0; i < nseg; ++i) {
+    std::pop_heap(heap.begin(), heap.end(), cmp);
+    auto top = heap.back();
+    heap.pop_back();
+    members[top.second].push_back(i);
+    load[top.second] += segs[i].cost;
+    heap.push_back({load[top.second], top.second});
+    std::push_heap(heap.begin(), heap.end(), cmp);
+  }
+  const int64_t maxload = *std::max_element(load.begin(), load.end());
+  if ((double)maxload > kBinSlack * (double)total / nbins) return false;
+
+  const int W = nbins * kBinWaves;
+  p->h_sched.assign((size_t)8 * W + 2 * (size_t)nseg + 4 * (size_t)nseg, 0);
+  int32_t* desc = p->h_sched.data();
+  int32_t* list = desc + (size_t)8 * W + 2 * (size_t)nseg;
+  int li = 0;
+  for (int b = 0; b < nbins; ++b) {
+    std::vector<int>& m = members[b];
+    std::sort(m.begin(), m.end(), [&](int a, int c) {
+      return segs[a].g != segs[c].g ? segs[a].g < segs[c].g : segs[a].s < segs[c].s;
+    });
+    const int li0 = li;
+    for (int i : m) {
+      const int s = segs[i].s;
+      int32_t* e = list + 4 * (size_t)li++;
+      e[0] = s;
+      e[1] = segs[i].g;
+      e[2] = p->h_ctx[s];
+      e[3] = p->h_bt[(size_t)s * p->up_stride];
+    }
+    // cut the bin's tiles into kBinWaves runs of equal cost
+    const int64_t cb = load[b];
+    std::vector<int64_t> start_tile(kBinWaves + 1, -1);  // bin-local tile index of each cut
+    int64_t cost = 0, x = 0;
+    int v = 1;
+    start_tile[0] = 0;
+    for (int i : m) {
+      cost += kSegStartCost;
+      const int64_t n = segs[i].cost - kSegStartCost;
+      for (int64_t j = 0; j < n; ++j, ++x) {
+        while (v < kBinWaves && cost * kBinWaves >= (int64_t)v * cb && x > start_tile[v - 1])
+          start_tile[v++] = x;
+        ++cost;
+      }
+    }
+    const int64_t tiles = x;
+    while (v <= kBinWaves) start_tile[v++] = tiles;
+    // descriptors: walk segments and waves together
+    int seg_i = 0;          // index into m
+    int64_t seg_x0 = 0;     // bin-local tile index where m[seg_i] starts
+    std::vector<int> first_wave_of(m.size(), -1), first_slot_of(m.size(), 0);
+    for (int wv = 0; wv < kBinWaves; ++wv) {
+      int32_t* d = desc + (size_t)8 * (b * kBinWaves + wv);
+      const int64_t x0 = start_tile[wv], x1 = std::max(start_tile[wv], start_tile[wv + 1]);
+      d[1] = (int32_t)(x1 - x0);
+      if (x1 <= x0) {
+        d[0] = li0;
+        continue;
+      }
+      while (seg_x0 + (segs[m[seg_i]].cost - kSegStartCost) <= x0) {
+        seg_x0 += segs[m[seg_i]].cost - kSegStartCost;
+        ++seg_i;
+      }
+      const Seg& sg = segs[m[seg_i]];
+      const int64_t j0 = x0 - seg_x0;
+      d[0] = li0 + seg_i;
+      d[2] = sg.s;
+      d[3] = sg.g;
+      d[4] = (int32_t)j0;
+      d[5] = p->h_ctx[sg.s];
+      d[6] = p->h_bt[(size_t)sg.s * p->up_stride + j0];
+      const int64_t n0 = sg.cost - kSegStartCost;
+      if (j0 == 0) {
+        first_wave_of[seg_i] = wv;
+        first_slot_of[seg_i] = 0;
+      } else if (seg_x0 + n0 <= x1) {
+        // this wave ends a segment that started in an earlier wave
+        d[7] = (1 << 16) | (first_slot_of[seg_i] << 8) | first_wave_of[seg_i];
+      }
+      // the wave's last segment, when different from its first and cut at x1,
+      // leaves its piece in slot 1
+      int64_t sx = seg_x0;
+      int k = seg_i;
+      while (sx + (segs[m[k]].cost - kSegStartCost) < x1) {
+        sx += segs[m[k]].cost - kSegStartCost;
+        ++k;
+      }
+      if (k != seg_i && first_wave_of[k] < 0) {
+        first_wave_of[k] = wv;
+        first_slot_of[k] = 1;
+      }
+    }
+  }
+  p->sched_nwaves = W;
+  p->sched_needs_merge = false;
+  p->sched_bins = true;
+  return true;
 }
 
 }  // namespace
@@ -428,7 +579,7 @@ int pkv_kv_pool_alloc(const pkv_shape* sh, void* dev_base, size_t dev_bytes, pkv
     p->num_cus = prop.multiProcessorCount;
     // balanced schedules need 8 ints per wave (at most 32 waves per CU); very
     // small fixed partitions may grow this buffer on first use
-    p->sched_cap = (size_t)8 * std::max(p->num_cus, 1) * 32 + 2 * (size_t)sh->max_seqs * sh->kv_heads;
+    p->sched_cap = (size_t)8 * std::max(p->num_cus, 1) * 32 + 6 * (size_t)sh->max_seqs * sh->kv_heads;
     p->pairs_cap = sh->max_seqs;
     const size_t bt_bytes = (size_t)sh->max_seqs * p->max_blocks_per_seq * 4;
     p->off_ctx = (size_t)sh->max_seqs * 8;
@@ -729,6 +880,7 @@ int pkv_block_table_upload(pkv_pool* p, const int32_t* bt, int batch, int max_bl
   size_t bytes = tbl_end;
   bool packed = false;
   if (p->sched_part >= 0) {
+    p->sched_gp_building = p->sched_gp;
     build_schedule(p, p->sched_part, waves_target(p, p->sched_gp));
     if (p->h_sched.size() <= p->sched_cap) {
       packed = true;
@@ -856,6 +1008,7 @@ int decode_impl(pkv_pool* p, int layer, const void* k_new, const void* v_new, co
   hipError_t e;
 
   if (p->sched_gen != p->up_gen || p->sched_part != partition_tokens || p->sched_gp != gp) {
+    p->sched_gp_building = gp;
     build_schedule(p, partition_tokens, waves_target(p, gp));
     int32_t* dst = reinterpret_cast<int32_t*>(p->d_meta + p->off_sched);
     if (p->h_sched.size() > p->sched_cap) {  // rare: very small fixed partitions
@@ -901,6 +1054,7 @@ int decode_impl(pkv_pool* p, int layer, const void* k_new, const void* v_new, co
   dp.wdesc = p->d_sched;
   dp.seg_w0 = p->d_sched + (size_t)8 * W;
   dp.seg_w1 = dp.seg_w0 + nseg;
+  dp.seglist = dp.seg_w1 + nseg;
   dp.q = q;
   dp.k_new = k_new;
   dp.v_new = v_new;
@@ -915,8 +1069,9 @@ int decode_impl(pkv_pool* p, int layer, const void* k_new, const void* v_new, co
   dp.q_heads = q_heads;
   dp.group = group;
   dp.nwaves = W;
-  dp.waves_per_xcd = (W + pkv::kNumXcd - 1) / pkv::kNumXcd;
-  e = pkv::launch_decode(p->shape.dtype, p->shape.head_dim, gp, dp, stream);
+  const int groups = p->sched_bins ? W / 8 : W;  // workgroups: bins, or one per wave
+  dp.waves_per_xcd = (groups + pkv::kNumXcd - 1) / pkv::kNumXcd;
+  e = pkv::launch_decode(p->shape.dtype, p->shape.head_dim, gp, p->sched_bins, dp, stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (p->sched_needs_merge) {
     pkv::ReduceParams rp{};

@@ -19,6 +19,8 @@ struct DecodeParams {
   const int32_t* wdesc;        // per wave: x0, x1, seq, kv head, j0, ctx, first block, 0
   const int32_t* seg_w0;       // first wave touching each (kv head, sequence) segment
   const int32_t* seg_w1;       // last wave touching it
+  const int32_t* seglist;      // bins form: per listed segment (sequence, kv head, length,
+                               // first block id), bins one after another
   const void* q;               // [batch][q_heads][head_dim], cache dtype
   const void* k_new;           // null, or new K rows [batch][kv_heads][head_dim] to append
   const void* v_new;           // new V rows (with k_new)
@@ -51,11 +53,13 @@ struct ReduceParams {
 // Padded group size used by the kernels: 1, 2, 4 or 8.
 inline int padded_group(int g) { return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : 8; }
 
-hipError_t launch_decode(int dtype, int head_dim, int gp, const DecodeParams& p,
+// bins: the eight-wave form that merges split segments in LDS (waves_per_xcd
+// then counts workgroups per XCD).
+hipError_t launch_decode(int dtype, int head_dim, int gp, bool bins, const DecodeParams& p,
                          hipStream_t stream);
 hipError_t launch_reduce(int head_dim, int gp, const ReduceParams& p, hipStream_t stream);
 // Workgroups of the decode kernel one CU can hold at once (occupancy), 0 on error.
-int decode_blocks_per_cu(int dtype, int head_dim, int gp);
+int decode_blocks_per_cu(int dtype, int head_dim, int gp, bool bins);
 
 hipError_t launch_append(const void* k_new, const void* v_new, const int64_t* slots, int batch,
                          void* k_layer, void* v_layer, int kv_heads, int row_bytes,

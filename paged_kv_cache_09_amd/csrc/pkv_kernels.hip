@@ -257,6 +257,15 @@ __device__ __forceinline__ float row_sum(float v) {
   return v + row_ror<0x121>(v);
 }
 
+// Orders this wavefront's LDS writes before its later LDS reads by other
+// lanes (a wave's LDS operations complete in order; this keeps the compiler
+// from moving them). Only this wave takes part.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -309,8 +318,17 @@ struct TileRegs<DT_Q8, D> {
   unsigned vs[NV / 2];  // fp16 pairs: scale of row NV*vr + i in half i % 2 of vs[i / 2]
 };
 
-template <int DT, int D, int GP>
-__global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
+// Two launch forms share this body:
+//   BINS = false: one wave per workgroup; a wave covers a contiguous run of
+//     the kv-head-major tile space; segments split between waves are merged
+//     by reduce_kernel from global partials.
+//   BINS = true: eight waves per workgroup, one workgroup per bin: a set of
+//     whole (kv head, sequence) segments packed by the host so that bins are
+//     equally loaded; the bin's tiles are split evenly between its waves and
+//     a segment split between them is merged in LDS at the end (no partials
+//     in HBM, no reduce launch).
+template <int DT, int D, int GP, bool BINS>
+__global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p) {
   constexpr bool Q8 = DT == DT_Q8;
   using TR = TileRegs<DT, D>;
   constexpr int RB = D * Elem<DT>::bytes;  // bytes per K/V row (codes only for q8_0)
@@ -328,27 +346,45 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   constexpr int NBUF = 2;
   static_assert(RB % 32 == 0 && CPR <= 64 && GP <= 16, "shape");
 
-  __shared__ float p_lds[2][16 * GP];  // softmax weights, [tile parity][row][head]
-  __shared__ float a_lds[GP];          // per-head rescale factors
-  __shared__ float l_lds[GP];          // per-head sums at the end of a run
-  __shared__ float m_lds[GP];          // per-head maxima at the end of a run
+  constexpr int NW = BINS ? 8 : 1;       // waves per workgroup
+  __shared__ float p_lds_all[NW][2][16 * GP];  // softmax weights, [wave][parity][row][head]
+  __shared__ float a_lds_all[NW][GP];          // per-head rescale factors
+  __shared__ float l_lds_all[NW][GP];          // per-head sums at the end of a run
+  __shared__ float m_lds_all[NW][GP];          // per-head maxima at the end of a run
+  // BINS: pieces (o, m, l) of segments split between this workgroup's waves,
+  // slot 0 = the wave's first segment, slot 1 = its last
+  __shared__ float piece_o[BINS ? NW * 2 * GP * D : 1];
+  __shared__ float piece_ml[BINS ? NW * 2 * GP * 2 : 1];
 
-  const int lane = threadIdx.x;
+  const int wl = BINS ? (int)(threadIdx.x >> 6) : 0;
+  const int lane = threadIdx.x & 63;
+  float (&p_lds)[2][16 * GP] = p_lds_all[wl];
+  float (&a_lds)[GP] = a_lds_all[wl];
+  float (&l_lds)[GP] = l_lds_all[wl];
+  float (&m_lds)[GP] = m_lds_all[wl];
   // Workgroups are dealt round-robin to the 8 XCDs; give each XCD one
-  // contiguous eighth of the tile space so a kv head's tiles share one L2.
-  const int w = (blockIdx.x % kNumXcd) * p.waves_per_xcd + blockIdx.x / kNumXcd;
-  if (w >= p.nwaves) return;
+  // contiguous eighth of the waves (bins) so neighbouring work shares an L2.
+  const int wg = (blockIdx.x % kNumXcd) * p.waves_per_xcd + blockIdx.x / kNumXcd;
+  const int w = BINS ? wg * NW + wl : wg;
+  const bool active = w < p.nwaves;
+  if (!BINS && !active) return;
 
-  // Per-wave descriptor: first tile, end tile, sequence, kv head, first block
-  // of the run inside the sequence, context length, physical id of that block.
-  const int* desc = p.wdesc + 8 * w;
-  int x = desc[0];
-  const int xend = desc[1];
+  // Per-wave descriptor: first tile (BINS: index of its first segment in the
+  // bin lists), end tile (BINS: tile count), sequence, kv head, first block of
+  // the run inside the sequence, context length, physical id of that block,
+  // and (BINS) the merge it owns.
+  const int* desc = p.wdesc + 8 * (active ? w : 0);
+  int li = BINS ? desc[0] : 0;
+  int x = BINS ? 0 : desc[0];
+  const int xend = active ? desc[1] : 0;
   int s = desc[2];
   int g = desc[3];
   int j0 = desc[4];
   int L = desc[5];
   int blk_first = desc[6];
+  const int merge_info = BINS ? desc[7] : 0;
+  const int s_first = s, g_first = g;
+  bool first_seg = true;
 
   const int t16 = lane & 15;  // K row (token) this lane feeds; q row (head) likewise
   const int kg = lane >> 4;   // which 16-byte piece of each 64 bytes
@@ -360,7 +396,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   const size_t blk_stride = (size_t)p.kv_heads * TILE;
   int parity = 0;
 
-  while (true) {
+  while (x < xend) {
     const int nblk = (L + 15) >> 4;
     const int take = min(xend - x, nblk - j0);
     const int j1 = j0 + take;
@@ -368,13 +404,23 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     // Prefetch the next segment's length and first block id (scalar loads
     // in flight while this segment's tiles stream).
     int next_s = s + 1, next_g = g, next_L = 0, next_blk = 0;
-    if (next_s == p.batch) {
-      next_s = 0;
-      ++next_g;
-    }
-    if (x + take < xend) {
-      next_L = p.ctx[next_s];
-      next_blk = p.bt[(size_t)next_s * p.bt_stride];
+    if constexpr (BINS) {
+      if (x + take < xend) {  // bin lists hold (sequence, kv head, length, first block)
+        const int* e = p.seglist + 4 * (li + 1);
+        next_s = e[0];
+        next_g = e[1];
+        next_L = e[2];
+        next_blk = e[3];
+      }
+    } else {
+      if (next_s == p.batch) {
+        next_s = 0;
+        ++next_g;
+      }
+      if (x + take < xend) {
+        next_L = p.ctx[next_s];
+        next_blk = p.bt[(size_t)next_s * p.bt_stride];
+      }
     }
     const char* kbase = reinterpret_cast<const char*>(p.k) + (size_t)g * TILE;
     const char* vbase = reinterpret_cast<const char*>(p.v) + (size_t)g * TILE;
@@ -493,7 +539,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
 #pragma unroll
           for (int i = 0; i < HPG; ++i) a_lds[4 * kg + i] = alpha[i];
         }
-        __syncthreads();
+        wave_sync();
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
           const float a = a_lds[h];
@@ -509,7 +555,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
         lsum[i] += pw;
         if (head_lane) pl[t16 * GP + 4 * kg + i] = pw;
       }
-      __syncthreads();
+      wave_sync();
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int tr = vrow(i);
@@ -655,7 +701,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
         m_lds[4 * kg + i] = m[i];
       }
     }
-    __syncthreads();
+    wave_sync();
     const bool whole = j0 == 0 && j1 == nblk;
     if (whole) {
       if (lane < CPR) {
@@ -668,6 +714,19 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
             for (int e = 0; e < EPC; ++e) o[(size_t)h * D + e] = acc[h][e] * inv;
           }
         }
+      }
+    } else if constexpr (BINS) {
+      const int slot = first_seg ? 0 : 1;
+      float* po = piece_o + (size_t)((wl * 2 + slot) * GP) * D + lane * EPC;
+      if (lane < CPR) {
+#pragma unroll
+        for (int h = 0; h < GP; ++h)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) po[(size_t)h * D + e] = acc[h][e];
+      }
+      if (lane < p.group) {
+        piece_ml[((wl * 2 + slot) * GP + lane) * 2 + 0] = m_lds[lane];
+        piece_ml[((wl * 2 + slot) * GP + lane) * 2 + 1] = l_lds[lane];
       }
     } else {
       const size_t idx = (size_t)seg + w;
@@ -686,7 +745,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
         p.part_ml[(idx * GP + lane) * 2 + 1] = l_lds[lane];
       }
     }
-    __syncthreads();  // l_lds / m_lds / a_lds are reused by the next run
+    wave_sync();  // l_lds / m_lds / a_lds are reused by the next run
 
     x += take;
     if (x >= xend) break;
@@ -695,6 +754,45 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     j0 = 0;
     L = next_L;
     blk_first = next_blk;
+    ++li;
+    first_seg = false;
+  }
+
+  if constexpr (BINS) {
+    // Every piece of this bin is in LDS: the wave holding the last tile of a
+    // segment split between waves wa .. wl merges its pieces (slot 0 of each
+    // wave, except wa's, whose slot the host gives):
+    //   out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i.
+    __syncthreads();
+    if (active && (merge_info & (1 << 16))) {
+      const int wa = merge_info & 0xff;
+      const int wa_slot = (merge_info >> 8) & 1;
+      constexpr int PER = D / 64;
+      for (int hh = 0; hh < p.group; ++hh) {
+        float M = -__builtin_inff();
+        for (int v = wa; v <= wl; ++v) {
+          const int sl = v == wa ? wa_slot : 0;
+          M = fmaxf(M, piece_ml[((v * 2 + sl) * GP + hh) * 2]);
+        }
+        float den = 0.f, o[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) o[e] = 0.f;
+        for (int v = wa; v <= wl; ++v) {
+          const int sl = v == wa ? wa_slot : 0;
+          const float* ml = piece_ml + ((v * 2 + sl) * GP + hh) * 2;
+          const float wgt = __builtin_amdgcn_exp2f(ml[0] - M);
+          den = __builtin_fmaf(wgt, ml[1], den);
+          const float* po = piece_o + (size_t)((v * 2 + sl) * GP + hh) * D + lane * PER;
+#pragma unroll
+          for (int e = 0; e < PER; ++e) o[e] = __builtin_fmaf(wgt, po[e], o[e]);
+        }
+        const float inv = 1.f / den;
+        float* dst = p.out + ((size_t)s_first * p.q_heads + (size_t)g_first * p.group + hh) * D +
+                     lane * PER;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) dst[e] = o[e] * inv;
+      }
+    }
   }
 }
 
@@ -810,36 +908,37 @@ __global__ __launch_bounds__(256) void upload_kernel(const u32x4* __restrict__ s
 }
 
 template <int DT, int D, int GP>
-const void* decode_fn() {
-  return reinterpret_cast<const void*>(&decode_kernel<DT, D, GP>);
+const void* decode_fn(bool bins) {
+  return bins ? reinterpret_cast<const void*>(&decode_kernel<DT, D, GP, true>)
+              : reinterpret_cast<const void*>(&decode_kernel<DT, D, GP, false>);
 }
 
 template <int DT, int D>
-const void* pick_gp(int gp) {
+const void* pick_gp(int gp, bool bins) {
   switch (gp) {
-    case 1: return decode_fn<DT, D, 1>();
-    case 2: return decode_fn<DT, D, 2>();
-    case 4: return decode_fn<DT, D, 4>();
-    case 8: return decode_fn<DT, D, 8>();
+    case 1: return decode_fn<DT, D, 1>(bins);
+    case 2: return decode_fn<DT, D, 2>(bins);
+    case 4: return decode_fn<DT, D, 4>(bins);
+    case 8: return decode_fn<DT, D, 8>(bins);
   }
   return nullptr;
 }
 
 template <int DT>
-const void* pick_d(int d, int gp) {
+const void* pick_d(int d, int gp, bool bins) {
   switch (d) {
-    case 64: return pick_gp<DT, 64>(gp);
-    case 128: return pick_gp<DT, 128>(gp);
+    case 64: return pick_gp<DT, 64>(gp, bins);
+    case 128: return pick_gp<DT, 128>(gp, bins);
   }
   return nullptr;
 }
 
-const void* decode_kernel_for(int dtype, int d, int gp) {
+const void* decode_kernel_for(int dtype, int d, int gp, bool bins) {
   switch (dtype) {
-    case DT_F32: return pick_d<DT_F32>(d, gp);
-    case DT_F16: return pick_d<DT_F16>(d, gp);
-    case DT_BF16: return pick_d<DT_BF16>(d, gp);
-    case DT_Q8: return pick_d<DT_Q8>(d, gp);
+    case DT_F32: return pick_d<DT_F32>(d, gp, bins);
+    case DT_F16: return pick_d<DT_F16>(d, gp, bins);
+    case DT_BF16: return pick_d<DT_BF16>(d, gp, bins);
+    case DT_Q8: return pick_d<DT_Q8>(d, gp, bins);
   }
   return nullptr;
 }
@@ -857,21 +956,22 @@ const void* reduce_for_gp(int gp) {
 
 }  // namespace
 
-hipError_t launch_decode(int dtype, int head_dim, int gp, const DecodeParams& p,
+hipError_t launch_decode(int dtype, int head_dim, int gp, bool bins, const DecodeParams& p,
                          hipStream_t stream) {
-  const void* fn = decode_kernel_for(dtype, head_dim, gp);
+  const void* fn = decode_kernel_for(dtype, head_dim, gp, bins);
   if (!fn) return hipErrorInvalidValue;
   DecodeParams args = p;
   void* argv[] = {&args};
-  dim3 grid((unsigned)(p.waves_per_xcd * kNumXcd)), block(64);
+  dim3 grid((unsigned)(p.waves_per_xcd * kNumXcd)), block(bins ? 512 : 64);
   return hipLaunchKernel(fn, grid, block, argv, 0, stream);
 }
 
-int decode_blocks_per_cu(int dtype, int head_dim, int gp) {
-  const void* fn = decode_kernel_for(dtype, head_dim, gp);
+int decode_blocks_per_cu(int dtype, int head_dim, int gp, bool bins) {
+  const void* fn = decode_kernel_for(dtype, head_dim, gp, bins);
   if (!fn) return 0;
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 64, 0) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, bins ? 512 : 64, 0) != hipSuccess)
+    return 0;
   return n;
 }
 
