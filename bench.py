@@ -69,7 +69,8 @@ def decode_algorithmic_bytes(cfg, ctx) -> int:
     from paged_kv_cache_09_amd import workloads as W
     e_in = W.TORCH_DTYPE[cfg.dtype].itemsize  # q, k_new, v_new (bf16 for q8_0)
     B = len(ctx)
-    nblk = int(((np.asarray(ctx, dtype=np.int64) + 15) // 16).sum())
+    bs = cfg.block_size
+    nblk = int(((np.asarray(ctx, dtype=np.int64) + bs - 1) // bs).sum())  # table entries
     # kv_bytes counts every row once, the new one included; that one is read
     # from k_new / v_new (input dtype) rather than the pool, and written to it
     new_rows = B * 2 * cfg.kv_heads * cfg.head_dim * e_in
@@ -163,6 +164,8 @@ def main():
                     help="instead of the decode step, run the block manager under a synthetic "
                          "request stream of STEPS scheduler steps (host only) and report "
                          "paged vs contiguous waste")
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="tokens per pool block (8, 16 or 32; default: the workload's, 16)")
     ap.add_argument("--write-chunk", type=int, default=0, metavar="TOKENS",
                     help="instead of the decode step, time the multi-token paged write of a "
                          "prompt chunk of TOKENS tokens per sequence (prefill side)")
@@ -176,6 +179,9 @@ def main():
     if args.request_stream:
         from paged_kv_cache_09_amd import stream as S
         cfg = S.StreamConfig(steps=args.request_stream)
+        if args.block_size:
+            cfg = S.dataclasses.replace(cfg, block_size=args.block_size,
+                                        num_blocks=cfg.num_blocks * 16 // args.block_size)
         sim = S.PagedStream(cfg)
         t0 = time.perf_counter()
         summary = sim.run(S.draw_requests(cfg))
@@ -211,13 +217,18 @@ def main():
     if args.write_chunk:
         return main_write(args)
     cfg = W.CONFIGS[args.config]
+    if args.block_size:
+        # same token capacity in blocks of another size
+        cfg = W.scaled(cfg, block_size=args.block_size,
+                       num_blocks=cfg.num_blocks * cfg.block_size // args.block_size)
     part = cfg.partition_tokens if args.partition is None else args.partition
     growth = args.warmup + args.steps + 1
     # spare blocks so every sequence can grow by `growth` tokens
-    cfg = W.scaled(cfg, num_blocks=cfg.num_blocks + cfg.batch * ((growth + 15) // 16 + 1))
+    bs = cfg.block_size
+    cfg = W.scaled(cfg, num_blocks=cfg.num_blocks + cfg.batch * ((growth + bs - 1) // bs + 1))
     log(f"building {cfg.name}: {cfg.layers} layers")
     w = W.make(cfg, device="cuda", layers=cfg.layers, form="step", fill="random",
-               extra_blocks=(growth + 15) // 16 + 1)
+               extra_blocks=(growth + bs - 1) // bs + 1)
     sess = DecodeSession(w)
     log("pool ready; warm-up")
     out = sess.new_out()
@@ -288,9 +299,10 @@ def main():
         "config": {
             "workload": f"{cfg.name}: {cfg.layers} layers x batch {cfg.batch}, "
                         f"{cfg.q_heads} q / {cfg.kv_heads} kv heads, head_dim {cfg.head_dim}, "
-                        f"block 16, context {int(w.ctx.min())}..{int(w.ctx.max())} growing 1/step",
+                        f"block {cfg.block_size}, context {int(w.ctx.min())}..{int(w.ctx.max())} "
+                        "growing 1/step",
             "layers": cfg.layers, "batch": cfg.batch, "q_heads": cfg.q_heads,
-            "kv_heads": cfg.kv_heads, "head_dim": cfg.head_dim, "block_size": 16,
+            "kv_heads": cfg.kv_heads, "head_dim": cfg.head_dim, "block_size": cfg.block_size,
             "partition_tokens": part, "pool_gib": round(w.pool.numel() / 2**30, 2),
         },
         "pct_of_hbm_peak": round(100 * total_kv / elapsed / 1e9 / HBM_PEAK_GBS, 2),

@@ -18,7 +18,7 @@ BLOCK = 16
 
 
 def run_step(k_layers, v_layers, pre_tables, shared, ctx, k_new_layers, v_new_layers, *,
-             dtype, num_blocks, max_blocks):
+             dtype, num_blocks, max_blocks, block_size=BLOCK):
     """Apply one decode step to host pools.
 
     k_layers / v_layers: lists (one per layer) of storage arrays [NB][Hkv][16][D]
@@ -31,14 +31,14 @@ def run_step(k_layers, v_layers, pre_tables, shared, ctx, k_new_layers, v_new_la
     model.claim(used)
     for b, rc in shared:
         model.ref([b] * (rc - 1))
-    kinds = model.plan_append(pre_tables, ctx)
+    kinds = model.plan_append(pre_tables, ctx, block_size)
     free_ids = iter(sorted(set(range(num_blocks)) - set(used)))
     B = len(pre_tables)
     table = np.full((B, max_blocks), -1, dtype=np.int32)
     for s, row in enumerate(pre_tables):
         table[s, :len(row)] = row
     for s, kind in enumerate(kinds):
-        j = (int(ctx[s]) - 1) // BLOCK
+        j = (int(ctx[s]) - 1) // block_size
         if kind == "new":
             table[s, j] = next(free_ids)
         elif kind == "cow":
@@ -49,12 +49,12 @@ def run_step(k_layers, v_layers, pre_tables, shared, ctx, k_new_layers, v_new_la
                 vl[dst] = vl[src]
             table[s, j] = dst
     for kl, vl, kn, vn in zip(k_layers, v_layers, k_new_layers, v_new_layers):
-        oracle.append(kl, vl, table, ctx, kn, vn, dtype=dtype)
+        oracle.append(kl, vl, table, ctx, kn, vn, dtype=dtype, block_size=block_size)
     return table, kinds
 
 
 def run_write(k_layers, v_layers, pre_tables, shared, ctx_before, n_new, k_rows_layers,
-              v_rows_layers, *, dtype, num_blocks, max_blocks):
+              v_rows_layers, *, dtype, num_blocks, max_blocks, block_size=BLOCK):
     """Write n_new[s] tokens per sequence after ctx_before[s] cached ones into host
     pools (every layer), the oracle's own block placement.
 
@@ -66,7 +66,7 @@ def run_write(k_layers, v_layers, pre_tables, shared, ctx_before, n_new, k_rows_
     model.claim(used)
     for b, rc in shared:
         model.ref([b] * (rc - 1))
-    plan = model.plan_write(pre_tables, ctx_before, n_new)
+    plan = model.plan_write(pre_tables, ctx_before, n_new, block_size)
     free_ids = iter(sorted(set(range(num_blocks)) - set(used)))
     B = len(pre_tables)
     table = np.full((B, max_blocks), -1, dtype=np.int32)
@@ -90,39 +90,39 @@ def run_write(k_layers, v_layers, pre_tables, shared, ctx_before, n_new, k_rows_
         rows = np.where(has, offsets[:-1] + t, 0)
         for kl, vl, kr, vr in zip(k_layers, v_layers, k_rows_layers, v_rows_layers):
             oracle.append(kl, vl, table, ctx, np.ascontiguousarray(kr[rows]),
-                          np.ascontiguousarray(vr[rows]), dtype=dtype)
+                          np.ascontiguousarray(vr[rows]), dtype=dtype, block_size=block_size)
     return table, plan
 
 
-def q8_row_bytes(pool, blocks, rows, is_v):
+def q8_row_bytes(pool, blocks, rows, is_v, block_size=BLOCK):
     """Bytes of q8_0 rows as [n][Hkv][D codes + 2 * D/32 scale bytes], scales in group
-    order. A tile is 16 x D int8 codes, then fp16 scales ordered [row][group]
-    (K region) or [group][row] (V region)."""
+    order. A tile is block_size x D int8 codes, then fp16 scales ordered
+    [row][group] (K region) or [group][row] (V region)."""
     tb = pool.shape[2]
-    D = tb * 2 // 34
+    D = tb * 16 // (17 * block_size)
     ng = D // 32
     rows = np.asarray(rows, dtype=np.int64)
     blocks = np.asarray(blocks, dtype=np.int64)
     code_idx = rows[:, None] * D + np.arange(D)[None, :]
     grp = np.arange(ng)[None, :]
-    si = grp * BLOCK + rows[:, None] if is_v else rows[:, None] * ng + grp
-    sb = BLOCK * D + 2 * si
+    si = grp * block_size + rows[:, None] if is_v else rows[:, None] * ng + grp
+    sb = block_size * D + 2 * si
     scale_idx = np.stack([sb, sb + 1], axis=2).reshape(len(rows), 2 * ng)
     idx = np.concatenate([code_idx, scale_idx], axis=1)
     return np.take_along_axis(pool[blocks], idx[:, None, :], axis=2)
 
 
-def logical_rows(k_pool, v_pool, table, ctx):
+def logical_rows(k_pool, v_pool, table, ctx, block_size=BLOCK):
     """Raw bytes of every sequence's K and V rows in logical order: list of (K, V)
     arrays [L][Hkv][D] (q8_0 pools [NB][Hkv][tile bytes]: codes then scale bytes)."""
     out = []
     for s, L in enumerate(ctx):
         t = np.arange(int(L))
-        blocks = table[s][t // BLOCK]
-        rows = t % BLOCK
+        blocks = table[s][t // block_size]
+        rows = t % block_size
         if k_pool.ndim == 3:
-            out.append((q8_row_bytes(k_pool, blocks, rows, False),
-                        q8_row_bytes(v_pool, blocks, rows, True)))
+            out.append((q8_row_bytes(k_pool, blocks, rows, False, block_size),
+                        q8_row_bytes(v_pool, blocks, rows, True, block_size)))
         else:
             out.append((k_pool[blocks, :, rows, :], v_pool[blocks, :, rows, :]))
     return out

@@ -56,8 +56,8 @@ int check_shape(const pkv_shape* sh) {
       sh->max_seq_len < 1)
     return fail(PKV_EINVAL, "layers, num_blocks, kv_heads, max_seqs and max_seq_len must be >= 1");
   if (elem_bytes(sh->dtype) == 0) return fail(PKV_EINVAL, "unknown dtype %d", sh->dtype);
-  if (sh->block_size != pkv::kBlock)
-    return fail(PKV_EUNSUPPORTED, "block_size %d is not supported (16 only)", sh->block_size);
+  if (sh->block_size != 8 && sh->block_size != 16 && sh->block_size != 32)
+    return fail(PKV_EUNSUPPORTED, "block_size %d is not supported (8, 16 or 32)", sh->block_size);
   if (sh->head_dim != 64 && sh->head_dim != 128)
     return fail(PKV_EUNSUPPORTED, "head_dim %d is not supported (64 or 128)", sh->head_dim);
   if ((int64_t)sh->num_blocks * sh->block_size > INT32_MAX)
@@ -267,7 +267,12 @@ int need_device(const pkv_pool* p) {
   return PKV_OK;
 }
 
-int64_t nblk(int32_t tokens) { return (tokens + pkv::kBlock - 1) / pkv::kBlock; }
+// 16-token decode tiles of a sequence (the unit of decode work whatever the block size).
+int64_t nblk(int32_t tokens) { return (tokens + pkv::kTile - 1) / pkv::kTile; }
+// Block-table entries (blocks) a sequence of `tokens` tokens needs.
+int64_t nent(const pkv_pool* p, int64_t tokens) {
+  return (tokens + p->shape.block_size - 1) / p->shape.block_size;
+}
 
 // Cost, in tiles, of starting a segment inside a wave (balanced schedule).
 #ifndef PKV_SEG_START_COST
@@ -285,9 +290,10 @@ constexpr int64_t kSegStartCost = PKV_SEG_START_COST;
 bool build_bins(pkv_pool* p, int nbins);
 
 void build_schedule(pkv_pool* p, int part, int target) {
-  if (part == 0 && p->shape.dtype != PKV_F32) {  // fp32 tiles spill in the eight-wave form
+  // the eight-wave form: 2-byte and q8_0 tiles of 16-token blocks (fp32 tiles spill)
+  if (part == 0 && p->shape.dtype != PKV_F32 && p->shape.block_size == 16) {
     const int per_cu = pkv::decode_blocks_per_cu(p->shape.dtype, p->shape.head_dim,
-                                                  p->sched_gp_building, true);
+                                                  p->sched_gp_building, true, 16);
     if (per_cu > 0 && build_bins(p, std::max(1, p->num_cus) * per_cu)) return;
   }
   const int B = p->up_batch;
@@ -296,7 +302,7 @@ void build_schedule(pkv_pool* p, int part, int target) {
   const int64_t T = tseq * H;
   std::vector<int64_t> ws;
   if (part > 0) {
-    const int64_t pb = part / pkv::kBlock;
+    const int64_t pb = part / pkv::kTile;
     for (int g = 0; g < H; ++g)
       for (int s = 0; s < B; ++s) {
         const int64_t n = nblk(p->h_ctx[s]);
@@ -348,8 +354,12 @@ void build_schedule(pkv_pool* p, int part, int target) {
     d[3] = g;
     d[4] = (int32_t)j0;
     d[5] = p->h_ctx[s];
-    d[6] = p->h_bt[(size_t)s * p->up_stride + j0];
+    d[6] = p->h_bt[(size_t)s * p->up_stride + j0 * pkv::kTile / p->shape.block_size];
+    // 8-token blocks: the block holding rows 8..15 of the first tile (any
+    // valid block when the context ends before them)
     d[7] = 0;
+    if (p->shape.block_size == 8)
+      d[7] = 16 * j0 + 8 < p->h_ctx[s] ? p->h_bt[(size_t)s * p->up_stride + 2 * j0 + 1] : d[6];
   }
   bool multi = false;
   int w = 0;
@@ -371,7 +381,8 @@ void build_schedule(pkv_pool* p, int part, int target) {
 }
 
 int waves_target(const pkv_pool* p, int gp) {
-  int per_cu = pkv::decode_blocks_per_cu(p->shape.dtype, p->shape.head_dim, gp, false);
+  int per_cu = pkv::decode_blocks_per_cu(p->shape.dtype, p->shape.head_dim, gp, false,
+                                         p->shape.block_size);
   per_cu = std::max(1, std::min(per_cu, 32));
   return std::max(1, p->num_cus) * per_cu;
 }
@@ -492,7 +503,7 @@ bool build_bins(pkv_pool* p, int nbins) {
       d[3] = sg.g;
       d[4] = (int32_t)j0;
       d[5] = p->h_ctx[sg.s];
-      d[6] = p->h_bt[(size_t)sg.s * p->up_stride + j0];
+      d[6] = p->h_bt[(size_t)sg.s * p->up_stride + j0 * pkv::kTile / p->shape.block_size];
       const int64_t n0 = sg.cost - kSegStartCost;
       if (j0 == 0) {
         first_wave_of[seg_i] = wv;
@@ -554,7 +565,7 @@ int pkv_kv_pool_alloc(const pkv_shape* sh, void* dev_base, size_t dev_bytes, pkv
   p->tile_bytes = tile_bytes_of(sh);
   p->block_bytes = p->tile_bytes * sh->kv_heads;
   p->layer_bytes = p->block_bytes * sh->num_blocks;
-  p->max_blocks_per_seq = (int32_t)nblk(sh->max_seq_len);
+  p->max_blocks_per_seq = (int32_t)((sh->max_seq_len + sh->block_size - 1) / sh->block_size);
   p->refcount.assign(sh->num_blocks, 0);
   p->free_pos.assign(sh->num_blocks, -1);
   p->free_list.reserve(sh->num_blocks);
@@ -801,7 +812,7 @@ int pkv_prepare_append(pkv_pool* p, int32_t* bt, int batch, int max_blocks,
   std::vector<int32_t> before(batch), one(batch, 1);
   for (int s = 0; s < batch; ++s) {
     if (ctx[s] < 1 || ctx[s] > p->shape.max_seq_len ||
-        nblk(ctx[s]) > max_blocks)
+        nent(p, ctx[s]) > max_blocks)
       return fail(PKV_EINVAL, "sequence %d: context length %d outside [1, %d]", s, ctx[s],
                   std::min<int64_t>(p->shape.max_seq_len,
                                     (int64_t)max_blocks * p->shape.block_size));
@@ -825,11 +836,12 @@ int pkv_block_table_upload(pkv_pool* p, const int32_t* bt, int batch, int max_bl
   cum[0] = 0;
   for (int s = 0; s < batch; ++s) {
     const int32_t L = ctx[s];
-    if (L < 1 || L > p->shape.max_seq_len || nblk(L) > max_blocks)
+    const int BS = p->shape.block_size;
+    if (L < 1 || L > p->shape.max_seq_len || nent(p, L) > max_blocks)
       return fail(PKV_EINVAL, "sequence %d: context length %d outside [1, %d]", s, L,
-                  std::min<int64_t>(p->shape.max_seq_len, (int64_t)max_blocks * pkv::kBlock));
-    const int64_t n = nblk(L);
-    for (int64_t j = 0; j < n; ++j) {
+                  std::min<int64_t>(p->shape.max_seq_len, (int64_t)max_blocks * BS));
+    const int64_t n = nblk(L);  // tiles
+    for (int64_t j = 0; j < nent(p, L); ++j) {
       const int32_t b = bt[(int64_t)s * max_blocks + j];
       if (b < 0 || b >= p->shape.num_blocks)
         return fail(PKV_EINVAL, "sequence %d: block table entry %lld = %d out of range", s,
@@ -840,7 +852,8 @@ int pkv_block_table_upload(pkv_pool* p, const int32_t* bt, int batch, int max_bl
     cum[s + 1] = cum[s] + (int32_t)n;
   }
   if (slots) {
-    const int64_t lim = (int64_t)p->shape.num_blocks * pkv::kBlock;
+    const int BS = p->shape.block_size;
+    const int64_t lim = (int64_t)p->shape.num_blocks * BS;
     std::vector<int64_t> seen;
     seen.reserve(batch);
     for (int s = 0; s < batch; ++s) {
@@ -851,7 +864,7 @@ int pkv_block_table_upload(pkv_pool* p, const int32_t* bt, int batch, int max_bl
       if (slots[s] < 0) continue;
       const int32_t pos = ctx[s] - 1;
       const int64_t want =
-          (int64_t)bt[(int64_t)s * max_blocks + pos / pkv::kBlock] * pkv::kBlock + pos % pkv::kBlock;
+          (int64_t)bt[(int64_t)s * max_blocks + pos / BS] * BS + pos % BS;
       if (slots[s] != want)
         return fail(PKV_EINVAL, "sequence %d: slot %lld is not the table position %lld of its "
                     "new token", s, (long long)slots[s], (long long)want);
@@ -951,9 +964,9 @@ int pkv_kv_append(pkv_pool* p, int layer, const void* k_new, const void* v_new,
   hipError_t e =
       p->shape.dtype == PKV_Q8_0
           ? pkv::launch_append_q8(k_new, v_new, slots, batch, kl, vl, p->shape.kv_heads,
-                                  p->shape.head_dim, stream)
+                                  p->shape.head_dim, p->shape.block_size, stream)
           : pkv::launch_append(k_new, v_new, slots, batch, kl, vl, p->shape.kv_heads,
-                               (int)p->row_bytes, stream);
+                               (int)p->row_bytes, p->shape.block_size, stream);
   if (e != hipSuccess) return hip_fail(e, "kv_append launch");
   return PKV_OK;
 }
@@ -967,8 +980,8 @@ size_t pkv_decode_workspace_bytes(const pkv_pool* p, int batch, int q_heads,
   const int64_t nseg = (int64_t)batch * p->shape.kv_heads;
   int64_t waves;
   if (partition_tokens > 0) {
-    const int64_t pb = std::max(1, partition_tokens / pkv::kBlock);
-    waves = nseg * ((p->max_blocks_per_seq + pb - 1) / pb);
+    const int64_t pb = std::max(1, partition_tokens / pkv::kTile);
+    waves = nseg * ((nblk(p->shape.max_seq_len) + pb - 1) / pb);  // tiles per sequence
   } else {
     waves = std::max<int64_t>(1, std::max(p->num_cus, 1) * 32);
   }
@@ -1000,7 +1013,7 @@ int decode_impl(pkv_pool* p, int layer, const void* k_new, const void* v_new, co
   if (group > pkv::kMaxGroup)
     return fail(PKV_EUNSUPPORTED, "GQA group %d exceeds %d", group, pkv::kMaxGroup);
   if (!std::isfinite(scale)) return fail(PKV_EINVAL, "scale must be finite");
-  if (partition_tokens < 0 || partition_tokens % pkv::kBlock)
+  if (partition_tokens < 0 || partition_tokens % pkv::kTile)
     return fail(PKV_EINVAL, "partition_tokens %d must be 0 or a positive multiple of 16",
                 partition_tokens);
   const int gp = pkv::padded_group(group);
@@ -1071,7 +1084,8 @@ int decode_impl(pkv_pool* p, int layer, const void* k_new, const void* v_new, co
   dp.nwaves = W;
   const int groups = p->sched_bins ? W / 8 : W;  // workgroups: bins, or one per wave
   dp.waves_per_xcd = (groups + pkv::kNumXcd - 1) / pkv::kNumXcd;
-  e = pkv::launch_decode(p->shape.dtype, p->shape.head_dim, gp, p->sched_bins, dp, stream);
+  e = pkv::launch_decode(p->shape.dtype, p->shape.head_dim, gp, p->sched_bins,
+                         p->shape.block_size, dp, stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (p->sched_needs_merge) {
     pkv::ReduceParams rp{};
@@ -1213,7 +1227,7 @@ int pkv_pool_stats(const pkv_pool* p, int64_t stats[4]) {
   int64_t shared = 0;
   for (int32_t r : p->refcount) shared += r > 1;
   int64_t waste = 0;
-  for (int32_t L : p->h_ctx) waste += nblk(L) * pkv::kBlock - L;
+  for (int32_t L : p->h_ctx) waste += nent(p, L) * p->shape.block_size - L;
   stats[0] = (int64_t)avail(p);
   stats[1] = p->shape.num_blocks - stats[0];
   stats[2] = shared;

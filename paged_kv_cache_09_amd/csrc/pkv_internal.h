@@ -7,7 +7,7 @@
 
 namespace pkv {
 
-constexpr int kBlock = 16;       // tokens per block
+constexpr int kTile = 16;        // tokens per decode tile (a block of 16, half of 32, two of 8)
 constexpr int kMaxGroup = 8;     // largest GQA group (q heads per kv head)
 constexpr int kNumXcd = 8;       // MI355X: workgroups are dealt round-robin to 8 XCDs
 
@@ -55,19 +55,19 @@ inline int padded_group(int g) { return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : 8
 
 // bins: the eight-wave form that merges split segments in LDS (waves_per_xcd
 // then counts workgroups per XCD).
-hipError_t launch_decode(int dtype, int head_dim, int gp, bool bins, const DecodeParams& p,
-                         hipStream_t stream);
+hipError_t launch_decode(int dtype, int head_dim, int gp, bool bins, int block_size,
+                         const DecodeParams& p, hipStream_t stream);
 hipError_t launch_reduce(int head_dim, int gp, const ReduceParams& p, hipStream_t stream);
 // Workgroups of the decode kernel one CU can hold at once (occupancy), 0 on error.
-int decode_blocks_per_cu(int dtype, int head_dim, int gp, bool bins);
+int decode_blocks_per_cu(int dtype, int head_dim, int gp, bool bins, int block_size);
 
 hipError_t launch_append(const void* k_new, const void* v_new, const int64_t* slots, int batch,
                          void* k_layer, void* v_layer, int kv_heads, int row_bytes,
-                         hipStream_t stream);
+                         int block_size, hipStream_t stream);
 // q8_0 cache: quantise bf16 new rows [batch][kv_heads][head_dim] into the rows at `slots`.
 hipError_t launch_append_q8(const void* k_new, const void* v_new, const int64_t* slots,
                             int batch, void* k_layer, void* v_layer, int kv_heads, int head_dim,
-                            hipStream_t stream);
+                            int block_size, hipStream_t stream);
 // Copy `bytes` (a multiple of 16, both pointers 16-byte aligned) from mapped
 // pinned host memory to device memory with a kernel on `stream`.
 hipError_t launch_upload(const void* host_src, void* dst, size_t bytes, hipStream_t stream);

@@ -327,7 +327,9 @@ struct TileRegs<DT_Q8, D> {
 //     equally loaded; the bin's tiles are split evenly between its waves and
 //     a segment split between them is merged in LDS at the end (no partials
 //     in HBM, no reduce launch).
-template <int DT, int D, int GP, bool BINS>
+// BS: tokens per pool block (8, 16 or 32). Work is always counted in 16-token
+// tiles: a tile is one block (16), half of one (32), or two blocks (8).
+template <int DT, int D, int GP, bool BINS, int BS>
 __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p) {
   constexpr bool Q8 = DT == DT_Q8;
   using TR = TileRegs<DT, D>;
@@ -340,7 +342,9 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
   constexpr int EPC = Q8 ? 8 : 16 / Elem<DT>::bytes;  // elements per V chunk
   constexpr int NG = GP >= 4 ? GP / 4 : 1;  // lane groups (of 16) holding real heads
   constexpr int HPG = GP >= 4 ? 4 : GP;     // heads per lane group
-  constexpr int TILE = Q8 ? 16 * D + 16 * (D / 32) * 2 : 16 * RB;
+  // bytes of one (block, kv head) tile of the pool: BS rows (+ q8_0 scales)
+  constexpr int TILE = Q8 ? BS * D + BS * (D / 32) * 2 : BS * RB;
+  static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   // Tile buffers per wave. Three or four (more bytes in flight per wave) ran
   // slower than two on MI355X for both bf16 and q8_0 tiles.
   constexpr int NBUF = 2;
@@ -383,6 +387,8 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
   int L = desc[5];
   int blk_first = desc[6];
   const int merge_info = BINS ? desc[7] : 0;
+  // 8-token blocks: id of the block holding rows 8..15 of the run's first tile
+  int blk_second = BINS ? 0 : desc[7];
   const int s_first = s, g_first = g;
   bool first_seg = true;
 
@@ -403,7 +409,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     const int seg = g * p.batch + s;
     // Prefetch the next segment's length and first block id (scalar loads
     // in flight while this segment's tiles stream).
-    int next_s = s + 1, next_g = g, next_L = 0, next_blk = 0;
+    int next_s = s + 1, next_g = g, next_L = 0, next_blk = 0, next_second = 0;
     if constexpr (BINS) {
       if (x + take < xend) {  // bin lists hold (sequence, kv head, length, first block)
         const int* e = p.seglist + 4 * (li + 1);
@@ -420,6 +426,10 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       if (x + take < xend) {
         next_L = p.ctx[next_s];
         next_blk = p.bt[(size_t)next_s * p.bt_stride];
+        // 8-token blocks: the second entry (padding -1 when absent: any block,
+        // its rows are past the context)
+        if constexpr (BS == 8)
+          next_second = p.bt_stride > 1 ? max(p.bt[(size_t)next_s * p.bt_stride + 1], 0) : 0;
       }
     }
     const char* kbase = reinterpret_cast<const char*>(p.k) + (size_t)g * TILE;
@@ -438,40 +448,57 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     const int Lc = L - (app ? 1 : 0);         // rows already in the pool
     const int j1c = min(j1, (Lc + 15) >> 4);  // tiles holding cached rows
 
-    auto load_tile = [&](int blk, TR& t) {
-      const char* ktile = kbase + (size_t)blk * blk_stride;
-      const char* vtile = vbase + (size_t)blk * blk_stride;
+    // Load tile rows 0..15 (tokens 16*j .. 16*j+15 of the sequence): block a
+    // holds them (BS = 16), or rows 16*half .. of it (BS = 32), or rows 0..7
+    // while block b holds rows 8..15 (BS = 8).
+    auto load_tile = [&](int a, int b, int half, TR& t) {
+      auto blk_of = [&](int r) { return BS == 8 ? (r < 8 ? a : b) : a; };
+      auto rib = [&](int r) { return BS == 8 ? (r & 7) : BS == 32 ? 16 * half + r : r; };
+      const char* ktile = kbase + (size_t)blk_of(t16) * blk_stride;
+      const int kr = rib(t16);
       if constexpr (Q8) {
-        const char* kt = ktile + t16 * D + kg * 8;
+        const char* kt = ktile + kr * D + kg * 8;
 #pragma unroll
         for (int k = 0; k < NP; ++k) t.k[k] = ld8(kt + k * 32);
-        const char* vt = vtile + NV * vr * D + vc * 8;
+        // the lane's NV consecutive V rows lie in one block
+        const int r0 = NV * vr;
+        const char* vtile = vbase + (size_t)blk_of(r0) * blk_stride;
+        const int vrr = rib(r0);
+        const char* vt = vtile + vrr * D + vc * 8;
 #pragma unroll
         for (int i = 0; i < NV; ++i) t.v[i] = ld8(vt + i * D);
-        // scales after the 16 x D codes: K [row][group], V [group][row]
-        const char* ksp = ktile + 16 * D + t16 * NP * 2;
-        const char* vsp = vtile + 16 * D + ((vc >> 2) * 16 + NV * vr) * 2;
+        // scales after the BS x D codes: K [row][group], V [group][row]
+        const char* ksp = ktile + BS * D + kr * NP * 2;
+        const char* vsp = vtile + BS * D + ((vc >> 2) * BS + vrr) * 2;
         if constexpr (NP == 4) {
-          const u32x2 a = ld8(ksp);
-          t.ks[0] = a[0];
-          t.ks[1] = a[1];
+          const u32x2 x2 = ld8(ksp);
+          t.ks[0] = x2[0];
+          t.ks[1] = x2[1];
         } else {
           t.ks[0] = ld4(ksp);
         }
         if constexpr (NV == 4) {
-          const u32x2 a = ld8(vsp);
-          t.vs[0] = a[0];
-          t.vs[1] = a[1];
+          const u32x2 x2 = ld8(vsp);
+          t.vs[0] = x2[0];
+          t.vs[1] = x2[1];
         } else {
           t.vs[0] = ld4(vsp);
         }
       } else {
-        const char* kt = ktile + t16 * RB + kg * 16;
+        const char* kt = ktile + kr * RB + kg * 16;
 #pragma unroll
         for (int k = 0; k < NP; ++k) t.k[k] = ld16(kt + k * 64);
-        const char* vt = vtile + vr * RB + vc * 16;
+        if constexpr (BS == 8) {
+          // row vr + RPI*i (vr < RPI, RPI divides 8) lies in block a iff RPI*i < 8
 #pragma unroll
-        for (int i = 0; i < NV; ++i) t.v[i] = ld16(vt + i * RPI * RB);
+          for (int i = 0; i < NV; ++i)
+            t.v[i] = ld16(vbase + (size_t)(RPI * i < 8 ? a : b) * blk_stride +
+                          ((vr + RPI * i) & 7) * RB + vc * 16);
+        } else {
+          const char* vt = vbase + (size_t)a * blk_stride + rib(vr) * RB + vc * 16;
+#pragma unroll
+          for (int i = 0; i < NV; ++i) t.v[i] = ld16(vt + i * RPI * RB);
+        }
       }
     };
 
@@ -588,23 +615,54 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     };
 
     // Tiles stream through NBUF register buffers: NBUF - 1 tiles are in
-    // flight while one is computed. Block ids come 64 at a time, one per lane.
-    for (int jb = j0; jb < j1c; jb += 64) {
-      const int nb = min(64, j1c - jb);
-      const int b0 = jb == j0 ? blk_first : bt_row[jb];
+    // flight while one is computed. Block-table entries come one per lane, 64
+    // at a time (the tiles of 64 entries: 64, 128 or 32 of them).
+    constexpr int CH = BS == 8 ? 32 : 64;  // tiles per chunk of entries
+    const int nent_seq = (L + BS - 1) / BS;
+    for (int jb = j0; jb < j1c; jb += CH) {
+      const int nb = min(CH, j1c - jb);
+      const int e0 = BS == 32 ? (jb >> 1) : BS == 8 ? 2 * jb : jb;
       TR t[NBUF];
-      load_tile(b0, t[0]);
-      const int my_blk = lane < nb ? bt_row[jb + lane] : 0;
+      // The run's first block id(s) are in the descriptor: the first tile is
+      // requested before the entries (the first wait must not cover that load).
+      if constexpr (BS == 16) {
+        load_tile(jb == j0 ? blk_first : bt_row[jb], 0, 0, t[0]);
+      } else if constexpr (BS == 32) {
+        load_tile(jb == j0 ? blk_first : bt_row[jb >> 1], 0, jb & 1, t[0]);
+      } else {
+        const int second = 2 * jb + 1 < nent_seq ? bt_row[2 * jb + 1] : 0;
+        load_tile(jb == j0 ? blk_first : bt_row[2 * jb], jb == j0 ? blk_second : second, 0, t[0]);
+      }
+      // up to 64 entries: CH tiles need CH (16), 2 * CH = 64 (8) or CH / 2 + 1 (32)
+      const int my_ent = e0 + lane < nent_seq ? bt_row[e0 + lane] : 0;
+      // block ids of chunk tile j: (a, b, half)
+      auto tile_ids = [&](int j, int& a, int& b, int& half) {
+        if constexpr (BS == 16) {
+          a = b = __builtin_amdgcn_readlane(my_ent, j);
+          half = 0;
+        } else if constexpr (BS == 32) {
+          a = b = __builtin_amdgcn_readlane(my_ent, ((jb + j) >> 1) - (jb >> 1));
+          half = (jb + j) & 1;
+        } else {
+          a = __builtin_amdgcn_readlane(my_ent, 2 * j);
+          b = __builtin_amdgcn_readlane(my_ent, 2 * j + 1);
+          half = 0;
+        }
+      };
+      auto load_j = [&](int j, TR& t) {
+        int a, b, half;
+        tile_ids(j, a, b, half);
+        load_tile(a, b, half, t);
+      };
 #pragma unroll
       for (int u = 1; u < NBUF - 1; ++u)
-        if (u < nb) load_tile(__builtin_amdgcn_readlane(my_blk, u), t[u]);
+        if (u < nb) load_j(u, t[u]);
       for (int jj = 0; jj < nb; jj += NBUF) {
 #pragma unroll
         for (int u = 0; u < NBUF; ++u) {
           const int j = jj + u;
           if (j < nb) {
-            if (j + NBUF - 1 < nb)
-              load_tile(__builtin_amdgcn_readlane(my_blk, j + NBUF - 1), t[(u + NBUF - 1) % NBUF]);
+            if (j + NBUF - 1 < nb) load_j(j + NBUF - 1, t[(u + NBUF - 1) % NBUF]);
             compute_tile(min(16, Lc - 16 * (jb + j)), t[u]);
           }
         }
@@ -613,8 +671,8 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     if (app && j1 == nblk) {
       // The new token: every lane loads the k_new / v_new row as row 0 of a
       // one-row tile; the lanes of row 0 store it into the pool.
-      const int blk_last = bt_row[nblk - 1];
-      const int t_new = (L - 1) & 15;
+      const int blk_last = bt_row[(L - 1) / BS];
+      const int t_new = (L - 1) % BS;  // the new row inside its block
       char* ktile = const_cast<char*>(kbase) + (size_t)blk_last * blk_stride;
       char* vtile = const_cast<char*>(vbase) + (size_t)blk_last * blk_stride;
       TR tn;
@@ -655,7 +713,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
           if (vr == 0) {
             *reinterpret_cast<u32x2*>(vtile + t_new * D + vc * 8) = c;
             if ((vc & 3) == 0)
-              *reinterpret_cast<unsigned short*>(vtile + 16 * D + ((vc >> 2) * 16 + t_new) * 2) =
+              *reinterpret_cast<unsigned short*>(vtile + BS * D + ((vc >> 2) * BS + t_new) * 2) =
                   (unsigned short)tn.vs[0];
           }
         }
@@ -664,7 +722,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
           for (int k = 0; k < NP; ++k)
             *reinterpret_cast<u32x2*>(ktile + t_new * D + kg * 8 + k * 32) = tn.k[k];
           if (kg == 0) {
-            char* ksp = ktile + 16 * D + t_new * NP * 2;
+            char* ksp = ktile + BS * D + t_new * NP * 2;
             if constexpr (NP == 4) *reinterpret_cast<u32x2*>(ksp) = u32x2{tn.ks[0], tn.ks[1]};
             else *reinterpret_cast<unsigned*>(ksp) = tn.ks[0];
           }
@@ -754,6 +812,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     j0 = 0;
     L = next_L;
     blk_first = next_blk;
+    blk_second = next_second;
     ++li;
     first_seg = false;
   }
@@ -818,7 +877,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
 __global__ __launch_bounds__(256) void append_kernel(const char* k_new, const char* v_new,
                                                      const int64_t* slots, int batch,
                                                      char* k_layer, char* v_layer, int kv_heads,
-                                                     int row_bytes) {
+                                                     int row_bytes, int block_size) {
   const int per_row = row_bytes / 16;
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   const int chunk = (int)(idx % per_row);
@@ -830,11 +889,11 @@ __global__ __launch_bounds__(256) void append_kernel(const char* k_new, const ch
   if (s >= batch) return;
   const int64_t slot = slots[s];
   if (slot < 0) return;
-  const int64_t blk = slot >> 4;
-  const int64_t pos = slot & 15;
+  const int64_t blk = slot / block_size;
+  const int64_t pos = slot % block_size;
   const char* src = (kv ? v_new : k_new) + ((size_t)s * kv_heads + g) * row_bytes + chunk * 16;
-  char* dst = (kv ? v_layer : k_layer) + (((size_t)blk * kv_heads + g) * 16 + pos) * row_bytes +
-              chunk * 16;
+  char* dst = (kv ? v_layer : k_layer) +
+              (((size_t)blk * kv_heads + g) * block_size + pos) * row_bytes + chunk * 16;
   *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
 }
 
@@ -845,9 +904,10 @@ template <int D>
 __global__ __launch_bounds__(256) void append_q8_kernel(const char* k_new, const char* v_new,
                                                         const int64_t* slots, int batch,
                                                         char* k_layer, char* v_layer,
-                                                        int kv_heads) {
+                                                        int kv_heads, int block_size) {
   constexpr int NGR = D / 32;
-  constexpr int TILE = 16 * D + 16 * NGR * 2;
+  const int BS = block_size;
+  const int TILE = BS * D + BS * NGR * 2;
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   const int grp = (int)(idx % NGR);
   long r = idx / NGR;
@@ -858,8 +918,8 @@ __global__ __launch_bounds__(256) void append_q8_kernel(const char* k_new, const
   if (s >= batch) return;
   const int64_t slot = slots[s];
   if (slot < 0) return;
-  const int64_t blk = slot >> 4;
-  const int pos = (int)(slot & 15);
+  const int64_t blk = slot / BS;
+  const int pos = (int)(slot % BS);
   const char* src = (kv ? v_new : k_new) + (((size_t)s * kv_heads + g) * D + grp * 32) * 2;
   float x[4][8];
   float a = 0.f;
@@ -878,8 +938,8 @@ __global__ __launch_bounds__(256) void append_q8_kernel(const char* k_new, const
     const u32x2 hi = q8_codes(x[c + 1], a, &d);
     *reinterpret_cast<u32x4*>(dst + c * 8) = u32x4{lo[0], lo[1], hi[0], hi[1]};
   }
-  const int si = kv ? grp * 16 + pos : pos * NGR + grp;
-  *reinterpret_cast<unsigned short*>(tile + 16 * D + si * 2) = (unsigned short)half_bits(d);
+  const int si = kv ? grp * BS + pos : pos * NGR + grp;
+  *reinterpret_cast<unsigned short*>(tile + BS * D + si * 2) = (unsigned short)half_bits(d);
 }
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(const int32_t* pairs, int layers,
@@ -907,38 +967,44 @@ __global__ __launch_bounds__(256) void upload_kernel(const u32x4* __restrict__ s
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
+// The bins form is built for 16-token blocks only.
 template <int DT, int D, int GP>
-const void* decode_fn(bool bins) {
-  return bins ? reinterpret_cast<const void*>(&decode_kernel<DT, D, GP, true>)
-              : reinterpret_cast<const void*>(&decode_kernel<DT, D, GP, false>);
+const void* decode_fn(bool bins, int bs) {
+  if (bs == 16)
+    return bins ? reinterpret_cast<const void*>(&decode_kernel<DT, D, GP, true, 16>)
+                : reinterpret_cast<const void*>(&decode_kernel<DT, D, GP, false, 16>);
+  if (bins) return nullptr;
+  if (bs == 8) return reinterpret_cast<const void*>(&decode_kernel<DT, D, GP, false, 8>);
+  if (bs == 32) return reinterpret_cast<const void*>(&decode_kernel<DT, D, GP, false, 32>);
+  return nullptr;
 }
 
 template <int DT, int D>
-const void* pick_gp(int gp, bool bins) {
+const void* pick_gp(int gp, bool bins, int bs) {
   switch (gp) {
-    case 1: return decode_fn<DT, D, 1>(bins);
-    case 2: return decode_fn<DT, D, 2>(bins);
-    case 4: return decode_fn<DT, D, 4>(bins);
-    case 8: return decode_fn<DT, D, 8>(bins);
+    case 1: return decode_fn<DT, D, 1>(bins, bs);
+    case 2: return decode_fn<DT, D, 2>(bins, bs);
+    case 4: return decode_fn<DT, D, 4>(bins, bs);
+    case 8: return decode_fn<DT, D, 8>(bins, bs);
   }
   return nullptr;
 }
 
 template <int DT>
-const void* pick_d(int d, int gp, bool bins) {
+const void* pick_d(int d, int gp, bool bins, int bs) {
   switch (d) {
-    case 64: return pick_gp<DT, 64>(gp, bins);
-    case 128: return pick_gp<DT, 128>(gp, bins);
+    case 64: return pick_gp<DT, 64>(gp, bins, bs);
+    case 128: return pick_gp<DT, 128>(gp, bins, bs);
   }
   return nullptr;
 }
 
-const void* decode_kernel_for(int dtype, int d, int gp, bool bins) {
+const void* decode_kernel_for(int dtype, int d, int gp, bool bins, int bs) {
   switch (dtype) {
-    case DT_F32: return pick_d<DT_F32>(d, gp, bins);
-    case DT_F16: return pick_d<DT_F16>(d, gp, bins);
-    case DT_BF16: return pick_d<DT_BF16>(d, gp, bins);
-    case DT_Q8: return pick_d<DT_Q8>(d, gp, bins);
+    case DT_F32: return pick_d<DT_F32>(d, gp, bins, bs);
+    case DT_F16: return pick_d<DT_F16>(d, gp, bins, bs);
+    case DT_BF16: return pick_d<DT_BF16>(d, gp, bins, bs);
+    case DT_Q8: return pick_d<DT_Q8>(d, gp, bins, bs);
   }
   return nullptr;
 }
@@ -956,9 +1022,9 @@ const void* reduce_for_gp(int gp) {
 
 }  // namespace
 
-hipError_t launch_decode(int dtype, int head_dim, int gp, bool bins, const DecodeParams& p,
-                         hipStream_t stream) {
-  const void* fn = decode_kernel_for(dtype, head_dim, gp, bins);
+hipError_t launch_decode(int dtype, int head_dim, int gp, bool bins, int block_size,
+                         const DecodeParams& p, hipStream_t stream) {
+  const void* fn = decode_kernel_for(dtype, head_dim, gp, bins, block_size);
   if (!fn) return hipErrorInvalidValue;
   DecodeParams args = p;
   void* argv[] = {&args};
@@ -966,8 +1032,8 @@ hipError_t launch_decode(int dtype, int head_dim, int gp, bool bins, const Decod
   return hipLaunchKernel(fn, grid, block, argv, 0, stream);
 }
 
-int decode_blocks_per_cu(int dtype, int head_dim, int gp, bool bins) {
-  const void* fn = decode_kernel_for(dtype, head_dim, gp, bins);
+int decode_blocks_per_cu(int dtype, int head_dim, int gp, bool bins, int block_size) {
+  const void* fn = decode_kernel_for(dtype, head_dim, gp, bins, block_size);
   if (!fn) return 0;
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, bins ? 512 : 64, 0) != hipSuccess)
@@ -987,19 +1053,19 @@ hipError_t launch_reduce(int head_dim, int gp, const ReduceParams& p, hipStream_
 
 hipError_t launch_append(const void* k_new, const void* v_new, const int64_t* slots, int batch,
                          void* k_layer, void* v_layer, int kv_heads, int row_bytes,
-                         hipStream_t stream) {
+                         int block_size, hipStream_t stream) {
   const long threads = (long)batch * kv_heads * 2 * (row_bytes / 16);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   hipLaunchKernelGGL(append_kernel, dim3(blocks), dim3(256), 0, stream,
                      static_cast<const char*>(k_new), static_cast<const char*>(v_new), slots,
                      batch, static_cast<char*>(k_layer), static_cast<char*>(v_layer), kv_heads,
-                     row_bytes);
+                     row_bytes, block_size);
   return hipGetLastError();
 }
 
 hipError_t launch_append_q8(const void* k_new, const void* v_new, const int64_t* slots,
                             int batch, void* k_layer, void* v_layer, int kv_heads, int head_dim,
-                            hipStream_t stream) {
+                            int block_size, hipStream_t stream) {
   const long threads = (long)batch * kv_heads * 2 * (head_dim / 32);
   const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
   const char* kn = static_cast<const char*>(k_new);
@@ -1008,10 +1074,10 @@ hipError_t launch_append_q8(const void* k_new, const void* v_new, const int64_t*
   char* vl = static_cast<char*>(v_layer);
   if (head_dim == 128)
     hipLaunchKernelGGL(append_q8_kernel<128>, grid, block, 0, stream, kn, vn, slots, batch, kl, vl,
-                       kv_heads);
+                       kv_heads, block_size);
   else if (head_dim == 64)
     hipLaunchKernelGGL(append_q8_kernel<64>, grid, block, 0, stream, kn, vn, slots, batch, kl, vl,
-                       kv_heads);
+                       kv_heads, block_size);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

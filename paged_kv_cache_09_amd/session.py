@@ -31,9 +31,9 @@ class DecodeSession:
         cfg = w.cfg
         self.w = w
         self.cfg = cfg
-        msl = max_seq_len if max_seq_len is not None else w.max_blocks * 16
+        msl = max_seq_len if max_seq_len is not None else w.max_blocks * cfg.block_size
         self.shape = pkv.make_shape(w.layers, cfg.num_blocks, cfg.kv_heads, cfg.head_dim,
-                                    cfg.dtype, msl, cfg.batch)
+                                    cfg.dtype, msl, cfg.batch, block_size=cfg.block_size)
         need = pkv.pool_bytes(self.shape)
         if w.pool.numel() < need:
             raise ValueError(f"pool tensor holds {w.pool.numel()} bytes, need {need}")

@@ -55,8 +55,8 @@ def row_bytes(cfg) -> int:
 
 
 def tile_bytes(cfg) -> int:
-    """Bytes of one (block, kv head) tile of K (or V)."""
-    return BLOCK * row_bytes(cfg)
+    """Bytes of one (block, kv head) tile of K (or V): block_size rows."""
+    return cfg.block_size * row_bytes(cfg)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -78,6 +78,7 @@ class Config:
     prefix_tokens: int = 0   # shared-prefix workloads
     suffix_hi: int = 0
     partition_tokens: int = 0  # split-K partition the workload is quoted with (0: none)
+    block_size: int = 16       # tokens per pool block (8, 16 or 32)
 
 
 CONFIGS = {
@@ -132,7 +133,7 @@ def draw_lengths(cfg: Config, rng: np.random.Generator) -> np.ndarray:
         ctx = rng.integers(cfg.ctx_lo, cfg.ctx_hi + 1, size=B)
         # redraw lengths whose last block would be exactly full
         while True:
-            full = ctx % BLOCK == 0
+            full = ctx % cfg.block_size == 0
             if not full.any():
                 break
             ctx[full] = rng.integers(cfg.ctx_lo, cfg.ctx_hi + 1, size=int(full.sum()))
@@ -145,8 +146,8 @@ def draw_lengths(cfg: Config, rng: np.random.Generator) -> np.ndarray:
     return ctx.astype(np.int32)
 
 
-def _nblk(n_tokens: int) -> int:
-    return (n_tokens + BLOCK - 1) // BLOCK
+def _nblk(n_tokens: int, block_size: int = BLOCK) -> int:
+    return (n_tokens + block_size - 1) // block_size
 
 
 @dataclasses.dataclass
@@ -207,7 +208,7 @@ def pool_layer_views(pool: torch.Tensor, cfg: Config, layers: int, layer: int):
     if cfg.dtype == Q8_0:
         shape = (layers, cfg.num_blocks, cfg.kv_heads, tile_bytes(cfg))
         return pool[:n].view(shape)[layer], pool[n:2 * n].view(shape)[layer]
-    shape = (layers, cfg.num_blocks, cfg.kv_heads, BLOCK, cfg.head_dim)
+    shape = (layers, cfg.num_blocks, cfg.kv_heads, cfg.block_size, cfg.head_dim)
     tdt = TORCH_DTYPE[cfg.dtype]
     return pool[:n].view(tdt).view(shape)[layer], pool[n:2 * n].view(tdt).view(shape)[layer]
 
@@ -220,12 +221,13 @@ def _fill_q8(pool: torch.Tensor, cfg: Config, layers: int, gen: torch.Generator,
     tiles = pool.view(2 * layers * cfg.num_blocks * cfg.kv_heads, tile_bytes(cfg))
     for i in range(0, tiles.shape[0], max(1, chunk // tiles.shape[1])):
         part = tiles[i:i + max(1, chunk // tiles.shape[1])]
-        codes = torch.randint(-127, 128, (part.shape[0], BLOCK * D), generator=gen,
+        BS = cfg.block_size
+        codes = torch.randint(-127, 128, (part.shape[0], BS * D), generator=gen,
                               device=pool.device, dtype=torch.int16)
-        part[:, :BLOCK * D].copy_(codes.to(torch.int8).view(torch.uint8))
-        sc = torch.rand((part.shape[0], BLOCK * (D // Q8_GROUP)), generator=gen,
+        part[:, :BS * D].copy_(codes.to(torch.int8).view(torch.uint8))
+        sc = torch.rand((part.shape[0], BS * (D // Q8_GROUP)), generator=gen,
                         device=pool.device, dtype=torch.float32) * 0.025 + 0.005
-        part[:, BLOCK * D:].copy_(sc.to(torch.float16).view(torch.uint8).view(part.shape[0], -1))
+        part[:, BS * D:].copy_(sc.to(torch.float16).view(torch.uint8).view(part.shape[0], -1))
 
 
 def _fill_normal(t: torch.Tensor, sigma: float, gen: torch.Generator, chunk: int = 1 << 26):
@@ -260,7 +262,7 @@ def make(cfg: Config, *, device="cpu", layers: int | None = None, form: str = "s
     pre_tables = [[] for _ in range(B)]
     shared = []
     if cfg.ctx_kind == "shared_prefix":
-        prefix = [next(take) for _ in range(_nblk(cfg.prefix_tokens))]
+        prefix = [next(take) for _ in range(_nblk(cfg.prefix_tokens, cfg.block_size))]
         for s in range(B):
             pre_tables[s] = list(prefix)
         shared = [(b, B) for b in prefix]
@@ -269,13 +271,13 @@ def make(cfg: Config, *, device="cpu", layers: int | None = None, form: str = "s
         first_private = 0
     for s in range(B):
         cached = int(ctx[s]) - 1
-        for _ in range(first_private, _nblk(cached)):
+        for _ in range(first_private, _nblk(cached, cfg.block_size)):
             pre_tables[s].append(next(take))
     new_blocks = np.full(B, -1, dtype=np.int32)
     for s in range(B):
-        if _nblk(int(ctx[s])) > len(pre_tables[s]):
+        if _nblk(int(ctx[s]), cfg.block_size) > len(pre_tables[s]):
             new_blocks[s] = next(take)
-    max_blocks = max(_nblk(int(c)) for c in ctx) + extra_blocks
+    max_blocks = max(_nblk(int(c), cfg.block_size) for c in ctx) + extra_blocks
     if not tensors:
         return Workload(cfg, layers, ctx, pre_tables, new_blocks, shared, max_blocks, None, None,
                         None, None, form)
@@ -299,14 +301,15 @@ def make(cfg: Config, *, device="cpu", layers: int | None = None, form: str = "s
 
     if fill == "nan":
         # rows that hold a token: cached ones (and the new one in "decode" form)
-        valid = np.zeros((cfg.num_blocks, BLOCK), dtype=bool)
+        BS = cfg.block_size
+        valid = np.zeros((cfg.num_blocks, BS), dtype=bool)
         for s in range(B):
             n_tok = int(ctx[s]) - (1 if form == "step" else 0)
             row_blocks = list(pre_tables[s])
             if form == "decode" and new_blocks[s] >= 0:
                 row_blocks.append(int(new_blocks[s]))
             for j, b in enumerate(row_blocks):
-                rows = min(BLOCK, n_tok - j * BLOCK)
+                rows = min(BS, n_tok - j * BS)
                 if rows > 0:
                     valid[b, :rows] = True
         mask = torch.from_numpy(~valid).to(device)
@@ -316,15 +319,15 @@ def make(cfg: Config, *, device="cpu", layers: int | None = None, form: str = "s
             ng = cfg.head_dim // Q8_GROUP
             shape = (layers, cfg.num_blocks, cfg.kv_heads, tile_bytes(cfg))
             for r, region in enumerate((pool[:nb], pool[nb:2 * nb])):
-                sc = region.view(shape)[..., BLOCK * cfg.head_dim:].view(torch.float16)
+                sc = region.view(shape)[..., BS * cfg.head_dim:].view(torch.float16)
                 if r == 0:
-                    sc.view(layers, cfg.num_blocks, cfg.kv_heads, BLOCK, ng).masked_fill_(
+                    sc.view(layers, cfg.num_blocks, cfg.kv_heads, BS, ng).masked_fill_(
                         mask[None, :, None, :, None], float("nan"))
                 else:
-                    sc.view(layers, cfg.num_blocks, cfg.kv_heads, ng, BLOCK).masked_fill_(
+                    sc.view(layers, cfg.num_blocks, cfg.kv_heads, ng, BS).masked_fill_(
                         mask[None, :, None, None, :], float("nan"))
         else:
-            shape = (layers, cfg.num_blocks, cfg.kv_heads, BLOCK, cfg.head_dim)
+            shape = (layers, cfg.num_blocks, cfg.kv_heads, BS, cfg.head_dim)
             typed = pool.view(tdt)
             n = nb // ELEM_BYTES[cfg.dtype]
             for region in (typed[:n], typed[n:2 * n]):

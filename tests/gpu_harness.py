@@ -71,17 +71,19 @@ class OracleSide:
         self.max_blocks = w.max_blocks
 
     def run(self):
+        bs = self.cfg.block_size
         self.table, self.kinds = ostep.run_step(
             self.k, self.v, self.pre, self.shared, self.ctx,
             [self.k_new] * self.layers, [self.v_new] * self.layers, dtype=self.cfg.dtype,
-            num_blocks=self.nb, max_blocks=self.max_blocks)
+            num_blocks=self.nb, max_blocks=self.max_blocks, block_size=bs)
         self.out = [oracle.decode(self.k[l], self.v[l], self.table, self.ctx, self.q,
-                                  W.attn_scale(self.cfg), dtype=self.cfg.dtype)
+                                  W.attn_scale(self.cfg), dtype=self.cfg.dtype, block_size=bs)
                     for l in range(self.layers)]
         return self
 
     def logical(self, layer):
-        return ostep.logical_rows(self.k[layer], self.v[layer], self.table, self.ctx)
+        return ostep.logical_rows(self.k[layer], self.v[layer], self.table, self.ctx,
+                                  self.cfg.block_size)
 
 
 def gpu_logical(sess: DecodeSession, layer: int, seqs):
@@ -92,13 +94,14 @@ def gpu_logical(sess: DecodeSession, layer: int, seqs):
     for s in seqs:
         L = int(sess.ctx[s])
         t = torch.arange(L, device=k.device)
-        blocks = torch.from_numpy(sess.table[s].astype(np.int64)).to(k.device)[t // 16]
-        rows = t % 16
+        bs = sess.cfg.block_size
+        blocks = torch.from_numpy(sess.table[s].astype(np.int64)).to(k.device)[t // bs]
+        rows = t % bs
         if k.dtype == torch.uint8:
             kt, vt = to_storage(k[blocks]), to_storage(v[blocks])
             idx = np.arange(L)
-            res.append((ostep.q8_row_bytes(kt, idx, rows.cpu().numpy(), False),
-                        ostep.q8_row_bytes(vt, idx, rows.cpu().numpy(), True)))
+            res.append((ostep.q8_row_bytes(kt, idx, rows.cpu().numpy(), False, bs),
+                        ostep.q8_row_bytes(vt, idx, rows.cpu().numpy(), True, bs)))
         else:
             res.append((to_storage(k[blocks, :, rows, :]), to_storage(v[blocks, :, rows, :])))
     return res
@@ -165,16 +168,17 @@ def _check_untouched(w, before, slots, pairs, layers):
     cfg = w.cfg
     if cfg.dtype == W.Q8_0:
         return _check_untouched_q8(w, before, slots, pairs, layers)
-    shape = (2, layers, cfg.num_blocks, cfg.kv_heads, 16, cfg.head_dim * W.ELEM_BYTES[cfg.dtype])
+    bs = cfg.block_size
+    shape = (2, layers, cfg.num_blocks, cfg.kv_heads, bs, cfg.head_dim * W.ELEM_BYTES[cfg.dtype])
     a = w.pool.view(shape)
     b = before.view(shape)
-    changed = (a != b).any(dim=-1)  # [2][layers][NB][Hkv][16]
+    changed = (a != b).any(dim=-1)  # [2][layers][NB][Hkv][block_size]
     allowed = torch.zeros_like(changed)
     for dst in (int(p[1]) for p in pairs):
         allowed[:, :, dst] = True
     for sl in slots:
         if sl >= 0:
-            allowed[:, :, int(sl) // 16, :, int(sl) % 16] = True
+            allowed[:, :, int(sl) // bs, :, int(sl) % bs] = True
     bad = changed & ~allowed
     assert not bool(bad.any()), f"{int(bad.sum())} rows changed outside the written slots"
 
@@ -195,11 +199,12 @@ def _check_untouched_q8(w, before, slots, pairs, layers):
     for sl in slots:
         if sl < 0:
             continue
-        b, r = int(sl) // 16, int(sl) % 16
+        bs = cfg.block_size
+        b, r = int(sl) // bs, int(sl) % bs
         allowed[:, :, b, :, r * D:(r + 1) * D] = True
         for grp in range(ng):
-            ik = 16 * D + 2 * (r * ng + grp)
-            iv = 16 * D + 2 * (grp * 16 + r)
+            ik = bs * D + 2 * (r * ng + grp)
+            iv = bs * D + 2 * (grp * bs + r)
             allowed[0, :, b, :, ik:ik + 2] = True
             allowed[1, :, b, :, iv:iv + 2] = True
     bad = changed & ~allowed
@@ -210,7 +215,7 @@ def run_write_case(cfg, n_lo, n_hi, *, layers=2, partitions=(0, 48, 1 << 20), la
     """Multi-token write (prefill chunk) of every layer, then decode; against the oracle."""
     say(f"write case {label}: build workload B={cfg.batch} layers={layers}")
     w = W.make(cfg, device="cuda", layers=layers, form="step", fill="nan",
-               extra_blocks=(n_hi + 15) // 16 + 1)
+               extra_blocks=(n_hi + cfg.block_size - 1) // cfg.block_size + 1)
     before_ctx, n_new, k_rows, v_rows = W.write_rows(w, n_lo, n_hi)
     after_ctx = before_ctx + n_new
     ks, vs = [], []
@@ -222,10 +227,12 @@ def run_write_case(cfg, n_lo, n_hi, *, layers=2, partitions=(0, 48, 1 << 20), la
     say(f"write case {label}: oracle, {int(n_new.sum())} rows")
     table_o, _ = ostep.run_write(ks, vs, w.pre_tables, w.shared, before_ctx, n_new,
                                  [kr] * layers, [vr] * layers, dtype=cfg.dtype,
-                                 num_blocks=cfg.num_blocks, max_blocks=w.max_blocks)
+                                 num_blocks=cfg.num_blocks, max_blocks=w.max_blocks,
+                                 block_size=cfg.block_size)
     q = to_storage(w.q)
     ora_out = [oracle.decode(ks[l], vs[l], table_o, after_ctx, q, W.attn_scale(cfg),
-                             dtype=cfg.dtype) for l in range(layers)]
+                             dtype=cfg.dtype, block_size=cfg.block_size)
+               for l in range(layers)]
     before = w.pool.clone()
     sess = DecodeSession(w)
     say(f"write case {label}: GPU write + decode partitions={list(partitions)}")
@@ -248,7 +255,7 @@ def run_write_case(cfg, n_lo, n_hi, *, layers=2, partitions=(0, 48, 1 << 20), la
     seqs = list(range(w.B))
     for layer in range(layers):
         mine = gpu_logical(sess, layer, seqs)
-        theirs = ostep.logical_rows(ks[layer], vs[layer], table_o, after_ctx)
+        theirs = ostep.logical_rows(ks[layer], vs[layer], table_o, after_ctx, cfg.block_size)
         for s in seqs:
             assert mine[s][0].tobytes() == theirs[s][0].tobytes(), f"K rows of seq {s} layer {layer}"
             assert mine[s][1].tobytes() == theirs[s][1].tobytes(), f"V rows of seq {s} layer {layer}"

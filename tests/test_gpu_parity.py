@@ -58,6 +58,21 @@ SMALL = {
                               num_blocks=200),
     "q8_long_small": W.scaled(W.CONFIGS["long_ctx_bf16"], dtype=W.Q8_0, batch=2,
                               ctx_fixed=(4097, 3001), num_blocks=500),
+    # block sizes 8 and 32 (tiles of two blocks / half a block)
+    "bs8_bf16": W.scaled(W.CONFIGS["llama8b_bf16"], batch=6, num_blocks=6 * 100, ctx_lo=1,
+                         ctx_hi=700, block_size=8),
+    "bs32_bf16": W.scaled(W.CONFIGS["llama8b_bf16"], batch=6, num_blocks=6 * 30, ctx_lo=1,
+                          ctx_hi=700, block_size=32),
+    "bs8_q8": W.scaled(W.CONFIGS["llama8b_q8"], batch=5, num_blocks=5 * 100, ctx_lo=1,
+                       ctx_hi=600, block_size=8),
+    "bs32_q8_d64": W.scaled(W.CONFIGS["llama8b_q8"], batch=4, q_heads=4, kv_heads=2,
+                            head_dim=64, num_blocks=4 * 30, ctx_lo=1, ctx_hi=700, block_size=32),
+    "bs8_f32_len": W.scaled(W.CONFIGS["tiny_f32"], ctx_fixed=(1, 8, 9, 33), num_blocks=64,
+                            block_size=8),
+    "bs32_f16_mha": W.scaled(W.CONFIGS["mha13b_f16"], batch=4, q_heads=4, kv_heads=4,
+                             num_blocks=4 * 30, ctx_lo=16, ctx_hi=700, block_size=32),
+    "bs32_shared_cow": W.scaled(W.CONFIGS["shared_prefix_cow_bf16"], batch=5, num_blocks=100,
+                                prefix_tokens=1000, block_size=32),
 }
 
 
@@ -107,6 +122,10 @@ WRITES = {
     "write_f32": (W.scaled(W.CONFIGS["tiny_f32"], num_blocks=64), 1, 30),
     "write_f16_d64": (W.scaled(W.CONFIGS["mha13b_f16"], batch=4, q_heads=4, kv_heads=2,
                                head_dim=64, num_blocks=4 * 100, ctx_lo=16, ctx_hi=700), 1, 600),
+    "write_bs8_q8": (W.scaled(W.CONFIGS["llama8b_q8"], batch=4, num_blocks=4 * 200, ctx_lo=1,
+                              ctx_hi=600, block_size=8), 1, 500),
+    "write_bs32_bf16": (W.scaled(W.CONFIGS["llama8b_bf16"], batch=4, num_blocks=4 * 50,
+                                 ctx_lo=1, ctx_hi=600, block_size=32), 1, 500),
 }
 
 

@@ -65,9 +65,13 @@ def test_unsupported_shapes_rejected():
     with pytest.raises(pkv.PkvError) as e:
         pkv.kv_pool_alloc(pkv.make_shape(1, 8, 2, 96, pkv.F32, 16, 1))
     assert e.value.code == pkv.EUNSUPPORTED
-    with pytest.raises(pkv.PkvError) as e:
-        pkv.kv_pool_alloc(pkv.make_shape(1, 8, 2, 64, pkv.F32, 16, 1, block_size=8))
-    assert e.value.code == pkv.EUNSUPPORTED
+    for bs in (4, 12, 64):
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.kv_pool_alloc(pkv.make_shape(1, 8, 2, 64, pkv.F32, 16, 1, block_size=bs))
+        assert e.value.code == pkv.EUNSUPPORTED
+    for bs in (8, 16, 32):  # the supported block sizes
+        pkv.kv_pool_free(pkv.kv_pool_alloc(pkv.make_shape(1, 8, 2, 64, pkv.F32, 16, 1,
+                                                          block_size=bs)))
     with pytest.raises(pkv.PkvError) as e:
         pkv.kv_pool_alloc(pkv.make_shape(1, 8, 2, 64, 7, 16, 1))
     assert e.value.code == pkv.EINVAL
