@@ -41,17 +41,18 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(config: str):
-    """HBM bytes per decode launch from the committed counter run, if it was taken
-    on this workload with the current kernel source (else None)."""
+    """HBM bytes per layer launch (decode + reduce) from the committed counter runs,
+    if they were taken on this workload with the current kernel source (else None)."""
     try:
         with open(TRAFFIC) as f:
             t = json.load(f)
         current = kernel_source_hash()
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != current or t.get("config") != config:
+    c = t.get("configs", {}).get(config)
+    if t.get("kernel_source_sha256") != current or c is None:
         return None
-    return int(t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"])
+    return int(c["fetch_bytes_per_launch"] + c["write_bytes_per_launch"])
 
 
 def kv_bytes(cfg, ctx) -> int:
