@@ -28,30 +28,41 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "liboracle.so")
 _SRC = os.path.join(_HERE, "oracle.c")
 
-F32, F16, BF16, Q8_0 = 0, 1, 2, 3
-_NP_STORAGE = {F32: np.float32, F16: np.uint16, BF16: np.uint16, Q8_0: np.uint8}
+F32, F16, BF16, Q8_0, Q4_0 = 0, 1, 2, 3, 4
+QUANTISED = (Q8_0, Q4_0)
+_NP_STORAGE = {F32: np.float32, F16: np.uint16, BF16: np.uint16, Q8_0: np.uint8, Q4_0: np.uint8}
 Q8_GROUP = 32
 
 
+def code_row_bytes(dtype: int, head_dim: int) -> int:
+    """Code bytes of one quantised row: head_dim (q8_0) or head_dim / 2 (q4_0)."""
+    return head_dim // 2 if dtype == Q4_0 else head_dim
+
+
+def q_tile_bytes(dtype: int, head_dim: int, block_size: int = 16) -> int:
+    """Bytes of one quantised (block, kv head) tile: codes, then fp16 scales."""
+    return block_size * code_row_bytes(dtype, head_dim) + block_size * (head_dim // Q8_GROUP) * 2
+
+
 def q8_tile_bytes(head_dim: int, block_size: int = 16) -> int:
-    """Bytes of one q8_0 (block, kv head) tile: int8 codes, then fp16 scales."""
-    return block_size * head_dim + block_size * (head_dim // Q8_GROUP) * 2
+    return q_tile_bytes(Q8_0, head_dim, block_size)
 
 
 def input_dtype(dtype: int) -> int:
-    """Storage type of q, k_new and v_new for a cache of `dtype` (bf16 for q8_0)."""
-    return BF16 if dtype == Q8_0 else dtype
+    """Storage type of q, k_new and v_new for a cache of `dtype` (bf16 when quantised)."""
+    return BF16 if dtype in QUANTISED else dtype
 
 
 _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile oracle.c with gcc (-O3 -fopenmp, no fast-math)."""
+    """Compile oracle.c with gcc (-O3 -fopenmp, no fast-math, no contraction of a*b+c)."""
     if force or not os.path.exists(_SO):
         tmp = _SO + ".tmp"
         subprocess.run(
             ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
+             "-ffp-contract=off",
              "-o", tmp, _SRC, "-lm"],
             check=True,
         )
@@ -83,6 +94,8 @@ def lib():
         L.orc_float_to_half.argtypes = [P, i64, P]
         L.orc_q8_quantize.restype = None
         L.orc_q8_quantize.argtypes = [P, i64, P, P]
+        L.orc_q4_quantize.restype = None
+        L.orc_q4_quantize.argtypes = [P, i64, P, P]
         L.orc_decode_partitioned.restype = None
         L.orc_decode_partitioned.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, i32, P,
                                              P, ctypes.c_double, i32, P]
@@ -129,10 +142,27 @@ def q8_quantize(x):
     return codes, d
 
 
+def q4_quantize(x):
+    """q4_0 groups of 32 fp32 values -> (4-bit codes 0..15 [n][32] as uint8, fp16 scale bits [n])."""
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1, Q8_GROUP)
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    d = np.zeros(x.shape[0], dtype=np.uint16)
+    lib().orc_q4_quantize(_ptr(x), x.shape[0], _ptr(codes), _ptr(d))
+    return codes, d
+
+
+def _head_dim_of_qtile(dtype, tile_bytes, block_size):
+    # tile = bs * (D * c) + bs * D / 16 with c = 1 (q8_0) or 1/2 (q4_0)
+    per_row = tile_bytes // block_size
+    D = per_row * 16 // 17 if dtype == Q8_0 else per_row * 16 // 9
+    assert q_tile_bytes(dtype, D, block_size) == tile_bytes
+    return D
+
+
 def _pool_shape(pool, dtype, block_size, head_dim):
-    """(NB, Hkv) of a layer array: [NB][Hkv][bs][D], or [NB][Hkv][tile bytes] for q8_0."""
-    if dtype == Q8_0:
-        assert pool.ndim == 3 and pool.shape[2] == q8_tile_bytes(head_dim, block_size)
+    """(NB, Hkv) of a layer array: [NB][Hkv][bs][D], or [NB][Hkv][tile bytes] when quantised."""
+    if dtype in QUANTISED:
+        assert pool.ndim == 3 and pool.shape[2] == q_tile_bytes(dtype, head_dim, block_size)
     else:
         assert pool.ndim == 4 and pool.shape[2] == block_size and pool.shape[3] == head_dim
     return pool.shape[0], pool.shape[1]
@@ -140,7 +170,7 @@ def _pool_shape(pool, dtype, block_size, head_dim):
 
 def append(k_pool, v_pool, block_table, ctx_lens, k_new, v_new, *, dtype, block_size=16):
     """In-place append into one layer's K/V pool arrays ([NB][Hkv][bs][D], or
-    [NB][Hkv][tile bytes] uint8 for q8_0, whose new rows come in bf16)."""
+    [NB][Hkv][tile bytes] uint8 for q8_0 / q4_0, whose new rows come in bf16)."""
     k_pool = _storage(k_pool, dtype)
     v_pool = _storage(v_pool, dtype)
     bt = np.ascontiguousarray(block_table, dtype=np.int32)
@@ -160,10 +190,9 @@ def gather(k_pool, v_pool, bt_row, n_tokens, g, *, dtype, block_size=16):
     k_pool = _storage(k_pool, dtype)
     v_pool = _storage(v_pool, dtype)
     row = np.ascontiguousarray(bt_row, dtype=np.int32)
-    if dtype == Q8_0:
+    if dtype in QUANTISED:
         NB, Hkv, tb = k_pool.shape
-        D = (tb // block_size) * Q8_GROUP // (Q8_GROUP + 2)
-        assert q8_tile_bytes(D, block_size) == tb
+        D = _head_dim_of_qtile(dtype, tb, block_size)
     else:
         NB, Hkv, bs, D = k_pool.shape
     _check_tables(row[None, :], np.array([n_tokens]), NB, block_size)

@@ -24,9 +24,10 @@
  *    head (ssdnodes.com, same section, the GQA paragraph); query head h reads
  *    kv head h / (q_heads / kv_heads).
  *
- *  - A quantised cache: q8_0 (ssdnodes.com, same page, "Four ways to make the
- *    KV cache smaller", item 2), read as llama.cpp's Q8_0 block format: per
- *    32 consecutive head_dim elements one fp16 scale and 32 int8 codes.
+ *  - Quantised caches: q8_0 and q4_0 (ssdnodes.com, same page, "Four ways to
+ *    make the KV cache smaller", item 2), read as llama.cpp's Q8_0 / Q4_0
+ *    block formats: per 32 consecutive head_dim elements one fp16 scale and
+ *    32 int8 codes / 32 4-bit codes.
  *
  * Physical layout of one layer of the pool (our choice; the pages fix only
  * "blocks of block_size tokens" and "a block table"): K and V are separate
@@ -34,7 +35,7 @@
  * is the token's position inside its block.
  *
  * Numbers are read exactly from their stored type (fp32, fp16, bf16, or a
- * q8_0 code times its fp16 scale) into double; all attention arithmetic is
+ * q8_0 / q4_0 code times its fp16 scale) into double; all attention arithmetic is
  * double. (Quantising a new q8_0 row makes its integer decisions in fp32, as
  * the format's definition does.) No blocking, no online softmax, no split:
  * gather to a contiguous array, then softmax(q.K^T * scale) . V.
@@ -44,7 +45,9 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_Q8_0 = 3 };
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_Q8_0 = 3, ORC_Q4_0 = 4 };
+
+static int orc_quantised(int dtype) { return dtype == ORC_Q8_0 || dtype == ORC_Q4_0; }
 
 static size_t orc_elem_bytes(int dtype) { return dtype == ORC_F32 ? 4u : 2u; }
 
@@ -148,29 +151,78 @@ void orc_q8_quantize(const float* x, int64_t n_groups, int8_t* codes, uint16_t* 
 }
 
 /*
- * q8_0 tile of one (block, kv head) in the pool (our layout; the pages fix
- * none): block_size rows x head_dim int8 codes, row-major, then
+ * q4_0 quantisation of one group of 32 consecutive values. The same page
+ * ("Four ways to make the KV cache smaller", item 2, and the FAQ) names q4_0
+ * as the cache type that takes about a quarter of an f16 cache; its
+ * definition is llama.cpp's Q4_0 block: m = the value of largest magnitude
+ * (the first one on ties), scale d = m / -8 stored as fp16, 4-bit codes
+ * q = min(15, trunc(x * (1 / d) + 8.5)), value = (q - 8) * d. Decisions in
+ * fp32 (the product and the sum rounded separately), codes from the fp32
+ * scale.
+ */
+static void orc_q4_quantize_group(const float* x, uint8_t* q, uint16_t* d_bits) {
+  float amax = 0.0f, m = 0.0f;
+  for (int i = 0; i < 32; ++i) {
+    if (amax < fabsf(x[i])) {
+      amax = fabsf(x[i]);
+      m = x[i];
+    }
+  }
+  float d = m / -8.0f;
+  float id = d != 0.0f ? 1.0f / d : 0.0f;
+  for (int i = 0; i < 32; ++i) {
+    float t = x[i] * id;
+    t = t + 8.5f;
+    int c = (int)(int8_t)t;
+    q[i] = (uint8_t)(c < 15 ? c : 15);
+  }
+  *d_bits = orc_float_to_half_bits(d);
+}
+
+void orc_q4_quantize(const float* x, int64_t n_groups, uint8_t* codes, uint16_t* d_bits) {
+  for (int64_t g = 0; g < n_groups; ++g) orc_q4_quantize_group(x + 32 * g, codes + 32 * g, d_bits + g);
+}
+
+/*
+ * Quantised tile of one (block, kv head) in the pool (our layout; the pages fix
+ * none): block_size rows of codes, row-major (q8_0: head_dim int8 codes; q4_0:
+ * head_dim/2 bytes, element d in byte d/2, low nibble for even d), then
  * block_size x head_dim/32 fp16 scales, ordered [row][group] in the K region
  * and [group][row] in the V region.
  */
-static size_t orc_q8_tile_bytes(int block_size, int head_dim) {
-  return (size_t)block_size * head_dim + (size_t)block_size * (head_dim / 32) * 2;
+static size_t orc_code_row_bytes(int dtype, int head_dim) {
+  return dtype == ORC_Q4_0 ? (size_t)head_dim / 2 : (size_t)head_dim;
 }
 
-static size_t orc_q8_scale_offset(int is_v, int row, int grp, int block_size, int head_dim) {
-  size_t codes = (size_t)block_size * head_dim;
+static size_t orc_qtile_bytes(int dtype, int block_size, int head_dim) {
+  return (size_t)block_size * orc_code_row_bytes(dtype, head_dim) +
+         (size_t)block_size * (head_dim / 32) * 2;
+}
+
+static size_t orc_qscale_offset(int dtype, int is_v, int row, int grp, int block_size,
+                                int head_dim) {
+  size_t codes = (size_t)block_size * orc_code_row_bytes(dtype, head_dim);
   int ng = head_dim / 32;
   return codes + 2 * (size_t)(is_v ? grp * block_size + row : row * ng + grp);
 }
 
-/* Value of element d of row `row` in a q8_0 tile: fp16 scale * int8 code, exact in double. */
-static double orc_q8_load(const char* tile, int is_v, int row, int d, int block_size,
-                          int head_dim) {
-  int8_t c;
+/* Value of element d of row `row` in a quantised tile, exact in double:
+ * q8_0 scale * code, q4_0 scale * (nibble - 8). */
+static double orc_qload(const char* tile, int dtype, int is_v, int row, int d, int block_size,
+                        int head_dim) {
   uint16_t h;
-  memcpy(&c, tile + (size_t)row * head_dim + d, 1);
-  memcpy(&h, tile + orc_q8_scale_offset(is_v, row, d / 32, block_size, head_dim), 2);
-  return orc_half_bits_to_double(h) * (double)c;
+  memcpy(&h, tile + orc_qscale_offset(dtype, is_v, row, d / 32, block_size, head_dim), 2);
+  double code;
+  if (dtype == ORC_Q4_0) {
+    uint8_t b;
+    memcpy(&b, tile + (size_t)row * (head_dim / 2) + d / 2, 1);
+    code = (double)((d & 1 ? b >> 4 : b & 15) - 8);
+  } else {
+    int8_t c;
+    memcpy(&c, tile + (size_t)row * head_dim + d, 1);
+    code = (double)c;
+  }
+  return orc_half_bits_to_double(h) * code;
 }
 
 /* ssdnodes.com, "KV cache vs prompt cache", "How much memory does the KV cache
@@ -205,9 +257,10 @@ void orc_append(int batch, int kv_heads, int head_dim, int block_size, int dtype
     int p = L - 1;
     int32_t blk = block_table[(size_t)s * max_blocks + p / block_size];
     int row = p % block_size;
-    if (dtype == ORC_Q8_0) {
+    if (orc_quantised(dtype)) {
       /* new rows arrive in bf16 and are quantised group by group */
-      size_t tb = orc_q8_tile_bytes(block_size, head_dim);
+      size_t tb = orc_qtile_bytes(dtype, block_size, head_dim);
+      size_t rb = orc_code_row_bytes(dtype, head_dim);
       for (int g = 0; g < kv_heads; ++g) {
         for (int is_v = 0; is_v < 2; ++is_v) {
           const void* src = is_v ? v_new : k_new;
@@ -217,11 +270,18 @@ void orc_append(int batch, int kv_heads, int head_dim, int block_size, int dtype
             for (int i = 0; i < 32; ++i)
               x[i] = (float)orc_load(src, ((size_t)s * kv_heads + g) * head_dim + grp * 32 + i,
                                      ORC_BF16);
-            int8_t codes[32];
             uint16_t d;
-            orc_q8_quantize_group(x, codes, &d);
-            memcpy(tile + (size_t)row * head_dim + grp * 32, codes, 32);
-            memcpy(tile + orc_q8_scale_offset(is_v, row, grp, block_size, head_dim), &d, 2);
+            if (dtype == ORC_Q4_0) {
+              uint8_t q[32], packed[16];
+              orc_q4_quantize_group(x, q, &d);
+              for (int i = 0; i < 16; ++i) packed[i] = (uint8_t)(q[2 * i] | (q[2 * i + 1] << 4));
+              memcpy(tile + (size_t)row * rb + grp * 16, packed, 16);
+            } else {
+              int8_t codes[32];
+              orc_q8_quantize_group(x, codes, &d);
+              memcpy(tile + (size_t)row * rb + grp * 32, codes, 32);
+            }
+            memcpy(tile + orc_qscale_offset(dtype, is_v, row, grp, block_size, head_dim), &d, 2);
           }
         }
       }
@@ -247,13 +307,13 @@ void orc_gather(int kv_heads, int head_dim, int block_size, int dtype, const voi
   for (int t = 0; t < n_tokens; ++t) {
     int32_t blk = bt_row[t / block_size];
     int row = t % block_size;
-    if (dtype == ORC_Q8_0) {
-      size_t off = ((size_t)blk * kv_heads + g) * orc_q8_tile_bytes(block_size, head_dim);
+    if (orc_quantised(dtype)) {
+      size_t off = ((size_t)blk * kv_heads + g) * orc_qtile_bytes(dtype, block_size, head_dim);
       for (int d = 0; d < head_dim; ++d) {
         out_k[(size_t)t * head_dim + d] =
-            orc_q8_load((const char*)k_pool + off, 0, row, d, block_size, head_dim);
+            orc_qload((const char*)k_pool + off, dtype, 0, row, d, block_size, head_dim);
         out_v[(size_t)t * head_dim + d] =
-            orc_q8_load((const char*)v_pool + off, 1, row, d, block_size, head_dim);
+            orc_qload((const char*)v_pool + off, dtype, 1, row, d, block_size, head_dim);
       }
       continue;
     }
@@ -298,7 +358,7 @@ void orc_attend(int n, int head_dim, const double* q, const double* kc, const do
  * Decode attention for a batch, reading the cache through the block tables:
  * for every sequence s and query head h, gather the first ctx_lens[s] rows of
  * kv head h / (q_heads / kv_heads) and attend with q[s][h].
- * q is stored in the cache dtype (bf16 for a q8_0 cache),
+ * q is stored in the cache dtype (bf16 for a quantised cache),
  * [batch][q_heads][head_dim]; out is double
  * [batch][q_heads][head_dim]. Parallel over (sequence, kv head) with OpenMP.
  */
@@ -308,7 +368,7 @@ void orc_decode(int batch, int q_heads, int kv_heads, int head_dim, int block_si
                 double* out) {
   int group = q_heads / kv_heads;
   int npairs = batch * kv_heads;
-  int qdt = dtype == ORC_Q8_0 ? ORC_BF16 : dtype; /* q of a q8_0 cache is bf16 */
+  int qdt = orc_quantised(dtype) ? ORC_BF16 : dtype; /* q of a quantised cache is bf16 */
 #pragma omp parallel for schedule(dynamic, 1)
   for (int pi = 0; pi < npairs; ++pi) {
     int s = pi / kv_heads;
@@ -362,7 +422,7 @@ void orc_decode_partitioned(int batch, int q_heads, int kv_heads, int head_dim, 
                block_table + (size_t)s * max_blocks, L, g, kc, vc);
     for (int d = 0; d < head_dim; ++d)
       qd[d] = orc_load(q, ((size_t)s * q_heads + h) * head_dim + d,
-                       dtype == ORC_Q8_0 ? ORC_BF16 : dtype);
+                       orc_quantised(dtype) ? ORC_BF16 : dtype);
     int nparts = (L + part_tokens - 1) / part_tokens;
     double* m = (double*)malloc(sizeof(double) * (size_t)(nparts > 0 ? nparts : 1));
     double* l = (double*)malloc(sizeof(double) * (size_t)(nparts > 0 ? nparts : 1));

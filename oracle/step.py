@@ -94,19 +94,31 @@ def run_write(k_layers, v_layers, pre_tables, shared, ctx_before, n_new, k_rows_
     return table, plan
 
 
+def q_format(tile_bytes, block_size=BLOCK):
+    """(code bytes per row, head_dim) of a quantised tile: rows of head_dim codes
+    (q8_0, 17 * head_dim / 16 bytes with the scales) or head_dim / 2 bytes of
+    nibbles (q4_0, 9 * head_dim / 16 bytes); the two never have equal sizes."""
+    per_row16 = tile_bytes * 16 // block_size
+    if per_row16 % 17 == 0:
+        D = per_row16 // 17
+        return D, D
+    assert per_row16 % 9 == 0, "not a quantised tile size"
+    D = per_row16 // 9
+    return D // 2, D
+
+
 def q8_row_bytes(pool, blocks, rows, is_v, block_size=BLOCK):
-    """Bytes of q8_0 rows as [n][Hkv][D codes + 2 * D/32 scale bytes], scales in group
-    order. A tile is block_size x D int8 codes, then fp16 scales ordered
-    [row][group] (K region) or [group][row] (V region)."""
-    tb = pool.shape[2]
-    D = tb * 16 // (17 * block_size)
+    """Bytes of quantised rows (q8_0 or q4_0) as [n][Hkv][code bytes + 2 * D/32 scale
+    bytes], scales in group order. A tile is block_size rows of codes, then fp16
+    scales ordered [row][group] (K region) or [group][row] (V region)."""
+    cb, D = q_format(pool.shape[2], block_size)
     ng = D // 32
     rows = np.asarray(rows, dtype=np.int64)
     blocks = np.asarray(blocks, dtype=np.int64)
-    code_idx = rows[:, None] * D + np.arange(D)[None, :]
+    code_idx = rows[:, None] * cb + np.arange(cb)[None, :]
     grp = np.arange(ng)[None, :]
     si = grp * block_size + rows[:, None] if is_v else rows[:, None] * ng + grp
-    sb = block_size * D + 2 * si
+    sb = block_size * cb + 2 * si
     scale_idx = np.stack([sb, sb + 1], axis=2).reshape(len(rows), 2 * ng)
     idx = np.concatenate([code_idx, scale_idx], axis=1)
     return np.take_along_axis(pool[blocks], idx[:, None, :], axis=2)

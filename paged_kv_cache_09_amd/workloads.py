@@ -20,8 +20,8 @@ Physical placement follows a seeded permutation of the pool's block ids,
 taken in (sequence, logical block) order, so logical neighbours are scattered
 through the pool. Cache values, q and the new K/V are N(0, sigma) draws made
 in fp32 and rounded to the cache dtype by torch (round to nearest even). A
-q8_0 cache holds random int8 codes and random fp16 scales (its q and new rows
-are bf16). Rows of the pool that hold no token are NaN (q8_0: NaN scales) for
+q8_0 / q4_0 cache holds random codes and random fp16 scales (its q and new
+rows are bf16). Rows of the pool that hold no token are NaN (quantised: NaN scales) for
 parity runs, so a kernel that reads them poisons its output.
 
 The five shapes follow the pages' statement of the problem (layers, kv heads,
@@ -36,21 +36,27 @@ import math
 import numpy as np
 import torch
 
-F32, F16, BF16, Q8_0 = 0, 1, 2, 3
-# element type of q, k_new and v_new (and of the cache itself, except q8_0)
+F32, F16, BF16, Q8_0, Q4_0 = 0, 1, 2, 3, 4
+QUANTISED = (Q8_0, Q4_0)
+# element type of q, k_new and v_new (and of the cache itself, unless quantised)
 TORCH_DTYPE = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16,
-               Q8_0: torch.bfloat16}
+               Q8_0: torch.bfloat16, Q4_0: torch.bfloat16}
 ELEM_BYTES = {F32: 4, F16: 2, BF16: 2}
-DTYPE_NAME = {F32: "f32", F16: "f16", BF16: "bf16", Q8_0: "q8_0"}
+DTYPE_NAME = {F32: "f32", F16: "f16", BF16: "bf16", Q8_0: "q8_0", Q4_0: "q4_0"}
 BLOCK = 16
 Q8_GROUP = 32
 
 
+def code_row_bytes(cfg) -> int:
+    """Code bytes of one quantised row: head_dim (q8_0) or head_dim / 2 (q4_0)."""
+    return cfg.head_dim // 2 if cfg.dtype == Q4_0 else cfg.head_dim
+
+
 def row_bytes(cfg) -> int:
     """Pool bytes of one token's K (or V) row of one kv head: head_dim elements,
-    or for q8_0 head_dim int8 codes plus one fp16 scale per 32 of them."""
-    if cfg.dtype == Q8_0:
-        return cfg.head_dim + 2 * (cfg.head_dim // Q8_GROUP)
+    or for q8_0 / q4_0 the codes plus one fp16 scale per 32 elements."""
+    if cfg.dtype in QUANTISED:
+        return code_row_bytes(cfg) + 2 * (cfg.head_dim // Q8_GROUP)
     return cfg.head_dim * ELEM_BYTES[cfg.dtype]
 
 
@@ -105,6 +111,9 @@ CONFIGS = {
     # The Llama-3.1-8B-shaped layer with a q8_0 cache (int8 codes, one fp16
     # scale per 32 elements); same lengths and placement as the bf16 one.
     "llama8b_q8": Config("llama8b_q8", 2, 64, 32, 8, 128, Q8_0, 1.0, 64 * 136, 32,
+                         "uniform", ctx_lo=128, ctx_hi=2048),
+    # ... and with a q4_0 cache (4-bit codes, one fp16 scale per 32 elements).
+    "llama8b_q4": Config("llama8b_q4", 2, 64, 32, 8, 128, Q4_0, 1.0, 64 * 136, 32,
                          "uniform", ctx_lo=128, ctx_hi=2048),
     # Long context: batch 4 x 131072 tokens (8192 blocks each), GQA 32/8, d 128,
     # bf16, 512-token split-K partitions.
@@ -203,9 +212,9 @@ def region_bytes(cfg: Config, layers: int) -> int:
 
 def pool_layer_views(pool: torch.Tensor, cfg: Config, layers: int, layer: int):
     """(K, V) views of one layer: typed [NB][Hkv][16][D], or uint8
-    [NB][Hkv][tile bytes] for q8_0."""
+    [NB][Hkv][tile bytes] when quantised."""
     n = region_bytes(cfg, layers)
-    if cfg.dtype == Q8_0:
+    if cfg.dtype in QUANTISED:
         shape = (layers, cfg.num_blocks, cfg.kv_heads, tile_bytes(cfg))
         return pool[:n].view(shape)[layer], pool[n:2 * n].view(shape)[layer]
     shape = (layers, cfg.num_blocks, cfg.kv_heads, cfg.block_size, cfg.head_dim)
@@ -215,19 +224,31 @@ def pool_layer_views(pool: torch.Tensor, cfg: Config, layers: int, layer: int):
 
 def _fill_q8(pool: torch.Tensor, cfg: Config, layers: int, gen: torch.Generator,
              chunk: int = 1 << 26):
-    """q8_0 pool contents: int8 codes uniform in [-127, 127] and fp16 scales drawn
-    uniform in [0.005, 0.03] (rounded to fp16 by torch)."""
+    """Quantised pool contents: q8_0 int8 codes uniform in [-127, 127] and fp16
+    scales uniform in [0.005, 0.03]; q4_0 code bytes uniform (two 4-bit codes
+    each) and scales of either sign with magnitude uniform in [0.05, 0.3]
+    (rounded to fp16 by torch)."""
     D = cfg.head_dim
+    CB = code_row_bytes(cfg) * cfg.block_size
     tiles = pool.view(2 * layers * cfg.num_blocks * cfg.kv_heads, tile_bytes(cfg))
     for i in range(0, tiles.shape[0], max(1, chunk // tiles.shape[1])):
         part = tiles[i:i + max(1, chunk // tiles.shape[1])]
         BS = cfg.block_size
-        codes = torch.randint(-127, 128, (part.shape[0], BS * D), generator=gen,
-                              device=pool.device, dtype=torch.int16)
-        part[:, :BS * D].copy_(codes.to(torch.int8).view(torch.uint8))
-        sc = torch.rand((part.shape[0], BS * (D // Q8_GROUP)), generator=gen,
-                        device=pool.device, dtype=torch.float32) * 0.025 + 0.005
-        part[:, BS * D:].copy_(sc.to(torch.float16).view(torch.uint8).view(part.shape[0], -1))
+        if cfg.dtype == Q8_0:
+            codes = torch.randint(-127, 128, (part.shape[0], CB), generator=gen,
+                                  device=pool.device, dtype=torch.int16)
+            part[:, :CB].copy_(codes.to(torch.int8).view(torch.uint8))
+            sc = torch.rand((part.shape[0], BS * (D // Q8_GROUP)), generator=gen,
+                            device=pool.device, dtype=torch.float32) * 0.025 + 0.005
+        else:
+            codes = torch.randint(0, 256, (part.shape[0], CB), generator=gen,
+                                  device=pool.device, dtype=torch.int16)
+            part[:, :CB].copy_(codes.to(torch.uint8))
+            sc = torch.rand((part.shape[0], BS * (D // Q8_GROUP)), generator=gen,
+                            device=pool.device, dtype=torch.float32) * 0.25 + 0.05
+            sign = torch.randint(0, 2, sc.shape, generator=gen, device=pool.device) * 2 - 1
+            sc = sc * sign
+        part[:, CB:].copy_(sc.to(torch.float16).view(torch.uint8).view(part.shape[0], -1))
 
 
 def _fill_normal(t: torch.Tensor, sigma: float, gen: torch.Generator, chunk: int = 1 << 26):
@@ -288,7 +309,7 @@ def make(cfg: Config, *, device="cpu", layers: int | None = None, form: str = "s
     tdt = TORCH_DTYPE[cfg.dtype]
     nb = region_bytes(cfg, layers)
     pool = torch.empty(2 * nb, dtype=torch.uint8, device=device)
-    if cfg.dtype == Q8_0:
+    if cfg.dtype in QUANTISED:
         _fill_q8(pool, cfg, layers, gen)
     else:
         _fill_normal(pool.view(tdt), cfg.sigma, gen)
@@ -313,13 +334,13 @@ def make(cfg: Config, *, device="cpu", layers: int | None = None, form: str = "s
                 if rows > 0:
                     valid[b, :rows] = True
         mask = torch.from_numpy(~valid).to(device)
-        if cfg.dtype == Q8_0:
+        if cfg.dtype in QUANTISED:
             # a row without a token gets NaN scales: K scales are [row][group],
-            # V scales [group][row] after the 16 x head_dim codes of a tile
+            # V scales [group][row] after the codes of a tile
             ng = cfg.head_dim // Q8_GROUP
             shape = (layers, cfg.num_blocks, cfg.kv_heads, tile_bytes(cfg))
             for r, region in enumerate((pool[:nb], pool[nb:2 * nb])):
-                sc = region.view(shape)[..., BS * cfg.head_dim:].view(torch.float16)
+                sc = region.view(shape)[..., BS * code_row_bytes(cfg):].view(torch.float16)
                 if r == 0:
                     sc.view(layers, cfg.num_blocks, cfg.kv_heads, BS, ng).masked_fill_(
                         mask[None, :, None, :, None], float("nan"))

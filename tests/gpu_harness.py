@@ -166,7 +166,7 @@ def run_step_case(cfg, *, layers=1, partitions=(0,), sample=None, check_untouche
 def _check_untouched(w, before, slots, pairs, layers):
     """Only the appended rows and copy-on-write destination blocks may change."""
     cfg = w.cfg
-    if cfg.dtype == W.Q8_0:
+    if cfg.dtype in W.QUANTISED:
         return _check_untouched_q8(w, before, slots, pairs, layers)
     bs = cfg.block_size
     shape = (2, layers, cfg.num_blocks, cfg.kv_heads, bs, cfg.head_dim * W.ELEM_BYTES[cfg.dtype])
@@ -184,12 +184,12 @@ def _check_untouched(w, before, slots, pairs, layers):
 
 
 def _check_untouched_q8(w, before, slots, pairs, layers):
-    """q8_0 form: byte by byte, only each new row's codes and scales (K scales
-    [row][group], V scales [group][row] after a tile's codes) and whole
+    """Quantised caches: byte by byte, only each new row's codes and scales (K
+    scales [row][group], V scales [group][row] after a tile's codes) and whole
     copy-on-write destination tiles may change."""
     cfg = w.cfg
-    D = cfg.head_dim
-    ng = D // 32
+    D = W.code_row_bytes(cfg)  # code bytes per row
+    ng = cfg.head_dim // 32
     tb = W.tile_bytes(cfg)
     shape = (2, layers, cfg.num_blocks, cfg.kv_heads, tb)
     changed = (w.pool.view(shape) != before.view(shape))
@@ -293,7 +293,7 @@ def run_prefix_case(cfg, *, num_blocks, n_prefixes, prefix_len, suffix_hi, na, n
     # an empty one-layer pool: every row NaN (q8_0: 0xff bytes, NaN scales)
     cfg_pool = W.scaled(cfg, num_blocks=num_blocks, batch=nb)
     dev_pool = torch.empty(2 * W.region_bytes(cfg_pool, 1), dtype=torch.uint8, device="cuda")
-    if cfg.dtype == W.Q8_0:
+    if cfg.dtype in W.QUANTISED:
         dev_pool.fill_(255)
     else:
         dev_pool.view(tdt).fill_(float("nan"))

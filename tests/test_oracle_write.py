@@ -19,6 +19,7 @@ from tests.helpers import to_storage
     ("shared_prefix_cow_bf16", dict(batch=6, num_blocks=64 + 6 * 20, layers=2), 1, 200),
     ("mha13b_f16", dict(batch=5, q_heads=4, kv_heads=4, num_blocks=5 * 150), 0, 100),
     ("llama8b_q8", dict(batch=4, num_blocks=4 * 180, layers=2), 1, 700),
+    ("llama8b_q4", dict(batch=4, num_blocks=4 * 180, layers=2), 1, 700),
 ])
 def test_write_reads_back_old_rows_then_new_rows(name, changes, n_lo, n_hi):
     cfg = W.scaled(W.CONFIGS[name], **changes)
@@ -45,16 +46,21 @@ def test_write_reads_back_old_rows_then_new_rows(name, changes, n_lo, n_hi):
                 got = new[s][which]
                 assert np.array_equal(got[:L0], old[layer][s][which])
                 want = rows[offs[s]:offs[s + 1]]
-                if cfg.dtype == W.Q8_0:
+                if cfg.dtype in W.QUANTISED:
                     x = (want.astype(np.uint32) << 16).view(np.float32)
-                    codes, d = oracle.q8_quantize(x.reshape(-1, 32))
                     n = want.shape[0]
-                    want = np.concatenate(
-                        [codes.reshape(n, cfg.kv_heads, cfg.head_dim).view(np.uint8),
-                         d.reshape(n, cfg.kv_heads, -1).view(np.uint8)], axis=2)
+                    if cfg.dtype == W.Q8_0:
+                        codes, d = oracle.q8_quantize(x.reshape(-1, 32))
+                        cb = codes.reshape(n, cfg.kv_heads, cfg.head_dim).view(np.uint8)
+                    else:  # q4_0: element i in byte i // 2, low nibble for even i
+                        codes, d = oracle.q4_quantize(x.reshape(-1, 32))
+                        c = codes.reshape(n, cfg.kv_heads, cfg.head_dim)
+                        cb = (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+                    want = np.concatenate([cb, d.reshape(n, cfg.kv_heads, -1).view(np.uint8)],
+                                          axis=2)
                 assert np.array_equal(got[L0:], want)
     # blocks that nobody's table names after the write are untouched
     named = {int(b) for b in table.ravel() if b >= 0} | {int(b) for r in w.pre_tables for b in r}
     for b in range(cfg.num_blocks):
         if b not in named:
-            assert np.array_equal(ks[0][b], k0[0][b], equal_nan=cfg.dtype != W.Q8_0)
+            assert np.array_equal(ks[0][b], k0[0][b], equal_nan=cfg.dtype not in W.QUANTISED)
