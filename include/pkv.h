@@ -45,9 +45,20 @@
  * group with d = max|x| / 127 and c = round(x * (1/d)) (halves away from
  * zero, fp32 arithmetic, d stored rounded to fp16).
  *
- * Supported: block_size 16, head_dim 64 or 128, dtype fp32/fp16/bf16/q8_0,
- * q_heads / kv_heads (the GQA group) from 1 to 8. Other shapes return
- * PKV_EUNSUPPORTED.
+ * q4_0 cache (PKV_Q4_0): the 4-bit cache type of the same passage (about a
+ * quarter of an f16 cache), in llama.cpp's Q4_0 block format: every 32
+ * consecutive elements of a row are one fp16 scale d and 32 4-bit codes q,
+ * value (q - 8) * d. A tile is block_size rows of head_dim/2 bytes (element
+ * i in byte i/2, low nibble for even i) followed by the scales as for q8_0
+ * (1152 bytes for head_dim 128). q, k_new and v_new are bf16; appends take m,
+ * the group's element of largest magnitude (the first on ties, +0 for an
+ * all-zero group), d = m / -8 and q = min(15, trunc(x * (1/d) + 8.5)) (fp32,
+ * product and sum rounded separately, 1/d taken as 0 when d is 0), d stored
+ * rounded to fp16.
+ *
+ * Supported: block_size 8, 16 or 32, head_dim 64 or 128, dtype
+ * fp32/fp16/bf16/q8_0/q4_0, q_heads / kv_heads (the GQA group) from 1 to 8.
+ * Other shapes return PKV_EUNSUPPORTED.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -61,7 +72,7 @@ extern "C" {
 
 typedef struct pkv_pool pkv_pool; /* opaque */
 
-enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_Q8_0 = 3 };
+enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_Q8_0 = 3, PKV_Q4_0 = 4 };
 
 enum {
   PKV_OK = 0,
@@ -207,11 +218,11 @@ int pkv_copy_blocks(pkv_pool* pool, const int32_t* host_pairs, int n, uintptr_t 
 
 /*
  * Append: for s < batch and every kv head g, write k_new[s][g][:] and
- * v_new[s][g][:] (cache dtype, [batch][kv_heads][head_dim]; bf16 for q8_0)
- * into the pool row of layer `layer` at slot[s] (block slot/16, row
- * slot%16); slot < 0 skips. dev_slots: device int64 [batch], or NULL for the
+ * v_new[s][g][:] (cache dtype, [batch][kv_heads][head_dim]; bf16 when quantised)
+ * into the pool row of layer `layer` at slot[s] (block slot / block_size, row
+ * slot % block_size); slot < 0 skips. dev_slots: device int64 [batch], or NULL for the
  * slots of the last upload (batch must then equal the uploaded batch). Bytes
- * are copied unchanged (q8_0: quantised as described above). With device
+ * are copied unchanged (q8_0 / q4_0: quantised as described above). With device
  * slots, "batch" is any number of rows: the multi-token write of a prefill
  * passes one row and one slot (from pkv_prepare_write) per token; the slots
  * must be distinct.
@@ -223,10 +234,10 @@ int pkv_kv_append(pkv_pool* pool, int layer, const void* k_new, const void* v_ne
  * Decode attention of layer `layer` for the uploaded batch:
  *   out[s][h][:] = sum_t softmax_t(scale * q[s][h] . K_s[t][g]) * V_s[t][g],
  *   g = h / (q_heads / kv_heads), t < ctx[s],
- * where K_s[t] is row t % 16 of block bt[s][t / 16] (news.hamidun.com
+ * where K_s[t] is row t % block_size of block bt[s][t / block_size] (news.hamidun.com
  * "KV-Cache", mechanism and prefill/decode paragraphs; the GQA head sharing of
  * ssdnodes.com, "KV cache vs prompt cache").
- * q: device [batch][q_heads][head_dim] in the cache dtype (bf16 for q8_0,
+ * q: device [batch][q_heads][head_dim] in the cache dtype (bf16 when quantised,
  * whose K/V values are scale * code). out: device fp32
  * [batch][q_heads][head_dim]. Softmax and accumulation are fp32.
  * partition_tokens: 0 = balanced split — every wavefront of a full-chip launch
@@ -248,7 +259,7 @@ int pkv_paged_attn_decode(pkv_pool* pool, int layer, const void* q, int q_heads,
  * kv_append followed by paged_attn_decode of the same layer, in one launch:
  * the wavefront that reads a sequence's last block takes the new token's row
  * from k_new / v_new ([batch][kv_heads][head_dim], cache dtype; bf16 for
- * q8_0, quantised as pkv_kv_append does), writes it to the pool at the
+ * quantised caches: quantised as pkv_kv_append does), writes it to the pool at the
  * uploaded slot and attends over it. The last upload must
  * carry slots. Same results, bit for bit in the pool, as the two calls.
  */

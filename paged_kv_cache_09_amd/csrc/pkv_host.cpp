@@ -35,18 +35,26 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Bytes of one stored element (a q8_0 code is one byte; its scales are extra).
+bool quantised(int dtype) { return dtype == PKV_Q8_0 || dtype == PKV_Q4_0; }
+
+// Bytes of one stored element (a q8_0 code is one byte; its scales are extra;
+// q4_0 is counted by code_row_bytes, two codes per byte). 0: unknown dtype.
 int elem_bytes(int dtype) {
   return dtype == PKV_F32 ? 4 : (dtype == PKV_F16 || dtype == PKV_BF16) ? 2
-                                : dtype == PKV_Q8_0 ? 1 : 0;
+                                : quantised(dtype) ? 1 : 0;
 }
 
-// Bytes of one (block, kv head) tile of K or V: block_size rows of head_dim
-// elements, plus for q8_0 one fp16 scale per 32 elements of each row.
+// Bytes of one stored row of head_dim elements (codes only when quantised).
+int64_t code_row_bytes(int dtype, int head_dim) {
+  return dtype == PKV_Q4_0 ? head_dim / 2 : (int64_t)head_dim * elem_bytes(dtype);
+}
+
+// Bytes of one (block, kv head) tile of K or V: block_size rows, plus for a
+// quantised cache one fp16 scale per 32 elements of each row.
 int64_t tile_bytes_of(const pkv_shape* sh) {
-  const int64_t codes = (int64_t)sh->block_size * sh->head_dim * elem_bytes(sh->dtype);
-  return sh->dtype == PKV_Q8_0 ? codes + (int64_t)sh->block_size * (sh->head_dim / 32) * 2
-                               : codes;
+  const int64_t codes = (int64_t)sh->block_size * code_row_bytes(sh->dtype, sh->head_dim);
+  return quantised(sh->dtype) ? codes + (int64_t)sh->block_size * (sh->head_dim / 32) * 2
+                              : codes;
 }
 
 // Shape checks shared by pkv_pool_bytes and pkv_kv_pool_alloc.
@@ -82,7 +90,7 @@ struct pkv_pool {
   int num_cus = 0;
   char* k_base = nullptr;
   char* v_base = nullptr;
-  int64_t row_bytes = 0;    // head_dim * elem (codes only for q8_0)
+  int64_t row_bytes = 0;    // bytes of one stored row (codes only when quantised)
   int64_t tile_bytes = 0;   // 16 rows (+ scales for q8_0)
   int64_t block_bytes = 0;  // kv_heads tiles: one block of one layer, K or V
   int64_t layer_bytes = 0;  // num_blocks blocks
@@ -290,7 +298,7 @@ constexpr int64_t kSegStartCost = PKV_SEG_START_COST;
 bool build_bins(pkv_pool* p, int nbins);
 
 void build_schedule(pkv_pool* p, int part, int target) {
-  // the eight-wave form: 2-byte and q8_0 tiles of 16-token blocks (fp32 tiles spill)
+  // the eight-wave form: 2-byte and quantised tiles of 16-token blocks (fp32 tiles spill)
   if (part == 0 && p->shape.dtype != PKV_F32 && p->shape.block_size == 16) {
     const int per_cu = pkv::decode_blocks_per_cu(p->shape.dtype, p->shape.head_dim,
                                                   p->sched_gp_building, true, 16);
@@ -561,7 +569,7 @@ int pkv_kv_pool_alloc(const pkv_shape* sh, void* dev_base, size_t dev_bytes, pkv
 
   pkv_pool* p = new pkv_pool();
   p->shape = *sh;
-  p->row_bytes = (int64_t)sh->head_dim * elem_bytes(sh->dtype);
+  p->row_bytes = code_row_bytes(sh->dtype, sh->head_dim);
   p->tile_bytes = tile_bytes_of(sh);
   p->block_bytes = p->tile_bytes * sh->kv_heads;
   p->layer_bytes = p->block_bytes * sh->num_blocks;
@@ -962,9 +970,10 @@ int pkv_kv_append(pkv_pool* p, int layer, const void* k_new, const void* v_new,
   char* vl = p->v_base + (size_t)layer * p->layer_bytes;
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_u);
   hipError_t e =
-      p->shape.dtype == PKV_Q8_0
-          ? pkv::launch_append_q8(k_new, v_new, slots, batch, kl, vl, p->shape.kv_heads,
-                                  p->shape.head_dim, p->shape.block_size, stream)
+      quantised(p->shape.dtype)
+          ? pkv::launch_append_quant(p->shape.dtype, k_new, v_new, slots, batch, kl, vl,
+                                     p->shape.kv_heads, p->shape.head_dim, p->shape.block_size,
+                                     stream)
           : pkv::launch_append(k_new, v_new, slots, batch, kl, vl, p->shape.kv_heads,
                                (int)p->row_bytes, p->shape.block_size, stream);
   if (e != hipSuccess) return hip_fail(e, "kv_append launch");

@@ -14,8 +14,9 @@
 //                   agent-scope release, an L2 write-back on this chip, which
 //                   measured ~3x slower than the extra launch.)
 //  append_kernel  — scatters each sequence's new K/V rows into the pool at its slot.
-//  append_q8_kernel — the same for a q8_0 cache: quantises each 32-value group
-//                   of the bf16 new rows to int8 codes and an fp16 scale.
+//  append_q8_kernel / append_q4_kernel — the same for a q8_0 / q4_0 cache:
+//                   quantise each 32-value group of the bf16 new rows to int8
+//                   or 4-bit codes and an fp16 scale.
 //  upload_kernel  — copies a packed metadata image from pinned host memory to
 //                   the device on the launch stream (no copy-engine hand-off).
 //  copy_blocks_kernel — copy-on-write: whole K/V blocks src -> dst for every layer.
@@ -35,17 +36,18 @@
 namespace pkv {
 namespace {
 
-enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_Q8 = 3 };
+enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_Q8 = 3, DT_Q4 = 4 };
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// Bytes of one stored element (q8_0: one int8 code; its scales are extra).
+// Bytes of one stored element (q8_0: one int8 code; q4_0: counted as one
+// here, the tile layout packs two codes per byte; scales are extra).
 template <int DT>
 struct Elem {
-  static constexpr int bytes = DT == DT_F32 ? 4 : DT == DT_Q8 ? 1 : 2;
+  static constexpr int bytes = DT == DT_F32 ? 4 : (DT == DT_Q8 || DT == DT_Q4) ? 1 : 2;
 };
 
 __device__ __forceinline__ u32x4 ld16(const char* p) {
@@ -92,6 +94,34 @@ __device__ __forceinline__ u32x4 codes_to_bf16(u32x2 c) {
   return r;
 }
 
+// 8 packed 4-bit codes (code j in bits 4j .. 4j+3) -> the 8 values code - 8
+// as bf16 (exact), an MFMA operand.
+__device__ __forceinline__ u32x4 codes_to_bf16(unsigned w) {
+  const unsigned lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;  // even, odd codes
+  u32x4 r;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    r[b] = bf16_pair((float)((lo >> (8 * b)) & 0xffu) - 8.f, (float)((hi >> (8 * b)) & 0xffu) - 8.f);
+  return r;
+}
+
+// Code values in fp32: 8 int8 codes (q8_0), or 8 packed 4-bit codes minus 8 (q4_0).
+__device__ __forceinline__ void code_vals(u32x2 c, float (&v)[8]) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    v[b] = sbyte(c[0], b);
+    v[4 + b] = sbyte(c[1], b);
+  }
+}
+__device__ __forceinline__ void code_vals(unsigned w, float (&v)[8]) {
+  const unsigned lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    v[2 * b] = (float)((lo >> (8 * b)) & 0xffu) - 8.f;
+    v[2 * b + 1] = (float)((hi >> (8 * b)) & 0xffu) - 8.f;
+  }
+}
+
 // q8_0 quantisation of 8 values of one 32-value group whose max |x| is amax:
 // scale d = amax / 127 (fp32, stored as fp16), codes round(x * (1 / d)),
 // halves away from zero (llama.cpp's Q8_0 format, the q8_0 cache type of
@@ -108,6 +138,60 @@ __device__ __forceinline__ u32x2 q8_codes(const float (&x)[8], float amax, float
   }
   *d_out = d;
   return u32x2{w[0], w[1]};
+}
+
+// q4_0 (llama.cpp's Q4_0 format, the q4_0 cache type of ssdnodes.com, "KV
+// cache vs prompt cache", "Four ways to make the KV cache smaller"): a group's
+// scale is d = m / -8, m its value of largest magnitude (the first on ties,
+// +0 for an all-zero group); codes q = min(15, trunc(x * (1 / d) + 8.5)) with
+// the product and the sum rounded separately; value (q - 8) * d.
+//
+// Largest-magnitude value among this lane's 8 values of a group (element
+// indices base .. base+7 inside the group): (|m|, m, index), (0, +0, 32) if
+// all are zero.
+__device__ __forceinline__ void q4_pick(const float (&x)[8], int base, float& a, float& m,
+                                        int& idx) {
+  a = 0.f;
+  m = 0.f;
+  idx = 32;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float ax = __builtin_fabsf(x[j]);
+    if (ax > a) {
+      a = ax;
+      m = x[j];
+      idx = base + j;
+    }
+  }
+}
+// Combine with the lane `off` away (both lanes end with the same pick).
+__device__ __forceinline__ void q4_pick_xor(float& a, float& m, int& idx, int off) {
+  const float a2 = __shfl_xor(a, off, 64), m2 = __shfl_xor(m, off, 64);
+  const int i2 = __shfl_xor(idx, off, 64);
+  if (a2 > a || (a2 == a && i2 < idx)) {
+    a = a2;
+    m = m2;
+    idx = i2;
+  }
+}
+// fp16 bits of the scale d = m / -8: -0 for an all-zero group (m = +0). The
+// zero case is spelled out: the compiler may fuse the fp16 conversion with
+// the product into one fma whose +0 addend turns -0 into +0.
+__device__ __forceinline__ unsigned q4_scale_bits(float m, float d) {
+  return m == 0.f ? 0x8000u : half_bits(d);
+}
+// The 8 codes (code j in bits 4j .. 4j+3) of 8 values under the fp32 scale d.
+__device__ __forceinline__ unsigned q4_codes(const float (&x)[8], float d) {
+#pragma clang fp contract(off)
+  const float id = d != 0.f ? 1.f / d : 0.f;
+  unsigned w = 0u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float t = x[j] * id;
+    t = t + 8.5f;
+    w |= (unsigned)min(15, (int)t) << (4 * j);
+  }
+  return w;
 }
 
 // Bit casts from one 32-bit lane of a u32x4. The element is copied to a
@@ -298,7 +382,7 @@ __device__ __forceinline__ f32x4 qk_piece(u32x4 q, u32x4 k, f32x4 acc) {
 //   fp32 / fp16 / bf16: NP 16-byte K pieces (lane (t16, kg) holds bytes
 //   kg*16 + 64*k of row t16) and NV 16-byte V chunks (chunk vc of rows
 //   vr + RPI*i).
-//   q8_0: NP 8-byte K pieces (codes 32*k + 8*kg .. +8 of row t16, one piece
+//   q8_0 / q4_0: NP 8-byte / 4-byte K pieces (codes 32*k + 8*kg .. +8 of row t16, one piece
 //   per 32-code scale group) with that row's NP fp16 scales, and NV 8-byte V
 //   chunks (codes 8*vc .. +8 of rows NV*vr + i) with those rows' scales of
 //   group vc/4.
@@ -317,6 +401,15 @@ struct TileRegs<DT_Q8, D> {
   unsigned ks[NP / 2];  // fp16 pairs: scale of group k in half k % 2 of ks[k / 2]
   unsigned vs[NV / 2];  // fp16 pairs: scale of row NV*vr + i in half i % 2 of vs[i / 2]
 };
+// q4_0: as q8_0 with 4-byte pieces and chunks (8 packed codes each).
+template <int D>
+struct TileRegs<DT_Q4, D> {
+  static constexpr int NP = D / 32, CPR = D / 8, RPI = 64 / CPR, NV = 16 / RPI;
+  unsigned k[NP];
+  unsigned v[NV];
+  unsigned ks[NP / 2];
+  unsigned vs[NV / 2];
+};
 
 // Two launch forms share this body:
 //   BINS = false: one wave per workgroup; a wave covers a contiguous run of
@@ -331,19 +424,20 @@ struct TileRegs<DT_Q8, D> {
 // tiles: a tile is one block (16), half of one (32), or two blocks (8).
 template <int DT, int D, int GP, bool BINS, int BS>
 __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p) {
-  constexpr bool Q8 = DT == DT_Q8;
+  constexpr bool Q8 = DT == DT_Q8, Q4 = DT == DT_Q4, QN = Q8 || Q4;
   using TR = TileRegs<DT, D>;
-  constexpr int RB = D * Elem<DT>::bytes;  // bytes per K/V row (codes only for q8_0)
-  constexpr int QB = Q8 ? 2 * D : RB;      // bytes per q / new K,V row (bf16 for q8_0)
+  constexpr int RB = D * Elem<DT>::bytes;  // bytes per K/V row (unquantised caches)
+  constexpr int CB = Q4 ? D / 2 : D;       // code bytes per row (quantised caches)
+  constexpr int QB = QN ? 2 * D : RB;      // bytes per q / new K,V row (bf16 when quantised)
   constexpr int NP = TR::NP;               // K pieces per lane per tile (= q pieces)
   constexpr int CPR = TR::CPR;             // V chunks per row
   constexpr int RPI = TR::RPI;             // rows covered by one V load instruction
   constexpr int NV = TR::NV;               // V loads per lane per tile
-  constexpr int EPC = Q8 ? 8 : 16 / Elem<DT>::bytes;  // elements per V chunk
+  constexpr int EPC = QN ? 8 : 16 / Elem<DT>::bytes;  // elements per V chunk
   constexpr int NG = GP >= 4 ? GP / 4 : 1;  // lane groups (of 16) holding real heads
   constexpr int HPG = GP >= 4 ? 4 : GP;     // heads per lane group
-  // bytes of one (block, kv head) tile of the pool: BS rows (+ q8_0 scales)
-  constexpr int TILE = Q8 ? BS * D + BS * (D / 32) * 2 : BS * RB;
+  // bytes of one (block, kv head) tile of the pool: BS rows (+ scales when quantised)
+  constexpr int TILE = QN ? BS * CB + BS * (D / 32) * 2 : BS * RB;
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   // Tile buffers per wave. Three or four (more bytes in flight per wave) ran
   // slower than two on MI355X for both bf16 and q8_0 tiles.
@@ -398,7 +492,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
   const int vc = lane % CPR;  // V chunk this lane owns
   const int vr = lane / CPR;  // V row group of this lane
   // V row held in the lane's i-th chunk
-  auto vrow = [&](int i) { return Q8 ? NV * vr + i : vr + RPI * i; };
+  auto vrow = [&](int i) { return QN ? NV * vr + i : vr + RPI * i; };
   const size_t blk_stride = (size_t)p.kv_heads * TILE;
   int parity = 0;
 
@@ -456,20 +550,29 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       auto rib = [&](int r) { return BS == 8 ? (r & 7) : BS == 32 ? 16 * half + r : r; };
       const char* ktile = kbase + (size_t)blk_of(t16) * blk_stride;
       const int kr = rib(t16);
-      if constexpr (Q8) {
-        const char* kt = ktile + kr * D + kg * 8;
+      if constexpr (QN) {
+        // piece k / chunk vc: codes 32*k + 8*kg .. +8 / 8*vc .. +8 of a row,
+        // 8 bytes (q8_0) or 4 bytes (q4_0)
+        constexpr int PB = Q4 ? 4 : 8;
+        const char* kt = ktile + kr * CB + kg * PB;
 #pragma unroll
-        for (int k = 0; k < NP; ++k) t.k[k] = ld8(kt + k * 32);
+        for (int k = 0; k < NP; ++k) {
+          if constexpr (Q4) t.k[k] = ld4(kt + k * 16);
+          else t.k[k] = ld8(kt + k * 32);
+        }
         // the lane's NV consecutive V rows lie in one block
         const int r0 = NV * vr;
         const char* vtile = vbase + (size_t)blk_of(r0) * blk_stride;
         const int vrr = rib(r0);
-        const char* vt = vtile + vrr * D + vc * 8;
+        const char* vt = vtile + vrr * CB + vc * PB;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) t.v[i] = ld8(vt + i * D);
-        // scales after the BS x D codes: K [row][group], V [group][row]
-        const char* ksp = ktile + BS * D + kr * NP * 2;
-        const char* vsp = vtile + BS * D + ((vc >> 2) * BS + vrr) * 2;
+        for (int i = 0; i < NV; ++i) {
+          if constexpr (Q4) t.v[i] = ld4(vt + i * CB);
+          else t.v[i] = ld8(vt + i * CB);
+        }
+        // scales after the BS rows of codes: K [row][group], V [group][row]
+        const char* ksp = ktile + BS * CB + kr * NP * 2;
+        const char* vsp = vtile + BS * CB + ((vc >> 2) * BS + vrr) * 2;
         if constexpr (NP == 4) {
           const u32x2 x2 = ld8(ksp);
           t.ks[0] = x2[0];
@@ -531,7 +634,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
 
     auto compute_tile = [&](int valid, const TR& t) {
       f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (Q8) {
+      if constexpr (QN) {
         // one MFMA per 32-code group, then that group's scale for this
         // lane's token: sum_k d_k * (q_k . c_k)
 #pragma unroll
@@ -587,14 +690,9 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       for (int i = 0; i < NV; ++i) {
         const int tr = vrow(i);
         float vals[EPC];
-        float dv = 1.f;  // q8_0: the row's scale for this lane's group
-        if constexpr (Q8) {
-          const unsigned w0 = t.v[i][0], w1 = t.v[i][1];
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            vals[b] = sbyte(w0, b);
-            vals[4 + b] = sbyte(w1, b);
-          }
+        float dv = 1.f;  // quantised: the row's scale for this lane's group
+        if constexpr (QN) {
+          code_vals(t.v[i], vals);
           dv = (i & 1) ? half_hi(t.vs[i >> 1]) : half_lo(t.vs[i >> 1]);
           if (tr >= valid) dv = 0.f;  // rows past the context may hold anything (NaN scales)
         } else {
@@ -606,7 +704,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         }
         float pt[GP];
 #pragma unroll
-        for (int h = 0; h < GP; ++h) pt[h] = Q8 ? pl[tr * GP + h] * dv : pl[tr * GP + h];
+        for (int h = 0; h < GP; ++h) pt[h] = QN ? pl[tr * GP + h] * dv : pl[tr * GP + h];
 #pragma unroll
         for (int h = 0; h < GP; ++h)
 #pragma unroll
@@ -676,7 +774,57 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       char* ktile = const_cast<char*>(kbase) + (size_t)blk_last * blk_stride;
       char* vtile = const_cast<char*>(vbase) + (size_t)blk_last * blk_stride;
       TR tn;
-      if constexpr (Q8) {
+      if constexpr (Q4) {
+        // As for q8_0 below, with the group's first largest-magnitude value
+        // found across the same lanes and 4-bit codes.
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+          float x[8];
+          to_f32<DT_BF16>(ld16(kn_row + kg * 16 + k * 64), x);
+          float a, mv;
+          int idx;
+          q4_pick(x, 8 * kg, a, mv, idx);
+          q4_pick_xor(a, mv, idx, 16);
+          q4_pick_xor(a, mv, idx, 32);
+          const float d = mv / -8.f;
+          tn.k[k] = q4_codes(x, d);
+          const unsigned hb = q4_scale_bits(mv, d);
+          if (k & 1) tn.ks[k >> 1] |= hb << 16;
+          else tn.ks[k >> 1] = hb;
+        }
+        {
+          float x[8];
+          to_f32<DT_BF16>(ld16(vn_row + vc * 16), x);
+          float a, mv;
+          int idx;
+          q4_pick(x, 8 * (vc & 3), a, mv, idx);
+          q4_pick_xor(a, mv, idx, 1);
+          q4_pick_xor(a, mv, idx, 2);
+          const float d = mv / -8.f;
+          const unsigned c = q4_codes(x, d);
+#pragma unroll
+          for (int i = 0; i < NV; ++i) tn.v[i] = c;  // only row 0 is attended
+#pragma unroll
+          for (int i = 0; i < NV / 2; ++i) tn.vs[i] = 0u;
+          tn.vs[0] = q4_scale_bits(mv, d);
+          if (vr == 0) {
+            *reinterpret_cast<unsigned*>(vtile + t_new * CB + vc * 4) = c;
+            if ((vc & 3) == 0)
+              *reinterpret_cast<unsigned short*>(vtile + BS * CB + ((vc >> 2) * BS + t_new) * 2) =
+                  (unsigned short)tn.vs[0];
+          }
+        }
+        if (t16 == 0) {
+#pragma unroll
+          for (int k = 0; k < NP; ++k)
+            *reinterpret_cast<unsigned*>(ktile + t_new * CB + kg * 4 + k * 16) = tn.k[k];
+          if (kg == 0) {
+            char* ksp = ktile + BS * CB + t_new * NP * 2;
+            if constexpr (NP == 4) *reinterpret_cast<u32x2*>(ksp) = u32x2{tn.ks[0], tn.ks[1]};
+            else *reinterpret_cast<unsigned*>(ksp) = tn.ks[0];
+          }
+        }
+      } else if constexpr (Q8) {
         // Quantise the bf16 row group by group (as the append kernel does):
         // K group k is spread over the four lanes kg of a token column, a V
         // group over four neighbouring chunks of one row.
@@ -942,6 +1090,54 @@ __global__ __launch_bounds__(256) void append_q8_kernel(const char* k_new, const
   *reinterpret_cast<unsigned short*>(tile + BS * D + si * 2) = (unsigned short)half_bits(d);
 }
 
+// q4_0 append: as append_q8_kernel, with the group's first largest-magnitude
+// value m, scale m / -8 and 16 bytes of packed 4-bit codes per group.
+template <int D>
+__global__ __launch_bounds__(256) void append_q4_kernel(const char* k_new, const char* v_new,
+                                                        const int64_t* slots, int batch,
+                                                        char* k_layer, char* v_layer,
+                                                        int kv_heads, int block_size) {
+  constexpr int NGR = D / 32;
+  constexpr int CB = D / 2;
+  const int BS = block_size;
+  const int TILE = BS * CB + BS * NGR * 2;
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const int grp = (int)(idx % NGR);
+  long r = idx / NGR;
+  const int kv = (int)(r & 1);
+  r >>= 1;
+  const int g = (int)(r % kv_heads);
+  const long s = r / kv_heads;
+  if (s >= batch) return;
+  const int64_t slot = slots[s];
+  if (slot < 0) return;
+  const int64_t blk = slot / BS;
+  const int pos = (int)(slot % BS);
+  const char* src = (kv ? v_new : k_new) + (((size_t)s * kv_heads + g) * D + grp * 32) * 2;
+  float x[4][8];
+  float a = 0.f, m = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    to_f32<DT_BF16>(ld16(src + c * 16), x[c]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float ax = __builtin_fabsf(x[c][j]);
+      if (ax > a) {
+        a = ax;
+        m = x[c][j];
+      }
+    }
+  }
+  const float d = m / -8.f;
+  u32x4 w;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) w[c] = q4_codes(x[c], d);
+  char* tile = (kv ? v_layer : k_layer) + ((size_t)blk * kv_heads + g) * TILE;
+  *reinterpret_cast<u32x4*>(tile + pos * CB + grp * 16) = w;
+  const int si = kv ? grp * BS + pos : pos * NGR + grp;
+  *reinterpret_cast<unsigned short*>(tile + BS * CB + si * 2) = (unsigned short)q4_scale_bits(m, d);
+}
+
 __global__ __launch_bounds__(256) void copy_blocks_kernel(const int32_t* pairs, int layers,
                                                           char* k_base, char* v_base,
                                                           int64_t layer_bytes,
@@ -1005,6 +1201,7 @@ const void* decode_kernel_for(int dtype, int d, int gp, bool bins, int bs) {
     case DT_F16: return pick_d<DT_F16>(d, gp, bins, bs);
     case DT_BF16: return pick_d<DT_BF16>(d, gp, bins, bs);
     case DT_Q8: return pick_d<DT_Q8>(d, gp, bins, bs);
+    case DT_Q4: return pick_d<DT_Q4>(d, gp, bins, bs);
   }
   return nullptr;
 }
@@ -1063,23 +1260,23 @@ hipError_t launch_append(const void* k_new, const void* v_new, const int64_t* sl
   return hipGetLastError();
 }
 
-hipError_t launch_append_q8(const void* k_new, const void* v_new, const int64_t* slots,
-                            int batch, void* k_layer, void* v_layer, int kv_heads, int head_dim,
-                            int block_size, hipStream_t stream) {
+hipError_t launch_append_quant(int dtype, const void* k_new, const void* v_new,
+                               const int64_t* slots, int batch, void* k_layer, void* v_layer,
+                               int kv_heads, int head_dim, int block_size, hipStream_t stream) {
   const long threads = (long)batch * kv_heads * 2 * (head_dim / 32);
   const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
   const char* kn = static_cast<const char*>(k_new);
   const char* vn = static_cast<const char*>(v_new);
   char* kl = static_cast<char*>(k_layer);
   char* vl = static_cast<char*>(v_layer);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(append_q8_kernel<128>, grid, block, 0, stream, kn, vn, slots, batch, kl, vl,
-                       kv_heads, block_size);
-  else if (head_dim == 64)
-    hipLaunchKernelGGL(append_q8_kernel<64>, grid, block, 0, stream, kn, vn, slots, batch, kl, vl,
-                       kv_heads, block_size);
-  else
-    return hipErrorInvalidValue;
+  void (*fn)(const char*, const char*, const int64_t*, int, char*, char*, int, int) = nullptr;
+  if (dtype == DT_Q8) fn = head_dim == 128 ? append_q8_kernel<128>
+                           : head_dim == 64 ? append_q8_kernel<64> : nullptr;
+  if (dtype == DT_Q4) fn = head_dim == 128 ? append_q4_kernel<128>
+                           : head_dim == 64 ? append_q4_kernel<64> : nullptr;
+  if (!fn) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fn, grid, block, 0, stream, kn, vn, slots, batch, kl, vl, kv_heads,
+                     block_size);
   return hipGetLastError();
 }
 

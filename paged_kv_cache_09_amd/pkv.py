@@ -16,7 +16,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
-F32, F16, BF16, Q8_0 = 0, 1, 2, 3
+F32, F16, BF16, Q8_0, Q4_0 = 0, 1, 2, 3, 4
 OK, EINVAL, ECAPACITY, EOUT_OF_BLOCKS, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -5
 
 if not os.path.exists(LIB_PATH):

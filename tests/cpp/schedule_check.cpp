@@ -16,7 +16,7 @@ hipError_t launch_decode(int, int, int, bool, int, const DecodeParams&, hipStrea
 hipError_t launch_reduce(int, int, const ReduceParams&, hipStream_t) { return hipSuccess; }
 int decode_blocks_per_cu(int, int, int, bool, int) { return 1; }
 hipError_t launch_append(const void*, const void*, const int64_t*, int, void*, void*, int, int, int, hipStream_t) { return hipSuccess; }
-hipError_t launch_append_q8(const void*, const void*, const int64_t*, int, void*, void*, int, int, int, hipStream_t) { return hipSuccess; }
+hipError_t launch_append_quant(int, const void*, const void*, const int64_t*, int, void*, void*, int, int, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_copy_blocks(const int32_t*, int, void*, void*, int, int64_t, int64_t, hipStream_t) { return hipSuccess; }
 hipError_t launch_upload(const void*, void*, size_t, hipStream_t) { return hipSuccess; }
 }

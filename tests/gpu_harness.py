@@ -119,10 +119,13 @@ def pick_seqs(w: W.Workload, sample: int | None, seed: int = 0):
 
 
 def run_step_case(cfg, *, layers=1, partitions=(0,), sample=None, check_untouched=True,
-                  label="", fused=False):
-    """Full step on both sides; returns a dict of max errors per (layer, partition)."""
+                  label="", fused=False, edit=None):
+    """Full step on both sides; returns a dict of max errors per (layer, partition).
+    ``edit(w)``, if given, may rewrite the generated inputs before either side runs."""
     say(f"case {label or cfg.name}: build workload B={cfg.batch} layers={layers}")
     w = W.make(cfg, device="cuda", layers=layers, form="step", fill="nan")
+    if edit is not None:
+        edit(w)
     seqs = pick_seqs(w, sample)
     say(f"case {label or cfg.name}: oracle on {len(seqs)} sequences")
     ora = OracleSide(w, seqs).run()

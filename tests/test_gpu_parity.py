@@ -58,6 +58,21 @@ SMALL = {
                               num_blocks=200),
     "q8_long_small": W.scaled(W.CONFIGS["long_ctx_bf16"], dtype=W.Q8_0, batch=2,
                               ctx_fixed=(4097, 3001), num_blocks=500),
+    # q4_0 cache: the same spread of GQA groups, head dims and sharing
+    "q4_llama_small": W.scaled(W.CONFIGS["llama8b_q4"], batch=6, num_blocks=6 * 50,
+                               ctx_lo=1, ctx_hi=700),
+    "q4_mha_small": W.scaled(W.CONFIGS["llama8b_q4"], batch=5, q_heads=6, kv_heads=6,
+                             num_blocks=5 * 40, ctx_lo=16, ctx_hi=600),
+    "q4_gqa8": W.scaled(W.CONFIGS["llama8b_q4"], batch=3, q_heads=16, kv_heads=2,
+                        num_blocks=150, ctx_lo=1, ctx_hi=600),
+    "q4_gqa3_d64": W.scaled(W.CONFIGS["llama8b_q4"], batch=4, q_heads=6, kv_heads=2,
+                            head_dim=64, num_blocks=200, ctx_lo=1, ctx_hi=700),
+    "q4_len1": W.scaled(W.CONFIGS["llama8b_q4"], batch=4, q_heads=4, kv_heads=2,
+                        ctx_kind="fixed", ctx_fixed=(1, 16, 17, 33), num_blocks=40),
+    "q4_shared_cow": W.scaled(W.CONFIGS["shared_prefix_cow_bf16"], dtype=W.Q4_0, batch=5,
+                              num_blocks=200),
+    "q4_long_small": W.scaled(W.CONFIGS["long_ctx_bf16"], dtype=W.Q4_0, batch=2,
+                              ctx_fixed=(4097, 3001), num_blocks=500),
     # block sizes 8 and 32 (tiles of two blocks / half a block)
     "bs8_bf16": W.scaled(W.CONFIGS["llama8b_bf16"], batch=6, num_blocks=6 * 100, ctx_lo=1,
                          ctx_hi=700, block_size=8),
@@ -66,6 +81,10 @@ SMALL = {
     "bs8_q8": W.scaled(W.CONFIGS["llama8b_q8"], batch=5, num_blocks=5 * 100, ctx_lo=1,
                        ctx_hi=600, block_size=8),
     "bs32_q8_d64": W.scaled(W.CONFIGS["llama8b_q8"], batch=4, q_heads=4, kv_heads=2,
+                            head_dim=64, num_blocks=4 * 30, ctx_lo=1, ctx_hi=700, block_size=32),
+    "bs8_q4": W.scaled(W.CONFIGS["llama8b_q4"], batch=5, num_blocks=5 * 100, ctx_lo=1,
+                       ctx_hi=600, block_size=8),
+    "bs32_q4_d64": W.scaled(W.CONFIGS["llama8b_q4"], batch=4, q_heads=2, kv_heads=2,
                             head_dim=64, num_blocks=4 * 30, ctx_lo=1, ctx_hi=700, block_size=32),
     "bs8_f32_len": W.scaled(W.CONFIGS["tiny_f32"], ctx_fixed=(1, 8, 9, 33), num_blocks=64,
                             block_size=8),
@@ -96,6 +115,7 @@ FULL = [
     ("shared_prefix_cow_bf16", 2, (0,), None),
     ("long_ctx_bf16", 1, (512, 0), None),
     ("llama8b_q8", 2, (0, 512), None),
+    ("llama8b_q4", 2, (0, 512), None),
 ]
 
 
@@ -124,6 +144,11 @@ WRITES = {
                                head_dim=64, num_blocks=4 * 100, ctx_lo=16, ctx_hi=700), 1, 600),
     "write_bs8_q8": (W.scaled(W.CONFIGS["llama8b_q8"], batch=4, num_blocks=4 * 200, ctx_lo=1,
                               ctx_hi=600, block_size=8), 1, 500),
+    "write_q4": (W.scaled(W.CONFIGS["llama8b_q4"], batch=5, num_blocks=5 * 100, ctx_lo=1,
+                          ctx_hi=600), 1, 600),
+    "write_bs32_q4_d64": (W.scaled(W.CONFIGS["llama8b_q4"], batch=4, q_heads=4, kv_heads=2,
+                                   head_dim=64, num_blocks=4 * 50, ctx_lo=1, ctx_hi=600,
+                                   block_size=32), 1, 500),
     "write_bs32_bf16": (W.scaled(W.CONFIGS["llama8b_bf16"], batch=4, num_blocks=4 * 50,
                                  ctx_lo=1, ctx_hi=600, block_size=32), 1, 500),
 }
@@ -147,6 +172,9 @@ PREFIX = {
     "prefix_q8_tight": (W.CONFIGS["llama8b_q8"], dict(num_blocks=160, n_prefixes=4,
                                                        prefix_len=200, suffix_hi=150, na=10,
                                                        nb=6, seed=2)),
+    "prefix_q4": (W.CONFIGS["llama8b_q4"], dict(num_blocks=300, n_prefixes=3,
+                                                 prefix_len=250, suffix_hi=150, na=8, nb=6,
+                                                 seed=4)),
     "prefix_f16_mha": (W.scaled(W.CONFIGS["mha13b_f16"], q_heads=4, kv_heads=4),
                        dict(num_blocks=400, n_prefixes=2, prefix_len=500, suffix_hi=100,
                             na=4, nb=6, seed=3)),
@@ -160,6 +188,50 @@ def test_prefix_cached_blocks_decode_like_written_ones(name):
     tol = tolerance(cfg)
     for key, e in errs.items():
         assert e <= tol, f"{name} partition {key}: max abs error {e} > {tol}"
+
+
+def _q4_edge_rows(w):
+    """New K/V rows built to hit the q4_0 decisions: an all +0 group, an all -0
+    group, largest magnitudes tied with opposite signs in different lanes'
+    eighths of a group (the first must win), a group whose largest value is
+    -8 (scale exactly 1, codes on the trunc boundaries x + 8.5 = integer) and
+    random groups with coarse bf16 values (many ties)."""
+    gen = torch.Generator().manual_seed(11)
+    rows = []
+    for t in (w.k_new, w.v_new):
+        B, H, D = t.shape
+        x = torch.randint(-6, 7, (B, H, D), generator=gen).float() * 0.25
+        for s in range(B):
+            for g in range(H):
+                r = x[s, g]
+                k = (s * H + g) % (D // 32)  # rotate the patterns over the groups
+                grp = lambda i: slice(32 * ((k + i) % (D // 32)), 32 * ((k + i) % (D // 32)) + 32)
+                r[grp(0)] = 0.0
+                if D // 32 > 1:
+                    r[grp(1)] = -0.0
+                if D // 32 > 2:
+                    a = r[grp(2)].clamp(-1.0, 1.0)
+                    a[5], a[20] = -1.5, 1.5  # tie across lanes: the first (-1.5) is m
+                    a[9], a[31] = 1.5, -1.5 if s % 2 else 1.5
+                    r[grp(2)] = a
+                if D // 32 > 3:
+                    b = torch.arange(32).float() * 0.5 - 7.5  # -7.5 .. 8.0
+                    b[0] = -8.0
+                    r[grp(3)] = b.clamp(max=7.5)
+        rows.append(x.to(t.dtype).to(t.device))
+    w.k_new.copy_(rows[0])
+    w.v_new.copy_(rows[1])
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["append+decode", "fused"])
+@pytest.mark.parametrize("head_dim", [128, 64])
+def test_q4_append_edge_rows(head_dim, fused):
+    cfg = W.scaled(W.CONFIGS["llama8b_q4"], batch=6, q_heads=8, kv_heads=2, head_dim=head_dim,
+                   num_blocks=6 * 20, ctx_lo=1, ctx_hi=300)
+    errs, _, _ = run_step_case(cfg, layers=1, partitions=(0, 16), label=f"q4 edge d{head_dim}",
+                               fused=fused, edit=_q4_edge_rows)
+    for key, e in errs.items():
+        assert e <= tolerance(cfg), f"q4 edge rows {key}: max abs error {e}"
 
 
 def _decode_form(cfg, device="cuda"):

@@ -60,6 +60,22 @@ def test_pool_bytes_13b_shape():
     assert pkv.pool_bytes(sh) == 2048 * oracle.kv_bytes_per_token(40, 40, 128, 2)
 
 
+def test_pool_bytes_quantised_caches():
+    """q8_0 / q4_0 pools: the oracle's tile size per (block, kv head) for every
+    layer, K and V; at the page's Llama-3.1-8B shape a q4_0 pool for 32k
+    tokens is about 1 GiB (the scales make it 9/8 of the codes alone)."""
+    g = json.load(open(GOLDEN))["quantised_cache_q4_0"]
+    L, H, D, T = g["layers"], g["kv_heads"], g["head_dim"], g["tokens"]
+    for dt, odt in ((pkv.Q8_0, oracle.Q8_0), (pkv.Q4_0, oracle.Q4_0)):
+        for bs in (8, 16, 32):
+            sh = pkv.make_shape(L, T // bs, H, D, dt, T, 1, block_size=bs)
+            assert pkv.pool_bytes(sh) == 2 * L * (T // bs) * H * oracle.q_tile_bytes(odt, D, bs)
+    q4 = pkv.pool_bytes(pkv.make_shape(L, T // 16, H, D, pkv.Q4_0, T, 1))
+    assert abs(q4 / (1 << 30) - g["q4_0_approx_gib"]) <= 0.15 * g["q4_0_approx_gib"]
+    f16 = pkv.pool_bytes(pkv.make_shape(L, T // 16, H, D, pkv.F16, T, 1))
+    assert q4 * 32 == f16 * 9  # 72 of 256 bytes per row
+
+
 def test_unsupported_shapes_rejected():
     assert pkv.pool_bytes(pkv.make_shape(1, 8, 2, 96, pkv.F32, 16, 1)) == 0
     with pytest.raises(pkv.PkvError) as e:
