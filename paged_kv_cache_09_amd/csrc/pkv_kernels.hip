@@ -94,18 +94,22 @@ __device__ __forceinline__ u32x4 codes_to_bf16(u32x2 c) {
   return r;
 }
 
-// 8 packed 4-bit codes (code j in bits 4j .. 4j+3) -> the 8 values code - 8
-// as bf16 (exact), an MFMA operand.
-__device__ __forceinline__ u32x4 codes_to_bf16(unsigned w) {
+// 8 packed 4-bit codes (code j in bits 4j .. 4j+3) -> the 8 values 128 + code
+// as bf16 (exact: bf16 0x4300 is 128 and its low mantissa bits count units), an
+// MFMA operand. The 136 that separates 128 + code from code - 8 is taken off
+// through the MFMA's accumulator input.
+__device__ __forceinline__ u32x4 nibbles_to_bf16_128(unsigned w) {
   const unsigned lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;  // even, odd codes
   u32x4 r;
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
-    r[b] = bf16_pair((float)((lo >> (8 * b)) & 0xffu) - 8.f, (float)((hi >> (8 * b)) & 0xffu) - 8.f);
+  for (int b = 0; b < 4; ++b)  // bytes (lo.b, 0, hi.b, 0), then the bf16 exponent bytes
+    r[b] = __builtin_amdgcn_perm(hi, lo, 0x0c000c00u | ((4u + b) << 16) | (unsigned)b) |
+           0x43004300u;
   return r;
 }
 
-// Code values in fp32: 8 int8 codes (q8_0), or 8 packed 4-bit codes minus 8 (q4_0).
+// Code values in fp32: 8 int8 codes (q8_0), or 8 packed 4-bit codes 0..15
+// (q4_0: the caller takes off 8 times the weight sum).
 __device__ __forceinline__ void code_vals(u32x2 c, float (&v)[8]) {
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -114,11 +118,14 @@ __device__ __forceinline__ void code_vals(u32x2 c, float (&v)[8]) {
   }
 }
 __device__ __forceinline__ void code_vals(unsigned w, float (&v)[8]) {
-  const unsigned lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+  unsigned lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+  // hide the masks from the optimiser: it would otherwise extract every
+  // nibble with its own bit-field op instead of converting bytes directly
+  asm("" : "+v"(lo), "+v"(hi));
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    v[2 * b] = (float)((lo >> (8 * b)) & 0xffu) - 8.f;
-    v[2 * b + 1] = (float)((hi >> (8 * b)) & 0xffu) - 8.f;
+    v[2 * b] = (float)((lo >> (8 * b)) & 0xffu);
+    v[2 * b + 1] = (float)((hi >> (8 * b)) & 0xffu);
   }
 }
 
@@ -618,19 +625,35 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         qv[k] = t16 < p.group ? v : u32x4{0u, 0u, 0u, 0u};
       }
     }
+    // q4_0: -136 times each q piece's sum over its group (an MFMA against
+    // ones), the accumulator input that turns q . (128 + code) into
+    // q . (code - 8).
+    f32x4 qb[Q4 ? NP : 1];
+    if constexpr (Q4) {
+      const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+#pragma unroll
+      for (int k = 0; k < NP; ++k) {
+        const f32x4 sq = qk_piece<DT_BF16>(qv[k], ones, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qb[k][i] = -136.f * sq[i];
+      }
+    }
 
     // Lane (t16, kg) keeps softmax state for heads 4*kg + i of its row.
     float m[HPG], lsum[HPG];
     float acc[GP][EPC];
+    float bsum[GP];  // q4_0: sum of the lane's scaled weights per head (8 x it is taken off)
 #pragma unroll
     for (int i = 0; i < HPG; ++i) {
       m[i] = -__builtin_inff();
       lsum[i] = 0.f;
     }
 #pragma unroll
-    for (int h = 0; h < GP; ++h)
+    for (int h = 0; h < GP; ++h) {
+      bsum[h] = 0.f;
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[h][e] = 0.f;
+    }
 
     auto compute_tile = [&](int valid, const TR& t) {
       f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
@@ -639,7 +662,9 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         // lane's token: sum_k d_k * (q_k . c_k)
 #pragma unroll
         for (int k = 0; k < NP; ++k) {
-          const f32x4 r = qk_piece<DT_BF16>(qv[k], codes_to_bf16(t.k[k]), f32x4{0.f, 0.f, 0.f, 0.f});
+          f32x4 r;
+          if constexpr (Q4) r = qk_piece<DT_BF16>(qv[k], nibbles_to_bf16_128(t.k[k]), qb[k]);
+          else r = qk_piece<DT_BF16>(qv[k], codes_to_bf16(t.k[k]), f32x4{0.f, 0.f, 0.f, 0.f});
           const float dk = (k & 1) ? half_hi(t.ks[k >> 1]) : half_lo(t.ks[k >> 1]);
 #pragma unroll
           for (int i = 0; i < 4; ++i) sacc[i] = __builtin_fmaf(dk, r[i], sacc[i]);
@@ -673,6 +698,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
           const float a = a_lds[h];
+          bsum[h] *= a;
 #pragma unroll
           for (int e = 0; e < EPC; ++e) acc[h][e] *= a;
         }
@@ -705,6 +731,10 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         float pt[GP];
 #pragma unroll
         for (int h = 0; h < GP; ++h) pt[h] = QN ? pl[tr * GP + h] * dv : pl[tr * GP + h];
+        if constexpr (Q4) {
+#pragma unroll
+          for (int h = 0; h < GP; ++h) bsum[h] += pt[h];
+        }
 #pragma unroll
         for (int h = 0; h < GP; ++h)
 #pragma unroll
@@ -721,17 +751,10 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       const int nb = min(CH, j1c - jb);
       const int e0 = BS == 32 ? (jb >> 1) : BS == 8 ? 2 * jb : jb;
       TR t[NBUF];
-      // The run's first block id(s) are in the descriptor: the first tile is
-      // requested before the entries (the first wait must not cover that load).
-      if constexpr (BS == 16) {
-        load_tile(jb == j0 ? blk_first : bt_row[jb], 0, 0, t[0]);
-      } else if constexpr (BS == 32) {
-        load_tile(jb == j0 ? blk_first : bt_row[jb >> 1], 0, jb & 1, t[0]);
-      } else {
-        const int second = 2 * jb + 1 < nent_seq ? bt_row[2 * jb + 1] : 0;
-        load_tile(jb == j0 ? blk_first : bt_row[2 * jb], jb == j0 ? blk_second : second, 0, t[0]);
-      }
-      // up to 64 entries: CH tiles need CH (16), 2 * CH = 64 (8) or CH / 2 + 1 (32)
+      // Block-table entries first, one per lane (up to 64: CH tiles need CH
+      // (16), 2 * CH = 64 (8) or CH / 2 + 1 (32)), then the first tile, whose
+      // id(s) the descriptor holds for the run's first chunk: the first wait
+      // for the entries then leaves that tile's loads in flight.
       const int my_ent = e0 + lane < nent_seq ? bt_row[e0 + lane] : 0;
       // block ids of chunk tile j: (a, b, half)
       auto tile_ids = [&](int j, int& a, int& b, int& half) {
@@ -752,15 +775,23 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         tile_ids(j, a, b, half);
         load_tile(a, b, half, t);
       };
+      if (jb == j0) load_tile(blk_first, BS == 8 ? blk_second : 0, BS == 32 ? (jb & 1) : 0, t[0]);
+      else load_j(0, t[0]);
 #pragma unroll
-      for (int u = 1; u < NBUF - 1; ++u)
-        if (u < nb) load_j(u, t[u]);
+      for (int u = 1; u < NBUF - 1; ++u) load_j(min(u, nb - 1), t[u]);
+      // Every step requests a tile, the chunk's last one again once the chunk
+      // is exhausted (a repeat the cache serves): with no conditional loads
+      // the compiler's wait counts stay static and only the tile about to be
+      // computed is waited for, never the one just requested.
       for (int jj = 0; jj < nb; jj += NBUF) {
 #pragma unroll
         for (int u = 0; u < NBUF; ++u) {
           const int j = jj + u;
           if (j < nb) {
-            if (j + NBUF - 1 < nb) load_j(j + NBUF - 1, t[(u + NBUF - 1) % NBUF]);
+            load_j(min(j + NBUF - 1, nb - 1), t[(u + NBUF - 1) % NBUF]);
+            // keep the scheduler from hoisting the compute (and its waits) above
+            // the request
+            __builtin_amdgcn_sched_barrier(0);
             compute_tile(min(16, Lc - 16 * (jb + j)), t[u]);
           }
         }
@@ -894,6 +925,12 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     float lt[HPG];
 #pragma unroll
     for (int i = 0; i < HPG; ++i) lt[i] = row_sum(lsum[i]);
+    if constexpr (Q4) {  // sum_t w_t (code_t - 8) = sum_t w_t code_t - 8 sum_t w_t
+#pragma unroll
+      for (int h = 0; h < GP; ++h)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[h][e] = __builtin_fmaf(-8.f, bsum[h], acc[h][e]);
+    }
 #pragma unroll
     for (int off = CPR; off < 64; off <<= 1)
 #pragma unroll
