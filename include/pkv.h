@@ -48,9 +48,14 @@
  * q4_0 cache (PKV_Q4_0): the 4-bit cache type of the same passage (about a
  * quarter of an f16 cache), in llama.cpp's Q4_0 block format: every 32
  * consecutive elements of a row are one fp16 scale d and 32 4-bit codes q,
- * value (q - 8) * d. A tile is block_size rows of head_dim/2 bytes (element
- * i in byte i/2, low nibble for even i) followed by the scales as for q8_0
- * (1152 bytes for head_dim 128). q, k_new and v_new are bf16; appends take m,
+ * value (q - 8) * d. A tile is block_size rows of CB = head_dim/2 code bytes
+ * followed by the scales as for q8_0 (1152 bytes for head_dim 128). Codes are
+ * kept in 4-byte words of 8 consecutive elements (element j of a word in byte
+ * j/2, low nibble for even j); with G = head_dim/32, word w = 4k + q of row r
+ * (group k, quarter q) is at byte r*CB + 4*(q*G + k) of a K tile and at
+ * (r - r%G)*CB + 4*(w*G + r%G) of a V tile, so that the decode kernel reads a
+ * lane's share of each tile with one 16-byte (head_dim 64: 8-byte) load.
+ * q, k_new and v_new are bf16; appends take m,
  * the group's element of largest magnitude (the first on ties, +0 for an
  * all-zero group), d = m / -8 and q = min(15, trunc(x * (1/d) + 8.5)) (fp32,
  * product and sum rounded separately, 1/d taken as 0 when d is 0), d stored

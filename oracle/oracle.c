@@ -185,10 +185,17 @@ void orc_q4_quantize(const float* x, int64_t n_groups, uint8_t* codes, uint16_t*
 
 /*
  * Quantised tile of one (block, kv head) in the pool (our layout; the pages fix
- * none): block_size rows of codes, row-major (q8_0: head_dim int8 codes; q4_0:
- * head_dim/2 bytes, element d in byte d/2, low nibble for even d), then
- * block_size x head_dim/32 fp16 scales, ordered [row][group] in the K region
- * and [group][row] in the V region.
+ * none): block_size rows of codes, then block_size x head_dim/32 fp16 scales,
+ * ordered [row][group] in the K region and [group][row] in the V region.
+ * q8_0: row r's head_dim int8 codes at bytes r*head_dim .. in element order.
+ * q4_0: a word is 4 bytes holding 8 consecutive elements of a row (element j of
+ * the word in byte j/2, low nibble for even j); with G = head_dim/32 groups and
+ * CB = head_dim/2 code bytes per row, word w = 4k + q of row r (group k,
+ * quarter q) lies at byte
+ *   K region: r*CB + 4*(q*G + k)                     (words transposed in the row)
+ *   V region: (r - r%G)*CB + 4*(w*G + r%G)           (rows interleaved by G)
+ * so that one reader's share of a tile (the G words of one quarter of a K row,
+ * or one word of G consecutive V rows) is one contiguous run.
  */
 static size_t orc_code_row_bytes(int dtype, int head_dim) {
   return dtype == ORC_Q4_0 ? (size_t)head_dim / 2 : (size_t)head_dim;
@@ -197,6 +204,12 @@ static size_t orc_code_row_bytes(int dtype, int head_dim) {
 static size_t orc_qtile_bytes(int dtype, int block_size, int head_dim) {
   return (size_t)block_size * orc_code_row_bytes(dtype, head_dim) +
          (size_t)block_size * (head_dim / 32) * 2;
+}
+
+static size_t orc_q4_word_offset(int is_v, int row, int word, int head_dim) {
+  const size_t G = (size_t)head_dim / 32, CB = (size_t)head_dim / 2;
+  if (is_v) return ((size_t)row - (size_t)row % G) * CB + 4 * ((size_t)word * G + (size_t)row % G);
+  return (size_t)row * CB + 4 * ((size_t)(word % 4) * G + (size_t)(word / 4));
 }
 
 static size_t orc_qscale_offset(int dtype, int is_v, int row, int grp, int block_size,
@@ -215,7 +228,7 @@ static double orc_qload(const char* tile, int dtype, int is_v, int row, int d, i
   double code;
   if (dtype == ORC_Q4_0) {
     uint8_t b;
-    memcpy(&b, tile + (size_t)row * (head_dim / 2) + d / 2, 1);
+    memcpy(&b, tile + orc_q4_word_offset(is_v, row, d / 8, head_dim) + (d % 8) / 2, 1);
     code = (double)((d & 1 ? b >> 4 : b & 15) - 8);
   } else {
     int8_t c;
@@ -275,7 +288,9 @@ void orc_append(int batch, int kv_heads, int head_dim, int block_size, int dtype
               uint8_t q[32], packed[16];
               orc_q4_quantize_group(x, q, &d);
               for (int i = 0; i < 16; ++i) packed[i] = (uint8_t)(q[2 * i] | (q[2 * i + 1] << 4));
-              memcpy(tile + (size_t)row * rb + grp * 16, packed, 16);
+              for (int w = 0; w < 4; ++w)  /* the group's four words */
+                memcpy(tile + orc_q4_word_offset(is_v, row, 4 * grp + w, head_dim),
+                       packed + 4 * w, 4);
             } else {
               int8_t codes[32];
               orc_q8_quantize_group(x, codes, &d);

@@ -107,15 +107,34 @@ def q_format(tile_bytes, block_size=BLOCK):
     return D // 2, D
 
 
+def q4_code_index(rows, is_v, head_dim):
+    """Tile byte offsets of each row's q4_0 code bytes in element order
+    ([n][head_dim/2]): word w (4 bytes, elements 8w .. 8w+7) of row r lies at
+    r*CB + 4*((w % 4)*G + w // 4) in the K region and at
+    (r - r % G)*CB + 4*(w*G + r % G) in the V region (G = head_dim/32,
+    CB = head_dim/2), as orc_append writes them."""
+    G, CB = head_dim // 32, head_dim // 2
+    r = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.arange(CB)[None, :]
+    w, b = j // 4, j % 4
+    if is_v:
+        return (r - r % G) * CB + 4 * (w * G + r % G) + b
+    return r * CB + 4 * ((w % 4) * G + w // 4) + b
+
+
 def q8_row_bytes(pool, blocks, rows, is_v, block_size=BLOCK):
     """Bytes of quantised rows (q8_0 or q4_0) as [n][Hkv][code bytes + 2 * D/32 scale
-    bytes], scales in group order. A tile is block_size rows of codes, then fp16
-    scales ordered [row][group] (K region) or [group][row] (V region)."""
+    bytes]: codes in element order, scales in group order. A tile is block_size rows
+    of codes (q4_0 words placed as q4_code_index says), then fp16 scales ordered
+    [row][group] (K region) or [group][row] (V region)."""
     cb, D = q_format(pool.shape[2], block_size)
     ng = D // 32
     rows = np.asarray(rows, dtype=np.int64)
     blocks = np.asarray(blocks, dtype=np.int64)
-    code_idx = rows[:, None] * cb + np.arange(cb)[None, :]
+    if cb == D:
+        code_idx = rows[:, None] * cb + np.arange(cb)[None, :]
+    else:
+        code_idx = q4_code_index(rows, is_v, D)
     grp = np.arange(ng)[None, :]
     si = grp * block_size + rows[:, None] if is_v else rows[:, None] * ng + grp
     sb = block_size * cb + 2 * si

@@ -450,6 +450,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
   // slower than two on MI355X for both bf16 and q8_0 tiles.
   constexpr int NBUF = 2;
   static_assert(RB % 32 == 0 && CPR <= 64 && GP <= 16, "shape");
+  static_assert(!Q4 || (NV == NP && BS % NV == 0), "q4_0 tile layout");
 
   constexpr int NW = BINS ? 8 : 1;       // waves per workgroup
   __shared__ float p_lds_all[NW][2][16 * GP];  // softmax weights, [wave][parity][row][head]
@@ -558,24 +559,39 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       const char* ktile = kbase + (size_t)blk_of(t16) * blk_stride;
       const int kr = rib(t16);
       if constexpr (QN) {
-        // piece k / chunk vc: codes 32*k + 8*kg .. +8 / 8*vc .. +8 of a row,
-        // 8 bytes (q8_0) or 4 bytes (q4_0)
-        constexpr int PB = Q4 ? 4 : 8;
-        const char* kt = ktile + kr * CB + kg * PB;
-#pragma unroll
-        for (int k = 0; k < NP; ++k) {
-          if constexpr (Q4) t.k[k] = ld4(kt + k * 16);
-          else t.k[k] = ld8(kt + k * 32);
-        }
+        // piece k / chunk vc: codes 32*k + 8*kg .. +8 / 8*vc .. +8 of a row
         // the lane's NV consecutive V rows lie in one block
         const int r0 = NV * vr;
         const char* vtile = vbase + (size_t)blk_of(r0) * blk_stride;
         const int vrr = rib(r0);
-        const char* vt = vtile + vrr * CB + vc * PB;
+        if constexpr (Q4) {
+          // 4-byte words; the tile layout puts the lane's NP K words (one
+          // quarter of row kr) and its NV V words (word vc of rows vrr ..
+          // vrr+NV-1, NV = NP = groups per row) each in one contiguous run
+          const char* kt = ktile + kr * CB + kg * NP * 4;
+          const char* vt = vtile + vrr * CB + vc * NV * 4;
+          if constexpr (NP == 4) {
+            const u32x4 a = ld16(kt), b = ld16(vt);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-          if constexpr (Q4) t.v[i] = ld4(vt + i * CB);
-          else t.v[i] = ld8(vt + i * CB);
+            for (int i = 0; i < 4; ++i) {
+              t.k[i] = a[i];
+              t.v[i] = b[i];
+            }
+          } else {
+            const u32x2 a = ld8(kt), b = ld8(vt);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              t.k[i] = a[i];
+              t.v[i] = b[i];
+            }
+          }
+        } else {
+          const char* kt = ktile + kr * CB + kg * 8;
+#pragma unroll
+          for (int k = 0; k < NP; ++k) t.k[k] = ld8(kt + k * 32);
+          const char* vt = vtile + vrr * CB + vc * 8;
+#pragma unroll
+          for (int i = 0; i < NV; ++i) t.v[i] = ld8(vt + i * CB);
         }
         // scales after the BS rows of codes: K [row][group], V [group][row]
         const char* ksp = ktile + BS * CB + kr * NP * 2;
@@ -839,16 +855,17 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
           for (int i = 0; i < NV / 2; ++i) tn.vs[i] = 0u;
           tn.vs[0] = q4_scale_bits(mv, d);
           if (vr == 0) {
-            *reinterpret_cast<unsigned*>(vtile + t_new * CB + vc * 4) = c;
+            *reinterpret_cast<unsigned*>(vtile + (t_new - t_new % NV) * CB +
+                                         (vc * NV + t_new % NV) * 4) = c;
             if ((vc & 3) == 0)
               *reinterpret_cast<unsigned short*>(vtile + BS * CB + ((vc >> 2) * BS + t_new) * 2) =
                   (unsigned short)tn.vs[0];
           }
         }
         if (t16 == 0) {
-#pragma unroll
-          for (int k = 0; k < NP; ++k)
-            *reinterpret_cast<unsigned*>(ktile + t_new * CB + kg * 4 + k * 16) = tn.k[k];
+          char* kw = ktile + t_new * CB + kg * NP * 4;  // the lane's NP words, contiguous
+          if constexpr (NP == 4) *reinterpret_cast<u32x4*>(kw) = u32x4{tn.k[0], tn.k[1], tn.k[2], tn.k[3]};
+          else *reinterpret_cast<u32x2*>(kw) = u32x2{tn.k[0], tn.k[1]};
           if (kg == 0) {
             char* ksp = ktile + BS * CB + t_new * NP * 2;
             if constexpr (NP == 4) *reinterpret_cast<u32x2*>(ksp) = u32x2{tn.ks[0], tn.ks[1]};
@@ -1166,11 +1183,16 @@ __global__ __launch_bounds__(256) void append_q4_kernel(const char* k_new, const
     }
   }
   const float d = m / -8.f;
-  u32x4 w;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) w[c] = q4_codes(x[c], d);
   char* tile = (kv ? v_layer : k_layer) + ((size_t)blk * kv_heads + g) * TILE;
-  *reinterpret_cast<u32x4*>(tile + pos * CB + grp * 16) = w;
+  // word w = 4 * grp + c of the row (elements 8w .. 8w+7): K words transposed
+  // within the row, V rows interleaved NGR at a time
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int wd = 4 * grp + c;
+    const int off = kv ? (pos - pos % NGR) * CB + (wd * NGR + pos % NGR) * 4
+                       : pos * CB + (c * NGR + grp) * 4;
+    *reinterpret_cast<unsigned*>(tile + off) = q4_codes(x[c], d);
+  }
   const int si = kv ? grp * BS + pos : pos * NGR + grp;
   *reinterpret_cast<unsigned short*>(tile + BS * CB + si * 2) = (unsigned short)q4_scale_bits(m, d);
 }

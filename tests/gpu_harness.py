@@ -187,9 +187,10 @@ def _check_untouched(w, before, slots, pairs, layers):
 
 
 def _check_untouched_q8(w, before, slots, pairs, layers):
-    """Quantised caches: byte by byte, only each new row's codes and scales (K
-    scales [row][group], V scales [group][row] after a tile's codes) and whole
-    copy-on-write destination tiles may change."""
+    """Quantised caches: byte by byte, only each new row's codes (q4_0 V rows
+    interleaved as the layout places them) and scales (K scales [row][group], V
+    scales [group][row] after a tile's codes) and whole copy-on-write
+    destination tiles may change."""
     cfg = w.cfg
     D = W.code_row_bytes(cfg)  # code bytes per row
     ng = cfg.head_dim // 32
@@ -204,7 +205,13 @@ def _check_untouched_q8(w, before, slots, pairs, layers):
             continue
         bs = cfg.block_size
         b, r = int(sl) // bs, int(sl) % bs
-        allowed[:, :, b, :, r * D:(r + 1) * D] = True
+        allowed[0, :, b, :, r * D:(r + 1) * D] = True  # K codes: within the row's bytes
+        if cfg.dtype == W.Q4_0:  # V rows interleaved: the row's words as the layout places them
+            idx = torch.from_numpy(ostep.q4_code_index([r], True, cfg.head_dim)[0]).to(
+                allowed.device)
+            allowed[1, :, b, :, idx] = True
+        else:
+            allowed[1, :, b, :, r * D:(r + 1) * D] = True
         for grp in range(ng):
             ik = bs * D + 2 * (r * ng + grp)
             iv = bs * D + 2 * (grp * bs + r)

@@ -96,15 +96,44 @@ def test_q4_error_bound_random():
     assert np.all(codes[np.arange(len(x)), first] == 0)
 
 
+def _words(codes):
+    """Codes [..][D] (0..15) -> bytes [..][D/8 words][4] in element order (element j
+    of a word in byte j // 2, low nibble for even j)."""
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return packed.reshape(packed.shape[:-1] + (packed.shape[-1] // 4, 4))
+
+
 def _pack_q4(codes, scales, is_v):
-    """One tile [Hkv] of q4_0 bytes from codes [Hkv][16][D] (0..15) and fp16 scales
-    [Hkv][16][D/32]: element i of a row in byte i // 2 (low nibble for even i),
+    """One tile [Hkv] of q4_0 bytes from codes [Hkv][R][D] (0..15) and fp16 scales
+    [Hkv][R][D/32], in the pool's q4_0 layout (G = D/32 groups, words of 8
+    elements, word w = 4k + q = group k, quarter q):
+      K: each row's words reordered [q][k] (the G words of one quarter together);
+      V: rows taken G at a time, words reordered [w][row of the G];
     then scales [row][group] (K) or [group][row] (V)."""
     H, R, D = codes.shape
-    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    G = D // 32
+    wd = _words(codes)                                    # [H][R][4G][4]
+    if is_v:
+        body = wd.reshape(H, R // G, G, 4 * G, 4).transpose(0, 1, 3, 2, 4)
+    else:
+        body = wd.reshape(H, R, G, 4, 4).transpose(0, 1, 3, 2, 4)
     sc = scales if not is_v else scales.transpose(0, 2, 1)
-    return np.concatenate([packed.reshape(H, R * D // 2),
+    return np.concatenate([np.ascontiguousarray(body).reshape(H, R * D // 2),
                            np.ascontiguousarray(sc).view(np.uint8).reshape(H, -1)], axis=1)
+
+
+def _unpack_q4_codes(tile, R, D, is_v):
+    """Inverse of _pack_q4's code part for one head: codes [R][D]."""
+    G = D // 32
+    body = tile[:R * D // 2]
+    if is_v:
+        wd = body.reshape(R // G, 4 * G, G, 4).transpose(0, 2, 1, 3).reshape(R, 4 * G * 4)
+    else:
+        wd = body.reshape(R, 4, G, 4).transpose(0, 2, 1, 3).reshape(R, 4 * G * 4)
+    out = np.empty((R, D), dtype=np.uint8)
+    out[:, 0::2] = wd & 15
+    out[:, 1::2] = wd >> 4
+    return out
 
 
 @pytest.mark.parametrize("D,Hq,Hkv", [(128, 8, 2), (64, 4, 4)])
@@ -159,5 +188,8 @@ def test_q4_append_writes_quantised_row_in_layout():
                                    d.reshape(Hkv, D // 32).view(np.uint8)], axis=1)
             got = ostep.q8_row_bytes(pool, [blk], [row], bool(is_v))[0]
             assert np.array_equal(got, want)
+            for h in range(Hkv):  # the same codes read back through this file's layout
+                unpacked = _unpack_q4_codes(pool[blk, h], 16, D, bool(is_v))[row]
+                assert np.array_equal(unpacked, c[h])
     changed = (kp != k0).sum() + (vp != v0).sum()
     assert changed <= 2 * 2 * Hkv * (D // 2 + 8)
