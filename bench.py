@@ -317,7 +317,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(cfg.name),
-            "kernel": "decode_kernel (fused append + paged attention + split merge), one launch per layer",
+            "kernel": "per-layer call: decode_kernel (fused append + paged attention) and, for "
+                      "split segments, reduce_kernel; timed together",
             "avg_launch_us": round(per_launch_s * 1e6, 3),
             "algorithmic_bytes_per_launch": alg,
         },
