@@ -13,8 +13,12 @@ from HBM). Every step grows each sequence by one token, as decode does.
 
 Prints one JSON line. `value` = KV bytes read by all layers of all timed
 steps / wall time between synchronisations (GB/s). The `roofline` object is
-for the decode kernel alone, timed with HIP events around back-to-back
-decode launches on the launch stream.
+for the per-layer decode call (decode_kernel with the append fused, and
+reduce_kernel when segments are split), timed with HIP events on the launch
+stream around repeats of back-to-back calls that rotate over the layers
+(mean, and p10 / p50 / p90 of the repeats). The unfused kv_append and the
+copy-on-write copies are also timed alone; `cpu_baseline` is the fp64 oracle
+on the host cores (and on one core) for a bounded sample of the same layer.
 """
 from __future__ import annotations
 
@@ -135,11 +139,29 @@ def cpu_baseline(w, budget_s: float = 12.0):
         total += dt
         reps += 1
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(kv_bytes(cfg, ctx) * reps / total / 1e9, 4), "unit": "GB/s",
-            "cores": cores, "kind": "oracle",
-            "sample": f"one layer of all {w.B} sequences ({int(ctx.sum())} context tokens) "
-                      f"decoded {reps} times, {total:.1f} s of oracle time",
-            "seq_tokens_per_s": round(float(ctx.sum()) * reps / total, 1)}
+    res = {"value": round(kv_bytes(cfg, ctx) * reps / total / 1e9, 4), "unit": "GB/s",
+           "cores": cores, "kind": "oracle",
+           "sample": f"one layer of all {w.B} sequences ({int(ctx.sum())} context tokens) "
+                     f"decoded {reps} times, {total:.1f} s of oracle time",
+           "seq_tokens_per_s": round(float(ctx.sum()) * reps / total, 1)}
+    # the same oracle on one core, on the first 8 sequences of that layer
+    oracle.set_threads(1)
+    try:
+        few = seqs[:8]
+        t1, ctx1 = run(few)
+        reps1, total1 = 1, t1
+        while total1 < budget_s / 4 and reps1 < 10000:
+            dt, _ = run(few)
+            total1 += dt
+            reps1 += 1
+    finally:
+        oracle.set_threads(cores)
+    res["single_core"] = {
+        "value": round(kv_bytes(cfg, ctx1) * reps1 / total1 / 1e9, 4), "unit": "GB/s",
+        "cores": 1,
+        "sample": f"one layer of {len(few)} sequences ({int(ctx1.sum())} context tokens) "
+                  f"decoded {reps1} times, {total1:.1f} s"}
+    return res
 
 
 def log(msg: str):
@@ -154,7 +176,8 @@ def main():
     ap.add_argument("--config", default="llama8b_bf16")
     ap.add_argument("--partition", type=int, default=None,
                     help="decode partition tokens (default: the workload's own; 0 = balanced)")
-    ap.add_argument("--decode-reps", type=int, default=3)
+    ap.add_argument("--decode-reps", type=int, default=50,
+                    help="timed repeats of the back-to-back per-layer launches (roofline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (3 times) and "
@@ -236,8 +259,13 @@ def main():
     stream = torch.cuda.current_stream()
     layers = list(range(cfg.layers))
 
+    cow_pairs = None  # the first copy-on-write pairs a step made (timed alone at the end)
+
     def one_step():
+        nonlocal cow_pairs
         sess.step(out, layers=layers, partition_tokens=part, fused=not args.unfused)
+        if cow_pairs is None and len(sess.pairs):
+            cow_pairs = sess.pairs.copy()
 
     total_kv = 0
     for _ in range(args.warmup):
@@ -273,16 +301,34 @@ def main():
     for layer in layers[:4]:
         layer_call(layer)
     torch.cuda.synchronize()
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    d0.record(stream)
-    for _ in range(reps):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    evs[0].record(stream)
+    for r in range(reps):
         for layer in layers:  # re-appending the same rows is idempotent
             layer_call(layer)
-    d1.record(stream)
+        evs[r + 1].record(stream)
     torch.cuda.synchronize()
-    per_launch_s = d0.elapsed_time(d1) / 1e3 / (reps * len(layers))
+    per_rep = np.array([evs[r].elapsed_time(evs[r + 1]) / 1e3 / len(layers)
+                        for r in range(reps)])
+    per_launch_s = float(per_rep.mean())
+    p10, p50, p90 = (float(x) for x in np.percentile(per_rep, [10, 50, 90]))
     alg = decode_algorithmic_bytes(cfg, ctx_now)
     achieved = alg / per_launch_s / 1e9
+
+    log("kv_append alone")
+    # the unfused append (kv_append through the uploaded slots), one launch per layer
+    a_reps = 20
+    for layer in layers[:4]:
+        sess.append(layer)
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for _ in range(a_reps):
+        for layer in layers:
+            sess.append(layer)
+    a1.record(stream)
+    torch.cuda.synchronize()
+    append_s = a0.elapsed_time(a1) / 1e3 / (a_reps * len(layers))
 
     res = {
         "metric": "paged decode KV-read GB/s (% of HBM peak) + seq-tokens/s, 8B-shaped layer",
@@ -320,8 +366,12 @@ def main():
             "kernel": "per-layer call: decode_kernel (fused append + paged attention) and, for "
                       "split segments, reduce_kernel; timed together",
             "avg_launch_us": round(per_launch_s * 1e6, 3),
+            "launch_us_p10_p50_p90": [round(p10 * 1e6, 3), round(p50 * 1e6, 3),
+                                      round(p90 * 1e6, 3)],
+            "timed_launches": reps * len(layers),
             "algorithmic_bytes_per_launch": alg,
         },
+        "kv_append_alone_us_per_layer": round(append_s * 1e6, 3),
     }
     if w.shared:  # shared blocks are read by every sharer but fetched from HBM once
         shared_rows = cfg.prefix_tokens * (cfg.batch - 1)
@@ -331,6 +381,24 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline")
         res["cpu_baseline"] = cpu_baseline(w)
+        res["gpu_over_cpu"] = round(res["value"] / res["cpu_baseline"]["value"], 1)
+    if cow_pairs is not None:
+        # copy-on-write copies alone, with the pairs of the step that made them; run last,
+        # since copying them again overwrites rows appended since (timing only)
+        log("copy_blocks alone")
+        from paged_kv_cache_09_amd import pkv
+        c_reps = 20
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(c_reps):
+            pkv.copy_blocks(sess.pool, cow_pairs, sess.stream)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_s = c0.elapsed_time(c1) / 1e3 / c_reps
+        copy_bytes = 2 * len(cow_pairs) * cfg.layers * 2 * W.tile_bytes(cfg) * cfg.kv_heads
+        res["copy_blocks_alone"] = {"pairs": int(len(cow_pairs)), "us": round(copy_s * 1e6, 3),
+                                    "GBps": round(copy_bytes / copy_s / 1e9, 2)}
     sess.close()
     print(json.dumps(res), flush=True)
 

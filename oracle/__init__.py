@@ -79,6 +79,8 @@ def lib():
         P = ctypes.c_void_p
         i32 = ctypes.c_int
         i64 = ctypes.c_int64
+        L.orc_set_threads.restype = None
+        L.orc_set_threads.argtypes = [i32]
         L.orc_kv_bytes_per_token.restype = i64
         L.orc_kv_bytes_per_token.argtypes = [i64, i64, i64, i64]
         L.orc_elem_to_double.restype = ctypes.c_double
@@ -113,6 +115,11 @@ def _storage(a: np.ndarray, dtype: int) -> np.ndarray:
     if a.dtype != want:
         raise TypeError(f"expected storage dtype {np.dtype(want)} for code {dtype}, got {a.dtype}")
     return np.ascontiguousarray(a)
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops (for timing; results do not depend on it)."""
+    lib().orc_set_threads(int(n))
 
 
 def kv_bytes_per_token(layers: int, kv_heads: int, head_dim: int, bytes_per_elem: int) -> int:

@@ -41,6 +41,7 @@
  * gather to a contiguous array, then softmax(q.K^T * scale) . V.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -240,6 +241,10 @@ static double orc_qload(const char* tile, int dtype, int is_v, int row, int d, i
 
 /* ssdnodes.com, "KV cache vs prompt cache", "How much memory does the KV cache
  * use?": bytes per token = 2 * layers * kv_heads * head_dim * bytes/element. */
+/* Thread count of the OpenMP loops below (timing runs only; results do not
+ * depend on it). */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+
 int64_t orc_kv_bytes_per_token(int64_t layers, int64_t kv_heads, int64_t head_dim,
                                int64_t bytes_per_elem) {
   return 2 * layers * kv_heads * head_dim * bytes_per_elem;
