@@ -195,8 +195,9 @@ def main():
                          "prompt chunk of TOKENS tokens per sequence (prefill side)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
-              "multi-GPU path; see DESIGN.md for how the decode path would shard.",
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the decode path has "
+              "no multi-GPU form here (it would shard by sequence or by kv-head group, with no "
+              "exchange; a sequence split across GPUs would exchange only its split partials).",
               file=sys.stderr)
         sys.exit(2)
 
