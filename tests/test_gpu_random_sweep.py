@@ -1,0 +1,57 @@
+"""GPU parity over a seeded sweep of small random configurations.
+
+Each case draws its own shape — cache dtype, head_dim, kv heads and GQA group,
+block size, batch, length mix (uniform lengths, or a shared prompt with short
+private suffixes, which brings copy-on-write) and value scale — then runs one
+full step (slot assignment, upload, copy-on-write, append, decode at several
+split sizes) through the C ABI against the fp64 oracle, unfused and fused on
+alternate seeds. The cases are small enough to compare every sequence.
+"""
+import numpy as np
+import pytest
+
+from paged_kv_cache_09_amd import workloads as W
+from tests.gpu_harness import run_step_case, tolerance
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = (W.F32, W.F16, W.BF16, W.Q8_0, W.Q4_0)
+
+
+def random_config(seed: int) -> W.Config:
+    rng = np.random.default_rng(7000 + seed)
+    dtype = DTYPES[seed % len(DTYPES)]
+    D = int(rng.choice([64, 128]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 3, 4, 8]))
+    bs = int(rng.choice([8, 16, 32]))
+    B = int(rng.integers(1, 9))
+    sigma = float(rng.choice([0.5, 1.0, 2.0]))
+    common = dict(seed=100 + seed, batch=B, q_heads=G * Hkv, kv_heads=Hkv, head_dim=D,
+                  dtype=dtype, sigma=sigma, layers=1, block_size=bs)
+    if seed % 4 == 3:
+        prefix = int(rng.integers(1, 300))
+        suffix_hi = int(rng.integers(0, 60))
+        nb = (prefix + bs - 1) // bs + B * ((suffix_hi + 1) // bs + 3) + 4
+        return W.Config(f"sweep{seed}", num_blocks=nb, ctx_kind="shared_prefix",
+                        prefix_tokens=prefix, suffix_hi=suffix_hi, **common)
+    lo = int(rng.integers(1, 40))
+    hi = int(rng.integers(lo, 700))
+    nb = B * ((hi + bs - 1) // bs + 2) + 4
+    return W.Config(f"sweep{seed}", num_blocks=nb, ctx_kind="uniform", ctx_lo=lo, ctx_hi=hi,
+                    **common)
+
+
+SEEDS = list(range(30))
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_config_step_parity(seed):
+    cfg = random_config(seed)
+    label = (f"sweep {seed}: {W.DTYPE_NAME[cfg.dtype]} D{cfg.head_dim} "
+             f"{cfg.q_heads}/{cfg.kv_heads} bs{cfg.block_size} B{cfg.batch} {cfg.ctx_kind}")
+    errs, _, _ = run_step_case(cfg, layers=1, partitions=(0, 32, 1 << 20), label=label,
+                               fused=seed % 2 == 1)
+    tol = tolerance(cfg)
+    for key, e in errs.items():
+        assert e <= tol, f"{label} {key}: max abs error {e} > {tol}"
