@@ -39,9 +39,15 @@ TRAFFIC = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 
 def kernel_source_hash() -> str:
+    """SHA-256 of the kernel source's code: comments removed and whitespace
+    collapsed, so that counters stay attached to unchanged code."""
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    import re
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return hashlib.sha256(" ".join(src.split()).encode()).hexdigest()
 
 
 def measured_traffic(config: str):

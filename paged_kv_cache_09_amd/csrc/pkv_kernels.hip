@@ -2,7 +2,7 @@
 //
 //  decode_kernel  — per wavefront: a contiguous run of (kv head, sequence,
 //                   block) tiles; gathers 16 x head_dim K and V tiles through
-//                   the block table with 128-bit loads, computes q.K^T for all
+//                   the block table with wide per-lane loads, computes q.K^T for all
 //                   query heads of the GQA group sharing the kv head, keeps an
 //                   fp32 online softmax and accumulates P.V. A run that covers a
 //                   whole (kv head, sequence) writes the normalised output;
@@ -29,8 +29,9 @@
 // heads share one stored K/V head (ssdnodes.com, "KV cache vs prompt cache",
 // GQA paragraph). Decode is bound by memory bandwidth (ssdnodes.com, same
 // page, "What the KV cache holds"), so every tile is read exactly once, with
-// full 16-byte lanes; q.K^T of the GQA group runs on 16x16 MFMA tiles, the
-// softmax and P.V on the fp32 VALU.
+// wide lanes (16 bytes for 2- and 4-byte elements and q4_0, 8 for q8_0 codes);
+// q.K^T of the GQA group runs on 16x16 MFMA tiles, the softmax and P.V on the
+// fp32 VALU.
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -389,10 +390,10 @@ __device__ __forceinline__ f32x4 qk_piece(u32x4 q, u32x4 k, f32x4 acc) {
 //   fp32 / fp16 / bf16: NP 16-byte K pieces (lane (t16, kg) holds bytes
 //   kg*16 + 64*k of row t16) and NV 16-byte V chunks (chunk vc of rows
 //   vr + RPI*i).
-//   q8_0 / q4_0: NP 8-byte / 4-byte K pieces (codes 32*k + 8*kg .. +8 of row t16, one piece
-//   per 32-code scale group) with that row's NP fp16 scales, and NV 8-byte V
-//   chunks (codes 8*vc .. +8 of rows NV*vr + i) with those rows' scales of
-//   group vc/4.
+//   q8_0 / q4_0: NP 8-byte / 4-byte K pieces (codes 32*k + 8*kg .. +8 of row
+//   t16, one piece per 32-code scale group) with that row's NP fp16 scales,
+//   and NV 8-byte / 4-byte V chunks (codes 8*vc .. +8 of rows NV*vr + i) with
+//   those rows' scales of group vc/4.
 template <int DT, int D>
 struct TileRegs {
   static constexpr int RB = D * Elem<DT>::bytes;
@@ -446,8 +447,8 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
   // bytes of one (block, kv head) tile of the pool: BS rows (+ scales when quantised)
   constexpr int TILE = QN ? BS * CB + BS * (D / 32) * 2 : BS * RB;
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
-  // Tile buffers per wave. Three or four (more bytes in flight per wave) ran
-  // slower than two on MI355X for both bf16 and q8_0 tiles.
+  // Tile buffers per wave. One, three or four ran slower than two on MI355X
+  // for bf16, q8_0 and q4_0 tiles.
   constexpr int NBUF = 2;
   static_assert(RB % 32 == 0 && CPR <= 64 && GP <= 16, "shape");
   static_assert(!Q4 || (NV == NP && BS % NV == 0), "q4_0 tile layout");
