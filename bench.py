@@ -93,7 +93,7 @@ def unique_kv_bytes(cfg, table, ctx) -> int:
 def decode_algorithmic_bytes(cfg, ctx) -> int:
     """Bytes one fused append + decode launch must move: every KV row once (the new
     row comes from k_new/v_new), the new rows written to the pool, q, the fp32
-    output, the block-table entries and the lengths."""
+    output, the block-table entries once, the lengths and the slots."""
     import numpy as np
     from paged_kv_cache_09_amd import workloads as W
     e_in = W.TORCH_DTYPE[cfg.dtype].itemsize  # q, k_new, v_new (bf16 for q8_0)
@@ -104,7 +104,7 @@ def decode_algorithmic_bytes(cfg, ctx) -> int:
     # from k_new / v_new (input dtype) rather than the pool, and written to it
     new_rows = B * 2 * cfg.kv_heads * cfg.head_dim * e_in
     return (kv_bytes(cfg, ctx) + new_rows + B * cfg.q_heads * cfg.head_dim * e_in +
-            B * cfg.q_heads * cfg.head_dim * 4 + nblk * 4 * cfg.kv_heads + B * 4)
+            B * cfg.q_heads * cfg.head_dim * 4 + nblk * 4 + B * 4 + B * 8)
 
 
 def cpu_baseline(w, budget_s: float = 12.0):
