@@ -18,9 +18,13 @@ BUILD = os.path.join(HERE, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-# Packed fp32 instructions are kept out of generated code on purpose.
+# Packed fp32 instructions are kept out of generated code on purpose. MFMA
+# results live in ordinary VGPRs (not AGPRs): the decode kernels feed them to
+# VALU work every tile, and the AGPR form added a copy each way and, for
+# q4_0, a register count that halved occupancy.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-Wall"]
 SOURCES = ["pkv_host.cpp", "pkv_kernels.hip"]
 EXTRA = os.environ.get("PKV_EXTRA_FLAGS", "").split()

@@ -97,15 +97,28 @@ __device__ __forceinline__ u32x4 codes_to_bf16(u32x2 c) {
 
 // 8 packed 4-bit codes (code j in bits 4j .. 4j+3) -> the 8 values 128 + code
 // as bf16 (exact: bf16 0x4300 is 128 and its low mantissa bits count units), an
-// MFMA operand. The 136 that separates 128 + code from code - 8 is taken off
-// through the MFMA's accumulator input.
+// MFMA operand, in the slot order codes 0 2 4 6 1 3 5 7 (each pair from one
+// word, its exponent bytes from a constant: one permute per pair); the q
+// operand is put in the same order (q_slots_0246). The 136 that separates
+// 128 + code from code - 8 is taken off through the MFMA's accumulator input.
 __device__ __forceinline__ u32x4 nibbles_to_bf16_128(unsigned w) {
   const unsigned lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;  // even, odd codes
+  constexpr unsigned kExp = 0x43434343u;
   u32x4 r;
-#pragma unroll
-  for (int b = 0; b < 4; ++b)  // bytes (lo.b, 0, hi.b, 0), then the bf16 exponent bytes
-    r[b] = __builtin_amdgcn_perm(hi, lo, 0x0c000c00u | ((4u + b) << 16) | (unsigned)b) |
-           0x43004300u;
+  r[0] = __builtin_amdgcn_perm(kExp, lo, 0x04010400u);  // (lo.b0, 0x43, lo.b1, 0x43)
+  r[1] = __builtin_amdgcn_perm(kExp, lo, 0x04030402u);
+  r[2] = __builtin_amdgcn_perm(kExp, hi, 0x04010400u);
+  r[3] = __builtin_amdgcn_perm(kExp, hi, 0x04030402u);
+  return r;
+}
+
+// 8 bf16 values in natural order -> slot order 0 2 4 6 1 3 5 7.
+__device__ __forceinline__ u32x4 q_slots_0246(u32x4 q) {
+  u32x4 r;
+  r[0] = __builtin_amdgcn_perm(q[1], q[0], 0x05040100u);  // elements 0, 2
+  r[1] = __builtin_amdgcn_perm(q[3], q[2], 0x05040100u);  // 4, 6
+  r[2] = __builtin_amdgcn_perm(q[1], q[0], 0x07060302u);  // 1, 3
+  r[3] = __builtin_amdgcn_perm(q[3], q[2], 0x07060302u);  // 5, 7
   return r;
 }
 
@@ -452,6 +465,9 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
   constexpr int NBUF = 2;
   static_assert(RB % 32 == 0 && CPR <= 64 && GP <= 16, "shape");
   static_assert(!Q4 || (NV == NP && BS % NV == 0), "q4_0 tile layout");
+  // q4_0 at head_dim 128 with up to 4 heads per group: P.V on MFMA (compute_tile).
+  constexpr bool MPV = Q4 && D == 128 && GP <= 4;
+  static_assert(!MPV || (CPR == 16 && NV == 4 && EPC == 8), "MFMA P.V lane layout");
 
   constexpr int NW = BINS ? 8 : 1;       // waves per workgroup
   __shared__ float p_lds_all[NW][2][16 * GP];  // softmax weights, [wave][parity][row][head]
@@ -638,7 +654,8 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
                        ((size_t)s * p.q_heads + (size_t)g * p.group + hq) * QB + kg * 16;
 #pragma unroll
       for (int k = 0; k < NP; ++k) {
-        const u32x4 v = ld16(qr + k * 64);
+        u32x4 v = ld16(qr + k * 64);
+        if constexpr (Q4) v = q_slots_0246(v);  // the K operand's slot order
         qv[k] = t16 < p.group ? v : u32x4{0u, 0u, 0u, 0u};
       }
     }
@@ -660,6 +677,12 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     float m[HPG], lsum[HPG];
     float acc[GP][EPC];
     float bsum[GP];  // q4_0: sum of the lane's scaled weights per head (8 x it is taken off)
+    // MFMA P.V: block nt of output columns (head-dim columns 8 * n + nt), rows
+    // 4 * (lane / 16) + i as the MFMA lays them out
+    f32x4 accm[MPV ? 8 : 1];
+#pragma unroll
+    for (int nt = 0; nt < (MPV ? 8 : 1); ++nt) accm[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 accs = {0.f, 0.f, 0.f, 0.f};  // MFMA P.V: per row, the sum of its A values
 #pragma unroll
     for (int i = 0; i < HPG; ++i) {
       m[i] = -__builtin_inff();
@@ -693,10 +716,21 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       // sacc[i] = q(head 4*kg + i) . K(token t16)
       float s2[HPG];
       bool over = false;
+      // MFMA P.V takes weight x scale as fp16: weights stay <= 2^kLazy, and a
+      // tile with a V scale above 2^8 - 1 raises the maxima on any increase
+      // (weights <= 1), so the products stay finite.
+      float lz = kLazy;
+      if constexpr (MPV) {
+        // fp16 magnitude bits above 255 (0x5bf8), NaN included (rows past the
+        // context may hold anything: that only costs a rescale)
+        const unsigned a0 = t.vs[0] & 0x7fff7fffu, a1 = t.vs[1] & 0x7fff7fffu;
+        const unsigned mx = max(max(a0 & 0xffffu, a0 >> 16), max(a1 & 0xffffu, a1 >> 16));
+        if (__any(mx > 0x5bf8u)) lz = 0.f;
+      }
 #pragma unroll
       for (int i = 0; i < HPG; ++i) {
         s2[i] = t16 < valid ? sacc[i] * p.scale_log2 : -__builtin_inff();
-        over |= head_lane && s2[i] > m[i] + kLazy;
+        over |= head_lane && s2[i] > m[i] + lz;
       }
       if (__any(over)) {  // raise the running maxima to this tile's
         float alpha[HPG];
@@ -712,12 +746,22 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
           for (int i = 0; i < HPG; ++i) a_lds[4 * kg + i] = alpha[i];
         }
         wave_sync();
+        if constexpr (MPV) {
 #pragma unroll
-        for (int h = 0; h < GP; ++h) {
-          const float a = a_lds[h];
-          bsum[h] *= a;
+          for (int i = 0; i < 4; ++i) {
+            const float a = i < GP ? a_lds[i < GP ? i : 0] : 1.f;
+            accs[i] *= a;
 #pragma unroll
-          for (int e = 0; e < EPC; ++e) acc[h][e] *= a;
+            for (int nt = 0; nt < 8; ++nt) accm[nt][i] *= a;
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < GP; ++h) {
+            const float a = a_lds[h];
+            bsum[h] *= a;
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) acc[h][e] *= a;
+          }
         }
       }
       float* pl = p_lds[parity];
@@ -729,6 +773,55 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         if (head_lane) pl[t16 * GP + 4 * kg + i] = pw;
       }
       wave_sync();
+      if constexpr (MPV) {
+        // P.V as one MFMA 16x16x32 per block of 16 output columns. A: row
+        // 4 * G + h holds head h's weights times each token's scale for group
+        // G (the spare rows of a group of <= 4 heads carry the four scale
+        // groups) as a high and a low fp16 part (~22 bits): the lane's 8 k
+        // slots are the high parts of its 4 tokens, then the low parts, and B
+        // repeats the 4 tokens' codes. B: column n of block nt is head-dim
+        // column 8 * n + nt, its code's byte taken as the fp16 bits: the
+        // subnormal code x 2^-24 (odd nt: code x 2^-20), exact, and kept by
+        // the MFMA. One more MFMA against ones sums each row's A values, so
+        // the 8 of code - 8 comes off at the end from the same fp16 parts.
+        // Row 4 * G + h of block nt is head h's output for the columns of
+        // group G, used by the lanes whose columns 8 * (lane % 16) + nt lie in
+        // group lane / 16.
+        const int hh = lane & 3;
+        float pa[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tr = 4 * vr + i;
+          float dv = (i & 1) ? half_hi(t.vs[i >> 1]) : half_lo(t.vs[i >> 1]);
+          if (tr >= valid) dv = 0.f;  // rows past the context may hold anything (NaN scales)
+          const float pw = pl[tr * GP + (hh < GP ? hh : 0)];
+          pa[i] = hh < GP ? pw * dv : 0.f;
+        }
+        const f16x2 h01 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(pa[0], pa[1]));
+        const f16x2 h23 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(pa[2], pa[3]));
+        const f16x8 av = {h01[0], h01[1], h23[0], h23[1],
+                          (_Float16)(pa[0] - (float)h01[0]), (_Float16)(pa[1] - (float)h01[1]),
+                          (_Float16)(pa[2] - (float)h23[0]), (_Float16)(pa[3] - (float)h23[1])};
+        unsigned ev[4], od[4];  // even codes (low nibbles), odd codes x 16 (high nibbles)
+        accs = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            av, __builtin_bit_cast(f16x8, u32x4{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u}),
+            accs, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ev[i] = t.v[i] & 0x0f0f0f0fu;
+          od[i] = t.v[i] & 0xf0f0f0f0u;
+        }
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          const unsigned* src = (nt & 1) ? od : ev;
+          // byte nt / 2 of rows 0, 1 (and 2, 3) into the low bytes of the two fp16 halves
+          const unsigned sel = 0x0c000c00u | ((4u + (nt >> 1)) << 16) | (unsigned)(nt >> 1);
+          const unsigned b01 = __builtin_amdgcn_perm(src[1], src[0], sel);
+          const unsigned b23 = __builtin_amdgcn_perm(src[3], src[2], sel);
+          const f16x8 bv = __builtin_bit_cast(f16x8, u32x4{b01, b23, b01, b23});
+          accm[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, accm[nt], 0, 0, 0);
+        }
+      } else
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int tr = vrow(i);
@@ -943,18 +1036,31 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     float lt[HPG];
 #pragma unroll
     for (int i = 0; i < HPG; ++i) lt[i] = row_sum(lsum[i]);
-    if constexpr (Q4) {  // sum_t w_t (code_t - 8) = sum_t w_t code_t - 8 sum_t w_t
+    if constexpr (MPV) {
+      // the MFMA summed over the tile's rows: sum A x code x 2^-24 (odd
+      // columns 2^-20), less 8 x sum A
 #pragma unroll
       for (int h = 0; h < GP; ++h)
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[h][e] = __builtin_fmaf(-8.f, bsum[h], acc[h][e]);
+        for (int e = 0; e < EPC; ++e)
+          acc[h][e] = __builtin_fmaf(accm[e][h], (e & 1) ? 1048576.f : 16777216.f, -8.f * accs[h]);
+    } else {
+      if constexpr (Q4) {  // sum_t w_t (code_t - 8) = sum_t w_t code_t - 8 sum_t w_t
+#pragma unroll
+        for (int h = 0; h < GP; ++h)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[h][e] = __builtin_fmaf(-8.f, bsum[h], acc[h][e]);
+      }
+#pragma unroll
+      for (int off = CPR; off < 64; off <<= 1)
+#pragma unroll
+        for (int h = 0; h < GP; ++h)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[h][e] += xor_f(acc[h][e], off);
     }
-#pragma unroll
-    for (int off = CPR; off < 64; off <<= 1)
-#pragma unroll
-      for (int h = 0; h < GP; ++h)
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[h][e] += xor_f(acc[h][e], off);
+    // lanes holding the output: columns pv_col .. pv_col + EPC - 1 of every head
+    const bool pv_lane = MPV ? (lane >> 4) == ((lane & 15) >> 2) : lane < CPR;
+    const int pv_col = (MPV ? (lane & 15) : lane) * EPC;
     if (head_lane && t16 == 0) {
 #pragma unroll
       for (int i = 0; i < HPG; ++i) {
@@ -965,8 +1071,8 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     wave_sync();
     const bool whole = j0 == 0 && j1 == nblk;
     if (whole) {
-      if (lane < CPR) {
-        float* o = p.out + ((size_t)s * p.q_heads + (size_t)g * p.group) * D + lane * EPC;
+      if (pv_lane) {
+        float* o = p.out + ((size_t)s * p.q_heads + (size_t)g * p.group) * D + pv_col;
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
           if (h < p.group) {
@@ -978,8 +1084,8 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       }
     } else if constexpr (BINS) {
       const int slot = first_seg ? 0 : 1;
-      float* po = piece_o + (size_t)((wl * 2 + slot) * GP) * D + lane * EPC;
-      if (lane < CPR) {
+      float* po = piece_o + (size_t)((wl * 2 + slot) * GP) * D + pv_col;
+      if (pv_lane) {
 #pragma unroll
         for (int h = 0; h < GP; ++h)
 #pragma unroll
@@ -991,8 +1097,8 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       }
     } else {
       const size_t idx = (size_t)seg + w;
-      if (lane < CPR) {
-        float* o = p.part_o + idx * GP * D + lane * EPC;
+      if (pv_lane) {
+        float* o = p.part_o + idx * GP * D + pv_col;
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
           if (h < p.group) {

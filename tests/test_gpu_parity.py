@@ -234,6 +234,35 @@ def test_q4_append_edge_rows(head_dim, fused):
         assert e <= tolerance(cfg), f"q4 edge rows {key}: max abs error {e}"
 
 
+def _scale_v_scales(factor_log2):
+    """Multiply the fp16 V scales of every even-numbered pool block by
+    2^factor_log2 (exact in fp16 while it does not overflow)."""
+    def edit(w):
+        cfg = w.cfg
+        tb = W.tile_bytes(cfg)
+        cb = W.code_row_bytes(cfg) * cfg.block_size
+        v = w.pool[W.region_bytes(cfg, w.layers):]
+        tiles = v.view(w.layers, cfg.num_blocks, cfg.kv_heads, tb)[:, 0::2]
+        sc = tiles[..., cb:].contiguous().view(torch.float16)
+        sc.mul_(2.0 ** factor_log2)
+        tiles[..., cb:] = sc.view(torch.uint8)
+    return edit
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["append+decode", "fused"])
+@pytest.mark.parametrize("group", [4, 2])
+def test_q4_large_v_scales(group, fused):
+    """V scales up to ~39,000 in half of the blocks (q4_0, head_dim 128): weight
+    x scale must stay finite wherever the decode forms it in fp16. The
+    tolerance is the quantised one scaled by the same 2^17."""
+    cfg = W.scaled(W.CONFIGS["llama8b_q4"], batch=6, q_heads=2 * group, kv_heads=2,
+                   num_blocks=6 * 40, ctx_lo=1, ctx_hi=600)
+    errs, _, _ = run_step_case(cfg, layers=1, partitions=(0, 32), label=f"q4 big scales g{group}",
+                               fused=fused, edit=_scale_v_scales(17))
+    for key, e in errs.items():
+        assert e <= tolerance(cfg) * 2.0 ** 17, f"q4 large V scales {key}: max abs error {e}"
+
+
 def _decode_form(cfg, device="cuda"):
     w = W.make(cfg, device=device, layers=1, form="decode", fill="nan")
     sess = DecodeSession(w, placement="post")
