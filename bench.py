@@ -34,20 +34,26 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
-KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_09_amd", "csrc", "pkv_kernels.hip")
+# the code HBM traffic depends on: the kernels and the host schedule that
+# decides between the split and the bins form
+KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_09_amd", "csrc", f)
+               for f in ("pkv_kernels.hip", "pkv_host.cpp")]
 TRAFFIC = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 
 def kernel_source_hash() -> str:
-    """SHA-256 of the kernel source's code: comments removed and whitespace
-    collapsed, so that counters stay attached to unchanged code."""
+    """SHA-256 of the kernel and schedule sources' code: comments removed and
+    whitespace collapsed, so that counters stay attached to unchanged code."""
     import hashlib
     import re
-    with open(KERNEL_SRC, encoding="utf-8") as f:
-        src = f.read()
-    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
-    src = re.sub(r"//[^\n]*", " ", src)
-    return hashlib.sha256(" ".join(src.split()).encode()).hexdigest()
+    parts = []
+    for path in KERNEL_SRCS:
+        with open(path, encoding="utf-8") as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        parts.append(" ".join(src.split()))
+    return hashlib.sha256("\n".join(parts).encode()).hexdigest()
 
 
 def measured_traffic(config: str):

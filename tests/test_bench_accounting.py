@@ -55,7 +55,7 @@ def test_unique_bytes_count_a_shared_block_once():
 def test_kernel_code_hash_ignores_comments_only(tmp_path, monkeypatch):
     src = tmp_path / "k.hip"
     src.write_text("// a\nint f(int x) { return x + 1; } /* b */\n")
-    monkeypatch.setattr(bench, "KERNEL_SRC", str(src))
+    monkeypatch.setattr(bench, "KERNEL_SRCS", [str(src)])
     h0 = bench.kernel_source_hash()
     src.write_text("// changed words\nint f(int x)  {\n  return x + 1;   }\n/* other\n words */")
     assert bench.kernel_source_hash() == h0
