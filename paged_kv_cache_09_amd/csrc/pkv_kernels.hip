@@ -373,6 +373,7 @@ __device__ __forceinline__ void wave_sync() {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // One 16-byte piece of the q.K^T contraction on the matrix cores:
@@ -470,7 +471,9 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
   static_assert(!MPV || (CPR == 16 && NV == 4 && EPC == 8), "MFMA P.V lane layout");
 
   constexpr int NW = BINS ? 8 : 1;       // waves per workgroup
-  __shared__ float p_lds_all[NW][2][16 * GP];  // softmax weights, [wave][parity][row][head]
+  // softmax weights, [wave][parity][row][head], then a spare slot the lanes
+  // without a head write to (a store every lane makes needs no branch)
+  __shared__ float p_lds_all[NW][2][16 * GP + 4];
   __shared__ float a_lds_all[NW][GP];          // per-head rescale factors
   __shared__ float l_lds_all[NW][GP];          // per-head sums at the end of a run
   __shared__ float m_lds_all[NW][GP];          // per-head maxima at the end of a run
@@ -481,7 +484,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
 
   const int wl = BINS ? (int)(threadIdx.x >> 6) : 0;
   const int lane = threadIdx.x & 63;
-  float (&p_lds)[2][16 * GP] = p_lds_all[wl];
+  float (&p_lds)[2][16 * GP + 4] = p_lds_all[wl];
   float (&a_lds)[GP] = a_lds_all[wl];
   float (&l_lds)[GP] = l_lds_all[wl];
   float (&m_lds)[GP] = m_lds_all[wl];
@@ -585,8 +588,8 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
           // 4-byte words; the tile layout puts the lane's NP K words (one
           // quarter of row kr) and its NV V words (word vc of rows vrr ..
           // vrr+NV-1, NV = NP = groups per row) each in one contiguous run
-          const char* kt = ktile + kr * CB + kg * NP * 4;
-          const char* vt = vtile + vrr * CB + vc * NV * 4;
+          const char* kt = ktile + (unsigned)(kr * CB + kg * NP * 4);
+          const char* vt = vtile + (unsigned)(vrr * CB + vc * NV * 4);
           if constexpr (NP == 4) {
             const u32x4 a = ld16(kt), b = ld16(vt);
 #pragma unroll
@@ -611,8 +614,8 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
           for (int i = 0; i < NV; ++i) t.v[i] = ld8(vt + i * CB);
         }
         // scales after the BS rows of codes: K [row][group], V [group][row]
-        const char* ksp = ktile + BS * CB + kr * NP * 2;
-        const char* vsp = vtile + BS * CB + ((vc >> 2) * BS + vrr) * 2;
+        const char* ksp = ktile + (unsigned)(BS * CB + kr * NP * 2);
+        const char* vsp = vtile + (unsigned)(BS * CB + ((vc >> 2) * BS + vrr) * 2);
         if constexpr (NP == 4) {
           const u32x2 x2 = ld8(ksp);
           t.ks[0] = x2[0];
@@ -766,20 +769,21 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       }
       float* pl = p_lds[parity];
       parity ^= 1;
+      float* pw_at = pl + (head_lane ? t16 * GP + 4 * kg : 16 * GP);
 #pragma unroll
       for (int i = 0; i < HPG; ++i) {
         const float pw = __builtin_amdgcn_exp2f(s2[i] - m[i]);
         lsum[i] += pw;
-        if (head_lane) pl[t16 * GP + 4 * kg + i] = pw;
+        pw_at[i] = pw;
       }
       wave_sync();
       if constexpr (MPV) {
-        // P.V as one MFMA 16x16x32 per block of 16 output columns. A: row
+        // P.V as MFMAs 16x16x16 per block of 16 output columns, one with the
+        // high and one with the low fp16 part of A (~22 bits together; all
+        // high parts first, so no MFMA waits on the one before). A: row
         // 4 * G + h holds head h's weights times each token's scale for group
         // G (the spare rows of a group of <= 4 heads carry the four scale
-        // groups) as a high and a low fp16 part (~22 bits): the lane's 8 k
-        // slots are the high parts of its 4 tokens, then the low parts, and B
-        // repeats the 4 tokens' codes. B: column n of block nt is head-dim
+        // groups), k = the lane's 4 tokens. B: column n of block nt is head-dim
         // column 8 * n + nt, its code's byte taken as the fp16 bits: the
         // subnormal code x 2^-24 (odd nt: code x 2^-20), exact, and kept by
         // the MFMA. One more MFMA against ones sums each row's A values, so
@@ -802,6 +806,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         const f16x8 av = {h01[0], h01[1], h23[0], h23[1],
                           (_Float16)(pa[0] - (float)h01[0]), (_Float16)(pa[1] - (float)h01[1]),
                           (_Float16)(pa[2] - (float)h23[0]), (_Float16)(pa[3] - (float)h23[1])};
+        const f16x4 ahi = {av[0], av[1], av[2], av[3]}, alo = {av[4], av[5], av[6], av[7]};
         unsigned ev[4], od[4];  // even codes (low nibbles), odd codes x 16 (high nibbles)
         accs = __builtin_amdgcn_mfma_f32_16x16x32_f16(
             av, __builtin_bit_cast(f16x8, u32x4{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u}),
@@ -811,16 +816,19 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
           ev[i] = t.v[i] & 0x0f0f0f0fu;
           od[i] = t.v[i] & 0xf0f0f0f0u;
         }
+        f16x4 bv[8];
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
           const unsigned* src = (nt & 1) ? od : ev;
           // byte nt / 2 of rows 0, 1 (and 2, 3) into the low bytes of the two fp16 halves
           const unsigned sel = 0x0c000c00u | ((4u + (nt >> 1)) << 16) | (unsigned)(nt >> 1);
-          const unsigned b01 = __builtin_amdgcn_perm(src[1], src[0], sel);
-          const unsigned b23 = __builtin_amdgcn_perm(src[3], src[2], sel);
-          const f16x8 bv = __builtin_bit_cast(f16x8, u32x4{b01, b23, b01, b23});
-          accm[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, accm[nt], 0, 0, 0);
+          bv[nt] = __builtin_bit_cast(f16x4, u32x2{__builtin_amdgcn_perm(src[1], src[0], sel),
+                                                   __builtin_amdgcn_perm(src[3], src[2], sel)});
+          accm[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bv[nt], accm[nt], 0, 0, 0);
         }
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+          accm[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, bv[nt], accm[nt], 0, 0, 0);
       } else
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
