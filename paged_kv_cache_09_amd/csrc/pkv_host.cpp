@@ -298,10 +298,11 @@ constexpr int64_t kSegStartCost = PKV_SEG_START_COST;
 bool build_bins(pkv_pool* p, int nbins);
 
 void build_schedule(pkv_pool* p, int part, int target) {
-  // the eight-wave form: 2-byte and quantised tiles of 16-token blocks (fp32 tiles spill)
-  if (part == 0 && p->shape.dtype != PKV_F32 && p->shape.block_size == 16) {
+  // the eight-wave form: 2-byte and quantised tiles (fp32 tiles spill)
+  if (part == 0 && p->shape.dtype != PKV_F32) {
     const int per_cu = pkv::decode_blocks_per_cu(p->shape.dtype, p->shape.head_dim,
-                                                  p->sched_gp_building, true, 16);
+                                                  p->sched_gp_building, true,
+                                                  p->shape.block_size);
     if (per_cu > 0 && build_bins(p, std::max(1, p->num_cus) * per_cu)) return;
   }
   const int B = p->up_batch;

@@ -510,7 +510,13 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
   int blk_first = desc[6];
   const int merge_info = BINS ? desc[7] : 0;
   // 8-token blocks: id of the block holding rows 8..15 of the run's first tile
-  int blk_second = BINS ? 0 : desc[7];
+  // (the split descriptor carries it; the bins form, whose descriptor word 7
+  // is the merge, reads it from the table; any block when the context ends
+  // before row 8)
+  int blk_second = 0;
+  if constexpr (!BINS) blk_second = desc[7];
+  else if constexpr (BS == 8)
+    blk_second = 16 * j0 + 8 < L ? p.bt[(size_t)s * p.bt_stride + 2 * j0 + 1] : blk_first;
   const int s_first = s, g_first = g;
   bool first_seg = true;
 
@@ -539,6 +545,8 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         next_g = e[1];
         next_L = e[2];
         next_blk = e[3];
+        if constexpr (BS == 8)  // rows 8..15 of the first tile
+          next_second = next_L > 8 ? p.bt[(size_t)next_s * p.bt_stride + 1] : next_blk;
       }
     } else {
       if (next_s == p.batch) {
@@ -1338,14 +1346,20 @@ __global__ __launch_bounds__(256) void upload_kernel(const u32x4* __restrict__ s
 }
 
 // The bins form is built for 16-token blocks only.
+template <int DT, int D, int GP, int BS>
+const void* decode_fn_bs(bool bins) {
+  if (!bins) return reinterpret_cast<const void*>(&decode_kernel<DT, D, GP, false, BS>);
+  if constexpr (DT == DT_F32) return nullptr;  // fp32 tiles spill in the eight-wave form
+  else return reinterpret_cast<const void*>(&decode_kernel<DT, D, GP, true, BS>);
+}
+
 template <int DT, int D, int GP>
 const void* decode_fn(bool bins, int bs) {
-  if (bs == 16)
-    return bins ? reinterpret_cast<const void*>(&decode_kernel<DT, D, GP, true, 16>)
-                : reinterpret_cast<const void*>(&decode_kernel<DT, D, GP, false, 16>);
-  if (bins) return nullptr;
-  if (bs == 8) return reinterpret_cast<const void*>(&decode_kernel<DT, D, GP, false, 8>);
-  if (bs == 32) return reinterpret_cast<const void*>(&decode_kernel<DT, D, GP, false, 32>);
+  switch (bs) {
+    case 8: return decode_fn_bs<DT, D, GP, 8>(bins);
+    case 16: return decode_fn_bs<DT, D, GP, 16>(bins);
+    case 32: return decode_fn_bs<DT, D, GP, 32>(bins);
+  }
   return nullptr;
 }
 

@@ -21,21 +21,21 @@ hipError_t launch_copy_blocks(const int32_t*, int, void*, void*, int, int64_t, i
 hipError_t launch_upload(const void*, void*, size_t, hipStream_t) { return hipSuccess; }
 }
 
-static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins) {
+static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins, int bs = 16) {
   pkv_pool P;
   pkv_pool* p = &P;
   p->shape.kv_heads = H;
-  p->shape.block_size = 16;
+  p->shape.block_size = bs;
   const int B = ctx.size();
   p->up_batch = B;
   int maxb = 0;
-  for (int L : ctx) maxb = std::max<int>(maxb, (L + 15) / 16);
+  for (int L : ctx) maxb = std::max<int>(maxb, (L + bs - 1) / bs);  // table entries
   p->up_stride = maxb;
   p->h_ctx = ctx;
   p->h_bt.assign((size_t)B * maxb, -1);
   int id = 0;
   for (int s = 0; s < B; ++s)
-    for (int j = 0; j < (ctx[s] + 15) / 16; ++j) p->h_bt[(size_t)s * maxb + j] = 1000 + id++;
+    for (int j = 0; j < (ctx[s] + bs - 1) / bs; ++j) p->h_bt[(size_t)s * maxb + j] = 1000 + id++;
   bool ok = build_bins(p, nbins);
   if (ok != expect_bins && expect_bins) { printf("bins refused (expected)\n"); return 1; }
   if (!ok) return 0;
@@ -56,7 +56,7 @@ static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins) {
       if (li < 0 || li >= nseg) { printf("bad li\n"); return 1; }
       const int32_t* e0 = list + 4 * li;
       if (e0[0] != s || e0[1] != g || e0[2] != L) { printf("desc/list mismatch\n"); return 1; }
-      if (blk != p->h_bt[(size_t)s * maxb + j0]) { printf("bad first blk\n"); return 1; }
+      if (blk != p->h_bt[(size_t)s * maxb + j0 * 16 / bs]) { printf("bad first blk\n"); return 1; }
       int x = 0; bool first = true;
       first_seg_of[wl] = {s, g};
       while (x < count) {
@@ -100,7 +100,7 @@ static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins) {
     for (int s = 0; s < B; ++s)
       for (int j = 0; j < (ctx[s] + 15) / 16; ++j)
         if (cov[{g, s, j}] != 1) { printf("tile (%d,%d,%d) covered %d\n", g, s, j, cov[{g,s,j}]); return 1; }
-  printf("ok: B=%d H=%d bins=%d waves=%d merges=%d errors=%d\n", B, H, nbins, W, merges, errors);
+  printf("ok: B=%d H=%d bs=%d bins=%d waves=%d merges=%d errors=%d\n", B, H, bs, nbins, W, merges, errors);
   return errors;
 }
 
@@ -111,10 +111,15 @@ int main() {
   { std::vector<int> c(256); std::uniform_int_distribution<int> u(16, 2048); for (auto& x : c) x = u(rng); rc |= check(c, 40, 256, true); }
   { std::vector<int> c(128); std::uniform_int_distribution<int> u(1025, 1537); for (auto& x : c) x = u(rng); rc |= check(c, 8, 256, true); }
   { std::vector<int> c(6); std::uniform_int_distribution<int> u(1, 700); for (auto& x : c) x = u(rng); rc |= check(c, 8, 4, false); }
-  for (int t = 0; t < 200; ++t) {
+  for (int bs : {8, 32}) {
+    std::vector<int> c(64); std::uniform_int_distribution<int> u(128, 2048); for (auto& x : c) x = u(rng);
+    rc |= check(c, 8, 256, true, bs);
+  }
+  for (int t = 0; t < 300; ++t) {
     std::uniform_int_distribution<int> nb(1, 64), lb(1, 3000), hb(1, 8), bb(1, 64);
     std::vector<int> c(nb(rng)); for (auto& x : c) x = lb(rng);
-    rc |= check(c, hb(rng), bb(rng), false);
+    const int bs = t % 3 == 0 ? 8 : t % 3 == 1 ? 16 : 32;
+    rc |= check(c, hb(rng), bb(rng), false, bs);
   }
   printf(rc ? "FAILED\n" : "ALL OK\n");
   return rc;

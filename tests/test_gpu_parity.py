@@ -190,6 +190,23 @@ def test_prefix_cached_blocks_decode_like_written_ones(name):
         assert e <= tol, f"{name} partition {key}: max abs error {e} > {tol}"
 
 
+BLOCK_SIZE_FULL = [("llama8b_bf16", 8), ("llama8b_bf16", 32), ("llama8b_q8", 8),
+                   ("llama8b_q4", 8), ("llama8b_q4", 32)]
+
+
+@pytest.mark.parametrize("name,bs", BLOCK_SIZE_FULL, ids=[f"{n}_bs{b}" for n, b in BLOCK_SIZE_FULL])
+def test_full_size_block_sizes(name, bs):
+    """The 8B-shaped batch with 8- and 32-token blocks: its 512 segments pack into the
+    256 bins within the slack (the same 16-token tiles as with 16-token blocks), so the
+    balanced decode runs the eight-wave bins form; 512-token split-K beside it."""
+    base = W.CONFIGS[name]
+    cfg = W.scaled(base, block_size=bs, num_blocks=base.num_blocks * 16 // bs)
+    errs, _, _ = run_step_case(cfg, layers=1, partitions=(0, 512), sample=24,
+                               label=f"{name} block {bs}")
+    for key, e in errs.items():
+        assert e <= tolerance(cfg), f"{name} block {bs} {key}: max abs error {e}"
+
+
 def _q4_edge_rows(w):
     """New K/V rows built to hit the q4_0 decisions: an all +0 group, an all -0
     group, largest magnitudes tied with opposite signs in different lanes'
