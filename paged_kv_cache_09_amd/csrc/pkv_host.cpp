@@ -406,8 +406,9 @@ constexpr int kBinWaves = 8;
 
 // Bins form of the balanced schedule: whole (kv head, sequence) segments are
 // packed into nbins bins, longest processing time first (each segment to the
-// least loaded bin; cost = tiles + kSegStartCost), and each bin's tiles are
-// cut into kBinWaves equal-cost runs. Returns false (schedule untouched) when
+// least loaded bin of its kv head's XCD group; cost = tiles + kSegStartCost),
+// and each bin's tiles are cut into kBinWaves equal-cost runs. Returns false
+// (schedule untouched) when
 // the packing is too uneven, e.g. a few very long sequences.
 //   wdesc per wave: [0] index of its first segment in the bin lists, [1] tile
 //   count, [2] sequence, [3] kv head, [4] first block index in that segment,
@@ -437,14 +438,27 @@ bool build_bins(pkv_pool* p, int nbins) {
                    [](const Seg& a, const Seg& b) { return a.cost > b.cost; });
   std::vector<int64_t> load(nbins, 0);
   std::vector<std::vector<int>> members(nbins);
-  // min-heap of (load, bin)
-  std::vector<std::pair<int64_t, int>> heap;
-  for (int b = 0; b < nbins; ++b) heap.push_back({0, b});
+  // XCD affinity: bins [x * nbins / 8, (x + 1) * nbins / 8) run on XCD x. When
+  // the kv heads divide evenly among the XCDs, a head's segments go only to
+  // its own XCD's bins (group g % ngroups), so tiles that several sequences
+  // share (a common prompt) are fetched into one XCD's L2 and re-read there.
+  int ngroups = 1;
+  if (nbins % pkv::kNumXcd == 0) {
+    if (H % pkv::kNumXcd == 0) ngroups = pkv::kNumXcd;
+    else if (pkv::kNumXcd % H == 0) ngroups = H;
+  }
+  const int per_group = nbins / ngroups;
+  // per group, a min-heap of (load, bin)
   auto cmp = [](const std::pair<int64_t, int>& a, const std::pair<int64_t, int>& b) {
     return a.first != b.first ? a.first > b.first : a.second > b.second;
   };
-  std::make_heap(heap.begin(), heap.end(), cmp);
+  std::vector<std::vector<std::pair<int64_t, int>>> heaps(ngroups);
+  for (int gr = 0; gr < ngroups; ++gr) {
+    for (int b = gr * per_group; b < (gr + 1) * per_group; ++b) heaps[gr].push_back({0, b});
+    std::make_heap(heaps[gr].begin(), heaps[gr].end(), cmp);
+  }
   for (int i = 0; i < nseg; ++i) {
+    auto& heap = heaps[segs[i].g % ngroups];
     std::pop_heap(heap.begin(), heap.end(), cmp);
     auto top = heap.back();
     heap.pop_back();
