@@ -251,10 +251,15 @@ int pkv_kv_append(pkv_pool* pool, int layer, const void* k_new, const void* v_ne
  * partitions of that many tokens per sequence, each keeping its own max/sum,
  * merged by the same reduce (a partition >= the longest context is the
  * single-pass form, no reduce).
+ * With a 2-byte cache of head_dim 128 (at most 4 q heads per kv head),
+ * sequences whose tables name the same blocks for their
+ * first tiles (a shared prompt, thienlv.com "Sharing") are grouped, up to
+ * 16 / group per group, and those shared tiles are read once per group; their
+ * partial results are merged with each sequence's own tiles by the reduce.
  * workspace / ws_bytes: device scratch of at least
  * pkv_decode_workspace_bytes(...) bytes, 16-byte aligned, for the split
- * partials (unused, may be NULL, when no sequence is split). Calls sharing
- * one workspace must not overlap.
+ * partials (unused, may be NULL, when no sequence is split and no prompt is
+ * shared). Calls sharing one workspace must not overlap.
  */
 int pkv_paged_attn_decode(pkv_pool* pool, int layer, const void* q, int q_heads, float scale,
                           float* out, int partition_tokens, void* workspace, size_t ws_bytes,

@@ -11,6 +11,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <list>
+#include <map>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -150,6 +151,11 @@ struct pkv_pool {
   int sched_nwaves = 0;
   bool sched_needs_merge = false;   // some segment spans several waves
   bool sched_bins = false;          // eight-wave bins form (merges in LDS)
+  // shared-prefix groups of the split form: h_sched continues with
+  // seqinfo[4 * batch] | items[kItemInts * nitems] | groups[kGroupInts * ngroups]
+  int sched_nitems = 0;
+  int sched_ngroups = 0;
+  int sched_seg_stride = 1;         // partial slots per segment (1 + most chunks)
   int sched_gp_building = 1;        // padded group of the schedule being built
   std::vector<int32_t> h_sched;     // wdesc[8 * nwaves] | seg_w0[nseg] | seg_w1[nseg]
 
@@ -288,6 +294,105 @@ int64_t nent(const pkv_pool* p, int64_t tokens) {
 #endif
 constexpr int64_t kSegStartCost = PKV_SEG_START_COST;
 
+// Shared-prefix groups (split form; 2-byte caches, head_dim 128, padded GQA
+// group <= 4). Sequences whose first tile names the same block(s) are taken in
+// batch order, in runs of up to kMaxMembers / gp; a run's shared tiles are the
+// leading tiles that name the same blocks in every member and hold only cached
+// rows in every member (16 (j + 1) <= ctx - 1: the newest row stays private),
+// at most kMaxChunks chunks of at most kChunkTiles tiles. A run of one
+// sequence, or sharing fewer than kMinSharedTiles tiles, is not a group.
+constexpr bool kPrefixGroups = true;
+constexpr int kMinSharedTiles = 4;
+constexpr int kPrefixChunk = 16;   // preferred tiles per work item
+constexpr int kChunkTiles = 32;    // at most (the chunk's table entries fit one per lane)
+constexpr int kMaxChunks = 16;
+
+size_t prefix_sched_ints(const pkv_shape* sh) {
+  if (!pkv::prefix_supported(sh->dtype, sh->head_dim, 4)) return 0;
+  const size_t half = ((size_t)sh->max_seqs + 1) / 2;  // at most this many groups
+  return 4 * (size_t)sh->max_seqs + half * pkv::kGroupInts +
+         half * sh->kv_heads * kMaxChunks * pkv::kItemInts;
+}
+
+// Whether sequences s and t read tile j from the same block(s).
+bool same_tile(const pkv_pool* p, int s, int t, int64_t j) {
+  const int32_t* a = p->h_bt.data() + (size_t)s * p->up_stride;
+  const int32_t* b = p->h_bt.data() + (size_t)t * p->up_stride;
+  switch (p->shape.block_size) {
+    case 16: return a[j] == b[j];
+    case 32: return a[j >> 1] == b[j >> 1];
+    default: return a[2 * j] == b[2 * j] && a[2 * j + 1] == b[2 * j + 1];
+  }
+}
+
+struct PrefixGroups {
+  std::vector<int32_t> pstart;  // per sequence: first private tile
+  std::vector<int32_t> nch;     // per sequence: chunks of its group (0: none)
+  std::vector<int32_t> items, recs;
+  int maxch = 0;
+};
+
+void find_groups(const pkv_pool* p, int gp, PrefixGroups& pg) {
+  const int B = p->up_batch, H = p->shape.kv_heads;
+  pg.pstart.assign(B, 0);
+  pg.nch.assign(B, 0);
+  const int nm = pkv::kMaxMembers / gp;
+  // sequences by the block(s) of their first tile, in batch order
+  std::map<int64_t, std::vector<int>> by_first;
+  for (int s = 0; s < B; ++s) {
+    if ((p->h_ctx[s] - 1) / pkv::kTile < kMinSharedTiles) continue;
+    const int32_t* row = p->h_bt.data() + (size_t)s * p->up_stride;
+    const int64_t key = p->shape.block_size == 8 ? ((int64_t)row[0] << 32) | (uint32_t)row[1]
+                                                 : (int64_t)row[0];
+    by_first[key].push_back(s);
+  }
+  for (auto& kv : by_first) {
+    const std::vector<int>& v = kv.second;
+    for (size_t a = 0; a + 1 < v.size(); a += nm) {
+      const int count = (int)std::min<size_t>(nm, v.size() - a);
+      if (count < 2) break;
+      int64_t P = (int64_t)kMaxChunks * kChunkTiles;
+      for (int k = 0; k < count; ++k) P = std::min<int64_t>(P, (p->h_ctx[v[a + k]] - 1) / pkv::kTile);
+      int64_t j = 0;
+      for (; j < P; ++j) {
+        bool same = true;
+        for (int k = 1; k < count && same; ++k) same = same_tile(p, v[a], v[a + k], j);
+        if (!same) break;
+      }
+      P = j;
+      if (P < kMinSharedTiles) continue;
+      const int nch = (int)std::min<int64_t>(kMaxChunks, (P + kPrefixChunk - 1) / kPrefixChunk);
+      const int grp = (int)(pg.recs.size() / pkv::kGroupInts);
+      pg.recs.resize(pg.recs.size() + pkv::kGroupInts, 0);
+      int32_t* r = pg.recs.data() + (size_t)grp * pkv::kGroupInts;
+      r[0] = count;
+      r[1] = v[a];
+      r[2] = nch;
+      for (int k = 0; k < count; ++k) {
+        r[3 + k] = v[a + k];
+        pg.pstart[v[a + k]] = (int32_t)P;
+        pg.nch[v[a + k]] = nch;
+      }
+      for (int g = 0; g < H; ++g)
+        for (int c = 0; c < nch; ++c) {
+          const int32_t it[pkv::kItemInts] = {grp, g, (int32_t)(c * P / nch),
+                                              (int32_t)((c + 1) * P / nch), c, 0, 0, 0};
+          pg.items.insert(pg.items.end(), it, it + pkv::kItemInts);
+        }
+      pg.maxch = std::max(pg.maxch, nch);
+    }
+  }
+}
+
+// Block id holding tile j's rows 0..7 (or all of them), and for 8-token
+// blocks the id holding rows 8..15 (any block when the context ends before).
+void tile_blocks(const pkv_pool* p, int s, int64_t j, int32_t& first, int32_t& second) {
+  const int32_t* row = p->h_bt.data() + (size_t)s * p->up_stride;
+  first = row[j * pkv::kTile / p->shape.block_size];
+  second = 0;
+  if (p->shape.block_size == 8) second = 16 * j + 8 < p->h_ctx[s] ? row[2 * j + 1] : first;
+}
+
 // Build the decode schedule for the current upload.
 //   part > 0: one wave per (kv head, sequence, part/16-block partition).
 //   part == 0: `target` waves, each an equal share of all tiles.
@@ -298,8 +403,16 @@ constexpr int64_t kSegStartCost = PKV_SEG_START_COST;
 bool build_bins(pkv_pool* p, int nbins);
 
 void build_schedule(pkv_pool* p, int part, int target) {
+  p->sched_nitems = 0;
+  p->sched_ngroups = 0;
+  p->sched_seg_stride = 1;
+  PrefixGroups pg;
+  if (kPrefixGroups &&
+      pkv::prefix_supported(p->shape.dtype, p->shape.head_dim, p->sched_gp_building))
+    find_groups(p, p->sched_gp_building, pg);
+  const bool groups = !pg.recs.empty();
   // the eight-wave form: 2-byte and quantised tiles (fp32 tiles spill)
-  if (part == 0 && p->shape.dtype != PKV_F32) {
+  if (!groups && part == 0 && p->shape.dtype != PKV_F32) {
     const int per_cu = pkv::decode_blocks_per_cu(p->shape.dtype, p->shape.head_dim,
                                                   p->sched_gp_building, true,
                                                   p->shape.block_size);
@@ -307,15 +420,22 @@ void build_schedule(pkv_pool* p, int part, int target) {
   }
   const int B = p->up_batch;
   const int H = p->shape.kv_heads;
-  const int64_t tseq = p->h_cum[B];
+  if (!groups) {
+    pg.pstart.assign(B, 0);
+    pg.nch.assign(B, 0);
+  }
+  // tiles each sequence's own runs cover: from its first private tile on
+  std::vector<int64_t> cum(B + 1, 0);
+  for (int s = 0; s < B; ++s) cum[s + 1] = cum[s] + nblk(p->h_ctx[s]) - pg.pstart[s];
+  const int64_t tseq = cum[B];
   const int64_t T = tseq * H;
   std::vector<int64_t> ws;
   if (part > 0) {
     const int64_t pb = part / pkv::kTile;
     for (int g = 0; g < H; ++g)
       for (int s = 0; s < B; ++s) {
-        const int64_t n = nblk(p->h_ctx[s]);
-        for (int64_t j = 0; j < n; j += pb) ws.push_back(g * tseq + p->h_cum[s] + j);
+        const int64_t n = nblk(p->h_ctx[s]) - pg.pstart[s];
+        for (int64_t j = 0; j < n; j += pb) ws.push_back(g * tseq + cum[s] + j);
       }
   } else {
     // Equal cost per wave, where starting a (kv head, sequence) segment costs
@@ -329,7 +449,7 @@ void build_schedule(pkv_pool* p, int part, int target) {
     for (int g = 0; g < H && (int64_t)ws.size() < W; ++g)
       for (int s = 0; s < B && (int64_t)ws.size() < W; ++s) {
         cost += kSegStartCost;
-        const int64_t n = nblk(p->h_ctx[s]);
+        const int64_t n = nblk(p->h_ctx[s]) - pg.pstart[s];
         for (int64_t j = 0; j < n; ++j, ++x) {
           // open a new wave at tile x when the cost before it passes the next cut
           while ((int64_t)ws.size() < W && cost * W >= (int64_t)ws.size() * total && x > ws.back())
@@ -341,7 +461,11 @@ void build_schedule(pkv_pool* p, int part, int target) {
   const int W = (int)ws.size();
   ws.push_back(T);
   const int nseg = B * H;
-  p->h_sched.assign((size_t)8 * W + 2 * (size_t)nseg, 0);
+  const size_t nitems = pg.items.size() / pkv::kItemInts;
+  const size_t ngroups = pg.recs.size() / pkv::kGroupInts;
+  p->h_sched.assign((size_t)8 * W + 2 * (size_t)nseg +
+                        (groups ? 4 * (size_t)B + pg.items.size() + pg.recs.size() : 0),
+                    0);
   int32_t* desc = p->h_sched.data();
   int32_t* w0 = desc + (size_t)8 * W;
   int32_t* w1 = w0 + nseg;
@@ -349,13 +473,13 @@ void build_schedule(pkv_pool* p, int part, int target) {
   int g = 0, s = 0;
   for (int w = 0; w < W; ++w) {
     const int64_t x0 = ws[w];
-    while (g * tseq + p->h_cum[s + 1] <= x0) {
+    while (g * tseq + cum[s + 1] <= x0) {
       if (++s == B) {
         s = 0;
         ++g;
       }
     }
-    const int64_t j0 = x0 - g * tseq - p->h_cum[s];
+    const int64_t j0 = x0 - g * tseq - cum[s] + pg.pstart[s];
     int32_t* d = desc + (size_t)8 * w;
     d[0] = (int32_t)x0;
     d[1] = (int32_t)ws[w + 1];
@@ -363,20 +487,16 @@ void build_schedule(pkv_pool* p, int part, int target) {
     d[3] = g;
     d[4] = (int32_t)j0;
     d[5] = p->h_ctx[s];
-    d[6] = p->h_bt[(size_t)s * p->up_stride + j0 * pkv::kTile / p->shape.block_size];
-    // 8-token blocks: the block holding rows 8..15 of the first tile (any
-    // valid block when the context ends before them)
-    d[7] = 0;
-    if (p->shape.block_size == 8)
-      d[7] = 16 * j0 + 8 < p->h_ctx[s] ? p->h_bt[(size_t)s * p->up_stride + 2 * j0 + 1] : d[6];
+    // the first tile's block(s): rows 8..15 of 8-token blocks in d[7]
+    tile_blocks(p, s, j0, d[6], d[7]);
   }
-  bool multi = false;
+  bool multi = groups;  // grouped sequences always merge their prefix partials
   int w = 0;
   for (int gg = 0; gg < H; ++gg)
     for (int ss = 0; ss < B; ++ss) {
       const int seg = gg * B + ss;
-      const int64_t first = gg * tseq + p->h_cum[ss];
-      const int64_t last = first + nblk(p->h_ctx[ss]) - 1;
+      const int64_t first = gg * tseq + cum[ss];
+      const int64_t last = first + nblk(p->h_ctx[ss]) - pg.pstart[ss] - 1;
       while (ws[w + 1] <= first) ++w;
       w0[seg] = w;
       int v = w;
@@ -384,6 +504,19 @@ void build_schedule(pkv_pool* p, int part, int target) {
       w1[seg] = v;
       multi |= v != w;
     }
+  if (groups) {
+    int32_t* info = w1 + nseg;
+    for (int q = 0; q < B; ++q) {
+      info[4 * q] = pg.pstart[q];
+      tile_blocks(p, q, pg.pstart[q], info[4 * q + 1], info[4 * q + 2]);
+      info[4 * q + 3] = pg.nch[q];
+    }
+    std::memcpy(info + 4 * (size_t)B, pg.items.data(), pg.items.size() * 4);
+    std::memcpy(info + 4 * (size_t)B + pg.items.size(), pg.recs.data(), pg.recs.size() * 4);
+    p->sched_nitems = (int)nitems;
+    p->sched_ngroups = (int)ngroups;
+    p->sched_seg_stride = 1 + pg.maxch;
+  }
   p->sched_nwaves = W;
   p->sched_needs_merge = multi;
   p->sched_bins = false;
@@ -616,7 +749,8 @@ int pkv_kv_pool_alloc(const pkv_shape* sh, void* dev_base, size_t dev_bytes, pkv
     p->num_cus = prop.multiProcessorCount;
     // balanced schedules need 8 ints per wave (at most 32 waves per CU); very
     // small fixed partitions may grow this buffer on first use
-    p->sched_cap = (size_t)8 * std::max(p->num_cus, 1) * 32 + 6 * (size_t)sh->max_seqs * sh->kv_heads;
+    p->sched_cap = (size_t)8 * std::max(p->num_cus, 1) * 32 + 6 * (size_t)sh->max_seqs * sh->kv_heads +
+                   prefix_sched_ints(sh);
     p->pairs_cap = sh->max_seqs;
     const size_t bt_bytes = (size_t)sh->max_seqs * p->max_blocks_per_seq * 4;
     p->off_ctx = (size_t)sh->max_seqs * 8;
@@ -1012,7 +1146,11 @@ size_t pkv_decode_workspace_bytes(const pkv_pool* p, int batch, int q_heads,
   } else {
     waves = std::max<int64_t>(1, std::max(p->num_cus, 1) * 32);
   }
-  return (size_t)(nseg + waves) * gp * (p->shape.head_dim + 2) * sizeof(float);
+  // shared-prefix partials: up to kMaxChunks slots before each segment's own
+  const int64_t stride =
+      kPrefixGroups && pkv::prefix_supported(p->shape.dtype, p->shape.head_dim, gp)
+          ? 1 + kMaxChunks : 1;
+  return (size_t)(nseg * stride + waves) * gp * (p->shape.head_dim + 2) * sizeof(float);
 }
 
 namespace {
@@ -1077,7 +1215,7 @@ int decode_impl(pkv_pool* p, int layer, const void* k_new, const void* v_new, co
   const int B = p->up_batch;
   const int W = p->sched_nwaves;
   const int64_t nseg = (int64_t)B * p->shape.kv_heads;
-  const int64_t nparts = nseg + W;
+  const int64_t nparts = nseg * p->sched_seg_stride + W;
   const size_t need = (size_t)nparts * gp * (p->shape.head_dim + 2) * sizeof(float);
   if (p->sched_needs_merge && (ws_bytes < need || !ws))
     return fail(PKV_EINVAL, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
@@ -1109,6 +1247,15 @@ int decode_impl(pkv_pool* p, int layer, const void* k_new, const void* v_new, co
   dp.q_heads = q_heads;
   dp.group = group;
   dp.nwaves = W;
+  dp.seg_stride = p->sched_seg_stride;
+  dp.seqinfo = p->sched_ngroups > 0 ? dp.seg_w1 + nseg : nullptr;
+  if (p->sched_ngroups > 0) {
+    // shared-prefix items run in the same launch, ahead of the private runs
+    dp.items = dp.seqinfo + 4 * (size_t)B;
+    dp.groups = dp.items + (size_t)pkv::kItemInts * p->sched_nitems;
+    dp.nitems = p->sched_nitems;
+    dp.nprefix = (p->sched_nitems + pkv::kNumXcd - 1) / pkv::kNumXcd * pkv::kNumXcd;
+  }
   const int groups = p->sched_bins ? W / 8 : W;  // workgroups: bins, or one per wave
   dp.waves_per_xcd = (groups + pkv::kNumXcd - 1) / pkv::kNumXcd;
   e = pkv::launch_decode(p->shape.dtype, p->shape.head_dim, gp, p->sched_bins,
@@ -1125,6 +1272,8 @@ int decode_impl(pkv_pool* p, int layer, const void* k_new, const void* v_new, co
     rp.kv_heads = p->shape.kv_heads;
     rp.q_heads = q_heads;
     rp.group = group;
+    rp.seqinfo = dp.seqinfo;
+    rp.seg_stride = dp.seg_stride;
     e = pkv::launch_reduce(p->shape.head_dim, gp, rp, stream);
     if (e != hipSuccess) return hip_fail(e, "reduce launch");
   }

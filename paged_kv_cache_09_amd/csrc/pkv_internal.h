@@ -36,6 +36,14 @@ struct DecodeParams {
   int32_t group;               // q_heads / kv_heads
   int32_t nwaves;
   int32_t waves_per_xcd;       // ceil(nwaves / 8)
+  // shared prefixes (split form): null, or per sequence [first private tile,
+  // its block id, (8-token blocks) the id of its rows 8..15, prefix chunks]
+  const int32_t* seqinfo;
+  int32_t seg_stride;          // partial slots per segment: 1 + most prefix chunks
+  const int32_t* items;        // shared-prefix work items [nitems][kItemInts]
+  const int32_t* groups;       // their groups [ngroups][kGroupInts]
+  int32_t nitems;
+  int32_t nprefix;             // leading workgroups for the items (multiple of 8)
 };
 
 struct ReduceParams {
@@ -48,7 +56,16 @@ struct ReduceParams {
   int32_t kv_heads;
   int32_t q_heads;
   int32_t group;
+  const int32_t* seqinfo;      // as in DecodeParams
+  int32_t seg_stride;
 };
+
+// Shared-prefix items: tiles that a group of sequences reads from the same
+// blocks (their common prompt), read once per group.
+constexpr int kGroupInts = 20;   // per group: count, leader, chunks, 17 member slots
+constexpr int kMaxMembers = 16;  // MFMA rows / padded heads per kv head
+constexpr int kItemInts = 8;     // per work item: group, kv head, t0, t1, chunk, 0, 0, 0
+
 
 // Padded group size used by the kernels: 1, 2, 4 or 8.
 inline int padded_group(int g) { return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : 8; }
@@ -58,6 +75,9 @@ inline int padded_group(int g) { return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : 8
 hipError_t launch_decode(int dtype, int head_dim, int gp, bool bins, int block_size,
                          const DecodeParams& p, hipStream_t stream);
 hipError_t launch_reduce(int head_dim, int gp, const ReduceParams& p, hipStream_t stream);
+// Whether the decode launch can take shared-prefix items for this cache dtype,
+// head_dim and padded group (split form).
+bool prefix_supported(int dtype, int head_dim, int gp);
 // Workgroups of the decode kernel one CU can hold at once (occupancy), 0 on error.
 int decode_blocks_per_cu(int dtype, int head_dim, int gp, bool bins, int block_size);
 

@@ -381,6 +381,19 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // the tile's tokens). Lane l supplies row/column l%16 and the same 16 bytes
 // of head_dim for both operands, so the products pair up correctly whatever
 // order the instruction walks its K dimension in.
+// One MFMA 16x16x16 of P.V in a 2-byte type: 4 weights (A) x 4 rows of one
+// column (B) per lane.
+template <int DT>
+__device__ __forceinline__ f32x4 pv_mfma(u32x2 a, u32x2 b, f32x4 acc) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  if constexpr (DT == DT_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), acc, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), acc, 0, 0, 0);
+}
+
 template <int DT>
 __device__ __forceinline__ f32x4 qk_piece(u32x4 q, u32x4 k, f32x4 acc) {
   if constexpr (DT == DT_BF16) {
@@ -433,6 +446,200 @@ struct TileRegs<DT_Q4, D> {
   unsigned vs[NV / 2];
 };
 
+// Shared-prefix work items (split form; run by the first workgroups of the
+// decode launch, next to the private runs): a group of up to 16 / GP sequences whose
+// tables name the same blocks for their first full tiles (a common prompt,
+// shared through the block table as the pages describe) reads those tiles
+// once. One wave per (group, kv head, chunk of the shared tiles): the MFMA's
+// 16 rows hold member x head (4 x 4 for 4 q heads per kv head, 8 x 2, 16 x 1)
+// in q.K^T and in P.V, so one tile read serves every member. Each (member,
+// head) leaves an unnormalised partial (max, sum, output) in the slot just
+// before its own private run's partials, where the reduce merges it. 2-byte
+// caches, head_dim 128: K pieces and V chunks are loaded as in decode_kernel;
+// P.V takes the weights as a high and a low part in the cache's 16-bit type
+// (bf16: 16 bits together, fp16: ~22; the weights are <= 2^kLazy).
+template <int DT, int GP, int BS>
+__device__ __forceinline__ void prefix_item(const DecodeParams& p, int item) {
+  static_assert(DT == DT_F16 || DT == DT_BF16, "2-byte caches");
+  constexpr int D = 128, RB = 2 * D, NP = 4, NV = 4;  // as TileRegs<DT, 128>
+  constexpr int TILE = BS * RB;
+  using TR = TileRegs<DT, D>;
+  __shared__ float pl_all[2][16 * 16];  // weights [token][row], by parity
+  const int lane = threadIdx.x;
+  const int* it = p.items + kItemInts * item;
+  const int grp = it[0], g = it[1], t0 = it[2], t1 = it[3], chunk = it[4];
+  const int* gr = p.groups + kGroupInts * grp;
+  const int count = gr[0], leader = gr[1], nchunks = gr[2];
+  const int* members = gr + 3;
+  const int t16 = lane & 15, kg = lane >> 4;  // q.K: token column, row block
+  const int vc = lane & 15, vr = lane >> 4;   // V chunk, row group (rows vr + 4i)
+
+  // q rows: A row r = member r / GP, head r % GP (zero past the group)
+  u32x4 qv[NP];
+  {
+    const int mq = t16 / GP, hq = t16 % GP;
+    const bool real = mq < count && hq < p.group;
+    const int sq = members[real ? mq : 0];
+    const char* qr = reinterpret_cast<const char*>(p.q) +
+                     ((size_t)sq * p.q_heads + (size_t)g * p.group + (real ? hq : 0)) * RB +
+                     kg * 16;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      const u32x4 v = ld16(qr + k * 64);
+      qv[k] = real ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  // block-table entries of the chunk, one per lane (<= 32 tiles: <= 64 entries)
+  const int32_t* bt_row = p.bt + (size_t)leader * p.bt_stride;
+  const int e0 = BS == 32 ? (t0 >> 1) : BS == 8 ? 2 * t0 : t0;
+  const int ne = BS == 32 ? ((t1 + 1) >> 1) - (t0 >> 1) : BS == 8 ? 2 * (t1 - t0) : t1 - t0;
+  const int my_ent = lane < ne ? bt_row[e0 + lane] : 0;
+  const char* kbase = reinterpret_cast<const char*>(p.k) + (size_t)g * TILE;
+  const char* vbase = reinterpret_cast<const char*>(p.v) + (size_t)g * TILE;
+  const size_t blk_stride = (size_t)p.kv_heads * TILE;
+  // tile j (absolute): rows r of the tile live in block (a or b), row rib(r)
+  auto load = [&](int j, TR& t) {
+    int a, b, half;
+    if constexpr (BS == 16) {
+      a = b = __builtin_amdgcn_readlane(my_ent, j - t0);
+      half = 0;
+    } else if constexpr (BS == 32) {
+      a = b = __builtin_amdgcn_readlane(my_ent, (j >> 1) - (t0 >> 1));
+      half = j & 1;
+    } else {
+      a = __builtin_amdgcn_readlane(my_ent, 2 * (j - t0));
+      b = __builtin_amdgcn_readlane(my_ent, 2 * (j - t0) + 1);
+      half = 0;
+    }
+    auto blk = [&](int r) { return BS == 8 && r >= 8 ? b : a; };
+    auto rib = [&](int r) { return BS == 8 ? (r & 7) : BS == 32 ? 16 * half + r : r; };
+    const char* kt = kbase + (size_t)blk(t16) * blk_stride + rib(t16) * RB + kg * 16;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) t.k[k] = ld16(kt + k * 64);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int r = vr + 4 * i;
+      t.v[i] = ld16(vbase + (size_t)blk(r) * blk_stride + rib(r) * RB + vc * 16);
+    }
+  };
+
+  float m[4], lsum[4];  // rows 4 * kg + i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -__builtin_inff();
+    lsum[i] = 0.f;
+  }
+  f32x4 acc[8];  // output block nt: rows 4 * (lane / 16) + i, column 8 * (lane % 16) + nt
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int parity = 0;
+
+  auto compute = [&](const TR& t) {
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < NP; ++k) sacc = qk_piece<DT>(qv[k], t.k[k], sacc);
+    float s2[4];
+    bool over = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s2[i] = sacc[i] * p.scale_log2;  // the shared tiles are full
+      over |= s2[i] > m[i] + kLazy;
+    }
+    if (__any(over)) {
+      // the rows of lane's scores are the rows of its output blocks
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float mn = fmaxf(m[i], row_max(s2[i]));
+        const float a = __builtin_amdgcn_exp2f(m[i] - mn);
+        lsum[i] *= a;
+        m[i] = mn;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) acc[nt][i] *= a;
+      }
+    }
+    float* pl = pl_all[parity];
+    parity ^= 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pw = __builtin_amdgcn_exp2f(s2[i] - m[i]);
+      lsum[i] += pw;
+      pl[t16 * 16 + 4 * kg + i] = pw;
+    }
+    wave_sync();
+    // A: row lane % 16, k = tokens vr + 4 * i (the rows of this lane's V chunks)
+    float pa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pa[i] = pl[(vr + 4 * i) * 16 + (lane & 15)];
+    u32x2 ahi, alo;
+    if constexpr (DT == DT_BF16) {  // truncated high part, then the rest truncated
+      unsigned hb[4], lb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hb[i] = __builtin_bit_cast(unsigned, pa[i]) & 0xffff0000u;
+        lb[i] = __builtin_bit_cast(unsigned, pa[i] - __builtin_bit_cast(float, hb[i]));
+      }
+      ahi = u32x2{__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u),
+                  __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u)};
+      alo = u32x2{__builtin_amdgcn_perm(lb[1], lb[0], 0x07060302u),
+                  __builtin_amdgcn_perm(lb[3], lb[2], 0x07060302u)};
+    } else {
+      const f16x2 h01 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(pa[0], pa[1]));
+      const f16x2 h23 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(pa[2], pa[3]));
+      const f16x2 l01 = {(_Float16)(pa[0] - (float)h01[0]), (_Float16)(pa[1] - (float)h01[1])};
+      const f16x2 l23 = {(_Float16)(pa[2] - (float)h23[0]), (_Float16)(pa[3] - (float)h23[1])};
+      ahi = u32x2{__builtin_bit_cast(unsigned, h01), __builtin_bit_cast(unsigned, h23)};
+      alo = u32x2{__builtin_bit_cast(unsigned, l01), __builtin_bit_cast(unsigned, l23)};
+    }
+    // B for block nt: column 8 * vc + nt of the 4 rows (element nt of each chunk)
+    u32x2 bv[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const unsigned sel = (nt & 1) ? 0x07060302u : 0x05040100u;
+      bv[nt] = u32x2{__builtin_amdgcn_perm(t.v[1][nt >> 1], t.v[0][nt >> 1], sel),
+                     __builtin_amdgcn_perm(t.v[3][nt >> 1], t.v[2][nt >> 1], sel)};
+      acc[nt] = pv_mfma<DT>(ahi, bv[nt], acc[nt]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[nt] = pv_mfma<DT>(alo, bv[nt], acc[nt]);
+  };
+
+  TR t[2];
+  load(t0, t[0]);
+  for (int j = t0; j < t1; j += 2) {
+    // request the next tile (the last one again past the end: a cache hit)
+    load(min(j + 1, t1 - 1), t[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(t[0]);
+    if (j + 1 < t1) {
+      load(min(j + 2, t1 - 1), t[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(t[1]);
+    }
+  }
+
+  // partials of the real (member, head) rows
+  float lt[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lt[i] = row_sum(lsum[i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * kg + i, mr = r / GP, hr = r % GP;
+    if (mr < count && hr < p.group) {
+      const int sm = members[mr];
+      const int seg = g * p.batch + sm;
+      const size_t idx =
+          (size_t)(seg + 1) * p.seg_stride - 1 + p.seg_w0[seg] - nchunks + chunk;
+      float* o = p.part_o + (idx * GP + hr) * D + 8 * vc;
+      *reinterpret_cast<f32x4*>(o) = f32x4{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+      *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
+      if (t16 == 0) {
+        p.part_ml[(idx * GP + hr) * 2 + 0] = m[i];
+        p.part_ml[(idx * GP + hr) * 2 + 1] = lt[i];
+      }
+    }
+  }
+}
+
 // Two launch forms share this body:
 //   BINS = false: one wave per workgroup; a wave covers a contiguous run of
 //     the kv-head-major tile space; segments split between waves are merged
@@ -482,6 +689,15 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
   __shared__ float piece_o[BINS ? NW * 2 * GP * D : 1];
   __shared__ float piece_ml[BINS ? NW * 2 * GP * 2 : 1];
 
+  // the first nprefix workgroups (split form) take the shared-prefix items
+  constexpr bool PFX = !BINS && D == 128 && (DT == DT_F16 || DT == DT_BF16) && GP <= 4;
+  if constexpr (PFX) {
+    if ((int)blockIdx.x < p.nprefix) {
+      if ((int)blockIdx.x < p.nitems) prefix_item<DT, GP, BS>(p, blockIdx.x);
+      return;
+    }
+  }
+  const int bid = (int)blockIdx.x - (PFX ? p.nprefix : 0);  // a multiple of 8 comes off
   const int wl = BINS ? (int)(threadIdx.x >> 6) : 0;
   const int lane = threadIdx.x & 63;
   float (&p_lds)[2][16 * GP + 4] = p_lds_all[wl];
@@ -490,7 +706,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
   float (&m_lds)[GP] = m_lds_all[wl];
   // Workgroups are dealt round-robin to the 8 XCDs; give each XCD one
   // contiguous eighth of the waves (bins) so neighbouring work shares an L2.
-  const int wg = (blockIdx.x % kNumXcd) * p.waves_per_xcd + blockIdx.x / kNumXcd;
+  const int wg = (bid % kNumXcd) * p.waves_per_xcd + bid / kNumXcd;
   const int w = BINS ? wg * NW + wl : wg;
   const bool active = w < p.nwaves;
   if (!BINS && !active) return;
@@ -537,7 +753,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     const int seg = g * p.batch + s;
     // Prefetch the next segment's length and first block id (scalar loads
     // in flight while this segment's tiles stream).
-    int next_s = s + 1, next_g = g, next_L = 0, next_blk = 0, next_second = 0;
+    int next_s = s + 1, next_g = g, next_L = 0, next_blk = 0, next_second = 0, next_j0 = 0;
     if constexpr (BINS) {
       if (x + take < xend) {  // bin lists hold (sequence, kv head, length, first block)
         const int* e = p.seglist + 4 * (li + 1);
@@ -555,11 +771,20 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       }
       if (x + take < xend) {
         next_L = p.ctx[next_s];
-        next_blk = p.bt[(size_t)next_s * p.bt_stride];
-        // 8-token blocks: the second entry (padding -1 when absent: any block,
-        // its rows are past the context)
-        if constexpr (BS == 8)
-          next_second = p.bt_stride > 1 ? max(p.bt[(size_t)next_s * p.bt_stride + 1], 0) : 0;
+        if (p.seqinfo) {
+          // shared prefixes: the sequence's run starts at its first private
+          // tile, whose block id(s) the host wrote beside it
+          const int* r = p.seqinfo + 4 * next_s;
+          next_j0 = r[0];
+          next_blk = r[1];
+          next_second = r[2];
+        } else {
+          next_blk = p.bt[(size_t)next_s * p.bt_stride];
+          // 8-token blocks: the second entry (padding -1 when absent: any
+          // block, its rows are past the context)
+          if constexpr (BS == 8)
+            next_second = p.bt_stride > 1 ? max(p.bt[(size_t)next_s * p.bt_stride + 1], 0) : 0;
+        }
       }
     }
     const char* kbase = reinterpret_cast<const char*>(p.k) + (size_t)g * TILE;
@@ -1112,7 +1337,9 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         piece_ml[((wl * 2 + slot) * GP + lane) * 2 + 1] = l_lds[lane];
       }
     } else {
-      const size_t idx = (size_t)seg + w;
+      // slots of segment seg: ((seg + 1) * stride - 1) + its waves; the
+      // stride - 1 slots before them hold its shared-prefix partials
+      const size_t idx = (size_t)(seg + 1) * p.seg_stride - 1 + w;
       if (pv_lane) {
         float* o = p.part_o + idx * GP * D + pv_col;
 #pragma unroll
@@ -1134,7 +1361,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     if (x >= xend) break;
     s = next_s;
     g = next_g;
-    j0 = 0;
+    j0 = next_j0;
     L = next_L;
     blk_first = next_blk;
     blk_second = next_second;
@@ -1194,9 +1421,11 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
   const int seg = g * p.batch + s;
   const int w0 = p.seg_w0[seg];
   const int w1 = p.seg_w1[seg];
-  if (w0 == w1) return;  // written directly by the decode kernel
-  merge_partials<D, GP>(p.part_o, p.part_ml, (size_t)seg + w0, w1 - w0 + 1, hh,
-                        p.out + ((size_t)s * p.q_heads + h) * D, lane);
+  // shared-prefix chunks: partials in the slots just before the run's own
+  const int npre = p.seqinfo ? p.seqinfo[4 * s + 3] : 0;
+  if (w0 == w1 && npre == 0) return;  // written directly by the decode kernel
+  merge_partials<D, GP>(p.part_o, p.part_ml, (size_t)(seg + 1) * p.seg_stride - 1 + w0 - npre,
+                        w1 - w0 + 1 + npre, hh, p.out + ((size_t)s * p.q_heads + h) * D, lane);
 }
 
 __global__ __launch_bounds__(256) void append_kernel(const char* k_new, const char* v_new,
@@ -1413,7 +1642,7 @@ hipError_t launch_decode(int dtype, int head_dim, int gp, bool bins, int block_s
   if (!fn) return hipErrorInvalidValue;
   DecodeParams args = p;
   void* argv[] = {&args};
-  dim3 grid((unsigned)(p.waves_per_xcd * kNumXcd)), block(bins ? 512 : 64);
+  dim3 grid((unsigned)(p.nprefix + p.waves_per_xcd * kNumXcd)), block(bins ? 512 : 64);
   return hipLaunchKernel(fn, grid, block, argv, 0, stream);
 }
 
@@ -1434,6 +1663,10 @@ hipError_t launch_reduce(int head_dim, int gp, const ReduceParams& p, hipStream_
   void* argv[] = {&args};
   dim3 grid((unsigned)((p.batch * p.q_heads + 3) / 4)), block(256);
   return hipLaunchKernel(fn, grid, block, argv, 0, stream);
+}
+
+bool prefix_supported(int dtype, int head_dim, int gp) {
+  return (dtype == DT_F16 || dtype == DT_BF16) && head_dim == 128 && (gp == 1 || gp == 2 || gp == 4);
 }
 
 hipError_t launch_append(const void* k_new, const void* v_new, const int64_t* slots, int batch,

@@ -19,6 +19,10 @@ hipError_t launch_append(const void*, const void*, const int64_t*, int, void*, v
 hipError_t launch_append_quant(int, const void*, const void*, const int64_t*, int, void*, void*, int, int, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_copy_blocks(const int32_t*, int, void*, void*, int, int64_t, int64_t, hipStream_t) { return hipSuccess; }
 hipError_t launch_upload(const void*, void*, size_t, hipStream_t) { return hipSuccess; }
+bool prefix_supported(int dtype, int head_dim, int gp) {
+  return (dtype == PKV_F16 || dtype == PKV_BF16) && head_dim == 128 && gp <= 4;
+}
+
 }
 
 static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins, int bs = 16) {
@@ -104,6 +108,147 @@ static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins, int b
   return errors;
 }
 
+// Shared-prefix groups in the split form: replays the prefix items and every
+// wave's runs the way the kernels walk them and checks that each (kv head,
+// sequence, tile) is covered once, that each partial slot has one writer, and
+// that the reduce of each (kv head, sequence) reads exactly the slots written
+// for it (or that a single wave writes it whole).
+static int check_groups(const std::vector<std::vector<int>>& tables, const std::vector<int>& ctx,
+                        int H, int bs, int gp, int part, int target, int expect_groups) {
+  pkv_pool P;
+  pkv_pool* p = &P;
+  p->shape.kv_heads = H;
+  p->shape.block_size = bs;
+  p->shape.dtype = PKV_BF16;
+  p->shape.head_dim = 128;
+  const int B = ctx.size();
+  p->up_batch = B;
+  int maxb = 0;
+  for (auto& t : tables) maxb = std::max<int>(maxb, t.size());
+  p->up_stride = maxb;
+  p->h_ctx = ctx;
+  p->h_bt.assign((size_t)B * maxb, -1);
+  for (int s = 0; s < B; ++s)
+    for (size_t j = 0; j < tables[s].size(); ++j) p->h_bt[(size_t)s * maxb + j] = tables[s][j];
+  p->sched_gp_building = gp;
+  build_schedule(p, part, target);
+  if (p->sched_bins) {  // no groups: the bins form (checked above) is allowed
+    if (expect_groups > 0) { printf("groups: bins form chosen\n"); return 1; }
+    return 0;
+  }
+  if (expect_groups >= 0 && p->sched_ngroups != expect_groups) {
+    printf("groups: %d groups, expected %d\n", p->sched_ngroups, expect_groups);
+    return 1;
+  }
+  const int W = p->sched_nwaves, nseg = B * H, K = p->sched_seg_stride;
+  const int32_t* desc = p->h_sched.data();
+  const int32_t* w0 = desc + 8 * (size_t)W;
+  const int32_t* w1 = w0 + nseg;
+  const int32_t* info = w1 + nseg;
+  const int32_t* items = info + 4 * (size_t)B;
+  const int32_t* recs = items + (size_t)pkv::kItemInts * p->sched_nitems;
+  const bool grouped = p->sched_ngroups > 0;
+  auto tiles = [&](int s) { return (ctx[s] + 15) / 16; };
+  std::map<std::tuple<int, int, int>, int> cov;
+  std::map<long, std::pair<int, int>> slot_owner;  // slot -> (g, s)
+  std::set<std::pair<int, int>> whole;
+  int errors = 0;
+  const long nparts = (long)nseg * K + W;
+  auto write_slot = [&](long slot, int g, int s) {
+    if (slot < 0 || slot >= nparts) { printf("slot %ld outside [0, %ld)\n", slot, nparts); ++errors; }
+    if (slot_owner.count(slot)) { printf("slot %ld written twice\n", slot); ++errors; }
+    slot_owner[slot] = {g, s};
+  };
+  for (int i = 0; i < p->sched_nitems; ++i) {
+    const int32_t* it = items + pkv::kItemInts * (size_t)i;
+    const int32_t* r = recs + pkv::kGroupInts * (size_t)it[0];
+    const int g = it[1], t0 = it[2], t1 = it[3], c = it[4], count = r[0], nch = r[2];
+    if (t1 - t0 < 1 || t1 - t0 > 32) { printf("item of %d tiles\n", t1 - t0); ++errors; }
+    for (int k = 0; k < count; ++k) {
+      const int s = r[3 + k];
+      if (info[4 * s + 3] != nch || info[4 * s] < t1) { printf("member info\n"); ++errors; }
+      for (int j = t0; j < t1; ++j) {
+        cov[{g, s, j}]++;
+        if (p->h_bt[(size_t)s * maxb + j * 16 / bs] != p->h_bt[(size_t)r[1] * maxb + j * 16 / bs]) {
+          printf("tile %d of member %d not the leader's block\n", j, s);
+          ++errors;
+        }
+        if (16 * (j + 1) > ctx[s] - 1) { printf("shared tile holds the newest row\n"); ++errors; }
+      }
+      const int seg = g * B + s;
+      write_slot((long)(seg + 1) * K - 1 + w0[seg] - nch + c, g, s);
+    }
+  }
+  for (int w = 0; w < W; ++w) {
+    const int32_t* d = desc + 8 * (size_t)w;
+    int x = d[0];
+    const int xend = d[1];
+    int s = d[2], g = d[3], j0 = d[4];
+    if (d[6] != p->h_bt[(size_t)s * maxb + j0 * 16 / bs]) { printf("first block\n"); ++errors; }
+    while (x < xend) {
+      const int take = std::min(xend - x, tiles(s) - j0);
+      if (take <= 0) { printf("empty run\n"); return 1; }
+      for (int j = j0; j < j0 + take; ++j) cov[{g, s, j}]++;
+      const int seg = g * B + s;
+      if (j0 == 0 && j0 + take == tiles(s)) whole.insert({g, s});
+      else write_slot((long)(seg + 1) * K - 1 + w, g, s);
+      x += take;
+      if (x >= xend) break;
+      if (++s == B) { s = 0; ++g; }
+      j0 = grouped ? info[4 * s] : 0;
+      if (grouped && info[4 * s + 1] != p->h_bt[(size_t)s * maxb + j0 * 16 / bs]) {
+        printf("info block\n");
+        ++errors;
+      }
+    }
+  }
+  for (int g = 0; g < H; ++g)
+    for (int s = 0; s < B; ++s) {
+      for (int j = 0; j < tiles(s); ++j)
+        if (cov[{g, s, j}] != 1) {
+          printf("tile (%d,%d,%d) covered %d\n", g, s, j, cov[{g, s, j}]);
+          return 1;
+        }
+      const int seg = g * B + s, npre = grouped ? info[4 * s + 3] : 0;
+      const bool merged = w0[seg] != w1[seg] || npre > 0;
+      std::set<long> want;
+      for (auto& kv : slot_owner)
+        if (kv.second == std::make_pair(g, s)) want.insert(kv.first);
+      if (!merged) {
+        if (!whole.count({g, s}) || !want.empty()) { printf("single-wave segment\n"); ++errors; }
+        continue;
+      }
+      if (whole.count({g, s})) { printf("merged segment written whole\n"); ++errors; }
+      std::set<long> got;
+      const long base = (long)(seg + 1) * K - 1;
+      for (long i = base + w0[seg] - npre; i <= base + w1[seg]; ++i) got.insert(i);
+      if (got != want) { printf("reduce range of (%d,%d) differs from its slots\n", g, s); ++errors; }
+    }
+  printf("ok groups: B=%d H=%d bs=%d gp=%d part=%d groups=%d items=%d stride=%d waves=%d errors=%d\n",
+         B, H, bs, gp, part, p->sched_ngroups, p->sched_nitems, K, W, errors);
+  return errors;
+}
+
+// Tables where runs of sequences share leading blocks (a common prompt of
+// `shared` tokens), then private blocks; lengths random.
+static void shared_tables(std::mt19937& rng, int B, int bs, int shared, int lo, int hi,
+                          std::vector<std::vector<int>>& tables, std::vector<int>& ctx,
+                          int prompts) {
+  std::uniform_int_distribution<int> u(lo, hi);
+  int next = 5000;
+  std::vector<std::vector<int>> prompt_blocks(prompts);
+  for (auto& pb : prompt_blocks)
+    for (int j = 0; j < shared / bs; ++j) pb.push_back(next++);
+  tables.assign(B, {});
+  ctx.assign(B, 0);
+  for (int s = 0; s < B; ++s) {
+    const int L = shared + u(rng);
+    ctx[s] = L;
+    tables[s] = prompt_blocks[s % prompts];
+    while ((int)tables[s].size() * bs < L) tables[s].push_back(next++);
+  }
+}
+
 int main() {
   std::mt19937 rng(1);
   int rc = 0;
@@ -120,6 +265,34 @@ int main() {
     std::vector<int> c(nb(rng)); for (auto& x : c) x = lb(rng);
     const int bs = t % 3 == 0 ? 8 : t % 3 == 1 ? 16 : 32;
     rc |= check(c, hb(rng), bb(rng), false, bs);
+  }
+  {
+    std::vector<std::vector<int>> t;
+    std::vector<int> c;
+    // 128 sequences of one 1024-token prompt: 32 groups of 4 (GQA 4)
+    shared_tables(rng, 128, 16, 1024, 1, 300, t, c, 1);
+    rc |= check_groups(t, c, 8, 16, 4, 0, 2048, 32);
+    rc |= check_groups(t, c, 8, 16, 4, 512, 0, 32);
+    rc |= check_groups(t, c, 8, 16, 1, 0, 2048, 8);   // 16 members per group
+    // three prompts interleaved, blocks of 8 and 32, GQA 2
+    for (int bs : {8, 32}) {
+      shared_tables(rng, 40, bs, 512, 1, 700, t, c, 3);
+      rc |= check_groups(t, c, 2, bs, 2, 0, 512, 6);
+      rc |= check_groups(t, c, 2, bs, 4, 256, 0, 10);
+    }
+    // a prompt shorter than the shared minimum: no groups
+    shared_tables(rng, 16, 16, 48, 1, 100, t, c, 1);
+    rc |= check_groups(t, c, 4, 16, 4, 0, 256, 0);
+    // random: prompts of random lengths, some sequences alone
+    for (int trial = 0; trial < 60; ++trial) {
+      std::uniform_int_distribution<int> nb(2, 70), pr(1, 5), sh(0, 40), hb(1, 4);
+      const int bs = trial % 3 == 0 ? 8 : trial % 3 == 1 ? 16 : 32;
+      const int B = nb(rng), prompts = pr(rng), H = hb(rng);
+      shared_tables(rng, B, bs, sh(rng) * 32, 1, 900, t, c, prompts);
+      const int gp = trial % 2 ? 4 : 2;
+      // expected group count is not fixed here: -1 skips that comparison
+      rc |= check_groups(t, c, H, bs, gp, trial % 4 == 0 ? 512 : 0, 64 + trial * 7, -1);
+    }
   }
   printf(rc ? "FAILED\n" : "ALL OK\n");
   return rc;

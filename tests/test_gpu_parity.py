@@ -92,6 +92,22 @@ SMALL = {
                              num_blocks=4 * 30, ctx_lo=16, ctx_hi=700, block_size=32),
     "bs32_shared_cow": W.scaled(W.CONFIGS["shared_prefix_cow_bf16"], batch=5, num_blocks=100,
                                 prefix_tokens=1000, block_size=32),
+    # a common prompt read once per group of sequences (the decode launch's
+    # shared-prefix items; 2-byte caches, head_dim 128): groups of 4 (GQA 4,
+    # 3 padded), 8 (GQA 2) and 16 (MHA) members with a smaller last group,
+    # blocks of 8 / 16 / 32, a prompt of 131 tiles (9 chunks)
+    "grp_bf16_g4": W.scaled(W.CONFIGS["shared_prefix_bf16"], batch=10, q_heads=16, kv_heads=4,
+                            prefix_tokens=200, suffix_hi=70, num_blocks=400),
+    "grp_f16_mha": W.scaled(W.CONFIGS["shared_prefix_bf16"], batch=20, q_heads=2, kv_heads=2,
+                            dtype=W.F16, prefix_tokens=130, suffix_hi=40, num_blocks=400),
+    "grp_bf16_g2_bs8": W.scaled(W.CONFIGS["shared_prefix_bf16"], batch=12, q_heads=4,
+                                kv_heads=2, prefix_tokens=160, suffix_hi=33, num_blocks=400,
+                                block_size=8),
+    "grp_f16_g3_bs32": W.scaled(W.CONFIGS["shared_prefix_bf16"], batch=9, q_heads=9,
+                                kv_heads=3, dtype=W.F16, prefix_tokens=300, suffix_hi=100,
+                                num_blocks=400, block_size=32),
+    "grp_bf16_long": W.scaled(W.CONFIGS["shared_prefix_bf16"], batch=6, prefix_tokens=2100,
+                              suffix_hi=300, num_blocks=400),
 }
 
 

@@ -1,5 +1,6 @@
-"""The bins decode schedule replayed on the CPU (no GPU): a C++ check built from
-the host source with the kernel launches stubbed (tests/cpp/schedule_check.cpp)."""
+"""The decode schedules replayed on the CPU (no GPU): a C++ check built from the
+host source with the kernel launches stubbed (tests/cpp/schedule_check.cpp) —
+the bins form, and the split form with shared-prefix groups."""
 import os
 import subprocess
 
@@ -17,3 +18,4 @@ def test_bins_schedule_covers_every_tile_once_and_merges_every_split(tmp_path):
     assert r.returncode == 0, r.stdout[-2000:]
     assert "ALL OK" in r.stdout
     assert r.stdout.count("ok: ") >= 50
+    assert r.stdout.count("ok groups: ") >= 40
