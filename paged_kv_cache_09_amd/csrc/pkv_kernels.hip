@@ -456,8 +456,9 @@ struct TileRegs<DT_Q4, D> {
 // head) leaves an unnormalised partial (max, sum, output) in the slot just
 // before its own private run's partials, where the reduce merges it. 2-byte
 // caches, head_dim 128: K pieces and V chunks are loaded as in decode_kernel;
-// P.V takes the weights as a high and a low part in the cache's 16-bit type
-// (bf16: 16 bits together, fp16: ~22; the weights are <= 2^kLazy).
+// P.V takes the weights in parts of the cache's 16-bit type (bf16: three, 24
+// bits together; fp16: a high and a low part, ~22 bits; the weights are
+// <= 2^kLazy).
 template <int DT, int GP, int BS>
 __device__ __forceinline__ void prefix_item(const DecodeParams& p, int item) {
   static_assert(DT == DT_F16 || DT == DT_BF16, "2-byte caches");
@@ -570,18 +571,24 @@ __device__ __forceinline__ void prefix_item(const DecodeParams& p, int item) {
     float pa[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) pa[i] = pl[(vr + 4 * i) * 16 + (lane & 15)];
-    u32x2 ahi, alo;
-    if constexpr (DT == DT_BF16) {  // truncated high part, then the rest truncated
-      unsigned hb[4], lb[4];
+    u32x2 ahi, alo, alo2;
+    if constexpr (DT == DT_BF16) {
+      // three truncated bf16 parts, each of what the ones before leave (exact
+      // fp32 differences): 24 bits together
+      unsigned hb[4], mb[4], lb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         hb[i] = __builtin_bit_cast(unsigned, pa[i]) & 0xffff0000u;
-        lb[i] = __builtin_bit_cast(unsigned, pa[i] - __builtin_bit_cast(float, hb[i]));
+        const float r1 = pa[i] - __builtin_bit_cast(float, hb[i]);
+        mb[i] = __builtin_bit_cast(unsigned, r1) & 0xffff0000u;
+        lb[i] = __builtin_bit_cast(unsigned, r1 - __builtin_bit_cast(float, mb[i]));
       }
       ahi = u32x2{__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u),
                   __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u)};
-      alo = u32x2{__builtin_amdgcn_perm(lb[1], lb[0], 0x07060302u),
-                  __builtin_amdgcn_perm(lb[3], lb[2], 0x07060302u)};
+      alo = u32x2{__builtin_amdgcn_perm(mb[1], mb[0], 0x07060302u),
+                  __builtin_amdgcn_perm(mb[3], mb[2], 0x07060302u)};
+      alo2 = u32x2{__builtin_amdgcn_perm(lb[1], lb[0], 0x07060302u),
+                   __builtin_amdgcn_perm(lb[3], lb[2], 0x07060302u)};
     } else {
       const f16x2 h01 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(pa[0], pa[1]));
       const f16x2 h23 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(pa[2], pa[3]));
@@ -601,6 +608,10 @@ __device__ __forceinline__ void prefix_item(const DecodeParams& p, int item) {
     }
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[nt] = pv_mfma<DT>(alo, bv[nt], acc[nt]);
+    if constexpr (DT == DT_BF16) {
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) acc[nt] = pv_mfma<DT>(alo2, bv[nt], acc[nt]);
+    }
   };
 
   TR t[2];

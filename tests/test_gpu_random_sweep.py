@@ -5,7 +5,10 @@ block size, batch, length mix (uniform lengths, or a shared prompt with short
 private suffixes, which brings copy-on-write) and value scale — then runs one
 full step (slot assignment, upload, copy-on-write, append, decode at several
 split sizes) through the C ABI against the fp64 oracle, unfused and fused on
-alternate seeds. The cases are small enough to compare every sequence.
+alternate seeds. The cases are small enough to compare every sequence. A
+second sweep draws shared prompts long enough (>= 64 tokens) for the decode to
+read them once per group of sequences (2-byte caches, head_dim 128, <= 4 q
+heads per kv head).
 """
 import numpy as np
 import pytest
@@ -52,6 +55,36 @@ def test_random_config_step_parity(seed):
              f"{cfg.q_heads}/{cfg.kv_heads} bs{cfg.block_size} B{cfg.batch} {cfg.ctx_kind}")
     errs, _, _ = run_step_case(cfg, layers=1, partitions=(0, 32, 1 << 20), label=label,
                                fused=seed % 2 == 1)
+    tol = tolerance(cfg)
+    for key, e in errs.items():
+        assert e <= tol, f"{label} {key}: max abs error {e} > {tol}"
+
+
+def random_shared_config(seed: int) -> W.Config:
+    rng = np.random.default_rng(9000 + seed)
+    dtype = (W.BF16, W.F16)[seed % 2]
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 3, 4]))
+    bs = int(rng.choice([8, 16, 32]))
+    B = int(rng.integers(2, 25))
+    prefix = int(rng.integers(64, 900))
+    suffix_hi = int(rng.integers(0, 200))
+    nb = (prefix + bs - 1) // bs + B * ((suffix_hi + 1) // bs + 3) + 4
+    return W.Config(f"shared_sweep{seed}", 200 + seed, B, G * Hkv, Hkv, 128, dtype,
+                    float(rng.choice([0.5, 1.0, 2.0])), nb, 1, "shared_prefix",
+                    prefix_tokens=prefix, suffix_hi=suffix_hi, block_size=bs)
+
+
+SHARED_SEEDS = list(range(12))
+
+
+@pytest.mark.parametrize("seed", SHARED_SEEDS)
+def test_random_shared_prompt_parity(seed):
+    cfg = random_shared_config(seed)
+    label = (f"shared sweep {seed}: {W.DTYPE_NAME[cfg.dtype]} {cfg.q_heads}/{cfg.kv_heads} "
+             f"bs{cfg.block_size} B{cfg.batch} prompt {cfg.prefix_tokens}")
+    errs, _, _ = run_step_case(cfg, layers=1, partitions=(0, 48, 1 << 20), label=label,
+                               fused=seed % 2 == 0)
     tol = tolerance(cfg)
     for key, e in errs.items():
         assert e <= tol, f"{label} {key}: max abs error {e} > {tol}"
