@@ -1,12 +1,17 @@
 // HIP kernels for paged KV-cache decode on MI355X (gfx950, wave64).
 //
-//  decode_kernel  — per wavefront: a contiguous run of (kv head, sequence,
-//                   block) tiles; gathers 16 x head_dim K and V tiles through
-//                   the block table with wide per-lane loads, computes q.K^T for all
-//                   query heads of the GQA group sharing the kv head, keeps an
-//                   fp32 online softmax and accumulates P.V. A run that covers a
+//  decode_kernel  — per wavefront: a run of (kv head, sequence, block) tiles;
+//                   gathers 16 x head_dim K and V tiles through the block table
+//                   with wide per-lane loads, computes q.K^T for all query
+//                   heads of the GQA group sharing the kv head, keeps an fp32
+//                   online softmax and accumulates P.V. A run that covers a
 //                   whole (kv head, sequence) writes the normalised output;
-//                   otherwise it writes an unnormalised partial (max, sum, o).
+//                   otherwise it leaves an unnormalised partial (max, sum, o)
+//                   in HBM (split form) or in LDS for another wave of its
+//                   eight-wave workgroup (bins form). In the split form the
+//                   first workgroups can be shared-prefix items: a prompt
+//                   several sequences share through their tables, read once
+//                   per group of them.
 //  reduce_kernel  — merges the partials of one (sequence, q head):
 //                   out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
 //                   (A merge by the last-finishing wavefront would save this
@@ -30,8 +35,9 @@
 // GQA paragraph). Decode is bound by memory bandwidth (ssdnodes.com, same
 // page, "What the KV cache holds"), so every tile is read exactly once, with
 // wide lanes (16 bytes for 2- and 4-byte elements and q4_0, 8 for q8_0 codes);
-// q.K^T of the GQA group runs on 16x16 MFMA tiles, the softmax and P.V on the
-// fp32 VALU.
+// q.K^T of the GQA group runs on 16x16 MFMA tiles, the softmax on the fp32
+// VALU, and P.V on the fp32 VALU or, where it bounds the loop (q4_0) or serves
+// 16 rows (shared-prefix items), on MFMA with the weights in 16-bit parts.
 #include "pkv_internal.h"
 
 namespace pkv {
