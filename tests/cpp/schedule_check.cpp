@@ -131,6 +131,8 @@ static int check_groups(const std::vector<std::vector<int>>& tables, const std::
   for (int s = 0; s < B; ++s)
     for (size_t j = 0; j < tables[s].size(); ++j) p->h_bt[(size_t)s * maxb + j] = tables[s][j];
   p->sched_gp_building = gp;
+  p->num_cus = 256;
+  p->shape.max_seq_len = *std::max_element(ctx.begin(), ctx.end());
   build_schedule(p, part, target);
   if (p->sched_bins) {  // no groups: the bins form (checked above) is allowed
     if (expect_groups > 0) { printf("groups: bins form chosen\n"); return 1; }
@@ -224,6 +226,12 @@ static int check_groups(const std::vector<std::vector<int>>& tables, const std::
       for (long i = base + w0[seg] - npre; i <= base + w1[seg]; ++i) got.insert(i);
       if (got != want) { printf("reduce range of (%d,%d) differs from its slots\n", g, s); ++errors; }
     }
+  // the workspace the caller sizes with pkv_decode_workspace_bytes holds them
+  if (target <= 256 * 32) {
+    const size_t need = (size_t)nparts * gp * (128 + 2) * sizeof(float);
+    const size_t bound = pkv_decode_workspace_bytes(p, B, H * gp, part);
+    if (need > bound) { printf("workspace %zu > bound %zu\n", need, bound); ++errors; }
+  }
   printf("ok groups: B=%d H=%d bs=%d gp=%d part=%d groups=%d items=%d stride=%d waves=%d errors=%d\n",
          B, H, bs, gp, part, p->sched_ngroups, p->sched_nitems, K, W, errors);
   return errors;
