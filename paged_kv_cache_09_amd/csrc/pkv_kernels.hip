@@ -36,8 +36,9 @@
 // page, "What the KV cache holds"), so every tile is read exactly once, with
 // wide lanes (16 bytes for 2- and 4-byte elements and q4_0, 8 for q8_0 codes);
 // q.K^T of the GQA group runs on 16x16 MFMA tiles, the softmax on the fp32
-// VALU, and P.V on the fp32 VALU or, where it bounds the loop (q4_0) or serves
-// 16 rows (shared-prefix items), on MFMA with the weights in 16-bit parts.
+// VALU, and P.V on the fp32 VALU or, where it bounds the loop (q4_0, q8_0) or
+// serves 16 rows (shared-prefix items), on MFMA with the weights in 16-bit
+// parts (quantised codes as exact fp16 subnormals).
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -98,6 +99,21 @@ __device__ __forceinline__ u32x4 codes_to_bf16(u32x2 c) {
   r[1] = bf16_pair(sbyte(w0, 2), sbyte(w0, 3));
   r[2] = bf16_pair(sbyte(w1, 0), sbyte(w1, 1));
   r[3] = bf16_pair(sbyte(w1, 2), sbyte(w1, 3));
+  return r;
+}
+
+// 8 int8 codes -> the 8 values (128 + code) x 2^-24 as fp16, in natural order,
+// an MFMA operand: 128 + code is the code's byte with its top bit flipped, and
+// as fp16 bits over a zero high byte it is that many units of the smallest
+// subnormal, exactly (the MFMA keeps subnormal inputs). The 128 is taken off
+// through the MFMA's accumulator input.
+__device__ __forceinline__ u32x4 codes_to_f16_128(u32x2 c) {
+  const unsigned w0 = c[0] ^ 0x80808080u, w1 = c[1] ^ 0x80808080u;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_perm(0u, w0, 0x0c010c00u);  // (w0.b0, 0, w0.b1, 0)
+  r[1] = __builtin_amdgcn_perm(0u, w0, 0x0c030c02u);
+  r[2] = __builtin_amdgcn_perm(0u, w1, 0x0c010c00u);
+  r[3] = __builtin_amdgcn_perm(0u, w1, 0x0c030c02u);
   return r;
 }
 
@@ -690,8 +706,10 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
   constexpr int NBUF = 2;
   static_assert(RB % 32 == 0 && CPR <= 64 && GP <= 16, "shape");
   static_assert(!Q4 || (NV == NP && BS % NV == 0), "q4_0 tile layout");
-  // q4_0 at head_dim 128 with up to 4 heads per group: P.V on MFMA (compute_tile).
-  constexpr bool MPV = Q4 && D == 128 && GP <= 4;
+  // q4_0 and q8_0 at head_dim 128 with up to 4 heads per group: P.V on MFMA
+  // (compute_tile); q8_0 there also takes q.K on fp16 MFMAs (Q8M).
+  constexpr bool MPV = QN && D == 128 && GP <= 4;
+  constexpr bool Q8M = Q8 && MPV;
   static_assert(!MPV || (CPR == 16 && NV == 4 && EPC == 8), "MFMA P.V lane layout");
 
   constexpr int NW = BINS ? 8 : 1;       // waves per workgroup
@@ -912,10 +930,45 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         qv[k] = t16 < p.group ? v : u32x4{0u, 0u, 0u, 0u};
       }
     }
+    // smul[i]: log2(e) x scale, times what turns score row i's MFMA result
+    // into q . K (q8_0: the head's 2^(24 - qsh)).
+    float smul[HPG];
+#pragma unroll
+    for (int i = 0; i < HPG; ++i) smul[i] = p.scale_log2;
+    if constexpr (Q8M) {
+      // q as fp16 for the MFMA against fp16 codes, each head scaled by 2^qsh
+      // so that its largest |q| lies in [2^14, 2^15): no overflow, and bf16's
+      // 8 significant bits are kept. Lanes t16, t16 + 16, +32, +48 hold head
+      // t16's pieces.
+      float qf[NP][8];
+      float mx = 0.f;
+#pragma unroll
+      for (int k = 0; k < NP; ++k) {
+        to_f32<DT_BF16>(qv[k], qf[k]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, __builtin_fabsf(qf[k][e]));
+      }
+      mx = fmaxf(mx, xor_f(mx, 16));
+      mx = fmaxf(mx, xor_f(mx, 32));
+      // mx = f 2^x with f in [0.5, 1) (x = 0 for 0); kept to a range where the
+      // factors below stay finite
+      const int qsh = min(100, max(-100, 15 - __builtin_amdgcn_frexp_expf(mx)));
+      const float f = __builtin_amdgcn_ldexpf(1.f, qsh);
+#pragma unroll
+      for (int k = 0; k < NP; ++k)
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          qv[k][w] = __builtin_bit_cast(
+              unsigned, __builtin_amdgcn_cvt_pkrtz(qf[k][2 * w] * f, qf[k][2 * w + 1] * f));
+#pragma unroll
+      for (int i = 0; i < HPG; ++i)
+        smul[i] = p.scale_log2 * __builtin_amdgcn_ldexpf(1.f, 24 - __shfl(qsh, 4 * kg + i, 64));
+    }
     // q4_0: -136 times each q piece's sum over its group (an MFMA against
     // ones), the accumulator input that turns q . (128 + code) into
-    // q . (code - 8).
-    f32x4 qb[Q4 ? NP : 1];
+    // q . (code - 8); q8_0: -128 x 2^-24 times it, for q . (128 + code) x
+    // 2^-24 into q . code x 2^-24.
+    f32x4 qb[QN ? NP : 1];
     if constexpr (Q4) {
       const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
 #pragma unroll
@@ -923,6 +976,14 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         const f32x4 sq = qk_piece<DT_BF16>(qv[k], ones, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int i = 0; i < 4; ++i) qb[k][i] = -136.f * sq[i];
+      }
+    } else if constexpr (Q8M) {
+      const u32x4 ones = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};
+#pragma unroll
+      for (int k = 0; k < NP; ++k) {
+        const f32x4 sq = qk_piece<DT_F16>(qv[k], ones, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qb[k][i] = -0x1p-17f * sq[i];
       }
     }
 
@@ -957,6 +1018,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         for (int k = 0; k < NP; ++k) {
           f32x4 r;
           if constexpr (Q4) r = qk_piece<DT_BF16>(qv[k], nibbles_to_bf16_128(t.k[k]), qb[k]);
+          else if constexpr (Q8M) r = qk_piece<DT_F16>(qv[k], codes_to_f16_128(t.k[k]), qb[k]);
           else r = qk_piece<DT_BF16>(qv[k], codes_to_bf16(t.k[k]), f32x4{0.f, 0.f, 0.f, 0.f});
           const float dk = (k & 1) ? half_hi(t.ks[k >> 1]) : half_lo(t.ks[k >> 1]);
 #pragma unroll
@@ -982,7 +1044,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       }
 #pragma unroll
       for (int i = 0; i < HPG; ++i) {
-        s2[i] = t16 < valid ? sacc[i] * p.scale_log2 : -__builtin_inff();
+        s2[i] = t16 < valid ? sacc[i] * smul[i] : -__builtin_inff();
         over |= head_lane && s2[i] > m[i] + lz;
       }
       if (__any(over)) {  // raise the running maxima to this tile's
@@ -1057,24 +1119,43 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
                           (_Float16)(pa[0] - (float)h01[0]), (_Float16)(pa[1] - (float)h01[1]),
                           (_Float16)(pa[2] - (float)h23[0]), (_Float16)(pa[3] - (float)h23[1])};
         const f16x4 ahi = {av[0], av[1], av[2], av[3]}, alo = {av[4], av[5], av[6], av[7]};
-        unsigned ev[4], od[4];  // even codes (low nibbles), odd codes x 16 (high nibbles)
         accs = __builtin_amdgcn_mfma_f32_16x16x32_f16(
             av, __builtin_bit_cast(f16x8, u32x4{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u}),
             accs, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ev[i] = t.v[i] & 0x0f0f0f0fu;
-          od[i] = t.v[i] & 0xf0f0f0f0u;
-        }
         f16x4 bv[8];
+        if constexpr (Q8) {
+          // 128 + code (the top bit flipped) of the 4 rows' chunks; column
+          // 8 * n + nt is byte nt & 3 of word nt >> 2
+          unsigned x[4][2];
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          const unsigned* src = (nt & 1) ? od : ev;
-          // byte nt / 2 of rows 0, 1 (and 2, 3) into the low bytes of the two fp16 halves
-          const unsigned sel = 0x0c000c00u | ((4u + (nt >> 1)) << 16) | (unsigned)(nt >> 1);
-          bv[nt] = __builtin_bit_cast(f16x4, u32x2{__builtin_amdgcn_perm(src[1], src[0], sel),
-                                                   __builtin_amdgcn_perm(src[3], src[2], sel)});
-          accm[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bv[nt], accm[nt], 0, 0, 0);
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int w = 0; w < 2; ++w) x[i][w] = t.v[i][w] ^ 0x80808080u;
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) {
+            const int w = nt >> 2;
+            const unsigned b = nt & 3;
+            const unsigned sel = 0x0c000c00u | ((4u + b) << 16) | b;
+            bv[nt] = __builtin_bit_cast(f16x4, u32x2{__builtin_amdgcn_perm(x[1][w], x[0][w], sel),
+                                                     __builtin_amdgcn_perm(x[3][w], x[2][w], sel)});
+            accm[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bv[nt], accm[nt], 0, 0, 0);
+          }
+        } else {
+          unsigned ev[4], od[4];  // even codes (low nibbles), odd codes x 16 (high nibbles)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            ev[i] = t.v[i] & 0x0f0f0f0fu;
+            od[i] = t.v[i] & 0xf0f0f0f0u;
+          }
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) {
+            const unsigned* src = (nt & 1) ? od : ev;
+            // byte nt / 2 of rows 0, 1 (and 2, 3) into the low bytes of the two fp16 halves
+            const unsigned sel = 0x0c000c00u | ((4u + (nt >> 1)) << 16) | (unsigned)(nt >> 1);
+            bv[nt] = __builtin_bit_cast(f16x4, u32x2{__builtin_amdgcn_perm(src[1], src[0], sel),
+                                                     __builtin_amdgcn_perm(src[3], src[2], sel)});
+            accm[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bv[nt], accm[nt], 0, 0, 0);
+          }
         }
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt)
@@ -1295,13 +1376,15 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
 #pragma unroll
     for (int i = 0; i < HPG; ++i) lt[i] = row_sum(lsum[i]);
     if constexpr (MPV) {
-      // the MFMA summed over the tile's rows: sum A x code x 2^-24 (odd
-      // columns 2^-20), less 8 x sum A
+      // the MFMA summed over the tile's rows: sum A x code x 2^-24 (q4_0's
+      // odd columns 2^-20), less 8 x sum A (q8_0: 128 + code, less 128 x sum A)
 #pragma unroll
       for (int h = 0; h < GP; ++h)
 #pragma unroll
         for (int e = 0; e < EPC; ++e)
-          acc[h][e] = __builtin_fmaf(accm[e][h], (e & 1) ? 1048576.f : 16777216.f, -8.f * accs[h]);
+          acc[h][e] = Q8 ? __builtin_fmaf(accm[e][h], 16777216.f, -128.f * accs[h])
+                         : __builtin_fmaf(accm[e][h], (e & 1) ? 1048576.f : 16777216.f,
+                                          -8.f * accs[h]);
     } else {
       if constexpr (Q4) {  // sum_t w_t (code_t - 8) = sum_t w_t code_t - 8 sum_t w_t
 #pragma unroll

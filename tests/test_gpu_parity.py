@@ -284,16 +284,19 @@ def _scale_v_scales(factor_log2):
 
 @pytest.mark.parametrize("fused", [False, True], ids=["append+decode", "fused"])
 @pytest.mark.parametrize("group", [4, 2])
-def test_q4_large_v_scales(group, fused):
-    """V scales up to ~39,000 in half of the blocks (q4_0, head_dim 128): weight
-    x scale must stay finite wherever the decode forms it in fp16. The
-    tolerance is the quantised one scaled by the same 2^17."""
-    cfg = W.scaled(W.CONFIGS["llama8b_q4"], batch=6, q_heads=2 * group, kv_heads=2,
+@pytest.mark.parametrize("base", ["llama8b_q4", "llama8b_q8"])
+def test_large_v_scales(base, group, fused):
+    """V scales multiplied by 2^17 in half of the blocks (q4_0: up to ~39,000;
+    q8_0: a few thousand; head_dim 128): weight x scale must stay finite
+    wherever the decode forms it in fp16. The tolerance is the quantised one
+    scaled by the same 2^17."""
+    cfg = W.scaled(W.CONFIGS[base], batch=6, q_heads=2 * group, kv_heads=2,
                    num_blocks=6 * 40, ctx_lo=1, ctx_hi=600)
-    errs, _, _ = run_step_case(cfg, layers=1, partitions=(0, 32), label=f"q4 big scales g{group}",
-                               fused=fused, edit=_scale_v_scales(17))
+    errs, _, _ = run_step_case(cfg, layers=1, partitions=(0, 32),
+                               label=f"{base} big scales g{group}", fused=fused,
+                               edit=_scale_v_scales(17))
     for key, e in errs.items():
-        assert e <= tolerance(cfg) * 2.0 ** 17, f"q4 large V scales {key}: max abs error {e}"
+        assert e <= tolerance(cfg) * 2.0 ** 17, f"{base} large V scales {key}: max abs error {e}"
 
 
 def _decode_form(cfg, device="cuda"):
