@@ -25,10 +25,12 @@ bool prefix_supported(int dtype, int head_dim, int gp) {
 
 }
 
-static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins, int bs = 16) {
+static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins, int bs = 16,
+                 int dtype = PKV_BF16) {
   pkv_pool P;
   pkv_pool* p = &P;
   p->shape.kv_heads = H;
+  p->shape.dtype = dtype;
   p->shape.block_size = bs;
   const int B = ctx.size();
   p->up_batch = B;
@@ -268,11 +270,15 @@ int main() {
     std::vector<int> c(64); std::uniform_int_distribution<int> u(128, 2048); for (auto& x : c) x = u(rng);
     rc |= check(c, 8, 256, true, bs);
   }
+  for (int dt : {PKV_Q8_0, PKV_Q4_0}) {  // waves 0..3 take a larger share of each bin
+    std::vector<int> c(64); std::uniform_int_distribution<int> u(128, 2048); for (auto& x : c) x = u(rng);
+    rc |= check(c, 8, 256, true, 16, dt);
+  }
   for (int t = 0; t < 300; ++t) {
     std::uniform_int_distribution<int> nb(1, 64), lb(1, 3000), hb(1, 8), bb(1, 64);
     std::vector<int> c(nb(rng)); for (auto& x : c) x = lb(rng);
     const int bs = t % 3 == 0 ? 8 : t % 3 == 1 ? 16 : 32;
-    rc |= check(c, hb(rng), bb(rng), false, bs);
+    rc |= check(c, hb(rng), bb(rng), false, bs, t % 4 == 0 ? PKV_Q8_0 : t % 4 == 1 ? PKV_Q4_0 : PKV_BF16);
   }
   {
     std::vector<std::vector<int>> t;
