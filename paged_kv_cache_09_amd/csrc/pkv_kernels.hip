@@ -837,6 +837,27 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         reinterpret_cast<const char*>(p.v_new) + ((size_t)s * p.kv_heads + g) * QB;
     const int Lc = L - (app ? 1 : 0);         // rows already in the pool
     const int j1c = min(j1, (Lc + 15) >> 4);  // tiles holding cached rows
+    // q4_0 (groups of up to 4 heads): the run that ends the sequence requests
+    // the new row now, beside the block-table entries, and appends it once
+    // the first tile is on its way. Fetched and quantised at the end of the
+    // run, it put a memory round trip (behind the run's own tile traffic) and
+    // the quantising on the wave's critical path: 26 % of an 8B-shaped q4_0
+    // layer, 12 % this way. The other caches keep the late form, which
+    // measured faster for them (bf16 by 0.6 us, q8_0 by 1-1.5 us per layer:
+    // the registers held early cost their loops more).
+    constexpr bool EARLY_NEW = Q4 && GP <= 4;
+    const bool app_here = app && j1 == nblk;
+    u32x4 nk[NP], nv = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < NP; ++k) nk[k] = u32x4{0u, 0u, 0u, 0u};
+    if (EARLY_NEW && app_here) {
+#pragma unroll
+      for (int k = 0; k < NP; ++k) nk[k] = ld16(kn_row + kg * 16 + k * 64);
+      nv = ld16(vn_row + vc * 16);
+    }
+    // the lane's K piece k and V chunk of the new row: requested early, or now
+    auto new_k = [&](int k) { return EARLY_NEW ? nk[k] : ld16(kn_row + kg * 16 + k * 64); };
+    auto new_v = [&]() { return EARLY_NEW ? nv : ld16(vn_row + vc * 16); };
 
     // Load tile rows 0..15 (tokens 16*j .. 16*j+15 of the sequence): block a
     // holds them (BS = 16), or rows 16*half .. of it (BS = 32), or rows 0..7
@@ -1196,59 +1217,13 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     // at a time (the tiles of 64 entries: 64, 128 or 32 of them).
     constexpr int CH = BS == 8 ? 32 : 64;  // tiles per chunk of entries
     const int nent_seq = (L + BS - 1) / BS;
-    for (int jb = j0; jb < j1c; jb += CH) {
-      const int nb = min(CH, j1c - jb);
-      const int e0 = BS == 32 ? (jb >> 1) : BS == 8 ? 2 * jb : jb;
-      TR t[NBUF];
-      // Block-table entries first, one per lane (up to 64: CH tiles need CH
-      // (16), 2 * CH = 64 (8) or CH / 2 + 1 (32)), then the first tile, whose
-      // id(s) the descriptor holds for the run's first chunk: the first wait
-      // for the entries then leaves that tile's loads in flight.
-      const int my_ent = e0 + lane < nent_seq ? bt_row[e0 + lane] : 0;
-      // block ids of chunk tile j: (a, b, half)
-      auto tile_ids = [&](int j, int& a, int& b, int& half) {
-        if constexpr (BS == 16) {
-          a = b = __builtin_amdgcn_readlane(my_ent, j);
-          half = 0;
-        } else if constexpr (BS == 32) {
-          a = b = __builtin_amdgcn_readlane(my_ent, ((jb + j) >> 1) - (jb >> 1));
-          half = (jb + j) & 1;
-        } else {
-          a = __builtin_amdgcn_readlane(my_ent, 2 * j);
-          b = __builtin_amdgcn_readlane(my_ent, 2 * j + 1);
-          half = 0;
-        }
-      };
-      auto load_j = [&](int j, TR& t) {
-        int a, b, half;
-        tile_ids(j, a, b, half);
-        load_tile(a, b, half, t);
-      };
-      if (jb == j0) load_tile(blk_first, BS == 8 ? blk_second : 0, BS == 32 ? (jb & 1) : 0, t[0]);
-      else load_j(0, t[0]);
-#pragma unroll
-      for (int u = 1; u < NBUF - 1; ++u) load_j(min(u, nb - 1), t[u]);
-      // Every step requests a tile, the chunk's last one again once the chunk
-      // is exhausted (a repeat the cache serves): with no conditional loads
-      // the compiler's wait counts stay static and only the tile about to be
-      // computed is waited for, never the one just requested.
-      for (int jj = 0; jj < nb; jj += NBUF) {
-#pragma unroll
-        for (int u = 0; u < NBUF; ++u) {
-          const int j = jj + u;
-          if (j < nb) {
-            load_j(min(j + NBUF - 1, nb - 1), t[(u + NBUF - 1) % NBUF]);
-            // keep the scheduler from hoisting the compute (and its waits) above
-            // the request
-            __builtin_amdgcn_sched_barrier(0);
-            compute_tile(min(16, Lc - 16 * (jb + j)), t[u]);
-          }
-        }
-      }
-    }
-    if (app && j1 == nblk) {
-      // The new token: every lane loads the k_new / v_new row as row 0 of a
-      // one-row tile; the lanes of row 0 store it into the pool.
+    // The new token: every lane takes the k_new / v_new row as row 0 of a
+    // one-row tile (quantised in registers for q8_0 / q4_0, as the append
+    // kernels do), the lanes of row 0 store it into the pool, and the tile is
+    // attended. With the row requested early this runs at the start of the
+    // run, while the first tile's loads are in flight (the pool row it writes
+    // is masked out of that run's own last tile, and no other run reads it).
+    auto append_new_row = [&]() {
       const int blk_last = bt_row[(L - 1) / BS];
       const int t_new = (L - 1) % BS;  // the new row inside its block
       char* ktile = const_cast<char*>(kbase) + (size_t)blk_last * blk_stride;
@@ -1260,7 +1235,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
 #pragma unroll
         for (int k = 0; k < NP; ++k) {
           float x[8];
-          to_f32<DT_BF16>(ld16(kn_row + kg * 16 + k * 64), x);
+          to_f32<DT_BF16>(new_k(k), x);
           float a, mv;
           int idx;
           q4_pick(x, 8 * kg, a, mv, idx);
@@ -1274,7 +1249,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         }
         {
           float x[8];
-          to_f32<DT_BF16>(ld16(vn_row + vc * 16), x);
+          to_f32<DT_BF16>(new_v(), x);
           float a, mv;
           int idx;
           q4_pick(x, 8 * (vc & 3), a, mv, idx);
@@ -1312,7 +1287,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
 #pragma unroll
         for (int k = 0; k < NP; ++k) {
           float x[8];
-          to_f32<DT_BF16>(ld16(kn_row + kg * 16 + k * 64), x);
+          to_f32<DT_BF16>(new_k(k), x);
           float a = 0.f;
 #pragma unroll
           for (int j = 0; j < 8; ++j) a = fmaxf(a, __builtin_fabsf(x[j]));
@@ -1326,7 +1301,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         }
         {
           float x[8];
-          to_f32<DT_BF16>(ld16(vn_row + vc * 16), x);
+          to_f32<DT_BF16>(new_v(), x);
           float a = 0.f;
 #pragma unroll
           for (int j = 0; j < 8; ++j) a = fmaxf(a, __builtin_fabsf(x[j]));
@@ -1358,9 +1333,9 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         }
       } else {
 #pragma unroll
-        for (int k = 0; k < NP; ++k) tn.k[k] = ld16(kn_row + kg * 16 + k * 64);
+        for (int k = 0; k < NP; ++k) tn.k[k] = new_k(k);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) tn.v[i] = ld16(vn_row + vc * 16);
+        for (int i = 0; i < NV; ++i) tn.v[i] = new_v();
         if (t16 == 0) {
 #pragma unroll
           for (int k = 0; k < NP; ++k)
@@ -1369,7 +1344,66 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         if (vr == 0) *reinterpret_cast<u32x4*>(vtile + t_new * RB + vc * 16) = tn.v[0];
       }
       compute_tile(1, tn);
+    };
+    TR t[NBUF];
+    int jb = j0, nb = 0, my_ent = 0;
+    // block ids of chunk tile j: (a, b, half)
+    auto tile_ids = [&](int j, int& a, int& b, int& half) {
+      if constexpr (BS == 16) {
+        a = b = __builtin_amdgcn_readlane(my_ent, j);
+        half = 0;
+      } else if constexpr (BS == 32) {
+        a = b = __builtin_amdgcn_readlane(my_ent, ((jb + j) >> 1) - (jb >> 1));
+        half = (jb + j) & 1;
+      } else {
+        a = __builtin_amdgcn_readlane(my_ent, 2 * j);
+        b = __builtin_amdgcn_readlane(my_ent, 2 * j + 1);
+        half = 0;
+      }
+    };
+    auto load_j = [&](int j, TR& t) {
+      int a, b, half;
+      tile_ids(j, a, b, half);
+      load_tile(a, b, half, t);
+    };
+    // Block-table entries first, one per lane (up to 64: CH tiles need CH
+    // (16), 2 * CH = 64 (8) or CH / 2 + 1 (32)), then the first tile, whose
+    // id(s) the descriptor holds for the run's first chunk: the first wait
+    // for the entries then leaves that tile's loads in flight.
+    auto start_chunk = [&]() {
+      nb = min(CH, j1c - jb);
+      const int e0 = BS == 32 ? (jb >> 1) : BS == 8 ? 2 * jb : jb;
+      my_ent = e0 + lane < nent_seq ? bt_row[e0 + lane] : 0;
+      if (jb == j0) load_tile(blk_first, BS == 8 ? blk_second : 0, BS == 32 ? (jb & 1) : 0, t[0]);
+      else load_j(0, t[0]);
+#pragma unroll
+      for (int u = 1; u < NBUF - 1; ++u) load_j(min(u, nb - 1), t[u]);
+    };
+    if constexpr (EARLY_NEW) {
+      if (jb < j1c) start_chunk();
+      if (app_here) append_new_row();
     }
+    for (; jb < j1c; jb += CH) {
+      if (!EARLY_NEW || jb != j0) start_chunk();
+      // Every step requests a tile, the chunk's last one again once the chunk
+      // is exhausted (a repeat the cache serves): with no conditional loads
+      // the compiler's wait counts stay static and only the tile about to be
+      // computed is waited for, never the one just requested.
+      for (int jj = 0; jj < nb; jj += NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+          const int j = jj + u;
+          if (j < nb) {
+            load_j(min(j + NBUF - 1, nb - 1), t[(u + NBUF - 1) % NBUF]);
+            // keep the scheduler from hoisting the compute (and its waits) above
+            // the request
+            __builtin_amdgcn_sched_barrier(0);
+            compute_tile(min(16, Lc - 16 * (jb + j)), t[u]);
+          }
+        }
+      }
+    }
+    if (!EARLY_NEW && app_here) append_new_row();
 
     // Totals over the 16 rows, and over the lanes sharing a V chunk.
     float lt[HPG];
