@@ -71,6 +71,8 @@ int check_shape(const pkv_shape* sh) {
     return fail(PKV_EUNSUPPORTED, "head_dim %d is not supported (64 or 128)", sh->head_dim);
   if ((int64_t)sh->num_blocks * sh->block_size > INT32_MAX)
     return fail(PKV_EUNSUPPORTED, "num_blocks * block_size must fit in int32");
+  if (sh->max_seq_len >= (1 << 30))
+    return fail(PKV_EUNSUPPORTED, "max_seq_len must be below 2^30");
   return PKV_OK;
 }
 
@@ -141,6 +143,7 @@ struct pkv_pool {
   int up_stride = 0;
   uint64_t up_gen = 0;
   std::vector<int32_t> h_ctx;
+  std::vector<int32_t> h_slotflag;  // per sequence: 1 << 30 when its uploaded slot is >= 0
   std::vector<int32_t> h_cum;
   std::vector<int32_t> h_bt;  // uploaded table (for per-wave descriptors)
 
@@ -486,7 +489,7 @@ void build_schedule(pkv_pool* p, int part, int target) {
     d[2] = s;
     d[3] = g;
     d[4] = (int32_t)j0;
-    d[5] = p->h_ctx[s];
+    d[5] = p->h_ctx[s] | p->h_slotflag[s];
     // the first tile's block(s): rows 8..15 of 8-token blocks in d[7]
     tile_blocks(p, s, j0, d[6], d[7]);
   }
@@ -549,6 +552,75 @@ constexpr int kBinWaves = 8;
 //   its first segment started in an earlier wave wa of the bin and ends in
 //   this one; bits 0-7 wa, bit 8 the LDS slot of wa's piece.
 //   seglist per listed segment: sequence, kv head, length, first block id.
+// Relative speed of the eight waves of a bin: waves 0-3 and 4-7 share the
+// four SIMDs, and the older wave of each pair wins issue arbitration.
+#ifndef PKV_SLOT_SKEW
+#define PKV_SLOT_SKEW 8
+#endif
+// Cost, in tiles, of a segment switch inside a bin wave's run, and of the
+// fused append at the end of a segment.
+#ifndef PKV_BIN_SWITCH_COST
+#define PKV_BIN_SWITCH_COST 4
+#endif
+#ifndef PKV_BIN_APPEND_COST
+#define PKV_BIN_APPEND_COST 0
+#endif
+constexpr double kBinSwitchCost = PKV_BIN_SWITCH_COST;
+constexpr double kBinAppendCost = PKV_BIN_APPEND_COST;
+double slot_capacity(int v) {
+  return v < kBinWaves / 2 ? 1.0 + PKV_SLOT_SKEW / 200.0 : 1.0 - PKV_SLOT_SKEW / 200.0;
+}
+
+// Cut a bin's segments (tile counts n[i], in order) into nruns contiguous
+// runs of its tile sequence (run v starts at bin-local tile start[v]; start[nruns]
+// = all tiles), minimising the largest run cost over the run's capacity. A run
+// costs one per tile plus kSegStartCost for each segment that starts inside
+// it; its own first tile is free, since every run has one start.
+void cut_runs(const std::vector<int64_t>& n, int nruns, int64_t* start) {
+  int64_t tiles = 0;
+  for (int64_t k : n) tiles += k;
+  double capsum = 0;
+  for (int v = 0; v < nruns; ++v) capsum += slot_capacity(v);
+  auto pack = [&](double M, int64_t* st) {
+    int v = 0;
+    double c = 0;
+    int64_t x = 0;
+    st[0] = 0;
+    for (int64_t k : n) {
+      int64_t left = k;
+      bool seg_start = true;
+      while (left > 0) {
+        const double sw = seg_start && c > 0 ? kBinSwitchCost : 0.0;
+        const double cap = M * slot_capacity(v) - c - sw;
+        // the run that ends the segment also appends its new row
+        int64_t room = (int64_t)std::floor(cap + 1e-9);
+        if (room >= left) room = (int64_t)std::floor(cap - kBinAppendCost + 1e-9) >= left ? left : left - 1;
+        if (room <= 0) {
+          if (++v == nruns) return false;
+          st[v] = x;
+          c = 0;
+          continue;
+        }
+        const int64_t take = std::min(left, room);
+        c += sw + (double)take + (take == left ? kBinAppendCost : 0.0);
+        x += take;
+        left -= take;
+        seg_start = false;
+      }
+    }
+    for (int u = v + 1; u <= nruns; ++u) st[u] = x;
+    return true;
+  };
+  double lo = std::max(1.0, (double)tiles / capsum) * 0.999;
+  double hi = (double)tiles + (kBinSwitchCost + kBinAppendCost) * (double)n.size() + 1.0;
+  for (int it = 0; it < 40 && hi - lo > 1e-3; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (pack(mid, start)) hi = mid;
+    else lo = mid;
+  }
+  pack(hi, start);
+}
+
 bool build_bins(pkv_pool* p, int nbins) {
   const int B = p->up_batch;
   const int H = p->shape.kv_heads;
@@ -619,26 +691,15 @@ bool build_bins(pkv_pool* p, int nbins) {
       int32_t* e = list + 4 * (size_t)li++;
       e[0] = s;
       e[1] = segs[i].g;
-      e[2] = p->h_ctx[s];
+      e[2] = p->h_ctx[s] | p->h_slotflag[s];
       e[3] = p->h_bt[(size_t)s * p->up_stride];
     }
-    // cut the bin's tiles into kBinWaves runs of equal cost
-    const int64_t cb = load[b];
-    std::vector<int64_t> start_tile(kBinWaves + 1, -1);  // bin-local tile index of each cut
-    int64_t cost = 0, x = 0;
-    int v = 1;
-    start_tile[0] = 0;
-    for (int i : m) {
-      cost += kSegStartCost;
-      const int64_t n = segs[i].cost - kSegStartCost;
-      for (int64_t j = 0; j < n; ++j, ++x) {
-        while (v < kBinWaves && cost * kBinWaves >= (int64_t)v * cb && x > start_tile[v - 1])
-          start_tile[v++] = x;
-        ++cost;
-      }
-    }
-    const int64_t tiles = x;
-    while (v <= kBinWaves) start_tile[v++] = tiles;
+    // cut the bin's tiles into kBinWaves runs of balanced cost
+    std::vector<int64_t> ntiles;
+    ntiles.reserve(m.size());
+    for (int i : m) ntiles.push_back(segs[i].cost - kSegStartCost);
+    int64_t start_tile[kBinWaves + 1];
+    cut_runs(ntiles, kBinWaves, start_tile);
     // descriptors: walk segments and waves together
     int seg_i = 0;          // index into m
     int64_t seg_x0 = 0;     // bin-local tile index where m[seg_i] starts
@@ -661,7 +722,7 @@ bool build_bins(pkv_pool* p, int nbins) {
       d[2] = sg.s;
       d[3] = sg.g;
       d[4] = (int32_t)j0;
-      d[5] = p->h_ctx[sg.s];
+      d[5] = p->h_ctx[sg.s] | p->h_slotflag[sg.s];
       d[6] = p->h_bt[(size_t)sg.s * p->up_stride + j0 * pkv::kTile / p->shape.block_size];
       const int64_t n0 = sg.cost - kSegStartCost;
       if (j0 == 0) {
@@ -1042,6 +1103,11 @@ int pkv_block_table_upload(pkv_pool* p, const int32_t* bt, int batch, int max_bl
   p->up_batch = batch;
   p->up_stride = max_blocks;
   p->h_ctx.assign(ctx, ctx + batch);
+  // the kernels read the lengths with bit 30 set where the sequence has a slot
+  // (its new row is appended by a fused decode)
+  p->h_slotflag.assign(batch, 0);
+  if (slots)
+    for (int s = 0; s < batch; ++s) p->h_slotflag[s] = slots[s] >= 0 ? (1 << 30) : 0;
   p->h_cum = std::move(cum);
   p->h_bt.assign(bt, bt + (size_t)batch * max_blocks);
   ++p->up_gen;
@@ -1063,7 +1129,8 @@ int pkv_block_table_upload(pkv_pool* p, const int32_t* bt, int batch, int max_bl
   p->h_stage.assign(bytes, 0);
   char* img = p->h_stage.data();
   if (slots) std::memcpy(img, slots, (size_t)batch * 8);
-  std::memcpy(img + p->off_ctx, ctx, (size_t)batch * 4);
+  for (int s = 0; s < batch; ++s)
+    reinterpret_cast<int32_t*>(img + p->off_ctx)[s] = ctx[s] | p->h_slotflag[s];
   std::memcpy(img + p->off_cum, p->h_cum.data(), (size_t)(batch + 1) * 4);
   std::memcpy(img + p->off_bt, bt, (size_t)batch * max_blocks * 4);
   if (packed) std::memcpy(img + off_sched, p->h_sched.data(), p->h_sched.size() * 4);
@@ -1397,6 +1464,14 @@ int pkv_prefix_stats(const pkv_pool* p, int64_t stats[4]) {
   stats[3] = p->prefix_evictions;
   return PKV_OK;
 }
+
+#ifdef PKV_TIMELINE
+int pkv_debug_timeline(void* host_dst, size_t bytes) {
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = pkv::copy_timeline(host_dst, bytes);
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "timeline copy");
+}
+#endif
 
 int pkv_pool_stats(const pkv_pool* p, int64_t stats[4]) {
   if (!p || !stats) return fail(PKV_EINVAL, "bad arguments");

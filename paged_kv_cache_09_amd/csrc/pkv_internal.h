@@ -96,4 +96,8 @@ hipError_t launch_copy_blocks(const int32_t* pairs, int n, void* k_base, void* v
                               int layers, int64_t layer_bytes, int64_t block_bytes,
                               hipStream_t stream);
 
+#ifdef PKV_TIMELINE
+hipError_t copy_timeline(void* dst, size_t bytes);
+#endif
+
 }  // namespace pkv

@@ -45,6 +45,15 @@ namespace pkv {
 namespace {
 
 enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_Q8 = 3, DT_Q4 = 4 };
+// Context lengths handed to the decode kernel carry a flag in bit 30.
+constexpr int kLenMask = (1 << 30) - 1;
+
+#ifdef PKV_TIMELINE
+// Diagnostic build only: per wave (start, first tile done, loop end, merge
+// end, xcc | tiles << 8 | segments << 24, wave id, after the barrier, 0) in
+// s_memrealtime ticks.
+__device__ long long pkv_tl[8 * 8192];
+#endif
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -67,6 +76,36 @@ __device__ __forceinline__ u32x2 ld8(const char* p) {
 __device__ __forceinline__ unsigned ld4(const char* p) {
   return *reinterpret_cast<const unsigned*>(p);
 }
+// A load of a wave-uniform int that stays on the vector memory path: a scalar
+// load would be counted by lgkmcnt, which the tile loop's LDS exchanges also
+// wait on, so a prefetch in flight would stall them. The zero offset is opaque
+// to the compiler (a per-lane register), which keeps the load a vector load.
+__device__ __forceinline__ int vld(const int32_t* p) {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return p[z];
+}
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// Pool tiles are read once per launch: nontemporal loads (the nt cache
+// policy) stream them past the caches.
+__device__ __forceinline__ u32x4 nt16(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x2 nt8(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+__device__ __forceinline__ unsigned nt4(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(p));
+}
+#ifndef PKV_NT_Q8
+#define PKV_NT_Q8 0
+#endif
+#ifndef PKV_NT_SCALES
+#define PKV_NT_SCALES 0
+#endif
+__device__ __forceinline__ u32x2 ldq8(const char* p) { return PKV_NT_Q8 ? nt8(p) : ld8(p); }
+__device__ __forceinline__ u32x2 ldsc8(const char* p) { return PKV_NT_SCALES ? nt8(p) : ld8(p); }
+__device__ __forceinline__ unsigned ldsc4(const char* p) { return PKV_NT_SCALES ? nt4(p) : ld4(p); }
 
 // fp16 halves of a 32-bit word, as fp32.
 __device__ __forceinline__ float half_lo(unsigned u) {
@@ -701,9 +740,17 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
   // bytes of one (block, kv head) tile of the pool: BS rows (+ scales when quantised)
   constexpr int TILE = QN ? BS * CB + BS * (D / 32) * 2 : BS * RB;
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
-  // Tile buffers per wave. One, three or four ran slower than two on MI355X
-  // for bf16, q8_0 and q4_0 tiles.
-  constexpr int NBUF = 2;
+  // Tile buffers per wave (tiles in flight while one is computed, plus one).
+  // With the nontemporal tile loads, one buffer (no tile in flight during
+  // the compute; the other wave of the SIMD overlaps it) ran fastest for
+  // 2-byte caches on MI355X; the quantised tiles keep two.
+#ifndef PKV_NBUF2B
+#define PKV_NBUF2B 1
+#endif
+#ifndef PKV_NBUFQ
+#define PKV_NBUFQ 2
+#endif
+  constexpr int NBUF = (DT == DT_F16 || DT == DT_BF16) ? PKV_NBUF2B : PKV_NBUFQ;
   static_assert(RB % 32 == 0 && CPR <= 64 && GP <= 16, "shape");
   static_assert(!Q4 || (NV == NP && BS % NV == 0), "q4_0 tile layout");
   // q4_0 and q8_0 at head_dim 128 with up to 4 heads per group: P.V on MFMA
@@ -733,7 +780,8 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     }
   }
   const int bid = (int)blockIdx.x - (PFX ? p.nprefix : 0);  // a multiple of 8 comes off
-  const int wl = BINS ? (int)(threadIdx.x >> 6) : 0;
+  // wave-uniform (scalar registers): the descriptor loads become scalar loads
+  const int wl = BINS ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;
   const int lane = threadIdx.x & 63;
   float (&p_lds)[2][16 * GP + 4] = p_lds_all[wl];
   float (&a_lds)[GP] = a_lds_all[wl];
@@ -745,6 +793,11 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
   const int w = BINS ? wg * NW + wl : wg;
   const bool active = w < p.nwaves;
   if (!BINS && !active) return;
+#ifdef PKV_TIMELINE
+  const long long tl_t0 = __builtin_amdgcn_s_memrealtime();
+  long long tl_t1 = 0;
+  int tl_tiles = 0, tl_segs = 0;
+#endif
 
   // Per-wave descriptor: first tile (BINS: index of its first segment in the
   // bin lists), end tile (BINS: tile count), sequence, kv head, first block of
@@ -757,7 +810,10 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
   int s = desc[2];
   int g = desc[3];
   int j0 = desc[4];
-  int L = desc[5];
+  // context length; bit 30 set when the uploaded slot of the sequence is >= 0
+  // (its new row is appended by a fused call)
+  int L = desc[5] & kLenMask;
+  int has_slot = desc[5] >> 30;
   int blk_first = desc[6];
   const int merge_info = BINS ? desc[7] : 0;
   // 8-token blocks: id of the block holding rows 8..15 of the run's first tile
@@ -786,18 +842,19 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     const int take = min(xend - x, nblk - j0);
     const int j1 = j0 + take;
     const int seg = g * p.batch + s;
-    // Prefetch the next segment's length and first block id (scalar loads
-    // in flight while this segment's tiles stream).
+    // Prefetch the next segment's length and first block id (vector loads in
+    // flight while this segment's tiles stream; read as wave-uniform values at
+    // the switch).
     int next_s = s + 1, next_g = g, next_L = 0, next_blk = 0, next_second = 0, next_j0 = 0;
     if constexpr (BINS) {
       if (x + take < xend) {  // bin lists hold (sequence, kv head, length, first block)
         const int* e = p.seglist + 4 * (li + 1);
-        next_s = e[0];
-        next_g = e[1];
-        next_L = e[2];
-        next_blk = e[3];
+        next_s = vld(e);
+        next_g = vld(e + 1);
+        next_L = vld(e + 2);
+        next_blk = vld(e + 3);
         if constexpr (BS == 8)  // rows 8..15 of the first tile
-          next_second = next_L > 8 ? p.bt[(size_t)next_s * p.bt_stride + 1] : next_blk;
+          next_second = (next_L & kLenMask) > 8 ? vld(p.bt + (size_t)uni(next_s) * p.bt_stride + 1) : next_blk;
       }
     } else {
       if (next_s == p.batch) {
@@ -805,20 +862,20 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         ++next_g;
       }
       if (x + take < xend) {
-        next_L = p.ctx[next_s];
+        next_L = vld(p.ctx + next_s);
         if (p.seqinfo) {
           // shared prefixes: the sequence's run starts at its first private
           // tile, whose block id(s) the host wrote beside it
           const int* r = p.seqinfo + 4 * next_s;
-          next_j0 = r[0];
-          next_blk = r[1];
-          next_second = r[2];
+          next_j0 = vld(r);
+          next_blk = vld(r + 1);
+          next_second = vld(r + 2);
         } else {
-          next_blk = p.bt[(size_t)next_s * p.bt_stride];
+          next_blk = vld(p.bt + (size_t)next_s * p.bt_stride);
           // 8-token blocks: the second entry (padding -1 when absent: any
           // block, its rows are past the context)
           if constexpr (BS == 8)
-            next_second = p.bt_stride > 1 ? max(p.bt[(size_t)next_s * p.bt_stride + 1], 0) : 0;
+            next_second = p.bt_stride > 1 ? max(vld(p.bt + (size_t)next_s * p.bt_stride + 1), 0) : 0;
         }
       }
     }
@@ -830,7 +887,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     // the last block also takes the new token's row from k_new / v_new as a
     // one-row tile, writes it to the pool where the table puts it and
     // attends over it.
-    const bool app = p.k_new != nullptr && p.slots[s] >= 0;
+    const bool app = p.k_new != nullptr && has_slot;
     const char* kn_row =
         reinterpret_cast<const char*>(p.k_new) + ((size_t)s * p.kv_heads + g) * QB;
     const char* vn_row =
@@ -845,7 +902,10 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     // layer, 12 % this way. The other caches keep the late form, which
     // measured faster for them (bf16 by 0.6 us, q8_0 by 1-1.5 us per layer:
     // the registers held early cost their loops more).
-    constexpr bool EARLY_NEW = Q4 && GP <= 4;
+#ifndef PKV_EARLY_2B
+#define PKV_EARLY_2B 0
+#endif
+    constexpr bool EARLY_NEW = (Q4 && GP <= 4) || (PKV_EARLY_2B && (DT == DT_F16 || DT == DT_BF16));
     const bool app_here = app && j1 == nblk;
     u32x4 nk[NP], nv = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -880,14 +940,14 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
           const char* kt = ktile + (unsigned)(kr * CB + kg * NP * 4);
           const char* vt = vtile + (unsigned)(vrr * CB + vc * NV * 4);
           if constexpr (NP == 4) {
-            const u32x4 a = ld16(kt), b = ld16(vt);
+            const u32x4 a = nt16(kt), b = nt16(vt);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               t.k[i] = a[i];
               t.v[i] = b[i];
             }
           } else {
-            const u32x2 a = ld8(kt), b = ld8(vt);
+            const u32x2 a = nt8(kt), b = nt8(vt);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
               t.k[i] = a[i];
@@ -897,49 +957,60 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         } else {
           const char* kt = ktile + kr * CB + kg * 8;
 #pragma unroll
-          for (int k = 0; k < NP; ++k) t.k[k] = ld8(kt + k * 32);
+          for (int k = 0; k < NP; ++k) t.k[k] = ldq8(kt + k * 32);
           const char* vt = vtile + vrr * CB + vc * 8;
 #pragma unroll
-          for (int i = 0; i < NV; ++i) t.v[i] = ld8(vt + i * CB);
+          for (int i = 0; i < NV; ++i) t.v[i] = ldq8(vt + i * CB);
         }
         // scales after the BS rows of codes: K [row][group], V [group][row]
         const char* ksp = ktile + (unsigned)(BS * CB + kr * NP * 2);
         const char* vsp = vtile + (unsigned)(BS * CB + ((vc >> 2) * BS + vrr) * 2);
         if constexpr (NP == 4) {
-          const u32x2 x2 = ld8(ksp);
+          const u32x2 x2 = ldsc8(ksp);
           t.ks[0] = x2[0];
           t.ks[1] = x2[1];
         } else {
-          t.ks[0] = ld4(ksp);
+          t.ks[0] = ldsc4(ksp);
         }
         if constexpr (NV == 4) {
-          const u32x2 x2 = ld8(vsp);
+          const u32x2 x2 = ldsc8(vsp);
           t.vs[0] = x2[0];
           t.vs[1] = x2[1];
         } else {
-          t.vs[0] = ld4(vsp);
+          t.vs[0] = ldsc4(vsp);
         }
       } else {
         const char* kt = ktile + kr * RB + kg * 16;
 #pragma unroll
-        for (int k = 0; k < NP; ++k) t.k[k] = ld16(kt + k * 64);
+        for (int k = 0; k < NP; ++k) t.k[k] = nt16(kt + k * 64);
         if constexpr (BS == 8) {
           // row vr + RPI*i (vr < RPI, RPI divides 8) lies in block a iff RPI*i < 8
 #pragma unroll
           for (int i = 0; i < NV; ++i)
-            t.v[i] = ld16(vbase + (size_t)(RPI * i < 8 ? a : b) * blk_stride +
+            t.v[i] = nt16(vbase + (size_t)(RPI * i < 8 ? a : b) * blk_stride +
                           ((vr + RPI * i) & 7) * RB + vc * 16);
         } else {
           const char* vt = vbase + (size_t)a * blk_stride + rib(vr) * RB + vc * 16;
 #pragma unroll
-          for (int i = 0; i < NV; ++i) t.v[i] = ld16(vt + i * RPI * RB);
+          for (int i = 0; i < NV; ++i) t.v[i] = nt16(vt + i * RPI * RB);
         }
       }
     };
 
-    // q rows of the GQA group (row = head t16, zero past the group), in the
-    // same pieces as K.
+    // q rows of the GQA group (row = head t16), in the same pieces as K. Rows
+    // past the group repeat its last head: their scores land in rows no
+    // output is taken from. Filled by setup_q once the run's first tile is
+    // requested, so that its wait does not hold back that request.
     u32x4 qv[NP];
+    // smul[i]: log2(e) x scale, times what turns score row i's MFMA result
+    // into q . K (q8_0: the head's 2^(24 - qsh)).
+    float smul[HPG];
+    // q4_0: -136 times each q piece's sum over its group (an MFMA against
+    // ones), the accumulator input that turns q . (128 + code) into
+    // q . (code - 8); q8_0: -128 x 2^-24 times it, for q . (128 + code) x
+    // 2^-24 into q . code x 2^-24.
+    f32x4 qb[QN ? NP : 1];
+    auto setup_q = [&]() {
     {
       const int hq = min(t16, p.group - 1);
       const char* qr = reinterpret_cast<const char*>(p.q) +
@@ -948,12 +1019,9 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       for (int k = 0; k < NP; ++k) {
         u32x4 v = ld16(qr + k * 64);
         if constexpr (Q4) v = q_slots_0246(v);  // the K operand's slot order
-        qv[k] = t16 < p.group ? v : u32x4{0u, 0u, 0u, 0u};
+        qv[k] = v;
       }
     }
-    // smul[i]: log2(e) x scale, times what turns score row i's MFMA result
-    // into q . K (q8_0: the head's 2^(24 - qsh)).
-    float smul[HPG];
 #pragma unroll
     for (int i = 0; i < HPG; ++i) smul[i] = p.scale_log2;
     if constexpr (Q8M) {
@@ -985,11 +1053,6 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       for (int i = 0; i < HPG; ++i)
         smul[i] = p.scale_log2 * __builtin_amdgcn_ldexpf(1.f, 24 - __shfl(qsh, 4 * kg + i, 64));
     }
-    // q4_0: -136 times each q piece's sum over its group (an MFMA against
-    // ones), the accumulator input that turns q . (128 + code) into
-    // q . (code - 8); q8_0: -128 x 2^-24 times it, for q . (128 + code) x
-    // 2^-24 into q . code x 2^-24.
-    f32x4 qb[QN ? NP : 1];
     if constexpr (Q4) {
       const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
 #pragma unroll
@@ -1007,6 +1070,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         for (int i = 0; i < 4; ++i) qb[k][i] = -0x1p-17f * sq[i];
       }
     }
+    };
 
     // Lane (t16, kg) keeps softmax state for heads 4*kg + i of its row.
     float m[HPG], lsum[HPG];
@@ -1212,6 +1276,10 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       }
     };
 
+    // Tile buffers; the chunk cursor, the block-table entries of the chunk
+    // (one per lane) and the entry index of its first lane.
+    TR t[NBUF];
+    int jb = j0, nb = 0, my_ent = 0, e0_cur = -(1 << 30);
     // Tiles stream through NBUF register buffers: NBUF - 1 tiles are in
     // flight while one is computed. Block-table entries come one per lane, 64
     // at a time (the tiles of 64 entries: 64, 128 or 32 of them).
@@ -1224,7 +1292,12 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     // run, while the first tile's loads are in flight (the pool row it writes
     // is masked out of that run's own last tile, and no other run reads it).
     auto append_new_row = [&]() {
-      const int blk_last = bt_row[(L - 1) / BS];
+      // the new row's block: from the entries of the last chunk requested
+      // when they hold it, else from the table
+      const int eidx = (L - 1) / BS;
+      const int rel = eidx - e0_cur;
+      const int blk_last = rel >= 0 && rel < 64 ? __builtin_amdgcn_readlane(my_ent, rel)
+                                                : bt_row[eidx];
       const int t_new = (L - 1) % BS;  // the new row inside its block
       char* ktile = const_cast<char*>(kbase) + (size_t)blk_last * blk_stride;
       char* vtile = const_cast<char*>(vbase) + (size_t)blk_last * blk_stride;
@@ -1345,8 +1418,6 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       }
       compute_tile(1, tn);
     };
-    TR t[NBUF];
-    int jb = j0, nb = 0, my_ent = 0;
     // block ids of chunk tile j: (a, b, half)
     auto tile_ids = [&](int j, int& a, int& b, int& half) {
       if constexpr (BS == 16) {
@@ -1374,17 +1445,18 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       nb = min(CH, j1c - jb);
       const int e0 = BS == 32 ? (jb >> 1) : BS == 8 ? 2 * jb : jb;
       my_ent = e0 + lane < nent_seq ? bt_row[e0 + lane] : 0;
+      e0_cur = e0;
       if (jb == j0) load_tile(blk_first, BS == 8 ? blk_second : 0, BS == 32 ? (jb & 1) : 0, t[0]);
       else load_j(0, t[0]);
 #pragma unroll
       for (int u = 1; u < NBUF - 1; ++u) load_j(min(u, nb - 1), t[u]);
     };
-    if constexpr (EARLY_NEW) {
-      if (jb < j1c) start_chunk();
-      if (app_here) append_new_row();
-    }
+    // the first chunk's entries and first tile are requested before q
+    if (jb < j1c) start_chunk();
+    setup_q();
+    if (EARLY_NEW && app_here) append_new_row();
     for (; jb < j1c; jb += CH) {
-      if (!EARLY_NEW || jb != j0) start_chunk();
+      if (jb != j0) start_chunk();
       // Every step requests a tile, the chunk's last one again once the chunk
       // is exhausted (a repeat the cache serves): with no conditional loads
       // the compiler's wait counts stay static and only the tile about to be
@@ -1394,11 +1466,17 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         for (int u = 0; u < NBUF; ++u) {
           const int j = jj + u;
           if (j < nb) {
-            load_j(min(j + NBUF - 1, nb - 1), t[(u + NBUF - 1) % NBUF]);
+            // one buffer: tile 0 of the chunk was requested by start_chunk
+            if constexpr (NBUF > 1) load_j(min(j + NBUF - 1, nb - 1), t[(u + NBUF - 1) % NBUF]);
+            else if (j > 0) load_j(j, t[0]);
             // keep the scheduler from hoisting the compute (and its waits) above
             // the request
             __builtin_amdgcn_sched_barrier(0);
             compute_tile(min(16, Lc - 16 * (jb + j)), t[u]);
+#ifdef PKV_TIMELINE
+            if (tl_t1 == 0) tl_t1 = __builtin_amdgcn_s_memrealtime();
+            ++tl_tiles;
+#endif
           }
         }
       }
@@ -1491,47 +1569,82 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     }
     wave_sync();  // l_lds / m_lds / a_lds are reused by the next run
 
+#ifdef PKV_TIMELINE
+    ++tl_segs;
+#endif
     x += take;
     if (x >= xend) break;
-    s = next_s;
-    g = next_g;
-    j0 = next_j0;
-    L = next_L;
-    blk_first = next_blk;
-    blk_second = next_second;
+    s = uni(next_s);
+    g = uni(next_g);
+    j0 = uni(next_j0);
+    L = uni(next_L) & kLenMask;
+    has_slot = uni(next_L) >> 30;
+    blk_first = uni(next_blk);
+    blk_second = uni(next_second);
     ++li;
     first_seg = false;
   }
 
+#ifdef PKV_TIMELINE
+  const long long tl_t2 = __builtin_amdgcn_s_memrealtime();
+  long long tl_tb = 0;
+#endif
   if constexpr (BINS) {
     // Every piece of this bin is in LDS: the wave holding the last tile of a
     // segment split between waves wa .. wl merges its pieces (slot 0 of each
     // wave, except wa's, whose slot the host gives):
     //   out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i.
-    __syncthreads();
+    // Only LDS is exchanged: the barrier orders LDS alone and does not wait
+    // for this wave's global stores (outputs, appended rows) to complete.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+#ifdef PKV_TIMELINE
+    tl_tb = __builtin_amdgcn_s_memrealtime();
+#endif
     if (active && (merge_info & (1 << 16))) {
       const int wa = merge_info & 0xff;
       const int wa_slot = (merge_info >> 8) & 1;
+      const int n = wl - wa + 1;  // pieces: waves wa .. wl
       constexpr int PER = D / 64;
-      for (int hh = 0; hh < p.group; ++hh) {
-        float M = -__builtin_inff();
-        for (int v = wa; v <= wl; ++v) {
-          const int sl = v == wa ? wa_slot : 0;
-          M = fmaxf(M, piece_ml[((v * 2 + sl) * GP + hh) * 2]);
-        }
-        float den = 0.f, o[PER];
+      auto piece = [&](int v) { return (min(wa + v, NW - 1) * 2 + (v == 0 ? wa_slot : 0)) * GP; };
+      // Lane (head lane / 8, piece lane % 8) reads that piece's max and sum;
+      // all LDS reads are issued before any arithmetic waits on them.
+      const int mv = lane & 7, mh = lane >> 3;
+      const bool mreal = mv < n && mh < GP;
+      float mm = -__builtin_inff(), ll = 0.f;
+      if (mreal) {
+        mm = piece_ml[(piece(mv) + mh) * 2];
+        ll = piece_ml[(piece(mv) + mh) * 2 + 1];
+      }
+      float M = fmaxf(mm, xor_f(mm, 1));
+      M = fmaxf(M, xor_f(M, 2));
+      M = fmaxf(M, xor_f(M, 4));
+      const float wgt = mreal ? __builtin_amdgcn_exp2f(mm - M) : 0.f;
+      float den = wgt * ll;
+      den += xor_f(den, 1);
+      den += xor_f(den, 2);
+      den += xor_f(den, 4);
+#pragma unroll
+      for (int hh = 0; hh < GP; ++hh) {
+        if (hh >= p.group) break;
+        float src[NW][PER];
+#pragma unroll
+        for (int v = 0; v < NW; ++v)
+#pragma unroll
+          for (int e = 0; e < PER; ++e) src[v][e] = piece_o[(size_t)(piece(v) + hh) * D + lane * PER + e];
+        float o[PER];
 #pragma unroll
         for (int e = 0; e < PER; ++e) o[e] = 0.f;
-        for (int v = wa; v <= wl; ++v) {
-          const int sl = v == wa ? wa_slot : 0;
-          const float* ml = piece_ml + ((v * 2 + sl) * GP + hh) * 2;
-          const float wgt = __builtin_amdgcn_exp2f(ml[0] - M);
-          den = __builtin_fmaf(wgt, ml[1], den);
-          const float* po = piece_o + (size_t)((v * 2 + sl) * GP + hh) * D + lane * PER;
 #pragma unroll
-          for (int e = 0; e < PER; ++e) o[e] = __builtin_fmaf(wgt, po[e], o[e]);
+        for (int v = 0; v < NW; ++v) {
+          const float wv = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgt), hh * 8 + v));
+#pragma unroll
+          for (int e = 0; e < PER; ++e) o[e] = v < n ? __builtin_fmaf(wv, src[v][e], o[e]) : o[e];
         }
-        const float inv = 1.f / den;
+        const float inv = 1.f / __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, den), hh * 8));
         float* dst = p.out + ((size_t)s_first * p.q_heads + (size_t)g_first * p.group + hh) * D +
                      lane * PER;
 #pragma unroll
@@ -1539,6 +1652,20 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       }
     }
   }
+#ifdef PKV_TIMELINE
+  if (active && lane == 0 && w < 8192) {
+    long long* r = pkv_tl + 8 * w;
+    r[6] = tl_tb;
+    r[7] = 0;
+    r[0] = tl_t0;
+    r[1] = tl_t1;
+    r[2] = tl_t2;
+    r[3] = __builtin_amdgcn_s_memrealtime();
+    r[4] = (__builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xf) | (tl_tiles << 8) |
+           ((long long)tl_segs << 24);
+    r[5] = w;
+  }
+#endif
 }
 
 // Four wavefronts per workgroup, one (sequence, q head) pair each: fewer,
@@ -1852,5 +1979,12 @@ hipError_t launch_upload(const void* host_src, void* dst, size_t bytes, hipStrea
                      static_cast<const u32x4*>(host_src), static_cast<u32x4*>(dst), n16);
   return hipGetLastError();
 }
+
+#ifdef PKV_TIMELINE
+hipError_t copy_timeline(void* dst, size_t bytes) {
+  return hipMemcpyFromSymbol(dst, HIP_SYMBOL(pkv_tl), bytes < sizeof(pkv_tl) ? bytes : sizeof(pkv_tl), 0,
+                             hipMemcpyDeviceToHost);
+}
+#endif
 
 }  // namespace pkv

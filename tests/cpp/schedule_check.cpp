@@ -38,6 +38,9 @@ static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins, int b
   for (int L : ctx) maxb = std::max<int>(maxb, (L + bs - 1) / bs);  // table entries
   p->up_stride = maxb;
   p->h_ctx = ctx;
+  // every other sequence has an uploaded slot: its lengths carry bit 30
+  p->h_slotflag.assign(ctx.size(), 0);
+  for (size_t q = 0; q < ctx.size(); q += 2) p->h_slotflag[q] = 1 << 30;
   p->h_bt.assign((size_t)B * maxb, -1);
   int id = 0;
   for (int s = 0; s < B; ++s)
@@ -57,11 +60,12 @@ static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins, int b
     std::vector<std::pair<int,int>> first_seg_of(8, {-1,-1});
     for (int wl = 0; wl < 8; ++wl) {
       const int32_t* d = desc + 8 * (size_t)(b * 8 + wl);
-      int li = d[0], count = d[1], s = d[2], g = d[3], j0 = d[4], L = d[5], blk = d[6];
+      int li = d[0], count = d[1], s = d[2], g = d[3], j0 = d[4], L = d[5] & ((1 << 30) - 1), blk = d[6];
       if (count == 0) continue;
+      if ((d[5] >> 30) != (p->h_slotflag[s] ? 1 : 0)) { printf("slot flag mismatch\n"); ++errors; }
       if (li < 0 || li >= nseg) { printf("bad li\n"); return 1; }
       const int32_t* e0 = list + 4 * li;
-      if (e0[0] != s || e0[1] != g || e0[2] != L) { printf("desc/list mismatch\n"); return 1; }
+      if (e0[0] != s || e0[1] != g || (e0[2] & ((1 << 30) - 1)) != L) { printf("desc/list mismatch\n"); return 1; }
       if (blk != p->h_bt[(size_t)s * maxb + j0 * 16 / bs]) { printf("bad first blk\n"); return 1; }
       int x = 0; bool first = true;
       first_seg_of[wl] = {s, g};
@@ -77,7 +81,8 @@ static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins, int b
         ++li;
         if (li >= nseg) { printf("li overflow\n"); return 1; }
         const int32_t* e = list + 4 * li;
-        s = e[0]; g = e[1]; L = e[2]; j0 = 0; first = false;
+        s = e[0]; g = e[1]; L = e[2] & ((1 << 30) - 1); j0 = 0; first = false;
+        if ((e[2] >> 30) != (p->h_slotflag[s] ? 1 : 0)) { printf("slot flag mismatch\n"); ++errors; }
         if (e[3] != p->h_bt[(size_t)s * maxb]) { printf("bad list blk\n"); return 1; }
       }
     }
@@ -129,6 +134,9 @@ static int check_groups(const std::vector<std::vector<int>>& tables, const std::
   for (auto& t : tables) maxb = std::max<int>(maxb, t.size());
   p->up_stride = maxb;
   p->h_ctx = ctx;
+  // every other sequence has an uploaded slot: its lengths carry bit 30
+  p->h_slotflag.assign(ctx.size(), 0);
+  for (size_t q = 0; q < ctx.size(); q += 2) p->h_slotflag[q] = 1 << 30;
   p->h_bt.assign((size_t)B * maxb, -1);
   for (int s = 0; s < B; ++s)
     for (size_t j = 0; j < tables[s].size(); ++j) p->h_bt[(size_t)s * maxb + j] = tables[s][j];
