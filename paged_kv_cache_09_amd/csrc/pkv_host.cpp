@@ -548,9 +548,8 @@ constexpr int kBinWaves = 8;
 // the packing is too uneven, e.g. a few very long sequences.
 //   wdesc per wave: [0] index of its first segment in the bin lists, [1] tile
 //   count, [2] sequence, [3] kv head, [4] first block index in that segment,
-//   [5] its length, [6] that block's id, [7] merge it owns: bit 16 set when
-//   its first segment started in an earlier wave wa of the bin and ends in
-//   this one; bits 0-7 wa, bit 8 the LDS slot of wa's piece.
+//   [5] its length (bit 30: has a slot), [6] that block's id, [7] the merges
+//   of split segments it takes part in (see below).
 //   seglist per listed segment: sequence, kv head, length, first block id.
 // Relative speed of the eight waves of a bin: waves 0-3 and 4-7 share the
 // four SIMDs, and the older wave of each pair wins issue arbitration.
@@ -703,7 +702,6 @@ bool build_bins(pkv_pool* p, int nbins) {
     // descriptors: walk segments and waves together
     int seg_i = 0;          // index into m
     int64_t seg_x0 = 0;     // bin-local tile index where m[seg_i] starts
-    std::vector<int> first_wave_of(m.size(), -1), first_slot_of(m.size(), 0);
     for (int wv = 0; wv < kBinWaves; ++wv) {
       int32_t* d = desc + (size_t)8 * (b * kBinWaves + wv);
       const int64_t x0 = start_tile[wv], x1 = std::max(start_tile[wv], start_tile[wv + 1]);
@@ -724,25 +722,36 @@ bool build_bins(pkv_pool* p, int nbins) {
       d[4] = (int32_t)j0;
       d[5] = p->h_ctx[sg.s] | p->h_slotflag[sg.s];
       d[6] = p->h_bt[(size_t)sg.s * p->up_stride + j0 * pkv::kTile / p->shape.block_size];
-      const int64_t n0 = sg.cost - kSegStartCost;
-      if (j0 == 0) {
-        first_wave_of[seg_i] = wv;
-        first_slot_of[seg_i] = 0;
-      } else if (seg_x0 + n0 <= x1) {
-        // this wave ends a segment that started in an earlier wave
-        d[7] = (1 << 16) | (first_slot_of[seg_i] << 8) | first_wave_of[seg_i];
-      }
-      // the wave's last segment, when different from its first and cut at x1,
-      // leaves its piece in slot 1
-      int64_t sx = seg_x0;
-      int k = seg_i;
-      while (sx + (segs[m[k]].cost - kSegStartCost) < x1) {
-        sx += segs[m[k]].cost - kSegStartCost;
-        ++k;
-      }
-      if (k != seg_i && first_wave_of[k] < 0) {
-        first_wave_of[k] = wv;
-        first_slot_of[k] = 1;
+    }
+    // Merges of segments split between waves: every wave holding a piece of
+    // such a segment merges some of its heads (head h goes to the piece
+    // holder h mod n of the n holders). A wave takes part in at most two:
+    // its first segment's (bit 16: waves wf .. in bits 0-2, wf's piece slot in
+    // bit 3, n in bits 4-7) and its last segment's when that starts in this
+    // wave and continues (bit 17: n in bits 8-11).
+    {
+      int64_t sx = 0;
+      for (size_t k = 0; k < m.size(); ++k) {
+        const int64_t n0 = segs[m[k]].cost - kSegStartCost;
+        const int64_t a = sx, e = sx + n0;  // the segment's bin-local tiles [a, e)
+        sx = e;
+        int wf = -1, wlast = -1;
+        for (int wv = 0; wv < kBinWaves; ++wv) {
+          const int64_t x0 = start_tile[wv], x1 = std::max(start_tile[wv], start_tile[wv + 1]);
+          if (x1 > x0 && x0 < e && x1 > a) {
+            if (wf < 0) wf = wv;
+            wlast = wv;
+          }
+        }
+        if (wf < 0 || wlast == wf) continue;
+        const int n = wlast - wf + 1;
+        // the first holder's piece is slot 0 when the segment is its first, else slot 1
+        const int slot = start_tile[wf] < a ? 1 : 0;
+        for (int wv = wf; wv <= wlast; ++wv) {
+          int32_t* d = desc + (size_t)8 * (b * kBinWaves + wv);
+          if (wv == wf && slot == 1) d[7] |= (1 << 17) | (n << 8);
+          else d[7] |= (1 << 16) | wf | (slot << 3) | (n << 4);
+        }
       }
     }
   }

@@ -416,6 +416,18 @@ __device__ __forceinline__ float row_max(float v) {
   v = fmaxf(v, row_ror<0x122>(v));  // row_ror:2
   return fmaxf(v, row_ror<0x121>(v));  // row_ror:1
 }
+// All-reductions over each group of 8 lanes (DPP within each quad, then
+// across the two quads of the 8 lanes).
+__device__ __forceinline__ float oct_max(float x) {
+  x = fmaxf(x, row_ror<0xB1>(x));      // quad_perm [1,0,3,2]
+  x = fmaxf(x, row_ror<0x4E>(x));      // quad_perm [2,3,0,1]
+  return fmaxf(x, row_ror<0x141>(x));  // row_half_mirror
+}
+__device__ __forceinline__ float oct_sum(float x) {
+  x += row_ror<0xB1>(x);
+  x += row_ror<0x4E>(x);
+  return x + row_ror<0x141>(x);
+}
 __device__ __forceinline__ float row_sum(float v) {
   v += row_ror<0x128>(v);
   v += row_ror<0x124>(v);
@@ -1590,9 +1602,9 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
   long long tl_tb = 0;
 #endif
   if constexpr (BINS) {
-    // Every piece of this bin is in LDS: the wave holding the last tile of a
-    // segment split between waves wa .. wl merges its pieces (slot 0 of each
-    // wave, except wa's, whose slot the host gives):
+    // Every piece of this bin is in LDS: each segment split between waves is
+    // merged head by head by the waves holding its pieces (slot 0 of each,
+    // except the first holder's, whose slot the host gives):
     //   out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i.
     // Only LDS is exchanged: the barrier orders LDS alone and does not wait
     // for this wave's global stores (outputs, appended rows) to complete.
@@ -1602,54 +1614,57 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
 #ifdef PKV_TIMELINE
     tl_tb = __builtin_amdgcn_s_memrealtime();
 #endif
-    if (active && (merge_info & (1 << 16))) {
-      const int wa = merge_info & 0xff;
-      const int wa_slot = (merge_info >> 8) & 1;
-      const int n = wl - wa + 1;  // pieces: waves wa .. wl
+    // Head hh of a segment whose n pieces are held by waves w0 .. w0+n-1
+    // (w0's piece in slot sl0, the others' in slot 0). Every LDS read is
+    // issued before the arithmetic: lane k < n of each 8 reads piece k's max
+    // and sum, and every lane its D/64 columns of every piece.
+    auto merge_head = [&](int ms, int mg, int w0, int sl0, int n, int hh) {
       constexpr int PER = D / 64;
-      auto piece = [&](int v) { return (min(wa + v, NW - 1) * 2 + (v == 0 ? wa_slot : 0)) * GP; };
-      // Lane (head lane / 8, piece lane % 8) reads that piece's max and sum;
-      // all LDS reads are issued before any arithmetic waits on them.
-      const int mv = lane & 7, mh = lane >> 3;
-      const bool mreal = mv < n && mh < GP;
+      auto slot_of = [&](int k) { return (min(w0 + k, NW - 1) * 2 + (k == 0 ? sl0 : 0)) * GP + hh; };
+      const int k8 = lane & 7;
+      const bool real = k8 < n;
       float mm = -__builtin_inff(), ll = 0.f;
-      if (mreal) {
-        mm = piece_ml[(piece(mv) + mh) * 2];
-        ll = piece_ml[(piece(mv) + mh) * 2 + 1];
+      if (real) {
+        mm = piece_ml[slot_of(k8) * 2];
+        ll = piece_ml[slot_of(k8) * 2 + 1];
       }
-      float M = fmaxf(mm, xor_f(mm, 1));
-      M = fmaxf(M, xor_f(M, 2));
-      M = fmaxf(M, xor_f(M, 4));
-      const float wgt = mreal ? __builtin_amdgcn_exp2f(mm - M) : 0.f;
-      float den = wgt * ll;
-      den += xor_f(den, 1);
-      den += xor_f(den, 2);
-      den += xor_f(den, 4);
+      float src[NW][PER];
 #pragma unroll
-      for (int hh = 0; hh < GP; ++hh) {
-        if (hh >= p.group) break;
-        float src[NW][PER];
+      for (int k = 0; k < NW; ++k)
 #pragma unroll
-        for (int v = 0; v < NW; ++v)
+        for (int e = 0; e < PER; ++e) src[k][e] = piece_o[(size_t)slot_of(k) * D + lane * PER + e];
+      const float M = oct_max(mm);
+      const float wgt = real ? __builtin_amdgcn_exp2f(mm - M) : 0.f;
+      const float den = oct_sum(wgt * ll);
+      float o[PER];
 #pragma unroll
-          for (int e = 0; e < PER; ++e) src[v][e] = piece_o[(size_t)(piece(v) + hh) * D + lane * PER + e];
-        float o[PER];
+      for (int e = 0; e < PER; ++e) o[e] = 0.f;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) o[e] = 0.f;
+      for (int k = 0; k < NW; ++k) {
+        if (k < n) {
+          const float wv =
+              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgt), k));
 #pragma unroll
-        for (int v = 0; v < NW; ++v) {
-          const float wv = __builtin_bit_cast(
-              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgt), hh * 8 + v));
-#pragma unroll
-          for (int e = 0; e < PER; ++e) o[e] = v < n ? __builtin_fmaf(wv, src[v][e], o[e]) : o[e];
+          for (int e = 0; e < PER; ++e) o[e] = __builtin_fmaf(wv, src[k][e], o[e]);
         }
-        const float inv = 1.f / __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, den), hh * 8));
-        float* dst = p.out + ((size_t)s_first * p.q_heads + (size_t)g_first * p.group + hh) * D +
-                     lane * PER;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) dst[e] = o[e] * inv;
       }
+      const float inv = __builtin_amdgcn_rcpf(
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, den), 0)));
+      float* dst =
+          p.out + ((size_t)ms * p.q_heads + (size_t)mg * p.group + hh) * D + lane * PER;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) dst[e] = o[e] * inv;
+    };
+    if (active && (merge_info & (1 << 16))) {
+      // this wave's first segment: held by waves wf .. wf+n-1, this one the
+      // (wl - wf)-th; it merges heads wl - wf, wl - wf + n, ...
+      const int wf = merge_info & 7, sl0 = (merge_info >> 3) & 1, n = (merge_info >> 4) & 15;
+      for (int hh = wl - wf; hh < p.group; hh += n) merge_head(s_first, g_first, wf, sl0, n, hh);
+    }
+    if (active && (merge_info & (1 << 17))) {
+      // this wave's last segment: started here (slot 1), held by n waves
+      const int n = (merge_info >> 8) & 15;
+      for (int hh = 0; hh < p.group; hh += n) merge_head(s, g, wl, 1, n, hh);
     }
   }
 #ifdef PKV_TIMELINE

@@ -57,7 +57,7 @@ static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins, int b
   for (int b = 0; b < nbins; ++b) {
     // pieces[(wave, slot)] = (s, g)
     std::map<std::pair<int,int>, std::pair<int,int>> pieces;
-    std::vector<std::pair<int,int>> first_seg_of(8, {-1,-1});
+    std::vector<std::pair<int,int>> first_seg_of(8, {-1,-1}), last_seg_of(8, {-1,-1});
     for (int wl = 0; wl < 8; ++wl) {
       const int32_t* d = desc + 8 * (size_t)(b * 8 + wl);
       int li = d[0], count = d[1], s = d[2], g = d[3], j0 = d[4], L = d[5] & ((1 << 30) - 1), blk = d[6];
@@ -74,6 +74,7 @@ static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins, int b
         int take = std::min(count - x, nblk - j0);
         if (take <= 0) { printf("empty take\n"); return 1; }
         for (int j = j0; j < j0 + take; ++j) cov[{g, s, j}]++;
+        last_seg_of[wl] = {s, g};
         bool whole = j0 == 0 && j0 + take == nblk;
         if (!whole) pieces[{wl, first ? 0 : 1}] = {s, g};
         x += take;
@@ -86,20 +87,43 @@ static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins, int b
         if (e[3] != p->h_bt[(size_t)s * maxb]) { printf("bad list blk\n"); return 1; }
       }
     }
-    // merges
-    std::set<std::pair<int,int>> merged;
+    // merges: every holder of a split segment's piece merges the heads
+    // h = its index (mod n) among the n holders; (segment -> n, indices)
+    std::map<std::pair<int,int>, std::vector<std::pair<int,int>>> parts;
+    auto check_pieces = [&](std::pair<int,int> seg, int wf, int slot0, int n, int wl) {
+      for (int k = 0; k < n; ++k) {
+        auto it = pieces.find({wf + k, k == 0 ? slot0 : 0});
+        if (wf + k > 7 || it == pieces.end() || it->second != seg) {
+          printf("merge piece missing b%d w%d k%d\n", b, wl, k);
+          errors++;
+        }
+      }
+    };
     for (int wl = 0; wl < 8; ++wl) {
       const int32_t* d = desc + 8 * (size_t)(b * 8 + wl);
+      if (d[1] == 0) continue;
       int mi = d[7];
-      if (!(mi & (1 << 16))) continue;
-      int wa = mi & 0xff, wa_slot = (mi >> 8) & 1;
-      auto seg = first_seg_of[wl];
-      for (int v = wa; v <= wl; ++v) {
-        int sl = v == wa ? wa_slot : 0;
-        auto it = pieces.find({v, sl});
-        if (it == pieces.end() || it->second != seg) { printf("merge piece missing b%d w%d v%d\n", b, wl, v); errors++; }
+      if (mi & (1 << 16)) {
+        int wf = mi & 7, slot0 = (mi >> 3) & 1, n = (mi >> 4) & 15;
+        check_pieces(first_seg_of[wl], wf, slot0, n, wl);
+        parts[first_seg_of[wl]].push_back({n, wl - wf});
       }
-      merged.insert(seg);
+      if (mi & (1 << 17)) {
+        int n = (mi >> 8) & 15;
+        check_pieces(last_seg_of[wl], wl, 1, n, wl);
+        parts[last_seg_of[wl]].push_back({n, 0});
+      }
+    }
+    std::set<std::pair<int,int>> merged;
+    for (auto& kv : parts) {
+      const int n = kv.second[0].first;
+      std::set<int> idx;
+      for (auto& q : kv.second) {
+        if (q.first != n || q.second < 0 || q.second >= n) { printf("bad merge part\n"); errors++; }
+        idx.insert(q.second);
+      }
+      if ((int)idx.size() != n || (int)kv.second.size() != n) { printf("merge parts incomplete\n"); errors++; }
+      merged.insert(kv.first);
       merges++;
     }
     // every split segment in this bin merged exactly once
