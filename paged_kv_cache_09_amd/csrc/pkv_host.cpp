@@ -723,14 +723,17 @@ bool build_bins(pkv_pool* p, int nbins) {
       d[5] = p->h_ctx[sg.s] | p->h_slotflag[sg.s];
       d[6] = p->h_bt[(size_t)sg.s * p->up_stride + j0 * pkv::kTile / p->shape.block_size];
     }
-    // Merges of segments split between waves: every wave holding a piece of
-    // such a segment merges some of its heads (head h goes to the piece
-    // holder h mod n of the n holders). A wave takes part in at most two:
-    // its first segment's (bit 16: waves wf .. in bits 0-2, wf's piece slot in
-    // bit 3, n in bits 4-7) and its last segment's when that starts in this
-    // wave and continues (bit 17: n in bits 8-11).
+    // Segments split between waves: their pieces go to consecutive LDS piece
+    // slots (base .. base + n - 1, in holder order), and every holder merges
+    // some of the heads (head h goes to holder h mod n). Word 7 of a wave:
+    //   bits 0-3  slot of its first segment's piece (when that is split),
+    //   bits 4-7  slot of its last segment's piece (split, not its first),
+    //   bit 8     it merges heads of its first segment: bits 9-12 base slot,
+    //             bits 13-16 holders n, bits 17-19 its index among them;
+    //   bit 20    it merges heads of its last segment (index 0): bits 21-24 n.
     {
       int64_t sx = 0;
+      int base = 0;
       for (size_t k = 0; k < m.size(); ++k) {
         const int64_t n0 = segs[m[k]].cost - kSegStartCost;
         const int64_t a = sx, e = sx + n0;  // the segment's bin-local tiles [a, e)
@@ -745,13 +748,17 @@ bool build_bins(pkv_pool* p, int nbins) {
         }
         if (wf < 0 || wlast == wf) continue;
         const int n = wlast - wf + 1;
-        // the first holder's piece is slot 0 when the segment is its first, else slot 1
-        const int slot = start_tile[wf] < a ? 1 : 0;
         for (int wv = wf; wv <= wlast; ++wv) {
           int32_t* d = desc + (size_t)8 * (b * kBinWaves + wv);
-          if (wv == wf && slot == 1) d[7] |= (1 << 17) | (n << 8);
-          else d[7] |= (1 << 16) | wf | (slot << 3) | (n << 4);
+          const int slot = base + (wv - wf);
+          if (wv == wf && start_tile[wf] < a) {
+            // the segment starts inside this wave's run: its last segment
+            d[7] |= (slot << 4) | (1 << 20) | (n << 21);
+          } else {
+            d[7] |= slot | (1 << 8) | (base << 9) | (n << 13) | ((wv - wf) << 17);
+          }
         }
+        base += n;
       }
     }
   }

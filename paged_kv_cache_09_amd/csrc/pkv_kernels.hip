@@ -779,9 +779,12 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
   __shared__ float l_lds_all[NW][GP];          // per-head sums at the end of a run
   __shared__ float m_lds_all[NW][GP];          // per-head maxima at the end of a run
   // BINS: pieces (o, m, l) of segments split between this workgroup's waves,
-  // slot 0 = the wave's first segment, slot 1 = its last
-  __shared__ float piece_o[BINS ? NW * 2 * GP * D : 1];
-  __shared__ float piece_ml[BINS ? NW * 2 * GP * 2 : 1];
+  // in the slots the host gives (a split segment's n pieces in n consecutive
+  // slots; at most two pieces per wave), plus NW - 1 spare slots that merges
+  // read past a segment's last piece without a bounds check
+  constexpr int NSLOT = NW * 2 + NW - 1;
+  __shared__ float piece_o[BINS ? NSLOT * GP * D : 1];
+  __shared__ float piece_ml[BINS ? NSLOT * GP * 2 : 1];
 
   // the first nprefix workgroups (split form) take the shared-prefix items
   constexpr bool PFX = !BINS && D == 128 && (DT == DT_F16 || DT == DT_BF16) && GP <= 4;
@@ -1548,8 +1551,8 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         }
       }
     } else if constexpr (BINS) {
-      const int slot = first_seg ? 0 : 1;
-      float* po = piece_o + (size_t)((wl * 2 + slot) * GP) * D + pv_col;
+      const int slot = first_seg ? (merge_info & 15) : ((merge_info >> 4) & 15);
+      float* po = piece_o + (size_t)(slot * GP) * D + pv_col;
       if (pv_lane) {
 #pragma unroll
         for (int h = 0; h < GP; ++h)
@@ -1557,8 +1560,8 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
           for (int e = 0; e < EPC; ++e) po[(size_t)h * D + e] = acc[h][e];
       }
       if (lane < p.group) {
-        piece_ml[((wl * 2 + slot) * GP + lane) * 2 + 0] = m_lds[lane];
-        piece_ml[((wl * 2 + slot) * GP + lane) * 2 + 1] = l_lds[lane];
+        piece_ml[(slot * GP + lane) * 2 + 0] = m_lds[lane];
+        piece_ml[(slot * GP + lane) * 2 + 1] = l_lds[lane];
       }
     } else {
       // slots of segment seg: ((seg + 1) * stride - 1) + its waves; the
@@ -1614,25 +1617,23 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
 #ifdef PKV_TIMELINE
     tl_tb = __builtin_amdgcn_s_memrealtime();
 #endif
-    // Head hh of a segment whose n pieces are held by waves w0 .. w0+n-1
-    // (w0's piece in slot sl0, the others' in slot 0). Every LDS read is
-    // issued before the arithmetic: lane k < n of each 8 reads piece k's max
-    // and sum, and every lane its D/64 columns of every piece.
-    auto merge_head = [&](int ms, int mg, int w0, int sl0, int n, int hh) {
+    // Head hh of a segment whose n pieces are in slots base .. base+n-1. All
+    // LDS reads are issued before the arithmetic: lane k < n of each 8 reads
+    // piece k's max and sum, and every lane its D/64 columns of every piece
+    // (slots past the last piece are spare ones).
+    auto merge_head = [&](int ms, int mg, int base, int n, int hh) {
       constexpr int PER = D / 64;
-      auto slot_of = [&](int k) { return (min(w0 + k, NW - 1) * 2 + (k == 0 ? sl0 : 0)) * GP + hh; };
       const int k8 = lane & 7;
       const bool real = k8 < n;
-      float mm = -__builtin_inff(), ll = 0.f;
-      if (real) {
-        mm = piece_ml[slot_of(k8) * 2];
-        ll = piece_ml[slot_of(k8) * 2 + 1];
-      }
+      const float* mlp = piece_ml + ((base + k8) * GP + hh) * 2;
+      float mm = real ? mlp[0] : -__builtin_inff();
+      float ll = real ? mlp[1] : 0.f;
+      const float* op = piece_o + (size_t)(base * GP + hh) * D + lane * PER;
       float src[NW][PER];
 #pragma unroll
       for (int k = 0; k < NW; ++k)
 #pragma unroll
-        for (int e = 0; e < PER; ++e) src[k][e] = piece_o[(size_t)slot_of(k) * D + lane * PER + e];
+        for (int e = 0; e < PER; ++e) src[k][e] = op[(size_t)k * GP * D + e];
       const float M = oct_max(mm);
       const float wgt = real ? __builtin_amdgcn_exp2f(mm - M) : 0.f;
       const float den = oct_sum(wgt * ll);
@@ -1655,16 +1656,18 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
 #pragma unroll
       for (int e = 0; e < PER; ++e) dst[e] = o[e] * inv;
     };
-    if (active && (merge_info & (1 << 16))) {
-      // this wave's first segment: held by waves wf .. wf+n-1, this one the
-      // (wl - wf)-th; it merges heads wl - wf, wl - wf + n, ...
-      const int wf = merge_info & 7, sl0 = (merge_info >> 3) & 1, n = (merge_info >> 4) & 15;
-      for (int hh = wl - wf; hh < p.group; hh += n) merge_head(s_first, g_first, wf, sl0, n, hh);
+    if (active && (merge_info & (1 << 8))) {
+      // this wave's first segment: n pieces from slot base, this wave the
+      // idx-th holder; it merges heads idx, idx + n, ...
+      const int base = (merge_info >> 9) & 15, n = (merge_info >> 13) & 15;
+      for (int hh = (merge_info >> 17) & 7; hh < p.group; hh += n)
+        merge_head(s_first, g_first, base, n, hh);
     }
-    if (active && (merge_info & (1 << 17))) {
-      // this wave's last segment: started here (slot 1), held by n waves
-      const int n = (merge_info >> 8) & 15;
-      for (int hh = 0; hh < p.group; hh += n) merge_head(s, g, wl, 1, n, hh);
+    if (active && (merge_info & (1 << 20))) {
+      // this wave's last segment: started here, its n pieces from this
+      // wave's slot on
+      const int base = (merge_info >> 4) & 15, n = (merge_info >> 21) & 15;
+      for (int hh = 0; hh < p.group; hh += n) merge_head(s, g, base, n, hh);
     }
   }
 #ifdef PKV_TIMELINE

@@ -55,8 +55,8 @@ static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins, int b
   std::map<std::tuple<int,int,int>, int> cov;
   int merges = 0, errors = 0;
   for (int b = 0; b < nbins; ++b) {
-    // pieces[(wave, slot)] = (s, g)
-    std::map<std::pair<int,int>, std::pair<int,int>> pieces;
+    // pieces[LDS slot] = (s, g)
+    std::map<int, std::pair<int,int>> pieces;
     std::vector<std::pair<int,int>> first_seg_of(8, {-1,-1}), last_seg_of(8, {-1,-1});
     for (int wl = 0; wl < 8; ++wl) {
       const int32_t* d = desc + 8 * (size_t)(b * 8 + wl);
@@ -76,7 +76,11 @@ static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins, int b
         for (int j = j0; j < j0 + take; ++j) cov[{g, s, j}]++;
         last_seg_of[wl] = {s, g};
         bool whole = j0 == 0 && j0 + take == nblk;
-        if (!whole) pieces[{wl, first ? 0 : 1}] = {s, g};
+        if (!whole) {
+          const int slot = first ? (d[7] & 15) : ((d[7] >> 4) & 15);
+          if (pieces.count(slot)) { printf("piece slot %d written twice in bin %d\n", slot, b); errors++; }
+          pieces[slot] = {s, g};
+        }
         x += take;
         if (x >= count) break;
         ++li;
@@ -90,10 +94,10 @@ static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins, int b
     // merges: every holder of a split segment's piece merges the heads
     // h = its index (mod n) among the n holders; (segment -> n, indices)
     std::map<std::pair<int,int>, std::vector<std::pair<int,int>>> parts;
-    auto check_pieces = [&](std::pair<int,int> seg, int wf, int slot0, int n, int wl) {
+    auto check_pieces = [&](std::pair<int,int> seg, int base, int n, int wl) {
       for (int k = 0; k < n; ++k) {
-        auto it = pieces.find({wf + k, k == 0 ? slot0 : 0});
-        if (wf + k > 7 || it == pieces.end() || it->second != seg) {
+        auto it = pieces.find(base + k);
+        if (base + k > 15 || it == pieces.end() || it->second != seg) {
           printf("merge piece missing b%d w%d k%d\n", b, wl, k);
           errors++;
         }
@@ -103,14 +107,14 @@ static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins, int b
       const int32_t* d = desc + 8 * (size_t)(b * 8 + wl);
       if (d[1] == 0) continue;
       int mi = d[7];
-      if (mi & (1 << 16)) {
-        int wf = mi & 7, slot0 = (mi >> 3) & 1, n = (mi >> 4) & 15;
-        check_pieces(first_seg_of[wl], wf, slot0, n, wl);
-        parts[first_seg_of[wl]].push_back({n, wl - wf});
+      if (mi & (1 << 8)) {
+        int base = (mi >> 9) & 15, n = (mi >> 13) & 15, idx = (mi >> 17) & 7;
+        check_pieces(first_seg_of[wl], base, n, wl);
+        parts[first_seg_of[wl]].push_back({n, idx});
       }
-      if (mi & (1 << 17)) {
-        int n = (mi >> 8) & 15;
-        check_pieces(last_seg_of[wl], wl, 1, n, wl);
+      if (mi & (1 << 20)) {
+        int n = (mi >> 21) & 15;
+        check_pieces(last_seg_of[wl], (mi >> 4) & 15, n, wl);
         parts[last_seg_of[wl]].push_back({n, 0});
       }
     }
