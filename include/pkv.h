@@ -91,11 +91,11 @@ enum {
 typedef struct {
   int32_t layers;      /* layers sharing one block id space                      */
   int32_t num_blocks;  /* physical blocks per layer                              */
-  int32_t block_size;  /* tokens per block; must be 16                           */
+  int32_t block_size;  /* tokens per block: 8, 16 (the pages' default) or 32     */
   int32_t kv_heads;    /* stored K/V heads                                       */
   int32_t head_dim;    /* 64 or 128                                              */
-  int32_t dtype;       /* PKV_F32 | PKV_F16 | PKV_BF16                           */
-  int32_t max_seq_len; /* longest context any sequence may reach                 */
+  int32_t dtype;       /* PKV_F32 | PKV_F16 | PKV_BF16 | PKV_Q8_0 | PKV_Q4_0     */
+  int32_t max_seq_len; /* longest context any sequence may reach (< 2^30)        */
   int32_t max_seqs;    /* largest batch passed to upload/prepare                 */
 } pkv_shape;
 
@@ -157,7 +157,14 @@ int pkv_block_free(pkv_pool* pool, const int32_t* ids, int n);
 int pkv_block_refcount(const pkv_pool* pool, int32_t id);
 
 /*
- * Slot assignment for one decode step. host_bt is the caller's block table,
+ * Slot assignment for one decode step: each sequence's new token gets the
+ * row after its cached ones, in a block taken on demand when the token starts
+ * a new one (thienlv.com, "PagedAttention là gì?", "How does PagedAttention
+ * work?": physical blocks are handed out only when needed and recorded in the
+ * block table), and a block still shared by other sequences is copied before
+ * it is written (ahmedhaies.com, "PagedAttention: why LLM serving wastes most
+ * GPU memory", the copy-on-write paragraph after "The solution: borrow virtual
+ * memory from the OS"). host_bt is the caller's block table,
  * int32 [batch][max_blocks] row-major, -1 for absent entries; ctx_lens[s] is
  * the context length with the new token included (>= 1). For each sequence in
  * batch order, with p = ctx_lens[s] - 1 and j = p / 16:
@@ -168,8 +175,10 @@ int pkv_block_refcount(const pkv_pool* pool, int32_t id);
  *   - otherwise the block is written in place.
  * slot_out[s] = host_bt[s][j] * 16 + p % 16 (int64).
  * cow_pairs_out receives n_cow (old, new) int32 pairs; cow_capacity is its
- * capacity in pairs (batch always suffices). On any failure (including
- * PKV_EOUT_OF_BLOCKS) every change made by this call is undone.
+ * capacity in pairs (batch always suffices). Every check and the count of
+ * blocks the call needs come before any change, so a failing call (including
+ * PKV_EOUT_OF_BLOCKS) changes nothing: no table entry, reference count or
+ * prefix-cache entry.
  */
 int pkv_prepare_append(pkv_pool* pool, int32_t* host_bt, int batch, int max_blocks,
                        const int32_t* ctx_lens, int64_t* slot_out, int32_t* cow_pairs_out,
@@ -196,7 +205,12 @@ int pkv_prepare_write(pkv_pool* pool, int32_t* host_bt, int batch, int max_block
                       int* n_cow);
 
 /*
- * Upload the block table int32 [batch][max_blocks] (-1 padded), the context
+ * Block-table upload: the per-sequence map from logical block to physical
+ * block that the decode kernels read the cache through (thienlv.com,
+ * "PagedAttention là gì?", "How does PagedAttention work?"; ahmedhaies.com,
+ * "PagedAttention: why LLM serving wastes most GPU memory", "The solution:
+ * borrow virtual memory from the OS", where it plays the role of the page
+ * table). Upload the block table int32 [batch][max_blocks] (-1 padded), the context
  * lengths int32 [batch] and optionally the slots int64 [batch] (NULL: keep
  * none) to the library's device copies, asynchronously on `stream`: the
  * data is packed into coherent pinned staging (a ring of four buffers, each
@@ -222,7 +236,9 @@ int pkv_block_table_upload(pkv_pool* pool, const int32_t* host_bt, int batch, in
 int pkv_copy_blocks(pkv_pool* pool, const int32_t* host_pairs, int n, uintptr_t stream);
 
 /*
- * Append: for s < batch and every kv head g, write k_new[s][g][:] and
+ * Append: each decode step stores the new token's key and value in the cache
+ * (news.hamidun.com glossary "KV-Cache", prefill/decode paragraph), here at
+ * the slot the block table gives it. For s < batch and every kv head g, write k_new[s][g][:] and
  * v_new[s][g][:] (cache dtype, [batch][kv_heads][head_dim]; bf16 when quantised)
  * into the pool row of layer `layer` at slot[s] (block slot / block_size, row
  * slot % block_size); slot < 0 skips. dev_slots: device int64 [batch], or NULL for the
@@ -230,7 +246,9 @@ int pkv_copy_blocks(pkv_pool* pool, const int32_t* host_pairs, int n, uintptr_t 
  * are copied unchanged (q8_0 / q4_0: quantised as described above). With device
  * slots, "batch" is any number of rows: the multi-token write of a prefill
  * passes one row and one slot (from pkv_prepare_write) per token; the slots
- * must be distinct.
+ * must be distinct. Device slots are not checked on the host; a slot outside
+ * [0, num_blocks * block_size) is skipped by the kernel (nothing is written
+ * for that row).
  */
 int pkv_kv_append(pkv_pool* pool, int layer, const void* k_new, const void* v_new,
                   const int64_t* dev_slots, int batch, uintptr_t stream);
@@ -289,8 +307,11 @@ size_t pkv_decode_workspace_bytes(const pkv_pool* pool, int batch, int q_heads,
  * ssdnodes.com, "KV cache vs prompt cache", "When local and remote caching
  * intersect"): a full block's K/V depend on every token up to its end, so a
  * block is keyed by its token ids together with the key of the block before
- * it (a chained FNV-1a 64-bit hash, confirmed by comparing the stored token
- * ids). Cached blocks whose last reference is released stay reusable
+ * it. A block is found through a chained FNV-1a 64-bit hash of the prefix and
+ * then confirmed exactly: its stored token ids must equal the request's, and
+ * the block it was cached behind must be the block matched just before (the
+ * same id with the same cache generation; a block id keyed again for other
+ * content gets a new generation). Cached blocks whose last reference is released stay reusable
  * ("evictable") instead of returning to the free list; when the free list is
  * empty, allocation takes the least recently released evictable block and
  * drops its cache entry. Writing into a cached block held by one sequence

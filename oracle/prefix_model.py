@@ -38,11 +38,16 @@ class PrefixModel:
     def available(self) -> int:
         return self.free + len(self.lru)
 
+    def key(self, tokens, j):
+        """Cache key of full block j of a prompt: every token from the first
+        through the block's last (the block's K/V depend on all of them)."""
+        return tuple(tokens[:(j + 1) * self.bs])
+
     def match(self, tokens):
         out = []
         j = 0
         while (j + 1) * self.bs <= len(tokens):
-            b = self.cache.get(tuple(tokens[:(j + 1) * self.bs]))
+            b = self.cache.get(self.key(tokens, j))
             if b is None:
                 break
             if b.ref == 0:
@@ -70,7 +75,7 @@ class PrefixModel:
     def insert(self, tokens, blocks):
         added = 0
         for j in range(min(len(tokens) // self.bs, len(blocks))):
-            key = tuple(tokens[:(j + 1) * self.bs])
+            key = self.key(tokens, j)
             b = blocks[j]
             if b.key is None and key not in self.cache:
                 b.key = key

@@ -111,7 +111,12 @@ struct pkv_pool {
   // empty.
   std::unordered_multimap<uint64_t, int32_t> by_hash;
   std::vector<char> cached;
-  std::vector<uint64_t> blk_hash, blk_parent;
+  std::vector<uint64_t> blk_hash;   // lookup key: chained hash of the prefix
+  // exact identity of a cached block's prefix: the cached block before it
+  // (-1 for a first block) and that block's cache generation when this one
+  // was registered (a block id reused for other content gets a new one)
+  std::vector<int32_t> blk_parent;
+  std::vector<uint32_t> blk_parent_gen, blk_gen;
   std::vector<int32_t> blk_tokens;  // block_size token ids per cached block
   std::list<int32_t> lru;           // evictable blocks, oldest first
   std::vector<std::list<int32_t>::iterator> lru_pos;
@@ -809,7 +814,9 @@ int pkv_kv_pool_alloc(const pkv_shape* sh, void* dev_base, size_t dev_bytes, pkv
   p->in_lru.assign(sh->num_blocks, 0);
   p->lru_pos.resize(sh->num_blocks);
   p->blk_hash.assign(sh->num_blocks, 0);
-  p->blk_parent.assign(sh->num_blocks, 0);
+  p->blk_parent.assign(sh->num_blocks, -1);
+  p->blk_parent_gen.assign(sh->num_blocks, 0);
+  p->blk_gen.assign(sh->num_blocks, 0);
   for (int32_t id = sh->num_blocks - 1; id >= 0; --id) free_push(p, id);  // pops 0, 1, 2, ...
 
   if (dev_base) {
@@ -941,7 +948,9 @@ namespace {
 // copied first when shared (refcount > 1), else written in place
 // (thienlv.com, "PagedAttention là gì?", "How does PagedAttention work?";
 // ahmedhaies.com, "PagedAttention: why LLM serving wastes most GPU memory",
-// copy-on-write paragraph). All-or-nothing: a failure undoes every change.
+// copy-on-write paragraph). All-or-nothing: every check and the block count
+// come first, so a failing call changes nothing (a taken block may evict a
+// cached one, which could not be undone).
 int prepare_core(pkv_pool* p, int32_t* bt, int batch, int max_blocks, const int32_t* ctx_before,
                  const int32_t* n_new, int64_t* slot_out, int64_t slot_capacity,
                  int32_t* cow_out, int cow_capacity, int* n_cow) {
@@ -962,6 +971,46 @@ int prepare_core(pkv_pool* p, int32_t* bt, int batch, int max_blocks, const int3
     }
     for (int32_t id : unref) ++p->refcount[id];
   };
+  // Check everything and count the blocks the call takes before changing
+  // anything: taking a block may evict a cached one, which a rollback could
+  // not restore. The second pass below then cannot fail.
+  {
+    std::unordered_map<int32_t, int32_t> rc_drop;  // references CoW moves off a block
+    int64_t need = 0, nslot_chk = 0;
+    int ncow_chk = 0;
+    for (int s = 0; s < batch; ++s) {
+      const int64_t L0 = ctx_before[s], n = n_new[s], L1 = L0 + n;
+      if (L0 < 0 || n < 0 || L1 > p->shape.max_seq_len || (L1 + BS - 1) / BS > max_blocks)
+        return fail(PKV_EINVAL, "sequence %d: tokens [%lld, %lld) outside [0, %lld)", s,
+                    (long long)L0, (long long)L1,
+                    (long long)std::min<int64_t>(p->shape.max_seq_len, (int64_t)max_blocks * BS));
+      if (nslot_chk + n > slot_capacity)
+        return fail(PKV_EINVAL, "slot buffer too small (%lld)", (long long)slot_capacity);
+      nslot_chk += n;
+      if (n == 0) continue;
+      for (int64_t jb = L0 / BS; jb <= (L1 - 1) / BS; ++jb) {
+        const int32_t b = bt[(int64_t)s * max_blocks + jb];
+        if (b < 0) {
+          ++need;
+          continue;
+        }
+        if (b >= p->shape.num_blocks || p->refcount[b] < 1)
+          return fail(PKV_EINVAL, "sequence %d: table entry %d is not an allocated block", s, b);
+        auto it = rc_drop.find(b);
+        const int32_t rc = p->refcount[b] - (it == rc_drop.end() ? 0 : it->second);
+        if (rc > 1) {
+          ++need;
+          ++ncow_chk;
+          ++rc_drop[b];
+        }
+      }
+    }
+    if (ncow_chk > 0 && (!cow_out || ncow_chk > cow_capacity))
+      return fail(PKV_EINVAL, "copy-on-write pair buffer too small (%d)", cow_capacity);
+    if ((size_t)need > avail(p))
+      return fail(PKV_EOUT_OF_BLOCKS, "the step needs %lld blocks, %zu free", (long long)need,
+                  avail(p));
+  }
   for (int s = 0; s < batch; ++s) {
     const int64_t L0 = ctx_before[s], n = n_new[s], L1 = L0 + n;
     if (L0 < 0 || n < 0 || L1 > p->shape.max_seq_len || (L1 + BS - 1) / BS > max_blocks) {
@@ -1203,14 +1252,15 @@ int pkv_kv_append(pkv_pool* p, int layer, const void* k_new, const void* v_new,
   }
   char* kl = p->k_base + (size_t)layer * p->layer_bytes;
   char* vl = p->v_base + (size_t)layer * p->layer_bytes;
+  const int64_t num_slots = (int64_t)p->shape.num_blocks * p->shape.block_size;
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_u);
   hipError_t e =
       quantised(p->shape.dtype)
           ? pkv::launch_append_quant(p->shape.dtype, k_new, v_new, slots, batch, kl, vl,
                                      p->shape.kv_heads, p->shape.head_dim, p->shape.block_size,
-                                     stream)
+                                     num_slots, stream)
           : pkv::launch_append(k_new, v_new, slots, batch, kl, vl, p->shape.kv_heads,
-                               (int)p->row_bytes, p->shape.block_size, stream);
+                               (int)p->row_bytes, p->shape.block_size, num_slots, stream);
   if (e != hipSuccess) return hip_fail(e, "kv_append launch");
   return PKV_OK;
 }
@@ -1401,12 +1451,16 @@ uint64_t block_hash(uint64_t parent, const int32_t* tokens, int n) {
   return h;
 }
 
-int32_t cache_find(const pkv_pool* p, uint64_t h, uint64_t parent, const int32_t* tokens) {
+// The cached block holding `tokens` right after the cached block `parent`
+// (-1: at the start of a prompt) whose cache generation is `parent_gen`, or
+// -1. The hash only narrows the search; the match is exact.
+int32_t cache_find(const pkv_pool* p, uint64_t h, int32_t parent, uint32_t parent_gen,
+                   const int32_t* tokens) {
   const int BS = p->shape.block_size;
   auto range = p->by_hash.equal_range(h);
   for (auto it = range.first; it != range.second; ++it) {
     const int32_t id = it->second;
-    if (p->blk_parent[id] == parent &&
+    if (p->blk_parent[id] == parent && (parent < 0 || p->blk_parent_gen[id] == parent_gen) &&
         std::memcmp(&p->blk_tokens[(size_t)id * BS], tokens, (size_t)BS * 4) == 0)
       return id;
   }
@@ -1423,17 +1477,21 @@ int pkv_prefix_match(pkv_pool* p, const int32_t* tokens, int n_tokens, int32_t* 
       (max_ids > 0 && !ids_out))
     return fail(PKV_EINVAL, "bad arguments");
   const int BS = p->shape.block_size;
-  uint64_t parent = 0;
+  uint64_t h_prev = 0;
+  int32_t parent = -1;
+  uint32_t parent_gen = 0;
   int k = 0;
   for (; k < max_ids && (int64_t)(k + 1) * BS <= n_tokens; ++k) {
     const int32_t* t = tokens + (size_t)k * BS;
-    const uint64_t h = block_hash(parent, t, BS);
-    const int32_t id = cache_find(p, h, parent, t);
+    const uint64_t h = block_hash(h_prev, t, BS);
+    const int32_t id = cache_find(p, h, parent, parent_gen, t);
     if (id < 0) break;
     if (p->refcount[id] == 0) lru_remove(p, id);
     ++p->refcount[id];
     ids_out[k] = id;
-    parent = h;
+    h_prev = h;
+    parent = id;
+    parent_gen = p->blk_gen[id];
   }
   p->prefix_hits += k;
   return k;
@@ -1450,22 +1508,33 @@ int pkv_prefix_insert(pkv_pool* p, const int32_t* tokens, int n_tokens, const in
     if (id < 0 || id >= p->shape.num_blocks || p->refcount[id] < 1)
       return fail(PKV_EINVAL, "entry %d = %d is not an allocated block", j, id);
   }
-  uint64_t parent = 0;
+  uint64_t h_prev = 0;
+  int32_t parent = -1;
+  uint32_t parent_gen = 0;
   int added = 0;
   for (int j = 0; j < full; ++j) {
     const int32_t id = bt_row[j];
     const int32_t* t = tokens + (size_t)j * BS;
-    const uint64_t h = block_hash(parent, t, BS);
-    if (!p->cached[id] && cache_find(p, h, parent, t) < 0) {
+    const uint64_t h = block_hash(h_prev, t, BS);
+    int32_t canon = cache_find(p, h, parent, parent_gen, t);
+    if (canon < 0) {
+      // a block cached under another prefix cannot be keyed again: the
+      // chain of this prompt stops here
+      if (p->cached[id]) break;
       p->cached[id] = 1;
       p->blk_hash[id] = h;
       p->blk_parent[id] = parent;
+      p->blk_parent_gen[id] = parent_gen;
+      ++p->blk_gen[id];
       if (p->blk_tokens.empty()) p->blk_tokens.assign((size_t)p->shape.num_blocks * BS, 0);
       std::memcpy(&p->blk_tokens[(size_t)id * BS], t, (size_t)BS * 4);
       p->by_hash.emplace(h, id);
       ++added;
+      canon = id;
     }
-    parent = h;
+    h_prev = h;
+    parent = canon;
+    parent_gen = p->blk_gen[canon];
   }
   return added;
 }

@@ -81,14 +81,16 @@ bool prefix_supported(int dtype, int head_dim, int gp);
 // Workgroups of the decode kernel one CU can hold at once (occupancy), 0 on error.
 int decode_blocks_per_cu(int dtype, int head_dim, int gp, bool bins, int block_size);
 
+// Slots outside [0, num_slots) are skipped.
 hipError_t launch_append(const void* k_new, const void* v_new, const int64_t* slots, int batch,
                          void* k_layer, void* v_layer, int kv_heads, int row_bytes,
-                         int block_size, hipStream_t stream);
+                         int block_size, int64_t num_slots, hipStream_t stream);
 // q8_0 / q4_0 cache (dtype 3 / 4): quantise bf16 new rows
 // [batch][kv_heads][head_dim] into the rows at `slots`.
 hipError_t launch_append_quant(int dtype, const void* k_new, const void* v_new,
                                const int64_t* slots, int batch, void* k_layer, void* v_layer,
-                               int kv_heads, int head_dim, int block_size, hipStream_t stream);
+                               int kv_heads, int head_dim, int block_size, int64_t num_slots,
+                               hipStream_t stream);
 // Copy `bytes` (a multiple of 16, both pointers 16-byte aligned) from mapped
 // pinned host memory to device memory with a kernel on `stream`.
 hipError_t launch_upload(const void* host_src, void* dst, size_t bytes, hipStream_t stream);

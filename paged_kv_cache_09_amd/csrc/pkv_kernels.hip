@@ -1707,10 +1707,13 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
                         w1 - w0 + 1 + npre, hh, p.out + ((size_t)s * p.q_heads + h) * D, lane);
 }
 
+// Appends skip a slot outside [0, num_slots) (num_blocks * block_size): a
+// stale or bad slot from the caller never becomes a store outside the pool.
 __global__ __launch_bounds__(256) void append_kernel(const char* k_new, const char* v_new,
                                                      const int64_t* slots, int batch,
                                                      char* k_layer, char* v_layer, int kv_heads,
-                                                     int row_bytes, int block_size) {
+                                                     int row_bytes, int block_size,
+                                                     int64_t num_slots) {
   const int per_row = row_bytes / 16;
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   const int chunk = (int)(idx % per_row);
@@ -1721,7 +1724,7 @@ __global__ __launch_bounds__(256) void append_kernel(const char* k_new, const ch
   const long s = r / kv_heads;
   if (s >= batch) return;
   const int64_t slot = slots[s];
-  if (slot < 0) return;
+  if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot / block_size;
   const int64_t pos = slot % block_size;
   const char* src = (kv ? v_new : k_new) + ((size_t)s * kv_heads + g) * row_bytes + chunk * 16;
@@ -1737,7 +1740,8 @@ template <int D>
 __global__ __launch_bounds__(256) void append_q8_kernel(const char* k_new, const char* v_new,
                                                         const int64_t* slots, int batch,
                                                         char* k_layer, char* v_layer,
-                                                        int kv_heads, int block_size) {
+                                                        int kv_heads, int block_size,
+                                                        int64_t num_slots) {
   constexpr int NGR = D / 32;
   const int BS = block_size;
   const int TILE = BS * D + BS * NGR * 2;
@@ -1750,7 +1754,7 @@ __global__ __launch_bounds__(256) void append_q8_kernel(const char* k_new, const
   const long s = r / kv_heads;
   if (s >= batch) return;
   const int64_t slot = slots[s];
-  if (slot < 0) return;
+  if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot / BS;
   const int pos = (int)(slot % BS);
   const char* src = (kv ? v_new : k_new) + (((size_t)s * kv_heads + g) * D + grp * 32) * 2;
@@ -1781,7 +1785,8 @@ template <int D>
 __global__ __launch_bounds__(256) void append_q4_kernel(const char* k_new, const char* v_new,
                                                         const int64_t* slots, int batch,
                                                         char* k_layer, char* v_layer,
-                                                        int kv_heads, int block_size) {
+                                                        int kv_heads, int block_size,
+                                                        int64_t num_slots) {
   constexpr int NGR = D / 32;
   constexpr int CB = D / 2;
   const int BS = block_size;
@@ -1795,7 +1800,7 @@ __global__ __launch_bounds__(256) void append_q4_kernel(const char* k_new, const
   const long s = r / kv_heads;
   if (s >= batch) return;
   const int64_t slot = slots[s];
-  if (slot < 0) return;
+  if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot / BS;
   const int pos = (int)(slot % BS);
   const char* src = (kv ? v_new : k_new) + (((size_t)s * kv_heads + g) * D + grp * 32) * 2;
@@ -1950,33 +1955,35 @@ bool prefix_supported(int dtype, int head_dim, int gp) {
 
 hipError_t launch_append(const void* k_new, const void* v_new, const int64_t* slots, int batch,
                          void* k_layer, void* v_layer, int kv_heads, int row_bytes,
-                         int block_size, hipStream_t stream) {
+                         int block_size, int64_t num_slots, hipStream_t stream) {
   const long threads = (long)batch * kv_heads * 2 * (row_bytes / 16);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   hipLaunchKernelGGL(append_kernel, dim3(blocks), dim3(256), 0, stream,
                      static_cast<const char*>(k_new), static_cast<const char*>(v_new), slots,
                      batch, static_cast<char*>(k_layer), static_cast<char*>(v_layer), kv_heads,
-                     row_bytes, block_size);
+                     row_bytes, block_size, num_slots);
   return hipGetLastError();
 }
 
 hipError_t launch_append_quant(int dtype, const void* k_new, const void* v_new,
                                const int64_t* slots, int batch, void* k_layer, void* v_layer,
-                               int kv_heads, int head_dim, int block_size, hipStream_t stream) {
+                               int kv_heads, int head_dim, int block_size, int64_t num_slots,
+                               hipStream_t stream) {
   const long threads = (long)batch * kv_heads * 2 * (head_dim / 32);
   const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
   const char* kn = static_cast<const char*>(k_new);
   const char* vn = static_cast<const char*>(v_new);
   char* kl = static_cast<char*>(k_layer);
   char* vl = static_cast<char*>(v_layer);
-  void (*fn)(const char*, const char*, const int64_t*, int, char*, char*, int, int) = nullptr;
+  void (*fn)(const char*, const char*, const int64_t*, int, char*, char*, int, int, int64_t) =
+      nullptr;
   if (dtype == DT_Q8) fn = head_dim == 128 ? append_q8_kernel<128>
                            : head_dim == 64 ? append_q8_kernel<64> : nullptr;
   if (dtype == DT_Q4) fn = head_dim == 128 ? append_q4_kernel<128>
                            : head_dim == 64 ? append_q4_kernel<64> : nullptr;
   if (!fn) return hipErrorInvalidValue;
   hipLaunchKernelGGL(fn, grid, block, 0, stream, kn, vn, slots, batch, kl, vl, kv_heads,
-                     block_size);
+                     block_size, num_slots);
   return hipGetLastError();
 }
 

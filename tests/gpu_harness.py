@@ -148,8 +148,10 @@ def run_step_case(cfg, *, layers=1, partitions=(0,), sample=None, check_untouche
             else:
                 sess.decode(layer, out, part)
             torch.cuda.synchronize()
+            # every sequence's output is finite, compared or not
+            assert bool(torch.isfinite(out).all()), \
+                f"non-finite output layer {layer} partition {part}"
             got = out.cpu().numpy()[seqs]
-            assert np.isfinite(got).all(), f"non-finite output layer {layer} partition {part}"
             errs[(layer, part)] = float(np.max(np.abs(got - ora.out[layer])))
             outs[(layer, part)] = out
     say(f"case {label or cfg.name}: max errors {errs}")

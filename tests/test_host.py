@@ -365,3 +365,49 @@ def test_prepare_write_rolls_back_and_checks_capacity():
     assert slots.tolist() == [table[0, 0] * 16 + i for i in range(16)] + \
         [table[0, 1] * 16 + i for i in range(4)] and len(pairs) == 0
     pkv.kv_pool_free(h)
+
+
+def test_failed_prepare_keeps_cached_blocks():
+    # two cached, evictable blocks in a 3-block pool; a write that needs 3
+    # blocks must fail without evicting them or dropping their entries
+    h = host_pool(num_blocks=3, max_seq_len=48)
+    toks = list(range(500, 532))                       # two full blocks
+    t1 = np.full((1, 3), -1, np.int32)
+    pkv.prepare_write(h, t1, [0], [32])
+    assert pkv.prefix_insert(h, toks, t1[0, :2]) == 2
+    pkv.block_free(h, t1[0, :2])
+    before = pkv.prefix_stats(h)
+    assert before["cached"] == 2 and before["evictable"] == 2 and before["evictions"] == 0
+    t3 = np.full((2, 3), -1, np.int32)
+    with pytest.raises(pkv.PkvError) as e:              # 2 + 2 blocks > 3
+        pkv.prepare_write(h, t3, [0, 0], [32, 17])
+    assert e.value.code == pkv.EOUT_OF_BLOCKS
+    assert (t3 == -1).all()
+    after = pkv.prefix_stats(h)
+    assert after["cached"] == 2 and after["evictable"] == 2 and after["evictions"] == 0
+    assert pkv.prefix_match(h, toks).tolist() == t1[0, :2].tolist()
+    pkv.kv_pool_free(h)
+
+
+def test_prefix_match_needs_the_same_previous_block():
+    # a cached block is reused only right after the block it was cached
+    # behind: once that one is evicted, the chain cannot be picked up again
+    # behind other content
+    h = host_pool(num_blocks=4, max_seq_len=64)
+    x, y, z = list(range(16)), list(range(100, 116)), list(range(200, 216))
+    t = np.full((1, 4), -1, np.int32)
+    pkv.prepare_write(h, t, [0], [32])
+    assert pkv.prefix_insert(h, x + y, t[0, :2]) == 2
+    pkv.block_free(h, t[0, :2])                         # evictable: x's block, then y's
+    t2 = np.full((1, 4), -1, np.int32)
+    pkv.prepare_write(h, t2, [0], [48])                 # 2 free + x's block evicted
+    assert pkv.prefix_stats(h)["evictions"] == 1
+    assert pkv.prefix_stats(h)["cached"] == 1           # y's block stays cached
+    assert pkv.prefix_match(h, x + y).size == 0
+    pkv.block_free(h, t2[0, :3])
+    t3 = np.full((1, 4), -1, np.int32)
+    pkv.prepare_write(h, t3, [0], [16])
+    assert pkv.prefix_insert(h, z, t3[0, :1]) == 1
+    assert pkv.prefix_match(h, z + y).size == 1          # y was cached behind x, not z
+    assert pkv.prefix_match(h, x + y).size == 0
+    pkv.kv_pool_free(h)
