@@ -296,6 +296,25 @@ int pkv_append_paged_attn_decode(pkv_pool* pool, int layer, const void* k_new, c
                                  int partition_tokens, void* workspace, size_t ws_bytes,
                                  uintptr_t stream);
 
+/*
+ * pkv_paged_attn_decode without a workspace, for callers that cannot
+ * allocate device memory around the call (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation). Same arguments, results
+ * and errors as pkv_paged_attn_decode; the split partials live in a static
+ * device array of PKV_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, held from the
+ * library's first pool on that GPU until the process ends, and the call
+ * allocates nothing (no hipMalloc, hipFree or pinned host memory). A decode
+ * whose partials need more than that array (pkv_decode_workspace_bytes gives
+ * the bound) returns PKV_EUNSUPPORTED; a decode whose schedule or staging
+ * would have to grow returns PKV_EINVAL. Every call on one GPU shares its
+ * array: calls that overlap on one GPU (other streams, other pools) race and
+ * must be ordered by the caller. Nothing in the array needs to start at zero.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+int pkv_paged_attn_decode_noalloc(pkv_pool* pool, int layer, const void* q, int q_heads,
+                                  float scale, float* out, int partition_tokens,
+                                  uintptr_t stream);
+
 /* Workspace bytes a decode of `batch` sequences with these settings may need (upper bound). */
 size_t pkv_decode_workspace_bytes(const pkv_pool* pool, int batch, int q_heads,
                                   int partition_tokens);

@@ -89,6 +89,7 @@ struct Staging {
 struct pkv_pool {
   pkv_shape shape{};
   bool device = false;
+  void* scratch = nullptr;  // this device's static scratch array (allocation-free decode)
   int dev_id = 0;
   int num_cus = 0;
   char* k_base = nullptr;
@@ -248,7 +249,16 @@ size_t round16(size_t n) { return (n + 15) & ~(size_t)15; }
 // `stream`: the kernel reads the coherent pinned memory over PCIe, which
 // avoids a hand-off to a copy engine and back for these small images. The
 // buffer is reused only after the kernel that last read it has finished.
-int stage_copy(pkv_pool* p, void* dst, const void* src, size_t bytes, hipStream_t stream) {
+// no_alloc: fail instead of growing a staging buffer or creating its event.
+int stage_copy(pkv_pool* p, void* dst, const void* src, size_t bytes, hipStream_t stream,
+               bool no_alloc = false) {
+  const size_t padded = round16(bytes);
+  if (no_alloc) {
+    const Staging& nx = p->ring[p->ring_next];
+    if (nx.bytes < padded || !nx.ev)
+      return fail(PKV_EINVAL, "the allocation-free call would need a larger staging buffer "
+                              "(%zu bytes)", padded);
+  }
   Staging& st = p->ring[p->ring_next];
   p->ring_next = (p->ring_next + 1) % 4;
   hipError_t e;
@@ -256,7 +266,6 @@ int stage_copy(pkv_pool* p, void* dst, const void* src, size_t bytes, hipStream_
     if ((e = hipEventSynchronize(st.ev)) != hipSuccess) return hip_fail(e, "staging wait");
     st.pending = false;
   }
-  const size_t padded = round16(bytes);
   if (st.bytes < padded) {
     if (st.host) (void)hipHostFree(st.host);
     st.host = st.dev = nullptr;
@@ -850,6 +859,21 @@ int pkv_kv_pool_alloc(const pkv_shape* sh, void* dev_base, size_t dev_bytes, pkv
     p->d_ctx = reinterpret_cast<int32_t*>(p->d_meta + p->off_ctx);
     p->d_cum = reinterpret_cast<int32_t*>(p->d_meta + p->off_cum);
     p->d_bt = reinterpret_cast<int32_t*>(p->d_meta + p->off_bt);
+    // Staging ring sized for the largest image an upload or a schedule can
+    // need, with its events: later calls need no allocation for it.
+    for (Staging& st : p->ring) {
+      const size_t want = std::max(round16(p->meta_bytes), (size_t)1 << 16);
+      if ((e = hipHostMalloc((void**)&st.host, want, hipHostMallocCoherent | hipHostMallocMapped)) !=
+              hipSuccess ||
+          (e = hipHostGetDevicePointer((void**)&st.dev, st.host, 0)) != hipSuccess ||
+          (e = hipEventCreateWithFlags(&st.ev, hipEventDisableTiming)) != hipSuccess) {
+        pkv_kv_pool_free(p);
+        return hip_fail(e, "pinned staging allocation");
+      }
+      st.bytes = want;
+    }
+    // the static scratch array of this device (allocation-free decode)
+    if ((e = pkv::scratch_address(p->dev_id, &p->scratch)) != hipSuccess) p->scratch = nullptr;
   }
   *out = p;
   return PKV_OK;
@@ -1288,11 +1312,18 @@ size_t pkv_decode_workspace_bytes(const pkv_pool* p, int batch, int q_heads,
 
 namespace {
 
+// no_alloc: the partials live in the device's static scratch array, and a
+// call that would allocate (schedule or staging growth) fails instead.
 int decode_impl(pkv_pool* p, int layer, const void* k_new, const void* v_new, const void* q,
                 int q_heads, float scale, float* out, int partition_tokens, void* ws,
-                size_t ws_bytes, uintptr_t stream_u) {
+                size_t ws_bytes, uintptr_t stream_u, bool no_alloc = false) {
   int rc = need_device(p);
   if (rc != PKV_OK) return rc;
+  if (no_alloc) {
+    if (!p->scratch) return fail(PKV_EHIP, "no scratch array on this device");
+    ws = p->scratch;
+    ws_bytes = pkv::kScratchBytes;
+  }
   if (!p->uploaded) return fail(PKV_EINVAL, "no block table uploaded");
   if (layer < 0 || layer >= p->shape.layers) return fail(PKV_EINVAL, "layer %d out of range", layer);
   if (!q || !out) return fail(PKV_EINVAL, "q and out must be device pointers");
@@ -1321,8 +1352,25 @@ int decode_impl(pkv_pool* p, int layer, const void* k_new, const void* v_new, co
   if (p->sched_gen != p->up_gen || p->sched_part != partition_tokens || p->sched_gp != gp) {
     p->sched_gp_building = gp;
     build_schedule(p, partition_tokens, waves_target(p, gp));
+    if (no_alloc && p->sched_needs_merge) {
+      // partials beyond the static array: refused before anything is staged
+      const int64_t np = (int64_t)p->up_batch * p->shape.kv_heads * p->sched_seg_stride +
+                         p->sched_nwaves;
+      const size_t nb = (size_t)np * gp * (p->shape.head_dim + 2) * sizeof(float);
+      if (nb > pkv::kScratchBytes) {
+        p->sched_gen = 0;
+        return fail(PKV_EUNSUPPORTED,
+                    "the split partials need %zu bytes, more than the static scratch array (%zu)",
+                    nb, pkv::kScratchBytes);
+      }
+    }
     int32_t* dst = reinterpret_cast<int32_t*>(p->d_meta + p->off_sched);
     if (p->h_sched.size() > p->sched_cap) {  // rare: very small fixed partitions
+      if (no_alloc && p->h_sched.size() > p->over_cap) {
+        p->sched_gen = 0;
+        return fail(PKV_EINVAL, "the allocation-free call would need a larger schedule buffer "
+                                "(%zu ints; partition %d)", p->h_sched.size(), partition_tokens);
+      }
       if (p->h_sched.size() > p->over_cap) {
         if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "sync");
         (void)hipFree(p->d_sched_over);
@@ -1336,7 +1384,7 @@ int decode_impl(pkv_pool* p, int layer, const void* k_new, const void* v_new, co
       }
       dst = p->d_sched_over;
     }
-    if ((rc = stage_copy(p, dst, p->h_sched.data(), p->h_sched.size() * 4, stream))) {
+    if ((rc = stage_copy(p, dst, p->h_sched.data(), p->h_sched.size() * 4, stream, no_alloc))) {
       p->sched_gen = 0;
       return rc;
     }
@@ -1351,8 +1399,9 @@ int decode_impl(pkv_pool* p, int layer, const void* k_new, const void* v_new, co
   const int64_t nparts = nseg * p->sched_seg_stride + W;
   const size_t need = (size_t)nparts * gp * (p->shape.head_dim + 2) * sizeof(float);
   if (p->sched_needs_merge && (ws_bytes < need || !ws))
-    return fail(PKV_EINVAL, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
-                need);
+    return fail(no_alloc ? PKV_EUNSUPPORTED : PKV_EINVAL,
+                "%s of %zu bytes is smaller than the %zu needed",
+                no_alloc ? "the static scratch array" : "workspace", ws_bytes, need);
   if (reinterpret_cast<uintptr_t>(ws) & 15)
     return fail(PKV_EINVAL, "workspace must be 16-byte aligned");
   float* part = static_cast<float*>(ws);
@@ -1420,6 +1469,13 @@ int pkv_paged_attn_decode(pkv_pool* p, int layer, const void* q, int q_heads, fl
                           uintptr_t stream) {
   return decode_impl(p, layer, nullptr, nullptr, q, q_heads, scale, out, partition_tokens, ws,
                      ws_bytes, stream);
+}
+
+int pkv_paged_attn_decode_noalloc(pkv_pool* p, int layer, const void* q, int q_heads,
+                                  float scale, float* out, int partition_tokens,
+                                  uintptr_t stream) {
+  return decode_impl(p, layer, nullptr, nullptr, q, q_heads, scale, out, partition_tokens,
+                     nullptr, 0, stream, true);
 }
 
 int pkv_append_paged_attn_decode(pkv_pool* p, int layer, const void* k_new, const void* v_new,

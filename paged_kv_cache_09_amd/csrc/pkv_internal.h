@@ -98,6 +98,12 @@ hipError_t launch_copy_blocks(const int32_t* pairs, int n, void* k_base, void* v
                               int layers, int64_t layer_bytes, int64_t block_bytes,
                               hipStream_t stream);
 
+// Static scratch array (one per device, held until the process ends) for the
+// allocation-free decode: its size, and its device address on device `dev`
+// (looked up once per device with that device current).
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+hipError_t scratch_address(int dev, void** out);
+
 #ifdef PKV_TIMELINE
 hipError_t copy_timeline(void* dst, size_t bytes);
 #endif

@@ -41,6 +41,8 @@
 // parts (quantised codes as exact fp16 subnormals).
 #include "pkv_internal.h"
 
+#include <mutex>
+
 namespace pkv {
 namespace {
 
@@ -2003,6 +2005,31 @@ hipError_t launch_upload(const void* host_src, void* dst, size_t bytes, hipStrea
   hipLaunchKernelGGL(upload_kernel, dim3((unsigned)wg), dim3(256), 0, stream,
                      static_cast<const u32x4*>(host_src), static_cast<u32x4*>(dst), n16);
   return hipGetLastError();
+}
+
+// Scratch for the split partials of the allocation-free decode. Host code
+// never uses this name as an address: the device address comes from
+// hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_address(int dev, void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev) return hipErrorInvalidDevice;  // the device must be current
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 #ifdef PKV_TIMELINE

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 F32, F16, BF16, Q8_0, Q4_0 = 0, 1, 2, 3, 4
 OK, EINVAL, ECAPACITY, EOUT_OF_BLOCKS, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES = 32 << 20  # static scratch array per GPU (allocation-free decode)
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
@@ -60,6 +61,7 @@ _SIGS = {
     "pkv_paged_attn_decode": (_I, [_P, _I, _P, _I, ctypes.c_float, _P, _I, _P, _SZ, _U]),
     "pkv_append_paged_attn_decode": (_I, [_P, _I, _P, _P, _P, _I, ctypes.c_float, _P, _I, _P,
                                           _SZ, _U]),
+    "pkv_paged_attn_decode_noalloc": (_I, [_P, _I, _P, _I, ctypes.c_float, _P, _I, _U]),
     "pkv_decode_workspace_bytes": (_SZ, [_P, _I, _I, _I]),
     "pkv_pool_stats": (_I, [_P, _P]),
     "pkv_prefix_match": (_I, [_P, _P, _I, _P, _I]),
@@ -208,6 +210,13 @@ def paged_attn_decode(pool, layer: int, q, q_heads: int, scale: float, out,
     _check(_lib.pkv_paged_attn_decode(pool, int(layer), _ptr(q), int(q_heads), float(scale),
                                       _ptr(out), int(partition_tokens), _ptr(workspace),
                                       int(ws_bytes), int(stream)))
+
+
+def paged_attn_decode_noalloc(pool, layer: int, q, q_heads: int, scale: float, out,
+                              partition_tokens: int = 0, stream: int = 0) -> None:
+    _check(_lib.pkv_paged_attn_decode_noalloc(pool, int(layer), _ptr(q), int(q_heads),
+                                              float(scale), _ptr(out), int(partition_tokens),
+                                              int(stream)))
 
 
 def append_paged_attn_decode(pool, layer: int, k_new, v_new, q, q_heads: int, scale: float,
