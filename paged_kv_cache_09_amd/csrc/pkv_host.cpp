@@ -566,10 +566,23 @@ constexpr int kBinWaves = 8;
 //   of split segments it takes part in (see below).
 //   seglist per listed segment: sequence, kv head, length, first block id.
 // Relative speed of the eight waves of a bin: waves 0-3 and 4-7 share the
-// four SIMDs, and the older wave of each pair wins issue arbitration.
+// four SIMDs, and the older wave of each pair wins issue arbitration. The
+// older wave's run is longer by the skew (in percent of the mean): a little
+// for the 2-byte caches, whose loop waits on memory, more for the quantised
+// ones, whose loop keeps the SIMD busy (measured end times of the two waves
+// of a pair agree with these).
 #ifndef PKV_SLOT_SKEW
 #define PKV_SLOT_SKEW 8
 #endif
+#ifndef PKV_SLOT_SKEW_Q8
+#define PKV_SLOT_SKEW_Q8 24
+#endif
+#ifndef PKV_SLOT_SKEW_Q4
+#define PKV_SLOT_SKEW_Q4 32
+#endif
+int slot_skew(int dtype) {
+  return dtype == PKV_Q4_0 ? PKV_SLOT_SKEW_Q4 : dtype == PKV_Q8_0 ? PKV_SLOT_SKEW_Q8 : PKV_SLOT_SKEW;
+}
 // Cost, in tiles, of a segment switch inside a bin wave's run, and of the
 // fused append at the end of a segment.
 #ifndef PKV_BIN_SWITCH_COST
@@ -580,8 +593,8 @@ constexpr int kBinWaves = 8;
 #endif
 constexpr double kBinSwitchCost = PKV_BIN_SWITCH_COST;
 constexpr double kBinAppendCost = PKV_BIN_APPEND_COST;
-double slot_capacity(int v) {
-  return v < kBinWaves / 2 ? 1.0 + PKV_SLOT_SKEW / 200.0 : 1.0 - PKV_SLOT_SKEW / 200.0;
+double slot_capacity(int v, int skew) {
+  return v < kBinWaves / 2 ? 1.0 + skew / 200.0 : 1.0 - skew / 200.0;
 }
 
 // Cut a bin's segments (tile counts n[i], in order) into nruns contiguous
@@ -589,11 +602,11 @@ double slot_capacity(int v) {
 // = all tiles), minimising the largest run cost over the run's capacity. A run
 // costs one per tile plus kSegStartCost for each segment that starts inside
 // it; its own first tile is free, since every run has one start.
-void cut_runs(const std::vector<int64_t>& n, int nruns, int64_t* start) {
+void cut_runs(const std::vector<int64_t>& n, int nruns, int skew, int64_t* start) {
   int64_t tiles = 0;
   for (int64_t k : n) tiles += k;
   double capsum = 0;
-  for (int v = 0; v < nruns; ++v) capsum += slot_capacity(v);
+  for (int v = 0; v < nruns; ++v) capsum += slot_capacity(v, skew);
   auto pack = [&](double M, int64_t* st) {
     int v = 0;
     double c = 0;
@@ -604,7 +617,7 @@ void cut_runs(const std::vector<int64_t>& n, int nruns, int64_t* start) {
       bool seg_start = true;
       while (left > 0) {
         const double sw = seg_start && c > 0 ? kBinSwitchCost : 0.0;
-        const double cap = M * slot_capacity(v) - c - sw;
+        const double cap = M * slot_capacity(v, skew) - c - sw;
         // the run that ends the segment also appends its new row
         int64_t room = (int64_t)std::floor(cap + 1e-9);
         if (room >= left) room = (int64_t)std::floor(cap - kBinAppendCost + 1e-9) >= left ? left : left - 1;
@@ -712,7 +725,7 @@ bool build_bins(pkv_pool* p, int nbins) {
     ntiles.reserve(m.size());
     for (int i : m) ntiles.push_back(segs[i].cost - kSegStartCost);
     int64_t start_tile[kBinWaves + 1];
-    cut_runs(ntiles, kBinWaves, start_tile);
+    cut_runs(ntiles, kBinWaves, slot_skew(p->shape.dtype), start_tile);
     // descriptors: walk segments and waves together
     int seg_i = 0;          // index into m
     int64_t seg_x0 = 0;     // bin-local tile index where m[seg_i] starts

@@ -774,9 +774,11 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
   static_assert(!MPV || (CPR == 16 && NV == 4 && EPC == 8), "MFMA P.V lane layout");
 
   constexpr int NW = BINS ? 8 : 1;       // waves per workgroup
-  // softmax weights, [wave][parity][row][head], then a spare slot the lanes
-  // without a head write to (a store every lane makes needs no branch)
-  __shared__ float p_lds_all[NW][2][16 * GP + 4];
+  // softmax weights, [wave][row][head], then a spare slot the lanes without
+  // a head write to (a store every lane makes needs no branch). One buffer
+  // serves every tile: a wave's LDS operations complete in order, so the
+  // next tile's writes cannot pass this tile's reads.
+  __shared__ float p_lds_all[NW][16 * GP + 4];
   __shared__ float a_lds_all[NW][GP];          // per-head rescale factors
   __shared__ float l_lds_all[NW][GP];          // per-head sums at the end of a run
   __shared__ float m_lds_all[NW][GP];          // per-head maxima at the end of a run
@@ -800,7 +802,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
   // wave-uniform (scalar registers): the descriptor loads become scalar loads
   const int wl = BINS ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;
   const int lane = threadIdx.x & 63;
-  float (&p_lds)[2][16 * GP + 4] = p_lds_all[wl];
+  float (&p_lds)[16 * GP + 4] = p_lds_all[wl];
   float (&a_lds)[GP] = a_lds_all[wl];
   float (&l_lds)[GP] = l_lds_all[wl];
   float (&m_lds)[GP] = m_lds_all[wl];
@@ -852,7 +854,6 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
   // V row held in the lane's i-th chunk
   auto vrow = [&](int i) { return QN ? NV * vr + i : vr + RPI * i; };
   const size_t blk_stride = (size_t)p.kv_heads * TILE;
-  int parity = 0;
 
   while (x < xend) {
     const int nblk = (L + 15) >> 4;
@@ -1090,7 +1091,8 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     };
 
     // Lane (t16, kg) keeps softmax state for heads 4*kg + i of its row.
-    float m[HPG], lsum[HPG];
+    // mlz: m + kLazy, the score above which a tile raises the maxima
+    float m[HPG], mlz[HPG], lsum[HPG];
     float acc[GP][EPC];
     float bsum[GP];  // q4_0: sum of the lane's scaled weights per head (8 x it is taken off)
     // MFMA P.V: block nt of output columns (head-dim columns 8 * n + nt), rows
@@ -1101,7 +1103,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     f32x4 accs = {0.f, 0.f, 0.f, 0.f};  // MFMA P.V: per row, the sum of its A values
 #pragma unroll
     for (int i = 0; i < HPG; ++i) {
-      m[i] = -__builtin_inff();
+      m[i] = mlz[i] = -__builtin_inff();
       lsum[i] = 0.f;
     }
 #pragma unroll
@@ -1111,7 +1113,25 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       for (int e = 0; e < EPC; ++e) acc[h][e] = 0.f;
     }
 
-    auto compute_tile = [&](int valid, const TR& t) {
+    // A tile of valid < 16 rows (a segment's last) masks the rows past the
+    // context, which may hold anything (NaN), in blocks that full tiles branch
+    // around (valid is uniform across the wave): their scores become -inf and
+    // their V values (q8_0 / q4_0: V scales) zero in the tile registers.
+    // (The V registers are masked where V is first used, so that full tiles
+    // do not wait for V before q.K.)
+    auto compute_tile = [&](int valid, TR& t) {
+      const bool part = __builtin_expect(valid < 16, 0);
+      auto mask_v = [&]() {
+        if (part) {
+#pragma unroll
+          for (int i = 0; i < NV; ++i) {
+            if (vrow(i) >= valid) {
+              if constexpr (QN) t.vs[i >> 1] &= (i & 1) ? 0x0000ffffu : 0xffff0000u;
+              else t.v[i] = u32x4{0u, 0u, 0u, 0u};
+            }
+          }
+        }
+      };
       f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
       if constexpr (QN) {
         // one MFMA per 32-code group, then that group's scale for this
@@ -1136,18 +1156,30 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       // MFMA P.V takes weight x scale as fp16: weights stay <= 2^kLazy, and a
       // tile with a V scale above 2^8 - 1 raises the maxima on any increase
       // (weights <= 1), so the products stay finite.
-      float lz = kLazy;
+      bool big = false;
       if constexpr (MPV) {
+        mask_v();
         // fp16 magnitude bits above 255 (0x5bf8), NaN included (rows past the
         // context may hold anything: that only costs a rescale)
         const unsigned a0 = t.vs[0] & 0x7fff7fffu, a1 = t.vs[1] & 0x7fff7fffu;
         const unsigned mx = max(max(a0 & 0xffffu, a0 >> 16), max(a1 & 0xffffu, a1 >> 16));
-        if (__any(mx > 0x5bf8u)) lz = 0.f;
+        big = __any(mx > 0x5bf8u);
       }
 #pragma unroll
       for (int i = 0; i < HPG; ++i) {
-        s2[i] = t16 < valid ? sacc[i] * smul[i] : -__builtin_inff();
-        over |= head_lane && s2[i] > m[i] + lz;
+        s2[i] = sacc[i] * smul[i];
+      }
+      if (part) {
+#pragma unroll
+        for (int i = 0; i < HPG; ++i)
+          if (t16 >= valid) s2[i] = -__builtin_inff();
+      }
+#pragma unroll
+      for (int i = 0; i < HPG; ++i) over |= head_lane && s2[i] > mlz[i];
+      if (big) {  // any increase
+        over = false;
+#pragma unroll
+        for (int i = 0; i < HPG; ++i) over |= head_lane && s2[i] > m[i];
       }
       if (__any(over)) {  // raise the running maxima to this tile's
         float alpha[HPG];
@@ -1157,6 +1189,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
           alpha[i] = __builtin_amdgcn_exp2f(m[i] - mn);
           lsum[i] *= alpha[i];
           m[i] = mn;
+          mlz[i] = mn + kLazy;
         }
         if (head_lane && t16 == 0) {
 #pragma unroll
@@ -1181,8 +1214,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
           }
         }
       }
-      float* pl = p_lds[parity];
-      parity ^= 1;
+      float* pl = p_lds;
       float* pw_at = pl + (head_lane ? t16 * GP + 4 * kg : 16 * GP);
 #pragma unroll
       for (int i = 0; i < HPG; ++i) {
@@ -1192,26 +1224,25 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       }
       wave_sync();
       if constexpr (MPV) {
-        // P.V as MFMAs 16x16x16 per block of 16 output columns, one with the
-        // high and one with the low fp16 part of A (~22 bits together; all
-        // high parts first, so no MFMA waits on the one before). A: row
-        // 4 * G + h holds head h's weights times each token's scale for group
-        // G (the spare rows of a group of <= 4 heads carry the four scale
-        // groups), k = the lane's 4 tokens. B: column n of block nt is head-dim
-        // column 8 * n + nt, its code's byte taken as the fp16 bits: the
-        // subnormal code x 2^-24 (odd nt: code x 2^-20), exact, and kept by
-        // the MFMA. One more MFMA against ones sums each row's A values, so
-        // the 8 of code - 8 comes off at the end from the same fp16 parts.
-        // Row 4 * G + h of block nt is head h's output for the columns of
-        // group G, used by the lanes whose columns 8 * (lane % 16) + nt lie in
-        // group lane / 16.
+        // P.V as one MFMA 16x16x32 per block of 16 output columns: k = the
+        // lane's 4 tokens twice, A holding the high fp16 part of each weight
+        // in the first four and the low part in the last four (~22 bits
+        // together), B the same 4 codes twice. A: row 4 * G + h holds head
+        // h's weights times each token's scale for group G (the spare rows of
+        // a group of <= 4 heads carry the four scale groups). B: column n of
+        // block nt is head-dim column 8 * n + nt, its code's byte taken as the
+        // fp16 bits: the subnormal code x 2^-24 (odd nt: code x 2^-20), exact,
+        // and kept by the MFMA. One more MFMA against ones sums each row's A
+        // values, so the 8 of code - 8 comes off at the end from the same fp16
+        // parts. Row 4 * G + h of block nt is head h's output for the columns
+        // of group G, used by the lanes whose columns 8 * (lane % 16) + nt lie
+        // in group lane / 16.
         const int hh = lane & 3;
         float pa[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tr = 4 * vr + i;
-          float dv = (i & 1) ? half_hi(t.vs[i >> 1]) : half_lo(t.vs[i >> 1]);
-          if (tr >= valid) dv = 0.f;  // rows past the context may hold anything (NaN scales)
+          const float dv = (i & 1) ? half_hi(t.vs[i >> 1]) : half_lo(t.vs[i >> 1]);
           const float pw = pl[tr * GP + (hh < GP ? hh : 0)];
           pa[i] = hh < GP ? pw * dv : 0.f;
         }
@@ -1220,7 +1251,6 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         const f16x8 av = {h01[0], h01[1], h23[0], h23[1],
                           (_Float16)(pa[0] - (float)h01[0]), (_Float16)(pa[1] - (float)h01[1]),
                           (_Float16)(pa[2] - (float)h23[0]), (_Float16)(pa[3] - (float)h23[1])};
-        const f16x4 ahi = {av[0], av[1], av[2], av[3]}, alo = {av[4], av[5], av[6], av[7]};
         accs = __builtin_amdgcn_mfma_f32_16x16x32_f16(
             av, __builtin_bit_cast(f16x8, u32x4{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u}),
             accs, 0, 0, 0);
@@ -1240,7 +1270,6 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
             const unsigned sel = 0x0c000c00u | ((4u + b) << 16) | b;
             bv[nt] = __builtin_bit_cast(f16x4, u32x2{__builtin_amdgcn_perm(x[1][w], x[0][w], sel),
                                                      __builtin_amdgcn_perm(x[3][w], x[2][w], sel)});
-            accm[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bv[nt], accm[nt], 0, 0, 0);
           }
         } else {
           unsigned ev[4], od[4];  // even codes (low nibbles), odd codes x 16 (high nibbles)
@@ -1256,13 +1285,16 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
             const unsigned sel = 0x0c000c00u | ((4u + (nt >> 1)) << 16) | (unsigned)(nt >> 1);
             bv[nt] = __builtin_bit_cast(f16x4, u32x2{__builtin_amdgcn_perm(src[1], src[0], sel),
                                                      __builtin_amdgcn_perm(src[3], src[2], sel)});
-            accm[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bv[nt], accm[nt], 0, 0, 0);
           }
         }
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-          accm[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, bv[nt], accm[nt], 0, 0, 0);
-      } else
+        for (int nt = 0; nt < 8; ++nt) {
+          const f16x8 b2 = {bv[nt][0], bv[nt][1], bv[nt][2], bv[nt][3],
+                            bv[nt][0], bv[nt][1], bv[nt][2], bv[nt][3]};
+          accm[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b2, accm[nt], 0, 0, 0);
+        }
+      } else {
+      mask_v();
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int tr = vrow(i);
@@ -1271,13 +1303,8 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         if constexpr (QN) {
           code_vals(t.v[i], vals);
           dv = (i & 1) ? half_hi(t.vs[i >> 1]) : half_lo(t.vs[i >> 1]);
-          if (tr >= valid) dv = 0.f;  // rows past the context may hold anything (NaN scales)
         } else {
           to_f32<DT>(t.v[i], vals);
-          if (tr >= valid) {  // rows past the context may hold anything (NaN)
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) vals[e] = 0.f;
-          }
         }
         float pt[GP];
 #pragma unroll
@@ -1290,6 +1317,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         for (int h = 0; h < GP; ++h)
 #pragma unroll
           for (int e = 0; e < EPC; ++e) acc[h][e] = __builtin_fmaf(pt[h], vals[e], acc[h][e]);
+      }
       }
     };
 
@@ -1489,7 +1517,8 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
             // keep the scheduler from hoisting the compute (and its waits) above
             // the request
             __builtin_amdgcn_sched_barrier(0);
-            compute_tile(min(16, Lc - 16 * (jb + j)), t[u]);
+            const int valid = min(16, Lc - 16 * (jb + j));
+            compute_tile(valid, t[u]);
 #ifdef PKV_TIMELINE
             if (tl_t1 == 0) tl_t1 = __builtin_amdgcn_s_memrealtime();
             ++tl_tiles;
