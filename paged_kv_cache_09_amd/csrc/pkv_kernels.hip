@@ -437,6 +437,13 @@ __device__ __forceinline__ float row_sum(float v) {
   return v + row_ror<0x121>(v);
 }
 
+// How compute_tile treats a tile's P.V on the MFMA path: at once (0), left
+// pending for the next tile (1), or together with the pending one (2).
+template <int M>
+struct PvMode {
+  static constexpr int value = M;
+};
+
 // Orders this wavefront's LDS writes before its later LDS reads by other
 // lanes (a wave's LDS operations complete in order; this keeps the compiler
 // from moving them). Only this wave takes part.
@@ -450,6 +457,22 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// 1.0 in every fp16 slot of an MFMA operand.
+__device__ __forceinline__ f16x8 ones_f16() {
+  return __builtin_bit_cast(f16x8, u32x4{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u});
+}
+
+// x ~ hi + lo: hi rounded toward zero to fp16, lo = x - hi (exact in fp32)
+// rounded to fp16: ~22 significant bits together.
+__device__ __forceinline__ void split_f16(const float (&x)[4], f16x4& hi, f16x4& lo) {
+  typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+  const f16x2v h01 = __builtin_bit_cast(f16x2v, __builtin_amdgcn_cvt_pkrtz(x[0], x[1]));
+  const f16x2v h23 = __builtin_bit_cast(f16x2v, __builtin_amdgcn_cvt_pkrtz(x[2], x[3]));
+  hi = f16x4{h01[0], h01[1], h23[0], h23[1]};
+  lo = f16x4{(_Float16)(x[0] - (float)h01[0]), (_Float16)(x[1] - (float)h01[1]),
+             (_Float16)(x[2] - (float)h23[0]), (_Float16)(x[3] - (float)h23[1])};
+}
 
 // One 16-byte piece of the q.K^T contraction on the matrix cores:
 // A = q (16 rows = heads of the group, zero-padded), B = K^T (16 columns =
@@ -1119,7 +1142,31 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
     // their V values (q8_0 / q4_0: V scales) zero in the tile registers.
     // (The V registers are masked where V is first used, so that full tiles
     // do not wait for V before q.K.)
-    auto compute_tile = [&](int valid, TR& t) {
+    // MFMA P.V: the A values (weight x V scale) and B operands of a tile
+    // whose P.V waits for the next tile's, so that one MFMA 16x16x32 takes
+    // the two tiles' high (then low) weight parts against their own codes.
+    // bt[nt]: B operands of column block nt, the pending tile's in words 0-1
+    // and the next tile's in words 2-3 (built in place).
+    float pa_p[4];
+    u32x4 bt[MPV ? 8 : 1];
+    // one tile: its high and low weight parts against its codes twice
+    auto pv_one = [&](const float (&pa)[4]) {
+      if constexpr (MPV) {
+        f16x4 h, l;
+        split_f16(pa, h, l);
+        const f16x8 av = {h[0], h[1], h[2], h[3], l[0], l[1], l[2], l[3]};
+        accs = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, ones_f16(), accs, 0, 0, 0);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          bt[nt][2] = bt[nt][0];
+          bt[nt][3] = bt[nt][1];
+          accm[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(f16x8, bt[nt]),
+                                                            accm[nt], 0, 0, 0);
+        }
+      }
+    };
+    auto compute_tile = [&](auto mode_tag, int valid, TR& t) {
+      constexpr int MODE = MPV ? decltype(mode_tag)::value : 0;
       const bool part = __builtin_expect(valid < 16, 0);
       auto mask_v = [&]() {
         if (part) {
@@ -1204,6 +1251,12 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) accm[nt][i] *= a;
           }
+          if constexpr (MODE == 2) {  // the pending tile's weights of head lane % 4
+            const int hh = lane & 3;
+            const float a = hh < GP ? a_lds[hh < GP ? hh : 0] : 1.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pa_p[i] *= a;
+          }
         } else {
 #pragma unroll
           for (int h = 0; h < GP; ++h) {
@@ -1224,19 +1277,19 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
       }
       wave_sync();
       if constexpr (MPV) {
-        // P.V as one MFMA 16x16x32 per block of 16 output columns: k = the
-        // lane's 4 tokens twice, A holding the high fp16 part of each weight
-        // in the first four and the low part in the last four (~22 bits
-        // together), B the same 4 codes twice. A: row 4 * G + h holds head
-        // h's weights times each token's scale for group G (the spare rows of
-        // a group of <= 4 heads carry the four scale groups). B: column n of
-        // block nt is head-dim column 8 * n + nt, its code's byte taken as the
-        // fp16 bits: the subnormal code x 2^-24 (odd nt: code x 2^-20), exact,
-        // and kept by the MFMA. One more MFMA against ones sums each row's A
-        // values, so the 8 of code - 8 comes off at the end from the same fp16
-        // parts. Row 4 * G + h of block nt is head h's output for the columns
-        // of group G, used by the lanes whose columns 8 * (lane % 16) + nt lie
-        // in group lane / 16.
+        // P.V as MFMAs 16x16x32, one per block of 16 output columns and
+        // weight part: A row 4 * G + h holds head h's weights times each
+        // token's scale for group G (the spare rows of a group of <= 4 heads
+        // carry the four scale groups), split into a high and a low fp16 part
+        // (~22 bits together); k = the lane's 4 tokens of two tiles (or of one
+        // tile twice, high and low parts side by side). B: column n of block
+        // nt is head-dim column 8 * n + nt, its code's byte taken as the fp16
+        // bits: the subnormal code x 2^-24 (odd nt: code x 2^-20), exact, and
+        // kept by the MFMA. MFMAs against ones sum each row's A values, so the
+        // 8 of code - 8 comes off at the end from the same fp16 parts. Row
+        // 4 * G + h of block nt is head h's output for the columns of group
+        // G, used by the lanes whose columns 8 * (lane % 16) + nt lie in
+        // group lane / 16.
         const int hh = lane & 3;
         float pa[4];
 #pragma unroll
@@ -1244,17 +1297,10 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
           const int tr = 4 * vr + i;
           const float dv = (i & 1) ? half_hi(t.vs[i >> 1]) : half_lo(t.vs[i >> 1]);
           const float pw = pl[tr * GP + (hh < GP ? hh : 0)];
-          pa[i] = hh < GP ? pw * dv : 0.f;
+          pa[i] = hh < GP ? __builtin_fmaf(pw, dv, 0.f) : 0.f;
         }
-        const f16x2 h01 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(pa[0], pa[1]));
-        const f16x2 h23 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(pa[2], pa[3]));
-        const f16x8 av = {h01[0], h01[1], h23[0], h23[1],
-                          (_Float16)(pa[0] - (float)h01[0]), (_Float16)(pa[1] - (float)h01[1]),
-                          (_Float16)(pa[2] - (float)h23[0]), (_Float16)(pa[3] - (float)h23[1])};
-        accs = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-            av, __builtin_bit_cast(f16x8, u32x4{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u}),
-            accs, 0, 0, 0);
-        f16x4 bv[8];
+        // this tile's B operands into words 0-1 (pending or alone) or 2-3
+        constexpr int BW = MODE == 2 ? 2 : 0;
         if constexpr (Q8) {
           // 128 + code (the top bit flipped) of the 4 rows' chunks; column
           // 8 * n + nt is byte nt & 3 of word nt >> 2
@@ -1268,8 +1314,8 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
             const int w = nt >> 2;
             const unsigned b = nt & 3;
             const unsigned sel = 0x0c000c00u | ((4u + b) << 16) | b;
-            bv[nt] = __builtin_bit_cast(f16x4, u32x2{__builtin_amdgcn_perm(x[1][w], x[0][w], sel),
-                                                     __builtin_amdgcn_perm(x[3][w], x[2][w], sel)});
+            bt[nt][BW] = __builtin_amdgcn_perm(x[1][w], x[0][w], sel);
+            bt[nt][BW + 1] = __builtin_amdgcn_perm(x[3][w], x[2][w], sel);
           }
         } else {
           unsigned ev[4], od[4];  // even codes (low nibbles), odd codes x 16 (high nibbles)
@@ -1283,15 +1329,31 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
             const unsigned* src = (nt & 1) ? od : ev;
             // byte nt / 2 of rows 0, 1 (and 2, 3) into the low bytes of the two fp16 halves
             const unsigned sel = 0x0c000c00u | ((4u + (nt >> 1)) << 16) | (unsigned)(nt >> 1);
-            bv[nt] = __builtin_bit_cast(f16x4, u32x2{__builtin_amdgcn_perm(src[1], src[0], sel),
-                                                     __builtin_amdgcn_perm(src[3], src[2], sel)});
+            bt[nt][BW] = __builtin_amdgcn_perm(src[1], src[0], sel);
+            bt[nt][BW + 1] = __builtin_amdgcn_perm(src[3], src[2], sel);
           }
         }
+        if constexpr (MODE == 1) {
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          const f16x8 b2 = {bv[nt][0], bv[nt][1], bv[nt][2], bv[nt][3],
-                            bv[nt][0], bv[nt][1], bv[nt][2], bv[nt][3]};
-          accm[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b2, accm[nt], 0, 0, 0);
+          for (int i = 0; i < 4; ++i) pa_p[i] = pa[i];
+        } else if constexpr (MODE == 2) {
+          f16x4 ah, al, bh, bl;
+          split_f16(pa_p, ah, al);
+          split_f16(pa, bh, bl);
+          const f16x8 ahi = {ah[0], ah[1], ah[2], ah[3], bh[0], bh[1], bh[2], bh[3]};
+          const f16x8 alo = {al[0], al[1], al[2], al[3], bl[0], bl[1], bl[2], bl[3]};
+          accs = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, ones_f16(), accs, 0, 0, 0);
+          accs = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, ones_f16(), accs, 0, 0, 0);
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt)
+            accm[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, __builtin_bit_cast(f16x8, bt[nt]),
+                                                              accm[nt], 0, 0, 0);
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt)
+            accm[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, __builtin_bit_cast(f16x8, bt[nt]),
+                                                              accm[nt], 0, 0, 0);
+        } else {
+          pv_one(pa);
         }
       } else {
       mask_v();
@@ -1461,7 +1523,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
         }
         if (vr == 0) *reinterpret_cast<u32x4*>(vtile + t_new * RB + vc * 16) = tn.v[0];
       }
-      compute_tile(1, tn);
+      compute_tile(PvMode<0>{}, 1, tn);
     };
     // block ids of chunk tile j: (a, b, half)
     auto tile_ids = [&](int j, int& a, int& b, int& half) {
@@ -1518,7 +1580,13 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
             // the request
             __builtin_amdgcn_sched_barrier(0);
             const int valid = min(16, Lc - 16 * (jb + j));
-            compute_tile(valid, t[u]);
+            if constexpr (MPV && NBUF == 2) {
+              // P.V of tile pairs (the pair's first tile waits)
+              if (u == 0) compute_tile(PvMode<1>{}, valid, t[u]);
+              else compute_tile(PvMode<2>{}, valid, t[u]);
+            } else {
+              compute_tile(PvMode<0>{}, valid, t[u]);
+            }
 #ifdef PKV_TIMELINE
             if (tl_t1 == 0) tl_t1 = __builtin_amdgcn_s_memrealtime();
             ++tl_tiles;
@@ -1526,6 +1594,12 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
           }
         }
       }
+    }
+    if constexpr (MPV && NBUF == 2) {
+      // Every chunk but the run's last has an even tile count (CH is even),
+      // so a tile is left pending only at the end of a run of odd length.
+      static_assert(CH % 2 == 0, "tile pairs within chunks");
+      if (j1c > j0 && ((j1c - j0) & 1)) pv_one(pa_p);
     }
     if (!EARLY_NEW && app_here) append_new_row();
 
