@@ -565,48 +565,47 @@ constexpr int kBinWaves = 8;
 //   [5] its length (bit 30: has a slot), [6] that block's id, [7] the merges
 //   of split segments it takes part in (see below).
 //   seglist per listed segment: sequence, kv head, length, first block id.
-// Relative speed of the eight waves of a bin: waves 0-3 and 4-7 share the
-// four SIMDs, and the older wave of each pair wins issue arbitration. The
-// older wave's run is longer by the skew (in percent of the mean): a little
-// for the 2-byte caches, whose loop waits on memory, more for the quantised
-// ones, whose loop keeps the SIMD busy (measured end times of the two waves
-// of a pair agree with these).
-#ifndef PKV_SLOT_SKEW
-#define PKV_SLOT_SKEW 8
+// Costs of a bin wave's run, per cache type (measured end times of the
+// waves of a bin agree with these):
+//   skew: waves 0-3 and 4-7 share the four SIMDs, and the older wave of each
+//     pair wins issue arbitration, so the older wave's run is longer by skew
+//     percent of the mean: a little for the 2-byte caches, whose loop waits
+//     on memory, more for the quantised ones, whose loop keeps the SIMD busy;
+//   sw: a segment switch inside a run, in tiles;
+//   app: the fused append of the new row at the end of a segment, in tiles
+//     (quantising the row costs the quantised caches more).
+#ifndef PKV_RUN_COSTS_2B
+#define PKV_RUN_COSTS_2B 8, 4, 0
 #endif
-#ifndef PKV_SLOT_SKEW_Q8
-#define PKV_SLOT_SKEW_Q8 24
+#ifndef PKV_RUN_COSTS_Q8
+#define PKV_RUN_COSTS_Q8 24, 8, 1
 #endif
-#ifndef PKV_SLOT_SKEW_Q4
-#define PKV_SLOT_SKEW_Q4 32
+#ifndef PKV_RUN_COSTS_Q4
+#define PKV_RUN_COSTS_Q4 40, 8, 2
 #endif
-int slot_skew(int dtype) {
-  return dtype == PKV_Q4_0 ? PKV_SLOT_SKEW_Q4 : dtype == PKV_Q8_0 ? PKV_SLOT_SKEW_Q8 : PKV_SLOT_SKEW;
+struct RunCosts {
+  double skew, sw, app;
+};
+RunCosts run_costs(int dtype) {
+  if (dtype == PKV_Q4_0) return RunCosts{PKV_RUN_COSTS_Q4};
+  if (dtype == PKV_Q8_0) return RunCosts{PKV_RUN_COSTS_Q8};
+  return RunCosts{PKV_RUN_COSTS_2B};
 }
-// Cost, in tiles, of a segment switch inside a bin wave's run, and of the
-// fused append at the end of a segment.
-#ifndef PKV_BIN_SWITCH_COST
-#define PKV_BIN_SWITCH_COST 4
-#endif
-#ifndef PKV_BIN_APPEND_COST
-#define PKV_BIN_APPEND_COST 0
-#endif
-constexpr double kBinSwitchCost = PKV_BIN_SWITCH_COST;
-constexpr double kBinAppendCost = PKV_BIN_APPEND_COST;
-double slot_capacity(int v, int skew) {
-  return v < kBinWaves / 2 ? 1.0 + skew / 200.0 : 1.0 - skew / 200.0;
+double slot_capacity(int v, const RunCosts& rc) {
+  return v < kBinWaves / 2 ? 1.0 + rc.skew / 200.0 : 1.0 - rc.skew / 200.0;
 }
 
 // Cut a bin's segments (tile counts n[i], in order) into nruns contiguous
 // runs of its tile sequence (run v starts at bin-local tile start[v]; start[nruns]
 // = all tiles), minimising the largest run cost over the run's capacity. A run
-// costs one per tile plus kSegStartCost for each segment that starts inside
-// it; its own first tile is free, since every run has one start.
-void cut_runs(const std::vector<int64_t>& n, int nruns, int skew, int64_t* start) {
+// costs one per tile, plus rc.sw for each segment that starts inside it (its
+// own first segment is free, since every run has one start) and rc.app for
+// each segment that ends in it.
+void cut_runs(const std::vector<int64_t>& n, int nruns, const RunCosts& rc, int64_t* start) {
   int64_t tiles = 0;
   for (int64_t k : n) tiles += k;
   double capsum = 0;
-  for (int v = 0; v < nruns; ++v) capsum += slot_capacity(v, skew);
+  for (int v = 0; v < nruns; ++v) capsum += slot_capacity(v, rc);
   auto pack = [&](double M, int64_t* st) {
     int v = 0;
     double c = 0;
@@ -616,11 +615,11 @@ void cut_runs(const std::vector<int64_t>& n, int nruns, int skew, int64_t* start
       int64_t left = k;
       bool seg_start = true;
       while (left > 0) {
-        const double sw = seg_start && c > 0 ? kBinSwitchCost : 0.0;
-        const double cap = M * slot_capacity(v, skew) - c - sw;
+        const double sw = seg_start && c > 0 ? rc.sw : 0.0;
+        const double cap = M * slot_capacity(v, rc) - c - sw;
         // the run that ends the segment also appends its new row
         int64_t room = (int64_t)std::floor(cap + 1e-9);
-        if (room >= left) room = (int64_t)std::floor(cap - kBinAppendCost + 1e-9) >= left ? left : left - 1;
+        if (room >= left) room = (int64_t)std::floor(cap - rc.app + 1e-9) >= left ? left : left - 1;
         if (room <= 0) {
           if (++v == nruns) return false;
           st[v] = x;
@@ -628,7 +627,7 @@ void cut_runs(const std::vector<int64_t>& n, int nruns, int skew, int64_t* start
           continue;
         }
         const int64_t take = std::min(left, room);
-        c += sw + (double)take + (take == left ? kBinAppendCost : 0.0);
+        c += sw + (double)take + (take == left ? rc.app : 0.0);
         x += take;
         left -= take;
         seg_start = false;
@@ -638,7 +637,7 @@ void cut_runs(const std::vector<int64_t>& n, int nruns, int skew, int64_t* start
     return true;
   };
   double lo = std::max(1.0, (double)tiles / capsum) * 0.999;
-  double hi = (double)tiles + (kBinSwitchCost + kBinAppendCost) * (double)n.size() + 1.0;
+  double hi = (double)tiles + (rc.sw + rc.app) * (double)n.size() + 1.0;
   for (int it = 0; it < 40 && hi - lo > 1e-3; ++it) {
     const double mid = 0.5 * (lo + hi);
     if (pack(mid, start)) hi = mid;
@@ -725,7 +724,7 @@ bool build_bins(pkv_pool* p, int nbins) {
     ntiles.reserve(m.size());
     for (int i : m) ntiles.push_back(segs[i].cost - kSegStartCost);
     int64_t start_tile[kBinWaves + 1];
-    cut_runs(ntiles, kBinWaves, slot_skew(p->shape.dtype), start_tile);
+    cut_runs(ntiles, kBinWaves, run_costs(p->shape.dtype), start_tile);
     // descriptors: walk segments and waves together
     int seg_i = 0;          // index into m
     int64_t seg_x0 = 0;     // bin-local tile index where m[seg_i] starts
