@@ -307,18 +307,22 @@ def main():
     log("timed steps")
 
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # each step's lengths and table, for the byte counts taken after the timed region
+    snaps = []
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        total_kv += kv_bytes(cfg, sess.ctx) * cfg.layers
         one_step()
-        total_unique += unique_kv_bytes(cfg, sess.table, sess.ctx) * cfg.layers
+        snaps.append((sess.ctx.copy(), sess.table.copy()))
         sess.ctx += 1
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ev_ms = ev0.elapsed_time(ev1)
     elapsed = max(wall, ev_ms / 1e3)
+    for ctx_s, table_s in snaps:
+        total_kv += kv_bytes(cfg, ctx_s) * cfg.layers
+        total_unique += unique_kv_bytes(cfg, table_s, ctx_s) * cfg.layers
 
     log("decode-only launches")
     # the per-layer kernel alone: back-to-back launches over all layers, same upload

@@ -363,6 +363,15 @@ int pkv_prefix_stats(const pkv_pool* pool, int64_t stats_out[4]);
  */
 int pkv_pool_stats(const pkv_pool* pool, int64_t stats_out[4]);
 
+/*
+ * Decode schedule counters (diagnostics): stats_out[0] schedules built in
+ * full, [1] bins schedules updated in place for an upload whose sequences
+ * only gained tokens (the previous packing and cuts kept, new tiles given to
+ * the wave holding each segment's last tile), [2] 1 when the current
+ * schedule is the bins form, [3] its waves.
+ */
+int pkv_schedule_stats(const pkv_pool* pool, int64_t stats_out[4]);
+
 /* Message for the last failing call on this host thread ("" if none). */
 const char* pkv_last_error(void);
 

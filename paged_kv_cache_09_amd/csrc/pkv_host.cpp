@@ -167,6 +167,14 @@ struct pkv_pool {
   int sched_seg_stride = 1;         // partial slots per segment (1 + most chunks)
   int sched_gp_building = 1;        // padded group of the schedule being built
   std::vector<int32_t> h_sched;     // wdesc[8 * nwaves] | seg_w0[nseg] | seg_w1[nseg]
+  // The last bins schedule built in full, for updating it while lengths only
+  // grow: its batch, bin count and group, each sequence's tile count then,
+  // each segment's (g * batch + s) wave holding its last tile, and each
+  // wave's tile count then.
+  bool bins_valid = false;
+  int bins_batch = 0, bins_nbins = 0, bins_gp = 0;
+  int64_t n_full_builds = 0, n_updates = 0;
+  std::vector<int32_t> bins_seq_tiles, bins_end_wave, bins_count0;
 
   Staging ring[4];
   int ring_next = 0;
@@ -418,6 +426,7 @@ void tile_blocks(const pkv_pool* p, int s, int64_t j, int32_t& first, int32_t& s
 // descriptor holds its first and end tile, the sequence, kv head and block
 // index of its first tile, that sequence's length and the first block's id.
 bool build_bins(pkv_pool* p, int nbins);
+bool update_bins(pkv_pool* p, int nbins);
 
 void build_schedule(pkv_pool* p, int part, int target) {
   p->sched_nitems = 0;
@@ -433,8 +442,17 @@ void build_schedule(pkv_pool* p, int part, int target) {
     const int per_cu = pkv::decode_blocks_per_cu(p->shape.dtype, p->shape.head_dim,
                                                   p->sched_gp_building, true,
                                                   p->shape.block_size);
-    if (per_cu > 0 && build_bins(p, std::max(1, p->num_cus) * per_cu)) return;
+    const int nbins = std::max(1, p->num_cus) * per_cu;
+    if (per_cu > 0 && update_bins(p, nbins)) {
+      ++p->n_updates;
+      return;
+    }
+    ++p->n_full_builds;
+    if (per_cu > 0 && build_bins(p, nbins)) return;
+  } else {
+    ++p->n_full_builds;
   }
+  p->bins_valid = false;  // h_sched now holds another form
   const int B = p->up_batch;
   const int H = p->shape.kv_heads;
   if (!groups) {
@@ -636,9 +654,13 @@ void cut_runs(const std::vector<int64_t>& n, int nruns, const RunCosts& rc, int6
     for (int u = v + 1; u <= nruns; ++u) st[u] = x;
     return true;
   };
+  // Bisection on the largest cost per unit of capacity, to a quarter tile
+  // (cuts fall on whole tiles), from a bracket a little above the lower bound
+  // (widened to the always feasible all-in-one-run bound if need be).
   double lo = std::max(1.0, (double)tiles / capsum) * 0.999;
-  double hi = (double)tiles + (rc.sw + rc.app) * (double)n.size() + 1.0;
-  for (int it = 0; it < 40 && hi - lo > 1e-3; ++it) {
+  double hi = lo * 1.1 + rc.sw + rc.app + 2.0;
+  if (!pack(hi, start)) hi = (double)tiles + (rc.sw + rc.app) * (double)n.size() + 1.0;
+  for (int it = 0; it < 40 && hi - lo > 0.25; ++it) {
     const double mid = 0.5 * (lo + hi);
     if (pack(mid, start)) hi = mid;
     else lo = mid;
@@ -650,6 +672,7 @@ bool build_bins(pkv_pool* p, int nbins) {
   const int B = p->up_batch;
   const int H = p->shape.kv_heads;
   const int nseg = B * H;
+  p->bins_valid = false;
   if (nbins < 1 || nseg < 1) return false;
   struct Seg {
     int64_t cost;
@@ -702,6 +725,7 @@ bool build_bins(pkv_pool* p, int nbins) {
 
   const int W = nbins * kBinWaves;
   p->h_sched.assign((size_t)8 * W + 2 * (size_t)nseg + 4 * (size_t)nseg, 0);
+  p->bins_end_wave.assign(nseg, 0);
   int32_t* desc = p->h_sched.data();
   int32_t* list = desc + (size_t)8 * W + 2 * (size_t)nseg;
   int li = 0;
@@ -772,6 +796,7 @@ bool build_bins(pkv_pool* p, int nbins) {
             wlast = wv;
           }
         }
+        if (wlast >= 0) p->bins_end_wave[segs[m[k]].g * B + segs[m[k]].s] = b * kBinWaves + wlast;
         if (wf < 0 || wlast == wf) continue;
         const int n = wlast - wf + 1;
         for (int wv = wf; wv <= wlast; ++wv) {
@@ -791,6 +816,75 @@ bool build_bins(pkv_pool* p, int nbins) {
   p->sched_nwaves = W;
   p->sched_needs_merge = false;
   p->sched_bins = true;
+  p->bins_seq_tiles.resize(B);
+  for (int s = 0; s < B; ++s) p->bins_seq_tiles[s] = (int32_t)nblk(p->h_ctx[s]);
+  p->bins_count0.resize(W);
+  for (int w = 0; w < W; ++w) p->bins_count0[w] = desc[(size_t)8 * w + 1];
+  p->bins_batch = B;
+  p->bins_nbins = nbins;
+  p->bins_gp = p->sched_gp_building;
+  p->bins_valid = true;
+  return true;
+}
+
+// A wave may grow by this share of its bin's mean run, rounded down to whole
+// tiles, before the bins are packed and cut again (0: always again). Short
+// runs (a few dozen tiles, where one tile is several percent of the launch)
+// take no growth; there the full build also costs little next to the step's
+// launches.
+#ifndef PKV_BIN_DRIFT
+#define PKV_BIN_DRIFT 0.02
+#endif
+constexpr double kBinDrift = PKV_BIN_DRIFT;
+
+// Update the last bins schedule built in full to the current upload, when the
+// batch is the same and no sequence has fewer tiles than then (decode steps
+// add one token per sequence): each segment's new tiles go to the wave that
+// holds its last tile (the cuts stay where they were, so the pieces and
+// merges of split segments are unchanged), and the lengths, slot flags and
+// block ids the descriptors and bin lists carry are refreshed. Returns false
+// (schedule untouched) when a full build is due: another batch, bin count or
+// group, a sequence with fewer tiles, or a wave grown by more than kBinDrift
+// of its bin's mean run since the full build.
+bool update_bins(pkv_pool* p, int nbins) {
+  const int B = p->up_batch;
+  const int H = p->shape.kv_heads;
+  const int nseg = B * H;
+  const int W = nbins * kBinWaves;
+  if (kBinDrift <= 0 || !p->bins_valid || !p->sched_bins || B != p->bins_batch || nbins != p->bins_nbins ||
+      p->sched_gp_building != p->bins_gp || (int)p->bins_count0.size() != W ||
+      p->h_sched.size() != (size_t)8 * W + 6 * (size_t)nseg)
+    return false;
+  std::vector<int32_t> cnt(p->bins_count0);
+  for (int s = 0; s < B; ++s) {
+    const int64_t d = nblk(p->h_ctx[s]) - p->bins_seq_tiles[s];
+    if (d < 0) return false;
+    if (d > 0)
+      for (int g = 0; g < H; ++g) cnt[p->bins_end_wave[(size_t)g * B + s]] += (int32_t)d;
+  }
+  for (int b = 0; b < nbins; ++b) {
+    int64_t sum = 0;
+    for (int v = 0; v < kBinWaves; ++v) sum += p->bins_count0[b * kBinWaves + v];
+    const int64_t lim = (int64_t)(kBinDrift * (double)sum / kBinWaves);
+    for (int v = 0; v < kBinWaves; ++v)
+      if (cnt[b * kBinWaves + v] - p->bins_count0[b * kBinWaves + v] > lim) return false;
+  }
+  int32_t* desc = p->h_sched.data();
+  for (int w = 0; w < W; ++w) {
+    int32_t* d = desc + (size_t)8 * w;
+    d[1] = cnt[w];
+    if (cnt[w] == 0) continue;
+    const int s = d[2];
+    d[5] = p->h_ctx[s] | p->h_slotflag[s];
+    d[6] = p->h_bt[(size_t)s * p->up_stride + (size_t)d[4] * pkv::kTile / p->shape.block_size];
+  }
+  int32_t* list = desc + (size_t)8 * W + 2 * (size_t)nseg;
+  for (int i = 0; i < nseg; ++i) {
+    int32_t* e = list + 4 * (size_t)i;
+    const int s = e[0];
+    e[2] = p->h_ctx[s] | p->h_slotflag[s];
+    e[3] = p->h_bt[(size_t)s * p->up_stride];
+  }
   return true;
 }
 
@@ -1636,6 +1730,15 @@ int pkv_pool_stats(const pkv_pool* p, int64_t stats[4]) {
   stats[1] = p->shape.num_blocks - stats[0];
   stats[2] = shared;
   stats[3] = waste;
+  return PKV_OK;
+}
+
+int pkv_schedule_stats(const pkv_pool* p, int64_t stats[4]) {
+  if (!p || !stats) return fail(PKV_EINVAL, "bad arguments");
+  stats[0] = p->n_full_builds;
+  stats[1] = p->n_updates;
+  stats[2] = p->sched_bins ? 1 : 0;
+  stats[3] = p->sched_nwaves;
   return PKV_OK;
 }
 

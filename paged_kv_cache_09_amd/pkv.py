@@ -64,6 +64,7 @@ _SIGS = {
     "pkv_paged_attn_decode_noalloc": (_I, [_P, _I, _P, _I, ctypes.c_float, _P, _I, _U]),
     "pkv_decode_workspace_bytes": (_SZ, [_P, _I, _I, _I]),
     "pkv_pool_stats": (_I, [_P, _P]),
+    "pkv_schedule_stats": (_I, [_P, _P]),
     "pkv_prefix_match": (_I, [_P, _P, _I, _P, _I]),
     "pkv_prefix_insert": (_I, [_P, _P, _I, _P, _I]),
     "pkv_prefix_stats": (_I, [_P, _P]),
@@ -238,6 +239,13 @@ def pool_stats(pool) -> dict:
     _check(_lib.pkv_pool_stats(pool, _addr(out)))
     return {"free": int(out[0]), "used": int(out[1]), "shared": int(out[2]),
             "waste_tokens": int(out[3])}
+
+
+def schedule_stats(pool) -> dict:
+    out = np.zeros(4, dtype=np.int64)
+    _check(_lib.pkv_schedule_stats(pool, _addr(out)))
+    return {"full_builds": int(out[0]), "updates": int(out[1]), "bins": bool(out[2]),
+            "waves": int(out[3])}
 
 
 def prefix_match(pool, tokens, max_ids: int | None = None) -> np.ndarray:

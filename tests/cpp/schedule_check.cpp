@@ -26,8 +26,10 @@ bool prefix_supported(int dtype, int head_dim, int gp) {
 
 }
 
+// grow_steps > 0: afterwards, that many decode steps (every length + 1, some
+// + 17) through update_bins, falling back to build_bins; each schedule checked.
 static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins, int bs = 16,
-                 int dtype = PKV_BF16) {
+                 int dtype = PKV_BF16, int grow_steps = 0) {
   pkv_pool P;
   pkv_pool* p = &P;
   p->shape.kv_heads = H;
@@ -37,6 +39,7 @@ static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins, int b
   p->up_batch = B;
   int maxb = 0;
   for (int L : ctx) maxb = std::max<int>(maxb, (L + bs - 1) / bs);  // table entries
+  maxb += (grow_steps * 18 + bs - 1) / bs + 1;  // room to grow
   p->up_stride = maxb;
   p->h_ctx = ctx;
   // every other sequence has an uploaded slot: its lengths carry bit 30
@@ -49,6 +52,8 @@ static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins, int b
   bool ok = build_bins(p, nbins);
   if (ok != expect_bins && expect_bins) { printf("bins refused (expected)\n"); return 1; }
   if (!ok) return 0;
+  int updates = 0, rebuilds = 0;
+  for (int step = 0;; ++step) {
   const int W = p->sched_nwaves, nseg = B * H;
   const int32_t* desc = p->h_sched.data();
   const int32_t* list = desc + 8 * (size_t)W + 2 * (size_t)nseg;
@@ -140,8 +145,26 @@ static int check(std::vector<int> ctx, int H, int nbins, bool expect_bins, int b
     for (int s = 0; s < B; ++s)
       for (int j = 0; j < (ctx[s] + 15) / 16; ++j)
         if (cov[{g, s, j}] != 1) { printf("tile (%d,%d,%d) covered %d\n", g, s, j, cov[{g,s,j}]); return 1; }
-  printf("ok: B=%d H=%d bs=%d bins=%d waves=%d merges=%d errors=%d\n", B, H, bs, nbins, W, merges, errors);
-  return errors;
+  if (step == 0 || errors)
+    printf("ok: B=%d H=%d bs=%d bins=%d waves=%d merges=%d errors=%d\n", B, H, bs, nbins, W, merges, errors);
+  if (errors) return errors;
+  if (step == grow_steps) break;
+  // next decode step: every sequence one token longer (every seventh 17),
+  // new blocks at the table's end, slot flags changed
+  for (int s = 0; s < B; ++s) {
+    ctx[s] += s % 7 == 3 ? 17 : 1;
+    for (int j = 0; j < (ctx[s] + bs - 1) / bs; ++j)
+      if (p->h_bt[(size_t)s * maxb + j] < 0) p->h_bt[(size_t)s * maxb + j] = 1000 + id++;
+    p->h_slotflag[s] = (s + step) % 3 == 0 ? 1 << 30 : 0;
+  }
+  p->h_ctx = ctx;
+  if (update_bins(p, nbins)) ++updates;
+  else if (build_bins(p, nbins)) ++rebuilds;
+  else { printf("bins refused after growth\n"); return 1; }
+  }
+  if (grow_steps)
+    printf("ok: %d grown steps, %d updates, %d rebuilds\n", grow_steps, updates, rebuilds);
+  return 0;
 }
 
 // Shared-prefix groups in the split form: replays the prefix items and every
@@ -306,6 +329,14 @@ int main() {
   for (int bs : {8, 32}) {
     std::vector<int> c(64); std::uniform_int_distribution<int> u(128, 2048); for (auto& x : c) x = u(rng);
     rc |= check(c, 8, 256, true, bs);
+  }
+  // decode steps: schedules updated in place while lengths grow
+  // (runs long enough that a wave may take a few tiles before a rebuild)
+  { std::vector<int> c(64); std::uniform_int_distribution<int> u(128, 2048); for (auto& x : c) x = u(rng); rc |= check(c, 8, 16, true, 16, PKV_BF16, 60); }
+  { std::vector<int> c(256); std::uniform_int_distribution<int> u(16, 2048); for (auto& x : c) x = u(rng); rc |= check(c, 40, 256, true, 16, PKV_F16, 40); }
+  for (int bs : {8, 32}) {
+    std::vector<int> c(48); std::uniform_int_distribution<int> u(100, 1500); for (auto& x : c) x = u(rng);
+    rc |= check(c, 4, 8, true, bs, PKV_Q4_0, 50);
   }
   for (int dt : {PKV_Q8_0, PKV_Q4_0}) {  // waves 0..3 take a larger share of each bin
     std::vector<int> c(64); std::uniform_int_distribution<int> u(128, 2048); for (auto& x : c) x = u(rng);

@@ -1,6 +1,7 @@
 """The decode schedules replayed on the CPU (no GPU): a C++ check built from the
 host source with the kernel launches stubbed (tests/cpp/schedule_check.cpp) —
-the bins form, and the split form with shared-prefix groups."""
+the bins form (built in full, and updated in place over decode steps), and the
+split form with shared-prefix groups."""
 import os
 import subprocess
 
@@ -19,3 +20,10 @@ def test_bins_schedule_covers_every_tile_once_and_merges_every_split(tmp_path):
     assert "ALL OK" in r.stdout
     assert r.stdout.count("ok: ") >= 50
     assert r.stdout.count("ok groups: ") >= 40
+    # schedules updated in place over decode steps were checked too, and both
+    # the update and the full rebuild took place
+    import re
+    grown = re.findall(r"ok: (\d+) grown steps, (\d+) updates, (\d+) rebuilds", r.stdout)
+    assert len(grown) >= 4
+    for steps, upd, reb in grown:
+        assert int(upd) > 0 and int(reb) > 0 and int(upd) + int(reb) == int(steps)
