@@ -212,6 +212,14 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (3 times) and "
                          "exit: reference for calibrating HBM byte counters")
+    ap.add_argument("--probe", choices=("stream", "gather"), default=None,
+                    help="instead of the decode step, time a bandwidth probe over one layer of "
+                         "--config: 'gather' reads every K/V tile the decode reads through the "
+                         "block table (equal shares per wave, no compute), 'stream' a contiguous "
+                         "buffer of the same bytes; both with the decode's 16-byte "
+                         "nontemporal loads")
+    ap.add_argument("--probe-waves", type=int, nargs="+", default=[2048, 4096],
+                    help="waves of the probe launch (one JSON line each)")
     ap.add_argument("--unfused", action="store_true",
                     help="kv_append and paged_attn_decode as two launches per layer")
     ap.add_argument("--request-stream", type=int, default=0, metavar="STEPS",
@@ -271,6 +279,8 @@ def main():
 
     if args.write_chunk:
         return main_write(args)
+    if args.probe:
+        return main_probe(args)
     cfg = W.CONFIGS[args.config]
     if args.block_size:
         # same token capacity in blocks of another size
@@ -439,6 +449,58 @@ def main():
                                     "GBps": round(copy_bytes / copy_s / 1e9, 2)}
     sess.close()
     print(json.dumps(res), flush=True)
+
+
+def main_probe(args):
+    """Bandwidth probes over one layer of a workload (measurements bounding the
+    decode from above; see pkv_probe_* in include/pkv.h)."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_09_amd import pkv, workloads as W
+    from paged_kv_cache_09_amd.session import DecodeSession
+    cfg = W.CONFIGS[args.config]
+    w = W.make(cfg, device="cuda", layers=1, form="step", fill="random", extra_blocks=1)
+    sess = DecodeSession(w)
+    sess.prepare()
+    sess.upload()
+    torch.cuda.synchronize()
+    tile = W.row_bytes(cfg) * 16
+    tiles = int(((np.asarray(sess.ctx, dtype=np.int64) + 15) // 16).sum()) * cfg.kv_heads
+    nbytes = 2 * tiles * tile  # K and V tiles of one layer
+    stream = torch.cuda.current_stream()
+    buf = None
+    if args.probe == "stream":
+        buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        buf.fill_(3)
+    reps = max(5, args.decode_reps)
+    for waves in args.probe_waves:
+        out = torch.empty(waves * 64, dtype=torch.int32, device="cuda")
+
+        def launch():
+            if args.probe == "stream":
+                pkv.probe_stream_read(buf, nbytes, out, waves, stream.cuda_stream)
+            else:
+                pkv.probe_gather(sess.pool, 0, out, waves, stream.cuda_stream)
+
+        for _ in range(3):
+            launch()
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        evs[0].record(stream)
+        for r in range(reps):
+            launch()
+            evs[r + 1].record(stream)
+        torch.cuda.synchronize()
+        per = np.array([evs[r].elapsed_time(evs[r + 1]) / 1e3 for r in range(reps)])
+        gbs = nbytes / per.mean() / 1e9
+        print(json.dumps({
+            "metric": f"probe: {args.probe} read GB/s", "value": round(gbs, 2), "unit": "GB/s",
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "avg_launch_us": round(per.mean() * 1e6, 3),
+            "launch_us_p10_p50_p90": [round(float(x) * 1e6, 3) for x in np.percentile(per, [10, 50, 90])],
+            "bytes_per_launch": nbytes, "waves": waves, "launches": reps,
+            "config": {"workload": f"{cfg.name}: one layer's K and V tiles "
+                                   f"({tiles} tiles of {tile} bytes each)"}}), flush=True)
+    sess.close()
 
 
 def main_write(args):

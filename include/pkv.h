@@ -372,6 +372,27 @@ int pkv_pool_stats(const pkv_pool* pool, int64_t stats_out[4]);
  */
 int pkv_schedule_stats(const pkv_pool* pool, int64_t stats_out[4]);
 
+/*
+ * Bandwidth probes (measurements that bound the decode from above; not part
+ * of the decode path). Both read with the decode's 16-byte nontemporal loads,
+ * do no arithmetic beyond an XOR of what they read, and write one uint32 per
+ * lane to dev_out (device memory of waves * 64 uint32, caller-owned); they
+ * are asynchronous on `stream`.
+ * pkv_probe_stream_read: `bytes` (a multiple of 16, dev_buf 16-byte aligned)
+ *   of a contiguous device buffer, each of `waves` waves reading one
+ *   contiguous share.
+ * pkv_probe_gather: every K and V tile (16 tokens of one kv head) the decode
+ *   of `layer` reads for the last upload, through the uploaded block table,
+ *   the (kv head, sequence, tile) space split into `waves` equal shares: the
+ *   decode's access pattern with perfect balance and no compute. 2-byte caches
+ *   in blocks of 16 tokens (PKV_EUNSUPPORTED otherwise); PKV_EINVAL before an
+ *   upload or for bad arguments.
+ */
+int pkv_probe_stream_read(const void* dev_buf, int64_t bytes, uint32_t* dev_out, int waves,
+                          uintptr_t stream);
+int pkv_probe_gather(const pkv_pool* pool, int layer, uint32_t* dev_out, int waves,
+                     uintptr_t stream);
+
 /* Message for the last failing call on this host thread ("" if none). */
 const char* pkv_last_error(void);
 

@@ -26,7 +26,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-Wall"]
-SOURCES = ["pkv_host.cpp", "pkv_kernels.hip"]
+SOURCES = ["pkv_host.cpp", "pkv_kernels.hip", "pkv_probes.hip"]
 EXTRA = os.environ.get("PKV_EXTRA_FLAGS", "").split()
 
 

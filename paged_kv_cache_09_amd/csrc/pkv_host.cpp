@@ -167,14 +167,16 @@ struct pkv_pool {
   int sched_seg_stride = 1;         // partial slots per segment (1 + most chunks)
   int sched_gp_building = 1;        // padded group of the schedule being built
   std::vector<int32_t> h_sched;     // wdesc[8 * nwaves] | seg_w0[nseg] | seg_w1[nseg]
-  // The last bins schedule built in full, for updating it while lengths only
-  // grow: its batch, bin count and group, each sequence's tile count then,
-  // each segment's (g * batch + s) wave holding its last tile, and each
-  // wave's tile count then.
+  // The bins schedule, for updating it while lengths only grow: its batch,
+  // bin count and group, and per segment (g * batch + s) its tile count and
+  // the wave holding its last tile, per wave its tile count, as of the last
+  // layout of their bin.
   bool bins_valid = false;
   int bins_batch = 0, bins_nbins = 0, bins_gp = 0;
+  double bins_imb0 = 1.0;  // imbalance when the bins were packed
   int64_t n_full_builds = 0, n_updates = 0;
-  std::vector<int32_t> bins_seq_tiles, bins_end_wave, bins_count0;
+  std::vector<int32_t> bins_seg_tiles, bins_end_wave, bins_count0;
+  std::vector<int32_t> bins_li0;  // per bin, its first bin list entry (then the total)
 
   Staging ring[4];
   int ring_next = 0;
@@ -442,7 +444,11 @@ void build_schedule(pkv_pool* p, int part, int target) {
     const int per_cu = pkv::decode_blocks_per_cu(p->shape.dtype, p->shape.head_dim,
                                                   p->sched_gp_building, true,
                                                   p->shape.block_size);
+#ifdef PKV_BINS_PER_CU_MAX
+    const int nbins = std::max(1, p->num_cus) * std::min(per_cu, PKV_BINS_PER_CU_MAX);
+#else
     const int nbins = std::max(1, p->num_cus) * per_cu;
+#endif
     if (per_cu > 0 && update_bins(p, nbins)) {
       ++p->n_updates;
       return;
@@ -570,7 +576,7 @@ int waves_target(const pkv_pool* p, int gp) {
 // the faster one up to an imbalance of about 1.39 (bf16), 1.36 (q8_0) and
 // 1.26 (q4_0).
 constexpr double kBinSlack = 1.25;
-constexpr int kBinWaves = 8;
+using pkv::kBinWaves;
 
 // Bins form of the balanced schedule: whole (kv head, sequence) segments are
 // packed into nbins bins, longest processing time first (each segment to the
@@ -668,6 +674,110 @@ void cut_runs(const std::vector<int64_t>& n, int nruns, const RunCosts& rc, int6
   pack(hi, start);
 }
 
+// Lay out bin b, whose segments are the bin list entries li0 .. li1 - 1 (in
+// kv head, then sequence order; words 0-1 of each entry set): refresh the
+// entries' lengths and first block ids, cut the bin's tiles into kBinWaves
+// runs of balanced cost and write the runs' descriptors, the merge words of
+// segments split between runs, each segment's end wave and tile count, and
+// each run's tile count (the reference of later in-place updates).
+void emit_bin(pkv_pool* p, int b, int li0, int li1) {
+  const int B = p->up_batch;
+  const int nseg = B * p->shape.kv_heads;
+  const int W = p->bins_nbins * kBinWaves;
+  int32_t* desc = p->h_sched.data();
+  int32_t* list = desc + (size_t)8 * W + 2 * (size_t)nseg;
+  std::fill(desc + (size_t)8 * b * kBinWaves, desc + (size_t)8 * (b + 1) * kBinWaves, 0);
+  std::vector<int64_t> ntiles;
+  ntiles.reserve(li1 - li0);
+  for (int li = li0; li < li1; ++li) {
+    int32_t* e = list + 4 * (size_t)li;
+    const int s = e[0];
+    e[2] = p->h_ctx[s] | p->h_slotflag[s];
+    e[3] = p->h_bt[(size_t)s * p->up_stride];
+    ntiles.push_back(nblk(p->h_ctx[s]));
+    p->bins_seg_tiles[(size_t)e[1] * B + s] = (int32_t)ntiles.back();
+  }
+  // cut the bin's tiles into kBinWaves runs of balanced cost
+  int64_t start_tile[kBinWaves + 1];
+  cut_runs(ntiles, kBinWaves, run_costs(p->shape.dtype), start_tile);
+  // descriptors: walk segments and waves together
+  int seg_i = 0;       // index into the bin's entries
+  int64_t seg_x0 = 0;  // bin-local tile index where entry seg_i starts
+  for (int wv = 0; wv < kBinWaves; ++wv) {
+    int32_t* d = desc + (size_t)8 * (b * kBinWaves + wv);
+    const int64_t x0 = start_tile[wv], x1 = std::max(start_tile[wv], start_tile[wv + 1]);
+    d[1] = (int32_t)(x1 - x0);
+    p->bins_count0[b * kBinWaves + wv] = d[1];
+    if (x1 <= x0) {
+      d[0] = li0;
+      continue;
+    }
+    while (seg_x0 + ntiles[seg_i] <= x0) seg_x0 += ntiles[seg_i++];
+    const int32_t* e = list + 4 * (size_t)(li0 + seg_i);
+    const int s = e[0];
+    const int64_t j0 = x0 - seg_x0;
+    d[0] = li0 + seg_i;
+    d[2] = s;
+    d[3] = e[1];
+    d[4] = (int32_t)j0;
+    d[5] = p->h_ctx[s] | p->h_slotflag[s];
+    d[6] = p->h_bt[(size_t)s * p->up_stride + j0 * pkv::kTile / p->shape.block_size];
+  }
+  // Segments split between waves: their pieces go to consecutive LDS piece
+  // slots (base .. base + n - 1, in holder order), and every holder merges
+  // some of the heads (head h goes to holder h mod n). Word 7 of a wave:
+  //   bits 0-3  slot of its first segment's piece (when that is split),
+  //   bits 4-7  slot of its last segment's piece (split, not its first),
+  //   bit 8     it merges heads of its first segment: bits 9-12 base slot,
+  //             bits 13-16 holders n, bits 17-19 its index among them;
+  //   bit 20    it merges heads of its last segment (index 0): bits 21-24 n.
+  int64_t sx = 0;
+  int base = 0;
+  for (int k = 0; k < li1 - li0; ++k) {
+    const int64_t a = sx, e = sx + ntiles[k];  // the segment's bin-local tiles [a, e)
+    sx = e;
+    int wf = -1, wlast = -1;
+    for (int wv = 0; wv < kBinWaves; ++wv) {
+      const int64_t x0 = start_tile[wv], x1 = std::max(start_tile[wv], start_tile[wv + 1]);
+      if (x1 > x0 && x0 < e && x1 > a) {
+        if (wf < 0) wf = wv;
+        wlast = wv;
+      }
+    }
+    const int32_t* le = list + 4 * (size_t)(li0 + k);
+    if (wlast >= 0) p->bins_end_wave[(size_t)le[1] * B + le[0]] = b * kBinWaves + wlast;
+    if (wf < 0 || wlast == wf) continue;
+    const int n = wlast - wf + 1;
+    for (int wv = wf; wv <= wlast; ++wv) {
+      int32_t* d = desc + (size_t)8 * (b * kBinWaves + wv);
+      const int slot = base + (wv - wf);
+      if (wv == wf && start_tile[wf] < a) {
+        // the segment starts inside this wave's run: its last segment
+        d[7] |= (slot << 4) | (1 << 20) | (n << 21);
+      } else {
+        d[7] |= slot | (1 << 8) | (base << 9) | (n << 13) | ((wv - wf) << 17);
+      }
+    }
+    base += n;
+  }
+}
+
+// Largest bin cost (tiles + kSegStartCost per segment) over the mean.
+double bins_imbalance(const pkv_pool* p) {
+  const int B = p->up_batch;
+  const int nseg = B * p->shape.kv_heads;
+  const int32_t* list = p->h_sched.data() + (size_t)8 * p->bins_nbins * kBinWaves + 2 * (size_t)nseg;
+  int64_t total = 0, maxload = 0;
+  for (int b = 0; b < p->bins_nbins; ++b) {
+    int64_t load = 0;
+    for (int li = p->bins_li0[b]; li < p->bins_li0[b + 1]; ++li)
+      load += nblk(p->h_ctx[list[4 * (size_t)li]]) + kSegStartCost;
+    total += load;
+    maxload = std::max(maxload, load);
+  }
+  return total > 0 ? (double)maxload * p->bins_nbins / (double)total : 1.0;
+}
+
 bool build_bins(pkv_pool* p, int nbins) {
   const int B = p->up_batch;
   const int H = p->shape.kv_heads;
@@ -725,165 +835,104 @@ bool build_bins(pkv_pool* p, int nbins) {
 
   const int W = nbins * kBinWaves;
   p->h_sched.assign((size_t)8 * W + 2 * (size_t)nseg + 4 * (size_t)nseg, 0);
+  p->bins_nbins = nbins;
   p->bins_end_wave.assign(nseg, 0);
-  int32_t* desc = p->h_sched.data();
-  int32_t* list = desc + (size_t)8 * W + 2 * (size_t)nseg;
+  p->bins_seg_tiles.assign(nseg, 0);
+  p->bins_count0.assign(W, 0);
+  p->bins_li0.assign(nbins + 1, 0);
+  int32_t* list = p->h_sched.data() + (size_t)8 * W + 2 * (size_t)nseg;
   int li = 0;
   for (int b = 0; b < nbins; ++b) {
     std::vector<int>& m = members[b];
     std::sort(m.begin(), m.end(), [&](int a, int c) {
       return segs[a].g != segs[c].g ? segs[a].g < segs[c].g : segs[a].s < segs[c].s;
     });
-    const int li0 = li;
+    p->bins_li0[b] = li;
     for (int i : m) {
-      const int s = segs[i].s;
       int32_t* e = list + 4 * (size_t)li++;
-      e[0] = s;
+      e[0] = segs[i].s;
       e[1] = segs[i].g;
-      e[2] = p->h_ctx[s] | p->h_slotflag[s];
-      e[3] = p->h_bt[(size_t)s * p->up_stride];
     }
-    // cut the bin's tiles into kBinWaves runs of balanced cost
-    std::vector<int64_t> ntiles;
-    ntiles.reserve(m.size());
-    for (int i : m) ntiles.push_back(segs[i].cost - kSegStartCost);
-    int64_t start_tile[kBinWaves + 1];
-    cut_runs(ntiles, kBinWaves, run_costs(p->shape.dtype), start_tile);
-    // descriptors: walk segments and waves together
-    int seg_i = 0;          // index into m
-    int64_t seg_x0 = 0;     // bin-local tile index where m[seg_i] starts
-    for (int wv = 0; wv < kBinWaves; ++wv) {
-      int32_t* d = desc + (size_t)8 * (b * kBinWaves + wv);
-      const int64_t x0 = start_tile[wv], x1 = std::max(start_tile[wv], start_tile[wv + 1]);
-      d[1] = (int32_t)(x1 - x0);
-      if (x1 <= x0) {
-        d[0] = li0;
-        continue;
-      }
-      while (seg_x0 + (segs[m[seg_i]].cost - kSegStartCost) <= x0) {
-        seg_x0 += segs[m[seg_i]].cost - kSegStartCost;
-        ++seg_i;
-      }
-      const Seg& sg = segs[m[seg_i]];
-      const int64_t j0 = x0 - seg_x0;
-      d[0] = li0 + seg_i;
-      d[2] = sg.s;
-      d[3] = sg.g;
-      d[4] = (int32_t)j0;
-      d[5] = p->h_ctx[sg.s] | p->h_slotflag[sg.s];
-      d[6] = p->h_bt[(size_t)sg.s * p->up_stride + j0 * pkv::kTile / p->shape.block_size];
-    }
-    // Segments split between waves: their pieces go to consecutive LDS piece
-    // slots (base .. base + n - 1, in holder order), and every holder merges
-    // some of the heads (head h goes to holder h mod n). Word 7 of a wave:
-    //   bits 0-3  slot of its first segment's piece (when that is split),
-    //   bits 4-7  slot of its last segment's piece (split, not its first),
-    //   bit 8     it merges heads of its first segment: bits 9-12 base slot,
-    //             bits 13-16 holders n, bits 17-19 its index among them;
-    //   bit 20    it merges heads of its last segment (index 0): bits 21-24 n.
-    {
-      int64_t sx = 0;
-      int base = 0;
-      for (size_t k = 0; k < m.size(); ++k) {
-        const int64_t n0 = segs[m[k]].cost - kSegStartCost;
-        const int64_t a = sx, e = sx + n0;  // the segment's bin-local tiles [a, e)
-        sx = e;
-        int wf = -1, wlast = -1;
-        for (int wv = 0; wv < kBinWaves; ++wv) {
-          const int64_t x0 = start_tile[wv], x1 = std::max(start_tile[wv], start_tile[wv + 1]);
-          if (x1 > x0 && x0 < e && x1 > a) {
-            if (wf < 0) wf = wv;
-            wlast = wv;
-          }
-        }
-        if (wlast >= 0) p->bins_end_wave[segs[m[k]].g * B + segs[m[k]].s] = b * kBinWaves + wlast;
-        if (wf < 0 || wlast == wf) continue;
-        const int n = wlast - wf + 1;
-        for (int wv = wf; wv <= wlast; ++wv) {
-          int32_t* d = desc + (size_t)8 * (b * kBinWaves + wv);
-          const int slot = base + (wv - wf);
-          if (wv == wf && start_tile[wf] < a) {
-            // the segment starts inside this wave's run: its last segment
-            d[7] |= (slot << 4) | (1 << 20) | (n << 21);
-          } else {
-            d[7] |= slot | (1 << 8) | (base << 9) | (n << 13) | ((wv - wf) << 17);
-          }
-        }
-        base += n;
-      }
-    }
+    emit_bin(p, b, p->bins_li0[b], li);
   }
+  p->bins_li0[nbins] = li;
   p->sched_nwaves = W;
   p->sched_needs_merge = false;
   p->sched_bins = true;
-  p->bins_seq_tiles.resize(B);
-  for (int s = 0; s < B; ++s) p->bins_seq_tiles[s] = (int32_t)nblk(p->h_ctx[s]);
-  p->bins_count0.resize(W);
-  for (int w = 0; w < W; ++w) p->bins_count0[w] = desc[(size_t)8 * w + 1];
   p->bins_batch = B;
-  p->bins_nbins = nbins;
   p->bins_gp = p->sched_gp_building;
+  p->bins_imb0 = (double)maxload * nbins / (double)total;
   p->bins_valid = true;
   return true;
 }
 
 // A wave may grow by this share of its bin's mean run, rounded down to whole
-// tiles, before the bins are packed and cut again (0: always again). Short
-// runs (a few dozen tiles, where one tile is several percent of the launch)
-// take no growth; there the full build also costs little next to the step's
-// launches.
+// tiles, before its bin is cut again (0: the whole schedule is built again
+// at every upload). Short runs (a few dozen tiles, where one tile is several
+// percent of the launch) take no growth.
 #ifndef PKV_BIN_DRIFT
 #define PKV_BIN_DRIFT 0.02
 #endif
 constexpr double kBinDrift = PKV_BIN_DRIFT;
+// The bins are packed again once their imbalance (largest over mean) has
+// grown this much since they were packed.
+constexpr double kBinRepack = 0.01;
 
-// Update the last bins schedule built in full to the current upload, when the
-// batch is the same and no sequence has fewer tiles than then (decode steps
-// add one token per sequence): each segment's new tiles go to the wave that
-// holds its last tile (the cuts stay where they were, so the pieces and
-// merges of split segments are unchanged), and the lengths, slot flags and
-// block ids the descriptors and bin lists carry are refreshed. Returns false
-// (schedule untouched) when a full build is due: another batch, bin count or
-// group, a sequence with fewer tiles, or a wave grown by more than kBinDrift
-// of its bin's mean run since the full build.
+// Update the last bins schedule to the current upload, when the batch is the
+// same and no (kv head, sequence) segment has fewer tiles than when its bin
+// was last laid out (decode steps add one token per sequence): each
+// segment's new tiles go to the wave that holds its last tile (the cuts stay
+// where they were, so the pieces and merges of split segments are
+// unchanged); a bin one of whose waves grew by more than kBinDrift of its
+// mean run is cut again; lengths, slot flags and block ids are refreshed.
+// Returns false (schedule untouched) when a full build is due: another batch,
+// bin count or group, a segment with fewer tiles, or bins whose imbalance has
+// grown by kBinRepack since they were packed.
 bool update_bins(pkv_pool* p, int nbins) {
   const int B = p->up_batch;
   const int H = p->shape.kv_heads;
   const int nseg = B * H;
   const int W = nbins * kBinWaves;
-  if (kBinDrift <= 0 || !p->bins_valid || !p->sched_bins || B != p->bins_batch || nbins != p->bins_nbins ||
-      p->sched_gp_building != p->bins_gp || (int)p->bins_count0.size() != W ||
-      p->h_sched.size() != (size_t)8 * W + 6 * (size_t)nseg)
+  if (kBinDrift <= 0 || !p->bins_valid || !p->sched_bins || B != p->bins_batch ||
+      nbins != p->bins_nbins || p->sched_gp_building != p->bins_gp ||
+      (int)p->bins_count0.size() != W || p->h_sched.size() != (size_t)8 * W + 6 * (size_t)nseg)
     return false;
   std::vector<int32_t> cnt(p->bins_count0);
-  for (int s = 0; s < B; ++s) {
-    const int64_t d = nblk(p->h_ctx[s]) - p->bins_seq_tiles[s];
-    if (d < 0) return false;
-    if (d > 0)
-      for (int g = 0; g < H; ++g) cnt[p->bins_end_wave[(size_t)g * B + s]] += (int32_t)d;
-  }
+  for (int g = 0; g < H; ++g)
+    for (int s = 0; s < B; ++s) {
+      const int64_t d = nblk(p->h_ctx[s]) - p->bins_seg_tiles[(size_t)g * B + s];
+      if (d < 0) return false;
+      if (d > 0) cnt[p->bins_end_wave[(size_t)g * B + s]] += (int32_t)d;
+    }
+  if (bins_imbalance(p) > p->bins_imb0 + kBinRepack) return false;
+  int32_t* desc = p->h_sched.data();
+  int32_t* list = desc + (size_t)8 * W + 2 * (size_t)nseg;
   for (int b = 0; b < nbins; ++b) {
     int64_t sum = 0;
+    bool recut = false;
     for (int v = 0; v < kBinWaves; ++v) sum += p->bins_count0[b * kBinWaves + v];
     const int64_t lim = (int64_t)(kBinDrift * (double)sum / kBinWaves);
     for (int v = 0; v < kBinWaves; ++v)
-      if (cnt[b * kBinWaves + v] - p->bins_count0[b * kBinWaves + v] > lim) return false;
-  }
-  int32_t* desc = p->h_sched.data();
-  for (int w = 0; w < W; ++w) {
-    int32_t* d = desc + (size_t)8 * w;
-    d[1] = cnt[w];
-    if (cnt[w] == 0) continue;
-    const int s = d[2];
-    d[5] = p->h_ctx[s] | p->h_slotflag[s];
-    d[6] = p->h_bt[(size_t)s * p->up_stride + (size_t)d[4] * pkv::kTile / p->shape.block_size];
-  }
-  int32_t* list = desc + (size_t)8 * W + 2 * (size_t)nseg;
-  for (int i = 0; i < nseg; ++i) {
-    int32_t* e = list + 4 * (size_t)i;
-    const int s = e[0];
-    e[2] = p->h_ctx[s] | p->h_slotflag[s];
-    e[3] = p->h_bt[(size_t)s * p->up_stride];
+      recut |= cnt[b * kBinWaves + v] - p->bins_count0[b * kBinWaves + v] > lim;
+    if (recut) {
+      emit_bin(p, b, p->bins_li0[b], p->bins_li0[b + 1]);
+      continue;
+    }
+    for (int v = 0; v < kBinWaves; ++v) {
+      const int w = b * kBinWaves + v;
+      int32_t* d = desc + (size_t)8 * w;
+      d[1] = cnt[w];
+      if (cnt[w] == 0) continue;
+      const int s = d[2];
+      d[5] = p->h_ctx[s] | p->h_slotflag[s];
+      d[6] = p->h_bt[(size_t)s * p->up_stride + (size_t)d[4] * pkv::kTile / p->shape.block_size];
+    }
+    for (int li = p->bins_li0[b]; li < p->bins_li0[b + 1]; ++li) {
+      int32_t* e = list + 4 * (size_t)li;
+      const int s = e[0];
+      e[2] = p->h_ctx[s] | p->h_slotflag[s];
+      e[3] = p->h_bt[(size_t)s * p->up_stride];
+    }
   }
   return true;
 }
@@ -1544,7 +1593,7 @@ int decode_impl(pkv_pool* p, int layer, const void* k_new, const void* v_new, co
     dp.nitems = p->sched_nitems;
     dp.nprefix = (p->sched_nitems + pkv::kNumXcd - 1) / pkv::kNumXcd * pkv::kNumXcd;
   }
-  const int groups = p->sched_bins ? W / 8 : W;  // workgroups: bins, or one per wave
+  const int groups = p->sched_bins ? W / kBinWaves : W;  // workgroups: bins, or one per wave
   dp.waves_per_xcd = (groups + pkv::kNumXcd - 1) / pkv::kNumXcd;
   e = pkv::launch_decode(p->shape.dtype, p->shape.head_dim, gp, p->sched_bins,
                          p->shape.block_size, dp, stream);
@@ -1731,6 +1780,42 @@ int pkv_pool_stats(const pkv_pool* p, int64_t stats[4]) {
   stats[2] = shared;
   stats[3] = waste;
   return PKV_OK;
+}
+
+int pkv_probe_stream_read(const void* dev_buf, int64_t bytes, uint32_t* dev_out, int waves,
+                          uintptr_t stream_u) {
+  if (!dev_buf || !dev_out || bytes < 16 || (bytes & 15) || waves < 1 || waves > (1 << 20) ||
+      (reinterpret_cast<uintptr_t>(dev_buf) & 15))
+    return fail(PKV_EINVAL, "bad arguments");
+  hipError_t e = pkv::launch_probe_stream(dev_buf, bytes, waves, dev_out,
+                                          reinterpret_cast<hipStream_t>(stream_u));
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "stream probe launch");
+}
+
+int pkv_probe_gather(const pkv_pool* p, int layer, uint32_t* dev_out, int waves,
+                     uintptr_t stream_u) {
+  int rc = need_device(p);
+  if (rc != PKV_OK) return rc;
+  if (!dev_out || waves < 1 || waves > (1 << 20) || layer < 0 || layer >= p->shape.layers)
+    return fail(PKV_EINVAL, "bad arguments");
+  if (!p->uploaded) return fail(PKV_EINVAL, "no block table uploaded");
+  if (p->shape.block_size != 16 || (p->tile_bytes != 1024 && p->tile_bytes != 2048 &&
+                                    p->tile_bytes != 4096))
+    return fail(PKV_EUNSUPPORTED, "the gather probe takes 2-byte caches in blocks of 16");
+  pkv::GatherParams g{};
+  g.k = p->k_base + (size_t)layer * p->layer_bytes;
+  g.v = p->v_base + (size_t)layer * p->layer_bytes;
+  g.bt = p->d_bt;
+  g.cum = p->d_cum;
+  g.out = dev_out;
+  g.blk_stride = p->block_bytes;
+  g.tile = (int32_t)p->tile_bytes;
+  g.bt_stride = p->up_stride;
+  g.batch = p->up_batch;
+  g.kv_heads = p->shape.kv_heads;
+  g.nwaves = waves;
+  hipError_t e = pkv::launch_probe_gather(g, reinterpret_cast<hipStream_t>(stream_u));
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "gather probe launch");
 }
 
 int pkv_schedule_stats(const pkv_pool* p, int64_t stats[4]) {

@@ -10,6 +10,10 @@ namespace pkv {
 constexpr int kTile = 16;        // tokens per decode tile (a block of 16, half of 32, two of 8)
 constexpr int kMaxGroup = 8;     // largest GQA group (q heads per kv head)
 constexpr int kNumXcd = 8;       // MI355X: workgroups are dealt round-robin to 8 XCDs
+#ifndef PKV_BIN_WAVES
+#define PKV_BIN_WAVES 8
+#endif
+constexpr int kBinWaves = PKV_BIN_WAVES;  // waves per workgroup (bin) of the bins form
 
 struct DecodeParams {
   const void* k;               // layer base of K: [num_blocks][kv_heads][16][head_dim]
@@ -103,6 +107,26 @@ hipError_t launch_copy_blocks(const int32_t* pairs, int n, void* k_base, void* v
 // (looked up once per device with that device current).
 constexpr size_t kScratchBytes = (size_t)32 << 20;
 hipError_t scratch_address(int dev, void** out);
+
+// Bandwidth probes (pkv_probes.hip). Gather: every K and V tile of one layer
+// the uploaded table names, 16 tokens of one kv head each; tile bytes 1024,
+// 2048 or 4096 (2-byte caches), blocks of 16 tokens.
+struct GatherParams {
+  const char* k;               // layer base of K
+  const char* v;               // layer base of V
+  const int32_t* bt;           // block table [batch][bt_stride]
+  const int32_t* cum;          // tiles' prefix sums over the sequences [batch + 1]
+  unsigned* out;               // [nwaves * 64] XOR of what each lane read
+  int64_t blk_stride;          // bytes per block of one layer (kv_heads tiles)
+  int32_t tile;                // bytes per (block, kv head) tile
+  int32_t bt_stride;
+  int32_t batch;
+  int32_t kv_heads;
+  int32_t nwaves;
+};
+hipError_t launch_probe_stream(const void* buf, int64_t bytes, int nwaves, unsigned* out,
+                               hipStream_t stream);
+hipError_t launch_probe_gather(const GatherParams& p, hipStream_t stream);
 
 #ifdef PKV_TIMELINE
 hipError_t copy_timeline(void* dst, size_t bytes);

@@ -761,7 +761,7 @@ __device__ __forceinline__ void prefix_item(const DecodeParams& p, int item) {
 // BS: tokens per pool block (8, 16 or 32). Work is always counted in 16-token
 // tiles: a tile is one block (16), half of one (32), or two blocks (8).
 template <int DT, int D, int GP, bool BINS, int BS>
-__global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(BINS ? 64 * kBinWaves : 64) void decode_kernel(DecodeParams p) {
   constexpr bool Q8 = DT == DT_Q8, Q4 = DT == DT_Q4, QN = Q8 || Q4;
   using TR = TileRegs<DT, D>;
   constexpr int RB = D * Elem<DT>::bytes;  // bytes per K/V row (unquantised caches)
@@ -796,7 +796,7 @@ __global__ __launch_bounds__(BINS ? 512 : 64) void decode_kernel(DecodeParams p)
   constexpr bool Q8M = Q8 && MPV;
   static_assert(!MPV || (CPR == 16 && NV == 4 && EPC == 8), "MFMA P.V lane layout");
 
-  constexpr int NW = BINS ? 8 : 1;       // waves per workgroup
+  constexpr int NW = BINS ? kBinWaves : 1;  // waves per workgroup
   // softmax weights, [wave][row][head], then a spare slot the lanes without
   // a head write to (a store every lane makes needs no branch). One buffer
   // serves every tile: a wave's LDS operations complete in order, so the
@@ -2031,7 +2031,7 @@ hipError_t launch_decode(int dtype, int head_dim, int gp, bool bins, int block_s
   if (!fn) return hipErrorInvalidValue;
   DecodeParams args = p;
   void* argv[] = {&args};
-  dim3 grid((unsigned)(p.nprefix + p.waves_per_xcd * kNumXcd)), block(bins ? 512 : 64);
+  dim3 grid((unsigned)(p.nprefix + p.waves_per_xcd * kNumXcd)), block(bins ? 64 * kBinWaves : 64);
   return hipLaunchKernel(fn, grid, block, argv, 0, stream);
 }
 
@@ -2039,7 +2039,7 @@ int decode_blocks_per_cu(int dtype, int head_dim, int gp, bool bins, int block_s
   const void* fn = decode_kernel_for(dtype, head_dim, gp, bins, block_size);
   if (!fn) return 0;
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, bins ? 512 : 64, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, bins ? 64 * kBinWaves : 64, 0) != hipSuccess)
     return 0;
   return n;
 }

@@ -65,6 +65,8 @@ _SIGS = {
     "pkv_decode_workspace_bytes": (_SZ, [_P, _I, _I, _I]),
     "pkv_pool_stats": (_I, [_P, _P]),
     "pkv_schedule_stats": (_I, [_P, _P]),
+    "pkv_probe_stream_read": (_I, [_P, ctypes.c_int64, _P, _I, _U]),
+    "pkv_probe_gather": (_I, [_P, _I, _P, _I, _U]),
     "pkv_prefix_match": (_I, [_P, _P, _I, _P, _I]),
     "pkv_prefix_insert": (_I, [_P, _P, _I, _P, _I]),
     "pkv_prefix_stats": (_I, [_P, _P]),
@@ -239,6 +241,14 @@ def pool_stats(pool) -> dict:
     _check(_lib.pkv_pool_stats(pool, _addr(out)))
     return {"free": int(out[0]), "used": int(out[1]), "shared": int(out[2]),
             "waste_tokens": int(out[3])}
+
+
+def probe_stream_read(buf, nbytes: int, out, waves: int, stream: int = 0) -> None:
+    _check(_lib.pkv_probe_stream_read(_ptr(buf), int(nbytes), _ptr(out), int(waves), int(stream)))
+
+
+def probe_gather(pool, layer: int, out, waves: int, stream: int = 0) -> None:
+    _check(_lib.pkv_probe_gather(pool, int(layer), _ptr(out), int(waves), int(stream)))
 
 
 def schedule_stats(pool) -> dict:

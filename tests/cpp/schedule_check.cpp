@@ -20,6 +20,8 @@ hipError_t launch_append_quant(int, const void*, const void*, const int64_t*, in
 hipError_t launch_copy_blocks(const int32_t*, int, void*, void*, int, int64_t, int64_t, hipStream_t) { return hipSuccess; }
 hipError_t launch_upload(const void*, void*, size_t, hipStream_t) { return hipSuccess; }
 hipError_t scratch_address(int, void**) { return hipErrorInvalidDevice; }
+hipError_t launch_probe_stream(const void*, int64_t, int, unsigned*, hipStream_t) { return hipSuccess; }
+hipError_t launch_probe_gather(const GatherParams&, hipStream_t) { return hipSuccess; }
 bool prefix_supported(int dtype, int head_dim, int gp) {
   return (dtype == PKV_F16 || dtype == PKV_BF16) && head_dim == 128 && gp <= 4;
 }
