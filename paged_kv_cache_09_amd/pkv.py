@@ -14,7 +14,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpkv.so")
+# PKV_LIB may name another build of the library in this directory (the
+# per-wave timeline build, libpkv_timeline.so); the default is libpkv.so.
+LIB_PATH = os.path.join(_HERE, os.path.basename(os.environ.get("PKV_LIB", "libpkv.so")))
 
 F32, F16, BF16, Q8_0, Q4_0 = 0, 1, 2, 3, 4
 OK, EINVAL, ECAPACITY, EOUT_OF_BLOCKS, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -5
