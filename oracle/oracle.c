@@ -188,7 +188,14 @@ void orc_q4_quantize(const float* x, int64_t n_groups, uint8_t* codes, uint16_t*
  * Quantised tile of one (block, kv head) in the pool (our layout; the pages fix
  * none): block_size rows of codes, then block_size x head_dim/32 fp16 scales,
  * ordered [row][group] in the K region and [group][row] in the V region.
- * q8_0: row r's head_dim int8 codes at bytes r*head_dim .. in element order.
+ * q8_0: the int8 codes in the order the decode's lanes read them. Rows are
+ * taken R = min(block_size, 16) at a time (u = r / R, rr = r % R); element d
+ * is code j = d % 8 of chunk w = d / 8 (P = head_dim / 8 chunks per row,
+ * NV = P / 4); with group k and quarter q of w = 4k + q:
+ *   K region: u*R*D + (k/2)*R*64 + (q*R + rr)*16 + (k%2)*8 + j
+ *   V region: u*R*D + ((rr%NV)/2)*R*64 + ((rr/NV)*P + w)*16 + (rr%2)*8 + j
+ * (one 16-byte unit holds a token's chunks of two groups in K, and one
+ * chunk of two consecutive rows in V).
  * q4_0: a word is 4 bytes holding 8 consecutive elements of a row (element j of
  * the word in byte j/2, low nibble for even j); with G = head_dim/32 groups and
  * CB = head_dim/2 code bytes per row, word w = 4k + q of row r (group k,
@@ -205,6 +212,15 @@ static size_t orc_code_row_bytes(int dtype, int head_dim) {
 static size_t orc_qtile_bytes(int dtype, int block_size, int head_dim) {
   return (size_t)block_size * orc_code_row_bytes(dtype, head_dim) +
          (size_t)block_size * (head_dim / 32) * 2;
+}
+
+static size_t orc_q8_code_offset(int is_v, int row, int d, int block_size, int head_dim) {
+  const size_t D = (size_t)head_dim, P = D / 8, NV = P / 4;
+  const size_t R = block_size < 16 ? (size_t)block_size : 16;
+  const size_t u = (size_t)row / R, rr = (size_t)row % R, w = (size_t)d / 8, j = (size_t)d % 8;
+  if (is_v) return u * R * D + ((rr % NV) / 2) * R * 64 + ((rr / NV) * P + w) * 16 + (rr % 2) * 8 + j;
+  const size_t k = w / 4, q = w % 4;
+  return u * R * D + (k / 2) * R * 64 + (q * R + rr) * 16 + (k % 2) * 8 + j;
 }
 
 static size_t orc_q4_word_offset(int is_v, int row, int word, int head_dim) {
@@ -233,7 +249,7 @@ static double orc_qload(const char* tile, int dtype, int is_v, int row, int d, i
     code = (double)((d & 1 ? b >> 4 : b & 15) - 8);
   } else {
     int8_t c;
-    memcpy(&c, tile + (size_t)row * head_dim + d, 1);
+    memcpy(&c, tile + orc_q8_code_offset(is_v, row, d, block_size, head_dim), 1);
     code = (double)c;
   }
   return orc_half_bits_to_double(h) * code;
@@ -278,7 +294,6 @@ void orc_append(int batch, int kv_heads, int head_dim, int block_size, int dtype
     if (orc_quantised(dtype)) {
       /* new rows arrive in bf16 and are quantised group by group */
       size_t tb = orc_qtile_bytes(dtype, block_size, head_dim);
-      size_t rb = orc_code_row_bytes(dtype, head_dim);
       for (int g = 0; g < kv_heads; ++g) {
         for (int is_v = 0; is_v < 2; ++is_v) {
           const void* src = is_v ? v_new : k_new;
@@ -299,7 +314,9 @@ void orc_append(int batch, int kv_heads, int head_dim, int block_size, int dtype
             } else {
               int8_t codes[32];
               orc_q8_quantize_group(x, codes, &d);
-              memcpy(tile + (size_t)row * rb + grp * 32, codes, 32);
+              for (int i = 0; i < 32; ++i)
+                memcpy(tile + orc_q8_code_offset(is_v, row, grp * 32 + i, block_size, head_dim),
+                       codes + i, 1);
             }
             memcpy(tile + orc_qscale_offset(dtype, is_v, row, grp, block_size, head_dim), &d, 2);
           }

@@ -122,17 +122,38 @@ def q4_code_index(rows, is_v, head_dim):
     return r * CB + 4 * ((w % 4) * G + w // 4) + b
 
 
+def q8_code_index(rows, is_v, head_dim, block_size=BLOCK):
+    """Tile byte offsets of each row's q8_0 codes in element order
+    ([n][head_dim]), as orc_append writes them: rows R = min(block_size, 16) at
+    a time (u = r // R, rr = r % R), element d = 8w + j in chunk w (P = D/8
+    chunks per row, NV = P/4); K: w = 4k + q at
+    u*R*D + (k//2)*R*64 + (q*R + rr)*16 + (k%2)*8 + j; V: at
+    u*R*D + ((rr%NV)//2)*R*64 + ((rr//NV)*P + w)*16 + (rr%2)*8 + j."""
+    D = head_dim
+    P, R = D // 8, min(block_size, 16)
+    NV = P // 4
+    r = np.asarray(rows, dtype=np.int64)[:, None]
+    u, rr = r // R, r % R
+    d = np.arange(D)[None, :]
+    w, j = d // 8, d % 8
+    if is_v:
+        return u * R * D + ((rr % NV) // 2) * R * 64 + ((rr // NV) * P + w) * 16 + (rr % 2) * 8 + j
+    k, q = w // 4, w % 4
+    return u * R * D + (k // 2) * R * 64 + (q * R + rr) * 16 + (k % 2) * 8 + j
+
+
 def q8_row_bytes(pool, blocks, rows, is_v, block_size=BLOCK):
     """Bytes of quantised rows (q8_0 or q4_0) as [n][Hkv][code bytes + 2 * D/32 scale
     bytes]: codes in element order, scales in group order. A tile is block_size rows
-    of codes (q4_0 words placed as q4_code_index says), then fp16 scales ordered
+    of codes (q8_0 codes placed as q8_code_index says, q4_0 words as
+    q4_code_index says), then fp16 scales ordered
     [row][group] (K region) or [group][row] (V region)."""
     cb, D = q_format(pool.shape[2], block_size)
     ng = D // 32
     rows = np.asarray(rows, dtype=np.int64)
     blocks = np.asarray(blocks, dtype=np.int64)
     if cb == D:
-        code_idx = rows[:, None] * cb + np.arange(cb)[None, :]
+        code_idx = q8_code_index(rows, is_v, D, block_size)
     else:
         code_idx = q4_code_index(rows, is_v, D)
     grp = np.arange(ng)[None, :]

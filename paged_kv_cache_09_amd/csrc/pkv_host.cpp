@@ -328,9 +328,15 @@ constexpr int64_t kSegStartCost = PKV_SEG_START_COST;
 // rows in every member (16 (j + 1) <= ctx - 1: the newest row stays private),
 // at most kMaxChunks chunks of at most kChunkTiles tiles. A run of one
 // sequence, or sharing fewer than kMinSharedTiles tiles, is not a group.
-constexpr bool kPrefixGroups = true;
+#ifndef PKV_PREFIX_GROUPS
+#define PKV_PREFIX_GROUPS 1
+#endif
+constexpr bool kPrefixGroups = PKV_PREFIX_GROUPS;
 constexpr int kMinSharedTiles = 4;
-constexpr int kPrefixChunk = 16;   // preferred tiles per work item
+#ifndef PKV_PREFIX_CHUNK
+#define PKV_PREFIX_CHUNK 16
+#endif
+constexpr int kPrefixChunk = PKV_PREFIX_CHUNK;   // preferred tiles per work item
 constexpr int kChunkTiles = 32;    // at most (the chunk's table entries fit one per lane)
 constexpr int kMaxChunks = 16;
 
@@ -483,6 +489,10 @@ void build_schedule(pkv_pool* p, int part, int target) {
     // kSegStartCost tiles on top of its tiles (q, lengths and the first block
     // id are fetched before the first tile can be requested). Cuts fall where
     // the running cost crosses multiples of total / W.
+#ifndef PKV_GROUP_TARGET
+#define PKV_GROUP_TARGET 50
+#endif
+    if (groups) target = (int)((int64_t)target * PKV_GROUP_TARGET / 100);
     const int64_t W = std::max<int64_t>(1, std::min<int64_t>(target, T));
     const int64_t total = T + kSegStartCost * (int64_t)B * H;
     ws.assign(1, 0);

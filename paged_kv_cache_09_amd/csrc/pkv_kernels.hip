@@ -34,7 +34,8 @@
 // heads share one stored K/V head (ssdnodes.com, "KV cache vs prompt cache",
 // GQA paragraph). Decode is bound by memory bandwidth (ssdnodes.com, same
 // page, "What the KV cache holds"), so every tile is read exactly once, with
-// wide lanes (16 bytes for 2- and 4-byte elements and q4_0, 8 for q8_0 codes);
+// 16-byte lanes (for q8_0 and q4_0 the tile layout puts each lane's codes in
+// one run);
 // q.K^T of the GQA group runs on 16x16 MFMA tiles, the softmax on the fp32
 // VALU, and P.V on the fp32 VALU or, where it bounds the loop (q4_0, q8_0) or
 // serves 16 rows (shared-prefix items), on MFMA with the weights in 16-bit
@@ -59,6 +60,28 @@ __device__ long long pkv_tl[8 * 8192];
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// q8_0 tile layout: the codes of a block (block_size rows of D int8 codes) are
+// stored in the order the decode's lanes read them, so that every 16-byte
+// load instruction of a wave reads 1 KiB (R = min(block size, 16) rows)
+// contiguously. Rows are taken R at a time (u = r / R, rr = r % R); with
+// P = D / 8 chunks of 8 codes per row and NV = P / 4:
+//   K: chunk w = 4k + q (group k, quarter q) of row r at
+//      u*R*D + (k/2)*R*64 + (q*R + rr)*16 + (k%2)*8
+//      (lane (token rr, quarter q) reads its groups 2c, 2c+1 as 16 bytes at
+//      c*R*64 + lane*16);
+//   V: chunk w of row r at u*R*D + ((rr%NV)/2)*R*64 + ((rr/NV)*P + w)*16 +
+//      (rr%2)*8 (lane (chunk w, rows NV*v .. NV*v+NV-1) reads two rows' chunks
+//      as 16 bytes at c*R*64 + lane*16).
+// Scales follow the codes as before: K [row][group], V [group][row].
+template <int D>
+__device__ __forceinline__ int q8_chunk_offset(bool is_v, int r, int w, int bs) {
+  constexpr int P = D / 8, NV = P / 4;
+  const int R = bs < 16 ? bs : 16, u = r / R, rr = r % R;
+  if (is_v) return u * R * D + ((rr % NV) >> 1) * R * 64 + ((rr / NV) * P + w) * 16 + (rr & 1) * 8;
+  const int k = w >> 2, q = w & 3;
+  return u * R * D + (k >> 1) * R * 64 + (q * R + rr) * 16 + (k & 1) * 8;
+}
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -99,13 +122,9 @@ __device__ __forceinline__ u32x2 nt8(const char* p) {
 __device__ __forceinline__ unsigned nt4(const char* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(p));
 }
-#ifndef PKV_NT_Q8
-#define PKV_NT_Q8 0
-#endif
 #ifndef PKV_NT_SCALES
 #define PKV_NT_SCALES 0
 #endif
-__device__ __forceinline__ u32x2 ldq8(const char* p) { return PKV_NT_Q8 ? nt8(p) : ld8(p); }
 __device__ __forceinline__ u32x2 ldsc8(const char* p) { return PKV_NT_SCALES ? nt8(p) : ld8(p); }
 __device__ __forceinline__ unsigned ldsc4(const char* p) { return PKV_NT_SCALES ? nt4(p) : ld4(p); }
 
@@ -996,12 +1015,25 @@ __global__ __launch_bounds__(BINS ? 64 * kBinWaves : 64) void decode_kernel(Deco
             }
           }
         } else {
-          const char* kt = ktile + kr * CB + kg * 8;
+          // the layout puts the lane's pieces of groups 2c, 2c+1 (and its V
+          // chunks of rows 2c, 2c+1 of its NV) as 16 bytes at c*R*64 +
+          // lane*16 of the R-row part of the block (lane index within that
+          // part): every load instruction reads R*64 contiguous bytes
+          constexpr int R = BS < 16 ? BS : 16;
+          const char* kt = ktile + (unsigned)((kr / R) * R * D + (kg * R + kr % R) * 16);
+          const char* vt = vtile + (unsigned)((vrr / R) * R * D + ((vrr % R) / NV * CPR + vc) * 16);
 #pragma unroll
-          for (int k = 0; k < NP; ++k) t.k[k] = ldq8(kt + k * 32);
-          const char* vt = vtile + vrr * CB + vc * 8;
+          for (int c = 0; c < NP / 2; ++c) {
+            const u32x4 a = nt16(kt + c * R * 64);
+            t.k[2 * c] = u32x2{a[0], a[1]};
+            t.k[2 * c + 1] = u32x2{a[2], a[3]};
+          }
 #pragma unroll
-          for (int i = 0; i < NV; ++i) t.v[i] = ldq8(vt + i * CB);
+          for (int c = 0; c < NV / 2; ++c) {
+            const u32x4 b = nt16(vt + c * R * 64);
+            t.v[2 * c] = u32x2{b[0], b[1]};
+            t.v[2 * c + 1] = u32x2{b[2], b[3]};
+          }
         }
         // scales after the BS rows of codes: K [row][group], V [group][row]
         const char* ksp = ktile + (unsigned)(BS * CB + kr * NP * 2);
@@ -1495,7 +1527,7 @@ __global__ __launch_bounds__(BINS ? 64 * kBinWaves : 64) void decode_kernel(Deco
           for (int i = 0; i < NV / 2; ++i) tn.vs[i] = 0u;
           tn.vs[0] = half_bits(d);
           if (vr == 0) {
-            *reinterpret_cast<u32x2*>(vtile + t_new * D + vc * 8) = c;
+            *reinterpret_cast<u32x2*>(vtile + q8_chunk_offset<D>(true, t_new, vc, BS)) = c;
             if ((vc & 3) == 0)
               *reinterpret_cast<unsigned short*>(vtile + BS * D + ((vc >> 2) * BS + t_new) * 2) =
                   (unsigned short)tn.vs[0];
@@ -1504,7 +1536,8 @@ __global__ __launch_bounds__(BINS ? 64 * kBinWaves : 64) void decode_kernel(Deco
         if (t16 == 0) {
 #pragma unroll
           for (int k = 0; k < NP; ++k)
-            *reinterpret_cast<u32x2*>(ktile + t_new * D + kg * 8 + k * 32) = tn.k[k];
+            *reinterpret_cast<u32x2*>(ktile + q8_chunk_offset<D>(false, t_new, 4 * k + kg, BS)) =
+                tn.k[k];
           if (kg == 0) {
             char* ksp = ktile + BS * D + t_new * NP * 2;
             if constexpr (NP == 4) *reinterpret_cast<u32x2*>(ksp) = u32x2{tn.ks[0], tn.ks[1]};
@@ -1872,14 +1905,11 @@ __global__ __launch_bounds__(256) void append_q8_kernel(const char* k_new, const
     for (int j = 0; j < 8; ++j) a = fmaxf(a, __builtin_fabsf(x[c][j]));
   }
   char* tile = (kv ? v_layer : k_layer) + ((size_t)blk * kv_heads + g) * TILE;
-  char* dst = tile + pos * D + grp * 32;
   float d = 0.f;
 #pragma unroll
-  for (int c = 0; c < 4; c += 2) {
-    const u32x2 lo = q8_codes(x[c], a, &d);
-    const u32x2 hi = q8_codes(x[c + 1], a, &d);
-    *reinterpret_cast<u32x4*>(dst + c * 8) = u32x4{lo[0], lo[1], hi[0], hi[1]};
-  }
+  for (int c = 0; c < 4; ++c)  // the group's four chunks of 8 codes
+    *reinterpret_cast<u32x2*>(tile + q8_chunk_offset<D>(kv, pos, 4 * grp + c, BS)) =
+        q8_codes(x[c], a, &d);
   const int si = kv ? grp * BS + pos : pos * NGR + grp;
   *reinterpret_cast<unsigned short*>(tile + BS * D + si * 2) = (unsigned short)half_bits(d);
 }

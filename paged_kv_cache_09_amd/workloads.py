@@ -108,6 +108,12 @@ CONFIGS = {
     "shared_prefix_cow_bf16": Config("shared_prefix_cow_bf16", 4, 128, 32, 8, 128, BF16, 1.0,
                                      8192, 8, "shared_prefix", prefix_tokens=1016,
                                      suffix_hi=0),
+    # The shared prefix with quantised caches (no grouped items: the bins form,
+    # whose XCD affinity has the prompt fetched from HBM once and re-read from L2).
+    "shared_prefix_q8": Config("shared_prefix_q8", 4, 128, 32, 8, 128, Q8_0, 1.0, 8192, 8,
+                               "shared_prefix", prefix_tokens=1024, suffix_hi=512),
+    "shared_prefix_q4": Config("shared_prefix_q4", 4, 128, 32, 8, 128, Q4_0, 1.0, 8192, 8,
+                               "shared_prefix", prefix_tokens=1024, suffix_hi=512),
     # The Llama-3.1-8B-shaped layer with a q8_0 cache (int8 codes, one fp16
     # scale per 32 elements); same lengths and placement as the bf16 one.
     "llama8b_q8": Config("llama8b_q8", 2, 64, 32, 8, 128, Q8_0, 1.0, 64 * 136, 32,

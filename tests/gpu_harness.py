@@ -189,8 +189,8 @@ def _check_untouched(w, before, slots, pairs, layers):
 
 
 def _check_untouched_q8(w, before, slots, pairs, layers):
-    """Quantised caches: byte by byte, only each new row's codes (q4_0 V rows
-    interleaved as the layout places them) and scales (K scales [row][group], V
+    """Quantised caches: byte by byte, only each new row's codes (where the tile
+    layout places them) and scales (K scales [row][group], V
     scales [group][row] after a tile's codes) and whole copy-on-write
     destination tiles may change."""
     cfg = w.cfg
@@ -207,13 +207,17 @@ def _check_untouched_q8(w, before, slots, pairs, layers):
             continue
         bs = cfg.block_size
         b, r = int(sl) // bs, int(sl) % bs
-        allowed[0, :, b, :, r * D:(r + 1) * D] = True  # K codes: within the row's bytes
-        if cfg.dtype == W.Q4_0:  # V rows interleaved: the row's words as the layout places them
+        if cfg.dtype == W.Q4_0:
+            # K words within the row's bytes; V rows interleaved as the layout places them
+            allowed[0, :, b, :, r * D:(r + 1) * D] = True
             idx = torch.from_numpy(ostep.q4_code_index([r], True, cfg.head_dim)[0]).to(
                 allowed.device)
             allowed[1, :, b, :, idx] = True
-        else:
-            allowed[1, :, b, :, r * D:(r + 1) * D] = True
+        else:  # q8_0: the row's codes where the layout places them
+            for kv in (0, 1):
+                idx = torch.from_numpy(
+                    ostep.q8_code_index([r], bool(kv), cfg.head_dim, bs)[0]).to(allowed.device)
+                allowed[kv, :, b, :, idx] = True
         for grp in range(ng):
             ik = bs * D + 2 * (r * ng + grp)
             iv = bs * D + 2 * (grp * bs + r)

@@ -134,6 +134,8 @@ FULL = [
     ("long_ctx_bf16", 1, (512, 0), None),
     ("llama8b_q8", 2, (0, 512), None),
     ("llama8b_q4", 2, (0, 512), None),
+    ("shared_prefix_q8", 1, (0,), None),
+    ("shared_prefix_q4", 1, (0,), None),
 ]
 
 

@@ -109,12 +109,37 @@ def test_q8_error_bound_random():
     assert np.array_equal(codes[:100], -oracle.q8_quantize(-x[:100])[0])
 
 
+def _lane_image_q8(codes, is_v):
+    """Code bytes of one 16-row q8_0 tile [16][D] as the decode's 64 lanes read
+    them, built lane by lane: 16-byte unit c of lane L at c*1024 + L*16.
+    K: lane L = 16*quarter + token holds its token's quarter of groups 2c and
+    2c + 1 (8 codes each); V: lane L = (D/8)*v + chunk holds that chunk of rows
+    NV*v + 2c and NV*v + 2c + 1 (NV = D/32)."""
+    R, D = codes.shape
+    P, G = D // 8, D // 32
+    out = np.zeros(R * D, dtype=np.uint8)
+    raw = codes.view(np.uint8)
+    for c in range(G // 2):
+        for lane in range(64):
+            if is_v:
+                chunk, v = lane % P, lane // P
+                rows = (G * v + 2 * c, G * v + 2 * c + 1)
+                unit = np.concatenate([raw[r, 8 * chunk:8 * chunk + 8] for r in rows])
+            else:
+                tok, quarter = lane % 16, lane // 16
+                unit = np.concatenate([raw[tok, 32 * k + 8 * quarter:32 * k + 8 * quarter + 8]
+                                       for k in (2 * c, 2 * c + 1)])
+            out[c * 1024 + lane * 16:c * 1024 + lane * 16 + 16] = unit
+    return out
+
+
 def _pack_q8(codes, scales, is_v):
     """One tile [Hkv] of q8_0 bytes from codes [Hkv][16][D] and fp16 scales
-    [Hkv][16][D/32], in the documented order (K: [row][group], V: [group][row])."""
+    [Hkv][16][D/32], in the documented order (codes as the decode's lanes read
+    them; scales K: [row][group], V: [group][row])."""
     H, R, D = codes.shape
     sc = scales if not is_v else scales.transpose(0, 2, 1)
-    return np.concatenate([codes.view(np.uint8).reshape(H, R * D),
+    return np.concatenate([np.stack([_lane_image_q8(codes[h], is_v) for h in range(H)]),
                            np.ascontiguousarray(sc).view(np.uint8).reshape(H, -1)], axis=1)
 
 
@@ -171,10 +196,15 @@ def test_q8_append_writes_quantised_row_in_layout():
     # nothing else changed: 2 rows x (D codes + 8 scale bytes) per head
     changed = (kp != k0).sum() + (vp != v0).sum()
     assert changed <= 2 * 2 * Hkv * (D + 8)
-    mask = np.zeros_like(kp, dtype=bool)
-    for blk, row in [(1, 4), (4, 8)]:
-        mask[blk, :, row * D:(row + 1) * D] = True
-        for grp in range(D // 32):
-            i = 16 * D + 2 * (row * (D // 32) + grp)
-            mask[blk, :, i:i + 2] = True
-    assert np.array_equal(kp[~mask], k0[~mask])
+    for is_v, (pool, before) in enumerate([(kp, k0), (vp, v0)]):
+        mask = np.zeros_like(pool, dtype=bool)
+        for blk, row in [(1, 4), (4, 8)]:
+            # the row's codes, placed as the lanes read them (built independently)
+            image = _lane_image_q8(np.full((16, D), 0, dtype=np.int8), bool(is_v))
+            marker = np.zeros((16, D), dtype=np.int8)
+            marker[row] = 1
+            mask[blk, :, :16 * D] |= (_lane_image_q8(marker, bool(is_v)) != image)[None, :]
+            for grp in range(D // 32):
+                i = 16 * D + 2 * (grp * 16 + row if is_v else row * (D // 32) + grp)
+                mask[blk, :, i:i + 2] = True
+        assert np.array_equal(pool[~mask], before[~mask])
