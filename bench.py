@@ -350,10 +350,14 @@ def main():
     torch.cuda.synchronize()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     evs[0].record(stream)
+    t_issue = time.perf_counter()
     for r in range(reps):
         for layer in layers:  # re-appending the same rows is idempotent
             layer_call(layer)
         evs[r + 1].record(stream)
+    # host time to issue one call: while it stays below the launch time the
+    # GPU never waits for the host and the events time the kernels alone
+    issue_s = (time.perf_counter() - t_issue) / (reps * len(layers))
     torch.cuda.synchronize()
     per_rep = np.array([evs[r].elapsed_time(evs[r + 1]) / 1e3 / len(layers)
                         for r in range(reps)])
@@ -416,6 +420,7 @@ def main():
             "kernel": "per-layer call: decode_kernel (fused append + paged attention) and, for "
                       "split segments, reduce_kernel; timed together",
             "avg_launch_us": round(per_launch_s * 1e6, 3),
+            "host_issue_us_per_call": round(issue_s * 1e6, 3),
             "launch_us_p10_p50_p90": [round(p10 * 1e6, 3), round(p50 * 1e6, 3),
                                       round(p90 * 1e6, 3)],
             "timed_launches": reps * len(layers),

@@ -1871,6 +1871,28 @@ __global__ __launch_bounds__(256) void append_kernel(const char* k_new, const ch
   *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
 }
 
+// Thread of the quantised appends -> (32-value group, K or V, kv head, row of
+// the batch): the group fastest, then 16 consecutive rows, then K/V and the
+// head. The tile layouts spread one row's codes over several lines that
+// neighbouring rows fill too, so a wave writing 16 consecutive rows of a
+// multi-token write covers whole lines instead of pieces of them.
+struct QuantAppendItem {
+  int grp, kv, g;
+  long s;
+};
+__device__ __forceinline__ QuantAppendItem quant_append_item(long idx, int ngr, int kv_heads) {
+  QuantAppendItem it;
+  it.grp = (int)(idx % ngr);
+  long t = idx / ngr;
+  const int rr = (int)(t & 15);
+  t >>= 4;
+  it.kv = (int)(t & 1);
+  t >>= 1;
+  it.g = (int)(t % kv_heads);
+  it.s = (t / kv_heads) * 16 + rr;
+  return it;
+}
+
 // q8_0 append: one thread per (sequence, kv head, K|V, 32-value group) of
 // the bf16 new rows; writes 32 codes into the row and the group's fp16 scale
 // (K scales [row][group], V scales [group][row] after the tile's codes).
@@ -1883,13 +1905,9 @@ __global__ __launch_bounds__(256) void append_q8_kernel(const char* k_new, const
   constexpr int NGR = D / 32;
   const int BS = block_size;
   const int TILE = BS * D + BS * NGR * 2;
-  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-  const int grp = (int)(idx % NGR);
-  long r = idx / NGR;
-  const int kv = (int)(r & 1);
-  r >>= 1;
-  const int g = (int)(r % kv_heads);
-  const long s = r / kv_heads;
+  const QuantAppendItem it = quant_append_item((long)blockIdx.x * 256 + threadIdx.x, NGR, kv_heads);
+  const int grp = it.grp, kv = it.kv, g = it.g;
+  const long s = it.s;
   if (s >= batch) return;
   const int64_t slot = slots[s];
   if (slot < 0 || slot >= num_slots) return;
@@ -1926,13 +1944,9 @@ __global__ __launch_bounds__(256) void append_q4_kernel(const char* k_new, const
   constexpr int CB = D / 2;
   const int BS = block_size;
   const int TILE = BS * CB + BS * NGR * 2;
-  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-  const int grp = (int)(idx % NGR);
-  long r = idx / NGR;
-  const int kv = (int)(r & 1);
-  r >>= 1;
-  const int g = (int)(r % kv_heads);
-  const long s = r / kv_heads;
+  const QuantAppendItem it = quant_append_item((long)blockIdx.x * 256 + threadIdx.x, NGR, kv_heads);
+  const int grp = it.grp, kv = it.kv, g = it.g;
+  const long s = it.s;
   if (s >= batch) return;
   const int64_t slot = slots[s];
   if (slot < 0 || slot >= num_slots) return;
@@ -2104,7 +2118,8 @@ hipError_t launch_append_quant(int dtype, const void* k_new, const void* v_new,
                                const int64_t* slots, int batch, void* k_layer, void* v_layer,
                                int kv_heads, int head_dim, int block_size, int64_t num_slots,
                                hipStream_t stream) {
-  const long threads = (long)batch * kv_heads * 2 * (head_dim / 32);
+  // rows in groups of 16 (quant_append_item); the padding rows' threads return
+  const long threads = (long)((batch + 15) / 16) * 16 * kv_heads * 2 * (head_dim / 32);
   const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
   const char* kn = static_cast<const char*>(k_new);
   const char* vn = static_cast<const char*>(v_new);
