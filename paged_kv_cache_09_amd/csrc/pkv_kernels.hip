@@ -466,6 +466,12 @@ struct PvMode {
 // Orders this wavefront's LDS writes before its later LDS reads by other
 // lanes (a wave's LDS operations complete in order; this keeps the compiler
 // from moving them). Only this wave takes part.
+// true when pred holds in any active lane: the ballot's mask compared in
+// scalar registers (no vector instructions, unlike a vote through a lane)
+__device__ __forceinline__ bool wave_any(bool pred) {
+  return __builtin_amdgcn_ballot_w64(pred) != 0;
+}
+
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -663,7 +669,7 @@ __device__ __forceinline__ void prefix_item(const DecodeParams& p, int item) {
       s2[i] = sacc[i] * p.scale_log2;  // the shared tiles are full
       over |= s2[i] > m[i] + kLazy;
     }
-    if (__any(over)) {
+    if (wave_any(over)) {
       // the rows of lane's scores are the rows of its output blocks
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -891,6 +897,7 @@ __global__ __launch_bounds__(BINS ? 64 * kBinWaves : 64) void decode_kernel(Deco
   const int t16 = lane & 15;  // K row (token) this lane feeds; q row (head) likewise
   const int kg = lane >> 4;   // which 16-byte piece of each 64 bytes
   const bool head_lane = kg < NG;  // this lane's score rows are real heads
+  const uint64_t head_mask = __builtin_amdgcn_ballot_w64(head_lane);
   const int vc = lane % CPR;  // V chunk this lane owns
   const int vr = lane / CPR;  // V row group of this lane
   // V row held in the lane's i-th chunk
@@ -1231,7 +1238,6 @@ __global__ __launch_bounds__(BINS ? 64 * kBinWaves : 64) void decode_kernel(Deco
       }
       // sacc[i] = q(head 4*kg + i) . K(token t16)
       float s2[HPG];
-      bool over = false;
       // MFMA P.V takes weight x scale as fp16: weights stay <= 2^kLazy, and a
       // tile with a V scale above 2^8 - 1 raises the maxima on any increase
       // (weights <= 1), so the products stay finite.
@@ -1242,33 +1248,34 @@ __global__ __launch_bounds__(BINS ? 64 * kBinWaves : 64) void decode_kernel(Deco
         // context may hold anything: that only costs a rescale)
         const unsigned a0 = t.vs[0] & 0x7fff7fffu, a1 = t.vs[1] & 0x7fff7fffu;
         const unsigned mx = max(max(a0 & 0xffffu, a0 >> 16), max(a1 & 0xffffu, a1 >> 16));
-        big = __any(mx > 0x5bf8u);
+        big = wave_any(mx > 0x5bf8u);
       }
+      // rows past the context (only a partial tile has them: in a full one
+      // valid = 16) score -inf; a select, as such rows may hold anything
+      const bool dead = t16 >= valid;
 #pragma unroll
-      for (int i = 0; i < HPG; ++i) {
-        s2[i] = sacc[i] * smul[i];
-      }
-      if (part) {
+      for (int i = 0; i < HPG; ++i) s2[i] = dead ? -__builtin_inff() : sacc[i] * smul[i];
+      // lanes with a score above its threshold, as wave masks (the compares'
+      // own scalar results, OR-ed in scalar registers)
+      uint64_t over = 0;
 #pragma unroll
-        for (int i = 0; i < HPG; ++i)
-          if (t16 >= valid) s2[i] = -__builtin_inff();
-      }
-#pragma unroll
-      for (int i = 0; i < HPG; ++i) over |= head_lane && s2[i] > mlz[i];
+      for (int i = 0; i < HPG; ++i) over |= __builtin_amdgcn_ballot_w64(s2[i] > mlz[i]);
       if (big) {  // any increase
-        over = false;
+        over = 0;
 #pragma unroll
-        for (int i = 0; i < HPG; ++i) over |= head_lane && s2[i] > m[i];
+        for (int i = 0; i < HPG; ++i) over |= __builtin_amdgcn_ballot_w64(s2[i] > m[i]);
       }
-      if (__any(over)) {  // raise the running maxima to this tile's
+      if (over & head_mask) {  // raise the running maxima to this tile's
         float alpha[HPG];
 #pragma unroll
         for (int i = 0; i < HPG; ++i) {
-          const float mn = fmaxf(m[i], row_max(s2[i]));
-          alpha[i] = __builtin_amdgcn_exp2f(m[i] - mn);
+          // m - max(m, r) is min(m - r, 0) bit for bit; written so, the new
+          // maximum replaces the old one in its register
+          const float r = row_max(s2[i]);
+          alpha[i] = __builtin_amdgcn_exp2f(fminf(m[i] - r, 0.f));
+          m[i] = fmaxf(m[i], r);
           lsum[i] *= alpha[i];
-          m[i] = mn;
-          mlz[i] = mn + kLazy;
+          mlz[i] = m[i] + kLazy;
         }
         if (head_lane && t16 == 0) {
 #pragma unroll
