@@ -167,13 +167,13 @@ int pkv_block_refcount(const pkv_pool* pool, int32_t id);
  * memory from the OS"). host_bt is the caller's block table,
  * int32 [batch][max_blocks] row-major, -1 for absent entries; ctx_lens[s] is
  * the context length with the new token included (>= 1). For each sequence in
- * batch order, with p = ctx_lens[s] - 1 and j = p / 16:
+ * batch order, with p = ctx_lens[s] - 1 and j = p / block_size:
  *   - host_bt[s][j] == -1: a free block is taken and written there;
  *   - host_bt[s][j] shared (refcount > 1): copy-on-write — a free block is
  *     taken, the pair (old, new) is appended to cow_pairs_out, the old block
  *     loses one reference and host_bt[s][j] becomes the new block;
  *   - otherwise the block is written in place.
- * slot_out[s] = host_bt[s][j] * 16 + p % 16 (int64).
+ * slot_out[s] = host_bt[s][j] * block_size + p % block_size (int64).
  * cow_pairs_out receives n_cow (old, new) int32 pairs; cow_capacity is its
  * capacity in pairs (batch always suffices). Every check and the count of
  * blocks the call needs come before any change, so a failing call (including
@@ -217,8 +217,8 @@ int pkv_prepare_write(pkv_pool* pool, int32_t* host_bt, int batch, int max_block
  * reused once the copy that last read it has finished) and copied by a small
  * kernel on `stream`, together with the decode schedule for the partition
  * setting and group of the previous decode call. Checked on the host first: 1 <= batch <= max_seqs,
- * max_blocks * 16 <= the pool's table width, 1 <= ctx <= max_seq_len, every
- * entry j < ceil(ctx/16) in [0, num_blocks); a non-negative slot must be the
+ * max_blocks * block_size <= the pool's table width, 1 <= ctx <= max_seq_len, every
+ * entry j < ceil(ctx / block_size) in [0, num_blocks); a non-negative slot must be the
  * table position of the sequence's new token (row ctx-1), as
  * pkv_prepare_append produces; negative slots skip the append.
  * Later kv_append / decode calls use this upload.
