@@ -177,31 +177,15 @@ __device__ __forceinline__ u32x4 codes_to_f16_128(u32x2 c) {
   return r;
 }
 
-// 8 packed 4-bit codes (code j in bits 4j .. 4j+3) -> the 8 values 128 + code
-// as bf16 (exact: bf16 0x4300 is 128 and its low mantissa bits count units), an
-// MFMA operand, in the slot order codes 0 2 4 6 1 3 5 7 (each pair from one
-// word, its exponent bytes from a constant: one permute per pair); the q
-// operand is put in the same order (q_slots_0246). The 136 that separates
-// 128 + code from code - 8 is taken off through the MFMA's accumulator input.
-__device__ __forceinline__ u32x4 nibbles_to_bf16_128(unsigned w) {
-  const unsigned lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;  // even, odd codes
-  constexpr unsigned kExp = 0x43434343u;
-  u32x4 r;
-  r[0] = __builtin_amdgcn_perm(kExp, lo, 0x04010400u);  // (lo.b0, 0x43, lo.b1, 0x43)
-  r[1] = __builtin_amdgcn_perm(kExp, lo, 0x04030402u);
-  r[2] = __builtin_amdgcn_perm(kExp, hi, 0x04010400u);
-  r[3] = __builtin_amdgcn_perm(kExp, hi, 0x04030402u);
-  return r;
-}
-
-// 8 bf16 values in natural order -> slot order 0 2 4 6 1 3 5 7.
-__device__ __forceinline__ u32x4 q_slots_0246(u32x4 q) {
-  u32x4 r;
-  r[0] = __builtin_amdgcn_perm(q[1], q[0], 0x05040100u);  // elements 0, 2
-  r[1] = __builtin_amdgcn_perm(q[3], q[2], 0x05040100u);  // 4, 6
-  r[2] = __builtin_amdgcn_perm(q[1], q[0], 0x07060302u);  // 1, 3
-  r[3] = __builtin_amdgcn_perm(q[3], q[2], 0x07060302u);  // 5, 7
-  return r;
+// 8 packed 4-bit codes (code j in bits 4j .. 4j+3) -> an fp16 MFMA operand
+// of subnormals, in the slot order 0 4 1 5 2 6 3 7: codes 0, 4, 2, 6 as c x
+// 2^-24 and codes 1, 5, 3, 7 as 16c x 2^-24 (exact: fp16 bits below 0x400
+// count units of the smallest subnormal, and the MFMA keeps them), each
+// dword one mask of the word or of the word shifted by 8. The q operand is
+// put in the same order, its odd elements divided by 16.
+__device__ __forceinline__ u32x4 nibbles_to_f16(unsigned w) {
+  const unsigned w8 = w >> 8;
+  return u32x4{w & 0x000f000fu, w & 0x00f000f0u, w8 & 0x000f000fu, w8 & 0x00f000f0u};
 }
 
 // Code values in fp32: 8 int8 codes (q8_0), or 8 packed 4-bit codes 0..15
@@ -574,7 +558,7 @@ struct TileRegs<DT_Q4, D> {
 // tables name the same blocks for their first full tiles (a common prompt,
 // shared through the block table as the pages describe) reads those tiles
 // once. One wave per (group, kv head, chunk of the shared tiles): the MFMA's
-// 16 rows hold member x head (4 x 4 for 4 q heads per kv head, 8 x 2, 16 x 1)
+// 16 rows hold member x head (2 x 8 for 8 q heads per kv head, 4 x 4, 8 x 2, 16 x 1)
 // in q.K^T and in P.V, so one tile read serves every member. Each (member,
 // head) leaves an unnormalised partial (max, sum, output) in the slot just
 // before its own private run's partials, where the reduce merges it. 2-byte
@@ -839,7 +823,7 @@ __global__ __launch_bounds__(BINS ? 64 * kBinWaves : 64) void decode_kernel(Deco
   __shared__ float piece_ml[BINS ? NSLOT * GP * 2 : 1];
 
   // the first nprefix workgroups (split form) take the shared-prefix items
-  constexpr bool PFX = !BINS && D == 128 && (DT == DT_F16 || DT == DT_BF16) && GP <= 4;
+  constexpr bool PFX = !BINS && D == 128 && (DT == DT_F16 || DT == DT_BF16);
   if constexpr (PFX) {
     if ((int)blockIdx.x < p.nprefix) {
       if ((int)blockIdx.x < p.nitems) prefix_item<DT, GP, BS>(p, blockIdx.x);
@@ -1083,12 +1067,12 @@ __global__ __launch_bounds__(BINS ? 64 * kBinWaves : 64) void decode_kernel(Deco
     // requested, so that its wait does not hold back that request.
     u32x4 qv[NP];
     // smul[i]: log2(e) x scale, times what turns score row i's MFMA result
-    // into q . K (q8_0: the head's 2^(24 - qsh)).
+    // into q . K (q8_0 and q4_0: the head's 2^(24 - qsh)).
     float smul[HPG];
-    // q4_0: -136 times each q piece's sum over its group (an MFMA against
-    // ones), the accumulator input that turns q . (128 + code) into
-    // q . (code - 8); q8_0: -128 x 2^-24 times it, for q . (128 + code) x
-    // 2^-24 into q . code x 2^-24.
+    // The accumulator input of each piece's MFMA, from the scaled q piece's
+    // sum over its group (an MFMA against ones): q4_0 -8 x 2^-24 times it,
+    // turning q . code x 2^-24 into q . (code - 8) x 2^-24; q8_0 -128 x 2^-24
+    // times it, for q . (128 + code) x 2^-24 into q . code x 2^-24.
     f32x4 qb[QN ? NP : 1];
     auto setup_q = [&]() {
     {
@@ -1096,14 +1080,39 @@ __global__ __launch_bounds__(BINS ? 64 * kBinWaves : 64) void decode_kernel(Deco
       const char* qr = reinterpret_cast<const char*>(p.q) +
                        ((size_t)s * p.q_heads + (size_t)g * p.group + hq) * QB + kg * 16;
 #pragma unroll
-      for (int k = 0; k < NP; ++k) {
-        u32x4 v = ld16(qr + k * 64);
-        if constexpr (Q4) v = q_slots_0246(v);  // the K operand's slot order
-        qv[k] = v;
-      }
+      for (int k = 0; k < NP; ++k) qv[k] = ld16(qr + k * 64);
     }
 #pragma unroll
     for (int i = 0; i < HPG; ++i) smul[i] = p.scale_log2;
+    if constexpr (Q4) {
+      // q as fp16 in nibbles_to_f16's slot order (odd elements divided by
+      // 16), each head scaled by the power of two 2^qsh that puts its
+      // largest |q| in [2^14, 2^15): bf16's 8 significant bits are kept and
+      // the products with the codes' 16c x 2^-24 stay far inside fp32.
+      float qf[NP][8];
+      float mx = 0.f;
+#pragma unroll
+      for (int k = 0; k < NP; ++k) {
+        to_f32<DT_BF16>(qv[k], qf[k]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, __builtin_fabsf(qf[k][e]));
+      }
+      mx = fmaxf(mx, xor_f(mx, 16));
+      mx = fmaxf(mx, xor_f(mx, 32));
+      const int qsh = min(100, max(-100, 15 - __builtin_amdgcn_frexp_expf(mx)));
+      const float f = __builtin_amdgcn_ldexpf(1.f, qsh), f16th = f * 0.0625f;
+#pragma unroll
+      for (int k = 0; k < NP; ++k) {
+        const float* x = qf[k];
+        qv[k][0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(x[0] * f, x[4] * f));
+        qv[k][1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(x[1] * f16th, x[5] * f16th));
+        qv[k][2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(x[2] * f, x[6] * f));
+        qv[k][3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(x[3] * f16th, x[7] * f16th));
+      }
+#pragma unroll
+      for (int i = 0; i < HPG; ++i)
+        smul[i] = p.scale_log2 * __builtin_amdgcn_ldexpf(1.f, 24 - __shfl(qsh, 4 * kg + i, 64));
+    }
     if constexpr (Q8M) {
       // q as fp16 for the MFMA against fp16 codes, each head scaled by 2^qsh
       // so that its largest |q| lies in [2^14, 2^15): no overflow, and bf16's
@@ -1134,12 +1143,14 @@ __global__ __launch_bounds__(BINS ? 64 * kBinWaves : 64) void decode_kernel(Deco
         smul[i] = p.scale_log2 * __builtin_amdgcn_ldexpf(1.f, 24 - __shfl(qsh, 4 * kg + i, 64));
     }
     if constexpr (Q4) {
-      const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+      // each head's scaled q piece summed (the slots' 1 or 16 undo the
+      // division), times -8 x 2^-24: q . c x 2^-24 becomes q . (c - 8) x 2^-24
+      const u32x4 ones = {0x3c003c00u, 0x4c004c00u, 0x3c003c00u, 0x4c004c00u};
 #pragma unroll
       for (int k = 0; k < NP; ++k) {
-        const f32x4 sq = qk_piece<DT_BF16>(qv[k], ones, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 sq = qk_piece<DT_F16>(qv[k], ones, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qb[k][i] = -136.f * sq[i];
+        for (int i = 0; i < 4; ++i) qb[k][i] = -0x1p-21f * sq[i];
       }
     } else if constexpr (Q8M) {
       const u32x4 ones = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};
@@ -1225,7 +1236,7 @@ __global__ __launch_bounds__(BINS ? 64 * kBinWaves : 64) void decode_kernel(Deco
 #pragma unroll
         for (int k = 0; k < NP; ++k) {
           f32x4 r;
-          if constexpr (Q4) r = qk_piece<DT_BF16>(qv[k], nibbles_to_bf16_128(t.k[k]), qb[k]);
+          if constexpr (Q4) r = qk_piece<DT_F16>(qv[k], nibbles_to_f16(t.k[k]), qb[k]);
           else if constexpr (Q8M) r = qk_piece<DT_F16>(qv[k], codes_to_f16_128(t.k[k]), qb[k]);
           else r = qk_piece<DT_BF16>(qv[k], codes_to_bf16(t.k[k]), f32x4{0.f, 0.f, 0.f, 0.f});
           const float dk = (k & 1) ? half_hi(t.ks[k >> 1]) : half_lo(t.ks[k >> 1]);
@@ -2106,7 +2117,8 @@ hipError_t launch_reduce(int head_dim, int gp, const ReduceParams& p, hipStream_
 }
 
 bool prefix_supported(int dtype, int head_dim, int gp) {
-  return (dtype == DT_F16 || dtype == DT_BF16) && head_dim == 128 && (gp == 1 || gp == 2 || gp == 4);
+  return (dtype == DT_F16 || dtype == DT_BF16) && head_dim == 128 &&
+         (gp == 1 || gp == 2 || gp == 4 || gp == 8);
 }
 
 hipError_t launch_append(const void* k_new, const void* v_new, const int64_t* slots, int batch,

@@ -23,7 +23,7 @@ hipError_t scratch_address(int, void**) { return hipErrorInvalidDevice; }
 hipError_t launch_probe_stream(const void*, int64_t, int, unsigned*, hipStream_t) { return hipSuccess; }
 hipError_t launch_probe_gather(const GatherParams&, hipStream_t) { return hipSuccess; }
 bool prefix_supported(int dtype, int head_dim, int gp) {
-  return (dtype == PKV_F16 || dtype == PKV_BF16) && head_dim == 128 && gp <= 4;
+  return (dtype == PKV_F16 || dtype == PKV_BF16) && head_dim == 128 && gp <= 8;
 }
 
 }
@@ -358,6 +358,7 @@ int main() {
     rc |= check_groups(t, c, 8, 16, 4, 0, 2048, 32);
     rc |= check_groups(t, c, 8, 16, 4, 512, 0, 32);
     rc |= check_groups(t, c, 8, 16, 1, 0, 2048, 8);   // 16 members per group
+    rc |= check_groups(t, c, 8, 16, 8, 0, 2048, 64);  // GQA 8: 2 members per group
     // three prompts interleaved, blocks of 8 and 32, GQA 2
     for (int bs : {8, 32}) {
       shared_tables(rng, 40, bs, 512, 1, 700, t, c, 3);
@@ -373,7 +374,7 @@ int main() {
       const int bs = trial % 3 == 0 ? 8 : trial % 3 == 1 ? 16 : 32;
       const int B = nb(rng), prompts = pr(rng), H = hb(rng);
       shared_tables(rng, B, bs, sh(rng) * 32, 1, 900, t, c, prompts);
-      const int gp = trial % 2 ? 4 : 2;
+      const int gp = trial % 3 == 0 ? 8 : trial % 2 ? 4 : 2;
       // expected group count is not fixed here: -1 skips that comparison
       rc |= check_groups(t, c, H, bs, gp, trial % 4 == 0 ? 512 : 0, 64 + trial * 7, -1);
     }
