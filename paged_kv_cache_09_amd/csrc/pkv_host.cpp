@@ -612,10 +612,10 @@ using pkv::kBinWaves;
 #define PKV_RUN_COSTS_2B 8, 4, 0
 #endif
 #ifndef PKV_RUN_COSTS_Q8
-#define PKV_RUN_COSTS_Q8 24, 8, 1
+#define PKV_RUN_COSTS_Q8 30, 8, 1
 #endif
 #ifndef PKV_RUN_COSTS_Q4
-#define PKV_RUN_COSTS_Q4 40, 8, 2
+#define PKV_RUN_COSTS_Q4 30, 8, 2
 #endif
 struct RunCosts {
   double skew, sw, app;
