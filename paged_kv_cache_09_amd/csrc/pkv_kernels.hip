@@ -877,6 +877,10 @@ __global__ __launch_bounds__(BINS ? 64 * kBinWaves : 64) void decode_kernel(Deco
     blk_second = 16 * j0 + 8 < L ? p.bt[(size_t)s * p.bt_stride + 2 * j0 + 1] : blk_first;
   const int s_first = s, g_first = g;
   bool first_seg = true;
+#ifdef PKV_TIMELINE
+  // when the descriptor has arrived (the branch waits for it)
+  const long long tl_td = uni(xend) < 0 ? 1 : __builtin_amdgcn_s_memrealtime();
+#endif
 
   const int t16 = lane & 15;  // K row (token) this lane feeds; q row (head) likewise
   const int kg = lane >> 4;   // which 16-byte piece of each 64 bytes
@@ -1830,7 +1834,7 @@ __global__ __launch_bounds__(BINS ? 64 * kBinWaves : 64) void decode_kernel(Deco
   if (active && lane == 0 && w < 8192) {
     long long* r = pkv_tl + 8 * w;
     r[6] = tl_tb;
-    r[7] = 0;
+    r[7] = tl_td;
     r[0] = tl_t0;
     r[1] = tl_t1;
     r[2] = tl_t2;

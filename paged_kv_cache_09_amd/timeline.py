@@ -1,7 +1,8 @@
 """Per-wave timeline of one decode launch (diagnostics).
 
 Needs the timeline build of the library, whose decode kernel records per
-wave its start, first tile, end of its runs and end of its merges
+wave its start, the arrival of its descriptor, first tile, end of its runs
+and end of its merges
 (s_memrealtime, 100 MHz), its XCD, tiles and segments:
 
     python -m paged_kv_cache_09_amd.build --timeline
@@ -48,6 +49,7 @@ def summarise(r: np.ndarray, nw: int = 8) -> dict:
     t0 = r[:, 0].min()
     us = lambda col: (r[:, col] - t0) / 100.0  # noqa: E731
     start, first, end, merged, barrier = us(0), (r[:, 1] - r[:, 0]) / 100.0, us(2), us(3), us(6)
+    desc = (r[:, 7] - r[:, 0]) / 100.0
     xcd = r[:, 4] & 0xF
     tiles = (r[:, 4] >> 8) & 0xFFFF
     segs = (r[:, 4] >> 24) & 0xFF
@@ -57,6 +59,7 @@ def summarise(r: np.ndarray, nw: int = 8) -> dict:
     out = {
         "waves": int(len(r)),
         "start_us": {"p50": q(start, 50), "max": q(start, 100)},
+        "descriptor_after_start_us": {"p10": q(desc, 10), "p50": q(desc, 50), "p90": q(desc, 90)},
         "first_tile_after_start_us": {"p10": q(first, 10), "p50": q(first, 50), "p90": q(first, 90)},
         "runs_end_us": {"min": q(end, 0), "p10": q(end, 10), "p50": q(end, 50), "p90": q(end, 90),
                         "max": q(end, 100)},
