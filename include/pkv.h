@@ -38,10 +38,15 @@
  * prompt cache", "Four ways to make the KV cache smaller", item 2) names as
  * halving an f16 cache, in llama.cpp's Q8_0 block format: every 32
  * consecutive head_dim elements of a row are one fp16 scale d and 32 int8
- * codes c, value d * c. A tile is block_size * head_dim int8 codes (row-major)
- * followed by block_size * head_dim/32 fp16 scales, ordered [row][group] in
- * the K region and [group][row] in the V region (2176 bytes for head_dim
- * 128). q, k_new and v_new are bf16 for a q8_0 cache; appends quantise each
+ * codes c, value d * c. A tile is block_size * head_dim int8 codes followed
+ * by block_size * head_dim/32 fp16 scales, ordered [row][group] in the K
+ * region and [group][row] in the V region (2176 bytes for head_dim 128). The
+ * codes are placed so that every 16-byte load of the decode kernel reads a
+ * contiguous run: rows are taken R = min(block_size, 16) at a time (u = r/R,
+ * rr = r%R), and with P = head_dim/8 chunks of 8 codes per row and NV = P/4,
+ * chunk w = 4k + q (codes 8w .. 8w+7) of row r starts at byte
+ *   K: u*R*head_dim + (k/2)*R*64 + (q*R + rr)*16 + (k%2)*8,
+ *   V: u*R*head_dim + ((rr%NV)/2)*R*64 + ((rr/NV)*P + w)*16 + (rr%2)*8. q, k_new and v_new are bf16 for a q8_0 cache; appends quantise each
  * group with d = max|x| / 127 and c = round(x * (1/d)) (halves away from
  * zero, fp32 arithmetic, d stored rounded to fp16).
  *
