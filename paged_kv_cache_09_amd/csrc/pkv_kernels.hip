@@ -421,18 +421,6 @@ __device__ __forceinline__ float row_max(float v) {
   v = fmaxf(v, row_ror<0x122>(v));  // row_ror:2
   return fmaxf(v, row_ror<0x121>(v));  // row_ror:1
 }
-// All-reductions over each group of 8 lanes (DPP within each quad, then
-// across the two quads of the 8 lanes).
-__device__ __forceinline__ float oct_max(float x) {
-  x = fmaxf(x, row_ror<0xB1>(x));      // quad_perm [1,0,3,2]
-  x = fmaxf(x, row_ror<0x4E>(x));      // quad_perm [2,3,0,1]
-  return fmaxf(x, row_ror<0x141>(x));  // row_half_mirror
-}
-__device__ __forceinline__ float oct_sum(float x) {
-  x += row_ror<0xB1>(x);
-  x += row_ror<0x4E>(x);
-  return x + row_ror<0x141>(x);
-}
 __device__ __forceinline__ float row_sum(float v) {
   v += row_ror<0x128>(v);
   v += row_ror<0x124>(v);
@@ -816,9 +804,8 @@ __global__ __launch_bounds__(BINS ? 64 * kBinWaves : 64) void decode_kernel(Deco
   __shared__ float m_lds_all[NW][GP];          // per-head maxima at the end of a run
   // BINS: pieces (o, m, l) of segments split between this workgroup's waves,
   // in the slots the host gives (a split segment's n pieces in n consecutive
-  // slots; at most two pieces per wave), plus NW - 1 spare slots that merges
-  // read past a segment's last piece without a bounds check
-  constexpr int NSLOT = NW * 2 + NW - 1;
+  // slots; at most two pieces per wave)
+  constexpr int NSLOT = NW * 2;
   __shared__ float piece_o[BINS ? NSLOT * GP * D : 1];
   __shared__ float piece_ml[BINS ? NSLOT * GP * 2 : 1];
 
@@ -1778,39 +1765,40 @@ __global__ __launch_bounds__(BINS ? 64 * kBinWaves : 64) void decode_kernel(Deco
     tl_tb = __builtin_amdgcn_s_memrealtime();
 #endif
     // Head hh of a segment whose n pieces are in slots base .. base+n-1. All
-    // LDS reads are issued before the arithmetic: lane k < n of each 8 reads
-    // piece k's max and sum, and every lane its D/64 columns of every piece
-    // (slots past the last piece are spare ones).
+    // LDS reads are issued before the arithmetic: every lane reads each
+    // piece's max and sum (the same words in every lane) and its D/64 columns
+    // of every piece, and weighs the pieces itself (no cross-lane steps).
     auto merge_head = [&](int ms, int mg, int base, int n, int hh) {
       constexpr int PER = D / 64;
-      const int k8 = lane & 7;
-      const bool real = k8 < n;
-      const float* mlp = piece_ml + ((base + k8) * GP + hh) * 2;
-      float mm = real ? mlp[0] : -__builtin_inff();
-      float ll = real ? mlp[1] : 0.f;
+      float mm[NW], ll[NW], src[NW][PER];
+      const float* mlp = piece_ml + (base * GP + hh) * 2;
       const float* op = piece_o + (size_t)(base * GP + hh) * D + lane * PER;
-      float src[NW][PER];
 #pragma unroll
-      for (int k = 0; k < NW; ++k)
+      for (int k = 0; k < NW; ++k) {
+        if (k < n) {
+          mm[k] = mlp[k * GP * 2];
+          ll[k] = mlp[k * GP * 2 + 1];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) src[k][e] = op[(size_t)k * GP * D + e];
-      const float M = oct_max(mm);
-      const float wgt = real ? __builtin_amdgcn_exp2f(mm - M) : 0.f;
-      const float den = oct_sum(wgt * ll);
-      float o[PER];
+          for (int e = 0; e < PER; ++e) src[k][e] = op[(size_t)k * GP * D + e];
+        }
+      }
+      float M = mm[0];
+#pragma unroll
+      for (int k = 1; k < NW; ++k)
+        if (k < n) M = fmaxf(M, mm[k]);
+      float den = 0.f, o[PER];
 #pragma unroll
       for (int e = 0; e < PER; ++e) o[e] = 0.f;
 #pragma unroll
       for (int k = 0; k < NW; ++k) {
         if (k < n) {
-          const float wv =
-              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgt), k));
+          const float wv = __builtin_amdgcn_exp2f(mm[k] - M);
+          den = __builtin_fmaf(wv, ll[k], den);
 #pragma unroll
           for (int e = 0; e < PER; ++e) o[e] = __builtin_fmaf(wv, src[k][e], o[e]);
         }
       }
-      const float inv = __builtin_amdgcn_rcpf(
-          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, den), 0)));
+      const float inv = __builtin_amdgcn_rcpf(den);
       float* dst =
           p.out + ((size_t)ms * p.q_heads + (size_t)mg * p.group + hh) * D + lane * PER;
 #pragma unroll
