@@ -159,6 +159,7 @@ struct pkv_pool {
   int sched_gp = 0;
   int sched_nwaves = 0;
   bool sched_needs_merge = false;   // some segment spans several waves
+  int sched_max_parts = 0;          // most partials one segment's merge reads
   bool sched_bins = false;          // eight-wave bins form (merges in LDS)
   // shared-prefix groups of the split form: h_sched continues with
   // seqinfo[4 * batch] | items[kItemInts * nitems] | groups[kGroupInts * ngroups]
@@ -542,6 +543,7 @@ void build_schedule(pkv_pool* p, int part, int target) {
     tile_blocks(p, s, j0, d[6], d[7]);
   }
   bool multi = groups;  // grouped sequences always merge their prefix partials
+  int max_parts = 0;
   int w = 0;
   for (int gg = 0; gg < H; ++gg)
     for (int ss = 0; ss < B; ++ss) {
@@ -554,6 +556,7 @@ void build_schedule(pkv_pool* p, int part, int target) {
       while (ws[v + 1] <= last) ++v;
       w1[seg] = v;
       multi |= v != w;
+      max_parts = std::max(max_parts, v - w + 1 + pg.nch[ss]);
     }
   if (groups) {
     int32_t* info = w1 + nseg;
@@ -570,6 +573,7 @@ void build_schedule(pkv_pool* p, int part, int target) {
   }
   p->sched_nwaves = W;
   p->sched_needs_merge = multi;
+  p->sched_max_parts = max_parts;
   p->sched_bins = false;
 }
 
@@ -586,6 +590,9 @@ int waves_target(const pkv_pool* p, int gp) {
 // the faster one up to an imbalance of about 1.39 (bf16), 1.36 (q8_0) and
 // 1.26 (q4_0).
 constexpr double kBinSlack = 1.25;
+// Merges of more partials than this (long contexts at a fixed split) take one
+// workgroup per (sequence, q head) instead of one wave.
+constexpr int kWideReduce = 64;
 using pkv::kBinWaves;
 
 // Bins form of the balanced schedule: whole (kv head, sequence) segments are
@@ -1621,7 +1628,7 @@ int decode_impl(pkv_pool* p, int layer, const void* k_new, const void* v_new, co
     rp.group = group;
     rp.seqinfo = dp.seqinfo;
     rp.seg_stride = dp.seg_stride;
-    e = pkv::launch_reduce(p->shape.head_dim, gp, rp, stream);
+    e = pkv::launch_reduce(p->shape.head_dim, gp, rp, p->sched_max_parts > kWideReduce, stream);
     if (e != hipSuccess) return hip_fail(e, "reduce launch");
   }
   return PKV_OK;

@@ -78,7 +78,10 @@ inline int padded_group(int g) { return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : 8
 // then counts workgroups per XCD).
 hipError_t launch_decode(int dtype, int head_dim, int gp, bool bins, int block_size,
                          const DecodeParams& p, hipStream_t stream);
-hipError_t launch_reduce(int head_dim, int gp, const ReduceParams& p, hipStream_t stream);
+// wide: one workgroup per (sequence, q head) (segments with many partials)
+// instead of one wave.
+hipError_t launch_reduce(int head_dim, int gp, const ReduceParams& p, bool wide,
+                         hipStream_t stream);
 // Whether the decode launch can take shared-prefix items for this cache dtype,
 // head_dim and padded group (split form).
 bool prefix_supported(int dtype, int head_dim, int gp);

@@ -1834,6 +1834,83 @@ __global__ __launch_bounds__(BINS ? 64 * kBinWaves : 64) void decode_kernel(Deco
 #endif
 }
 
+// Segments with many partials (a long context at a fixed split): one
+// workgroup of four waves per (sequence, q head). The maximum of the
+// partials' m comes first (a block reduction), then each wave takes every
+// fourth group of partials, a lane 4 columns of one partial (lanes past the
+// first D/4 the next partials), U groups of loads in flight, and the waves'
+// sums meet in LDS:
+//   out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i.
+template <int D, int GP>
+__global__ __launch_bounds__(256) void reduce_wide_kernel(ReduceParams p) {
+  constexpr int LPP = D / 4;     // lanes per partial (4 columns each)
+  constexpr int PPW = 64 / LPP;  // partials per wave per load step
+  constexpr int U = 8;           // load steps in flight
+  __shared__ float red[4];
+  __shared__ float osum[4 * PPW][D];
+  __shared__ float dsum[4 * PPW];
+  const int pair = blockIdx.x;  // one (sequence, q head) per workgroup
+  const int s = pair / p.q_heads;
+  const int h = pair % p.q_heads;
+  const int g = h / p.group;
+  const int hh = h - g * p.group;
+  const int seg = g * p.batch + s;
+  const int w0 = p.seg_w0[seg];
+  const int w1 = p.seg_w1[seg];
+  const int npre = p.seqinfo ? p.seqinfo[4 * s + 3] : 0;
+  if (w0 == w1 && npre == 0) return;  // written directly by the decode kernel
+  const size_t first = (size_t)(seg + 1) * p.seg_stride - 1 + w0 - npre;
+  const int n = w1 - w0 + 1 + npre;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const float* ml = p.part_ml + (first * GP + hh) * 2;  // partial i at ml[i * GP * 2]
+  float M = -__builtin_inff();
+  for (int i = tid; i < n; i += 256) M = fmaxf(M, ml[(size_t)i * GP * 2]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, xor_f(M, off));
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int sub = lane / LPP, col = (lane % LPP) * 4;
+  const float* po = p.part_o + (first * GP + hh) * D + col;  // partial i at po[i * GP * D]
+  float o[4] = {0.f, 0.f, 0.f, 0.f}, den = 0.f;
+  for (int base = 0; base < n; base += 4 * PPW * U) {
+    float4 v[U];
+    float mm[U], ll[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + (u * 4 + wave) * PPW + sub;
+      const bool ok = i < n;
+      v[u] = ok ? *reinterpret_cast<const float4*>(po + (size_t)i * GP * D)
+                : float4{0.f, 0.f, 0.f, 0.f};
+      mm[u] = ok ? ml[(size_t)i * GP * 2] : -__builtin_inff();
+      ll[u] = ok ? ml[(size_t)i * GP * 2 + 1] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = mm[u] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mm[u] - M);
+      den = __builtin_fmaf(w, ll[u], den);
+      o[0] = __builtin_fmaf(w, v[u].x, o[0]);
+      o[1] = __builtin_fmaf(w, v[u].y, o[1]);
+      o[2] = __builtin_fmaf(w, v[u].z, o[2]);
+      o[3] = __builtin_fmaf(w, v[u].w, o[3]);
+    }
+  }
+  const int slot = wave * PPW + sub;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) osum[slot][col + e] = o[e];
+  if (lane % LPP == 0) dsum[slot] = den;
+  __syncthreads();
+  if (tid < D) {
+    float acc = 0.f, dd = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4 * PPW; ++k) {
+      acc += osum[k][tid];
+      dd += dsum[k];
+    }
+    p.out[((size_t)s * p.q_heads + h) * D + tid] = acc * __builtin_amdgcn_rcpf(dd);
+  }
+}
+
 // Four wavefronts per workgroup, one (sequence, q head) pair each: fewer,
 // larger workgroups keep the dispatch ramp of this short kernel small.
 template <int D, int GP>
@@ -2067,12 +2144,16 @@ const void* decode_kernel_for(int dtype, int d, int gp, bool bins, int bs) {
 }
 
 template <int D>
-const void* reduce_for_gp(int gp) {
+const void* reduce_for_gp(int gp, bool wide) {
   switch (gp) {
-    case 1: return reinterpret_cast<const void*>(&reduce_kernel<D, 1>);
-    case 2: return reinterpret_cast<const void*>(&reduce_kernel<D, 2>);
-    case 4: return reinterpret_cast<const void*>(&reduce_kernel<D, 4>);
-    case 8: return reinterpret_cast<const void*>(&reduce_kernel<D, 8>);
+    case 1: return wide ? reinterpret_cast<const void*>(&reduce_wide_kernel<D, 1>)
+                        : reinterpret_cast<const void*>(&reduce_kernel<D, 1>);
+    case 2: return wide ? reinterpret_cast<const void*>(&reduce_wide_kernel<D, 2>)
+                        : reinterpret_cast<const void*>(&reduce_kernel<D, 2>);
+    case 4: return wide ? reinterpret_cast<const void*>(&reduce_wide_kernel<D, 4>)
+                        : reinterpret_cast<const void*>(&reduce_kernel<D, 4>);
+    case 8: return wide ? reinterpret_cast<const void*>(&reduce_wide_kernel<D, 8>)
+                        : reinterpret_cast<const void*>(&reduce_kernel<D, 8>);
   }
   return nullptr;
 }
@@ -2098,13 +2179,15 @@ int decode_blocks_per_cu(int dtype, int head_dim, int gp, bool bins, int block_s
   return n;
 }
 
-hipError_t launch_reduce(int head_dim, int gp, const ReduceParams& p, hipStream_t stream) {
-  const void* fn = head_dim == 64 ? reduce_for_gp<64>(gp)
-                   : head_dim == 128 ? reduce_for_gp<128>(gp) : nullptr;
+hipError_t launch_reduce(int head_dim, int gp, const ReduceParams& p, bool wide,
+                         hipStream_t stream) {
+  const void* fn = head_dim == 64 ? reduce_for_gp<64>(gp, wide)
+                   : head_dim == 128 ? reduce_for_gp<128>(gp, wide) : nullptr;
   if (!fn) return hipErrorInvalidValue;
   ReduceParams args = p;
   void* argv[] = {&args};
-  dim3 grid((unsigned)((p.batch * p.q_heads + 3) / 4)), block(256);
+  const unsigned pairs = (unsigned)(p.batch * p.q_heads);
+  dim3 grid(wide ? pairs : (pairs + 3) / 4), block(256);
   return hipLaunchKernel(fn, grid, block, argv, 0, stream);
 }
 

@@ -13,7 +13,7 @@
 // stubs for the GPU launch helpers referenced by pkv_host.cpp
 namespace pkv {
 hipError_t launch_decode(int, int, int, bool, int, const DecodeParams&, hipStream_t) { return hipSuccess; }
-hipError_t launch_reduce(int, int, const ReduceParams&, hipStream_t) { return hipSuccess; }
+hipError_t launch_reduce(int, int, const ReduceParams&, bool, hipStream_t) { return hipSuccess; }
 int decode_blocks_per_cu(int, int, int, bool, int) { return 1; }
 hipError_t launch_append(const void*, const void*, const int64_t*, int, void*, void*, int, int, int, int64_t, hipStream_t) { return hipSuccess; }
 hipError_t launch_append_quant(int, const void*, const void*, const int64_t*, int, void*, void*, int, int, int, int64_t, hipStream_t) { return hipSuccess; }
