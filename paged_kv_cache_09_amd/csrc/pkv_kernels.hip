@@ -1835,17 +1835,19 @@ __global__ __launch_bounds__(BINS ? 64 * kBinWaves : 64) void decode_kernel(Deco
 }
 
 // Segments with many partials (a long context at a fixed split): one
-// workgroup of four waves per (sequence, q head). The maximum of the
-// partials' m comes first (a block reduction), then each wave takes every
+// workgroup of four waves per (sequence, q head). Each wave takes every
 // fourth group of partials, a lane 4 columns of one partial (lanes past the
-// first D/4 the next partials), U groups of loads in flight, and the waves'
-// sums meet in LDS:
+// first D/4 the next partials); up to 4 * PPW * U partials are loaded at once,
+// with their (m, l), and M comes from those registers (a block reduction),
+// so the merge waits on memory once; more partials take a first pass for M
+// and then U groups of loads at a time. The waves' sums meet in LDS:
 //   out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i.
 template <int D, int GP>
 __global__ __launch_bounds__(256) void reduce_wide_kernel(ReduceParams p) {
   constexpr int LPP = D / 4;     // lanes per partial (4 columns each)
   constexpr int PPW = 64 / LPP;  // partials per wave per load step
-  constexpr int U = 8;           // load steps in flight
+  constexpr int U = 32;          // load steps in flight
+  constexpr int STEP = 4 * PPW * U;
   __shared__ float red[4];
   __shared__ float osum[4 * PPW][D];
   __shared__ float dsum[4 * PPW];
@@ -1863,17 +1865,24 @@ __global__ __launch_bounds__(256) void reduce_wide_kernel(ReduceParams p) {
   const int n = w1 - w0 + 1 + npre;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const float* ml = p.part_ml + (first * GP + hh) * 2;  // partial i at ml[i * GP * 2]
-  float M = -__builtin_inff();
-  for (int i = tid; i < n; i += 256) M = fmaxf(M, ml[(size_t)i * GP * 2]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, xor_f(M, off));
-  if (lane == 0) red[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const int sub = lane / LPP, col = (lane % LPP) * 4;
   const float* po = p.part_o + (first * GP + hh) * D + col;  // partial i at po[i * GP * D]
+  auto block_max = [&](float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, xor_f(x, off));
+    if (lane == 0) red[wave] = x;
+    __syncthreads();
+    x = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();  // red is written again only after every wave has read it
+    return x;
+  };
   float o[4] = {0.f, 0.f, 0.f, 0.f}, den = 0.f;
-  for (int base = 0; base < n; base += 4 * PPW * U) {
+  float M = -__builtin_inff();
+  if (n > STEP) {
+    for (int i = tid; i < n; i += 256) M = fmaxf(M, ml[(size_t)i * GP * 2]);
+    M = block_max(M);
+  }
+  for (int base = 0; base < n; base += STEP) {
     float4 v[U];
     float mm[U], ll[U];
 #pragma unroll
@@ -1884,6 +1893,11 @@ __global__ __launch_bounds__(256) void reduce_wide_kernel(ReduceParams p) {
                 : float4{0.f, 0.f, 0.f, 0.f};
       mm[u] = ok ? ml[(size_t)i * GP * 2] : -__builtin_inff();
       ll[u] = ok ? ml[(size_t)i * GP * 2 + 1] : 0.f;
+    }
+    if (n <= STEP) {  // every partial is in registers: M from them
+#pragma unroll
+      for (int u = 0; u < U; ++u) M = fmaxf(M, mm[u]);
+      M = block_max(M);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
