@@ -33,6 +33,11 @@ SMALL = {
     "shared_cow_small": W.scaled(W.CONFIGS["shared_prefix_cow_bf16"], batch=5, num_blocks=200),
     "long_small": W.scaled(W.CONFIGS["long_ctx_bf16"], batch=2, ctx_fixed=(4097, 3001),
                            num_blocks=500),
+    # head_dim 64 and fp16 at a long context: at the 16-token split, 257 and
+    # 563 partials per (sequence, head) merge in one workgroup each
+    "long_d64_f16_small": W.scaled(W.CONFIGS["long_ctx_bf16"], batch=2, head_dim=64,
+                                   q_heads=8, kv_heads=2, dtype=W.F16,
+                                   ctx_fixed=(4097, 9000), num_blocks=900),
     # GQA groups 3 (padded to 4) and 8, head_dim 64 in 2-byte types
     "gqa3_d64_bf16": W.scaled(W.CONFIGS["llama8b_bf16"], batch=3, q_heads=6, kv_heads=2,
                               head_dim=64, num_blocks=150, ctx_lo=1, ctx_hi=600),
