@@ -445,6 +445,25 @@ void build_schedule(pkv_pool* p, int part, int target) {
   if (kPrefixGroups &&
       pkv::prefix_supported(p->shape.dtype, p->shape.head_dim, p->sched_gp_building))
     find_groups(p, p->sched_gp_building, pg);
+#ifndef PKV_ITEMS_BY_HEAD
+#define PKV_ITEMS_BY_HEAD 1
+#endif
+  if (PKV_ITEMS_BY_HEAD && !pg.items.empty()) {
+    // items ordered by kv head (then group, chunk): the decode launch gives
+    // each XCD a contiguous share of them, so a head's prompt tiles are
+    // fetched into few L2s
+    const size_t n = pg.items.size() / pkv::kItemInts;
+    std::vector<int> ord(n);
+    for (size_t i = 0; i < n; ++i) ord[i] = (int)i;
+    std::stable_sort(ord.begin(), ord.end(), [&](int a, int b) {
+      return pg.items[(size_t)a * pkv::kItemInts + 1] < pg.items[(size_t)b * pkv::kItemInts + 1];
+    });
+    std::vector<int32_t> sorted(pg.items.size());
+    for (size_t i = 0; i < n; ++i)
+      std::copy_n(pg.items.begin() + (size_t)ord[i] * pkv::kItemInts, pkv::kItemInts,
+                  sorted.begin() + i * pkv::kItemInts);
+    pg.items.swap(sorted);
+  }
   const bool groups = !pg.recs.empty();
   // the eight-wave form: 2-byte and quantised tiles (fp32 tiles spill)
   if (!groups && part == 0 && p->shape.dtype != PKV_F32) {

@@ -813,7 +813,12 @@ __global__ __launch_bounds__(BINS ? 64 * kBinWaves : 64) void decode_kernel(Deco
   constexpr bool PFX = !BINS && D == 128 && (DT == DT_F16 || DT == DT_BF16);
   if constexpr (PFX) {
     if ((int)blockIdx.x < p.nprefix) {
-      if ((int)blockIdx.x < p.nitems) prefix_item<DT, GP, BS>(p, blockIdx.x);
+      // Workgroups are dealt round-robin to the XCDs: XCD x takes items
+      // [x * n / 8, (x + 1) * n / 8), which the host orders by kv head, so the
+      // prompt tiles of a head are re-read from one XCD's L2.
+      const int per = p.nprefix / kNumXcd;
+      const int item = ((int)blockIdx.x % kNumXcd) * per + (int)blockIdx.x / kNumXcd;
+      if (item < p.nitems) prefix_item<DT, GP, BS>(p, item);
       return;
     }
   }
