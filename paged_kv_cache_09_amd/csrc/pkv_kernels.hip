@@ -1953,28 +1953,32 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
 
 // Appends skip a slot outside [0, num_slots) (num_blocks * block_size): a
 // stale or bad slot from the caller never becomes a store outside the pool.
+// Workgroups in row order, nslice per new row (each 256 of its (K|V, kv
+// head, 16-byte chunk) pieces, one per thread; the row's slot is one scalar
+// load). Row bytes and block sizes are powers of two, so every index below
+// the row is a shift or a mask. The new rows are read once and the pool rows
+// written once: nontemporal accesses stream both past the caches.
 __global__ __launch_bounds__(256) void append_kernel(const char* k_new, const char* v_new,
-                                                     const int64_t* slots, int batch,
-                                                     char* k_layer, char* v_layer, int kv_heads,
-                                                     int row_bytes, int block_size,
-                                                     int64_t num_slots) {
-  const int per_row = row_bytes / 16;
-  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-  const int chunk = (int)(idx % per_row);
-  long r = idx / per_row;
-  const int kv = (int)(r & 1);
-  r >>= 1;
-  const int g = (int)(r % kv_heads);
-  const long s = r / kv_heads;
-  if (s >= batch) return;
+                                                     const int64_t* slots, char* k_layer,
+                                                     char* v_layer, int kv_heads, int row_shift,
+                                                     int bs_shift, int nslice, int64_t num_slots) {
+  const unsigned bid = blockIdx.x;
+  const unsigned row = bid / (unsigned)nslice;
+  const size_t s = row;
   const int64_t slot = slots[s];
   if (slot < 0 || slot >= num_slots) return;
-  const int64_t blk = slot / block_size;
-  const int64_t pos = slot % block_size;
-  const char* src = (kv ? v_new : k_new) + ((size_t)s * kv_heads + g) * row_bytes + chunk * 16;
+  const int cshift = row_shift - 4;  // 16-byte chunks per row: 1 << cshift
+  const int t = (int)(bid - row * (unsigned)nslice) * 256 + (int)threadIdx.x;
+  const int chunk = t & ((1 << cshift) - 1);
+  const int r = t >> cshift;
+  const int kv = r & 1, g = r >> 1;
+  if (g >= kv_heads) return;
+  const size_t blk = (size_t)(slot >> bs_shift);
+  const size_t pos = (size_t)(slot & ((1 << bs_shift) - 1));
+  const char* src = (kv ? v_new : k_new) + ((s * kv_heads + g) << row_shift) + chunk * 16;
   char* dst = (kv ? v_layer : k_layer) +
-              (((size_t)blk * kv_heads + g) * block_size + pos) * row_bytes + chunk * 16;
-  *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+              ((((blk * kv_heads + g) << bs_shift) + pos) << row_shift) + chunk * 16;
+  __builtin_nontemporal_store(nt16(src), reinterpret_cast<u32x4*>(dst));
 }
 
 // Thread of the quantised appends -> (32-value group, K or V, kv head, row of
@@ -2218,12 +2222,18 @@ bool prefix_supported(int dtype, int head_dim, int gp) {
 hipError_t launch_append(const void* k_new, const void* v_new, const int64_t* slots, int batch,
                          void* k_layer, void* v_layer, int kv_heads, int row_bytes,
                          int block_size, int64_t num_slots, hipStream_t stream) {
-  const long threads = (long)batch * kv_heads * 2 * (row_bytes / 16);
-  const unsigned blocks = (unsigned)((threads + 255) / 256);
-  hipLaunchKernelGGL(append_kernel, dim3(blocks), dim3(256), 0, stream,
+  if (batch <= 0) return hipSuccess;
+  if (row_bytes < 16 || block_size < 1) return hipErrorInvalidValue;
+  const int row_shift = __builtin_ctz((unsigned)row_bytes);
+  const int bs_shift = __builtin_ctz((unsigned)block_size);
+  if ((1 << row_shift) != row_bytes || (1 << bs_shift) != block_size) return hipErrorInvalidValue;
+  const int pieces = 2 * kv_heads * (row_bytes / 16);  // per new row
+  const int nslice = (pieces + 255) / 256;
+  if ((int64_t)batch * nslice > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)(batch * nslice)), dim3(256), 0, stream,
                      static_cast<const char*>(k_new), static_cast<const char*>(v_new), slots,
-                     batch, static_cast<char*>(k_layer), static_cast<char*>(v_layer), kv_heads,
-                     row_bytes, block_size, num_slots);
+                     static_cast<char*>(k_layer), static_cast<char*>(v_layer), kv_heads,
+                     row_shift, bs_shift, nslice, num_slots);
   return hipGetLastError();
 }
 
