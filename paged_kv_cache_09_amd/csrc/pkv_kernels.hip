@@ -1987,19 +1987,21 @@ __global__ __launch_bounds__(256) void append_kernel(const char* k_new, const ch
 // neighbouring rows fill too, so a wave writing 16 consecutive rows of a
 // multi-token write covers whole lines instead of pieces of them.
 struct QuantAppendItem {
-  int grp, kv, g;
-  long s;
+  int grp, kv, g, s;
 };
-__device__ __forceinline__ QuantAppendItem quant_append_item(long idx, int ngr, int kv_heads) {
+// 32-bit thread indices (the launcher checks the count), ngr a power of two.
+__device__ __forceinline__ QuantAppendItem quant_append_item(unsigned idx, int ngr,
+                                                             unsigned kv_heads) {
   QuantAppendItem it;
-  it.grp = (int)(idx % ngr);
-  long t = idx / ngr;
+  it.grp = (int)(idx & (unsigned)(ngr - 1));
+  unsigned t = idx / (unsigned)ngr;
   const int rr = (int)(t & 15);
   t >>= 4;
   it.kv = (int)(t & 1);
   t >>= 1;
-  it.g = (int)(t % kv_heads);
-  it.s = (t / kv_heads) * 16 + rr;
+  const unsigned q = t / kv_heads;
+  it.g = (int)(t - q * kv_heads);
+  it.s = (int)(q * 16 + rr);
   return it;
 }
 
@@ -2015,14 +2017,16 @@ __global__ __launch_bounds__(256) void append_q8_kernel(const char* k_new, const
   constexpr int NGR = D / 32;
   const int BS = block_size;
   const int TILE = BS * D + BS * NGR * 2;
-  const QuantAppendItem it = quant_append_item((long)blockIdx.x * 256 + threadIdx.x, NGR, kv_heads);
+  const QuantAppendItem it =
+      quant_append_item(blockIdx.x * 256u + threadIdx.x, NGR, (unsigned)kv_heads);
   const int grp = it.grp, kv = it.kv, g = it.g;
-  const long s = it.s;
+  const int s = it.s;
   if (s >= batch) return;
   const int64_t slot = slots[s];
   if (slot < 0 || slot >= num_slots) return;
-  const int64_t blk = slot / BS;
-  const int pos = (int)(slot % BS);
+  const int bs_shift = __builtin_ctz((unsigned)BS);  // block sizes are powers of two
+  const int64_t blk = slot >> bs_shift;
+  const int pos = (int)(slot & (BS - 1));
   const char* src = (kv ? v_new : k_new) + (((size_t)s * kv_heads + g) * D + grp * 32) * 2;
   float x[4][8];
   float a = 0.f;
@@ -2054,14 +2058,16 @@ __global__ __launch_bounds__(256) void append_q4_kernel(const char* k_new, const
   constexpr int CB = D / 2;
   const int BS = block_size;
   const int TILE = BS * CB + BS * NGR * 2;
-  const QuantAppendItem it = quant_append_item((long)blockIdx.x * 256 + threadIdx.x, NGR, kv_heads);
+  const QuantAppendItem it =
+      quant_append_item(blockIdx.x * 256u + threadIdx.x, NGR, (unsigned)kv_heads);
   const int grp = it.grp, kv = it.kv, g = it.g;
-  const long s = it.s;
+  const int s = it.s;
   if (s >= batch) return;
   const int64_t slot = slots[s];
   if (slot < 0 || slot >= num_slots) return;
-  const int64_t blk = slot / BS;
-  const int pos = (int)(slot % BS);
+  const int bs_shift = __builtin_ctz((unsigned)BS);  // block sizes are powers of two
+  const int64_t blk = slot >> bs_shift;
+  const int pos = (int)(slot & (BS - 1));
   const char* src = (kv ? v_new : k_new) + (((size_t)s * kv_heads + g) * D + grp * 32) * 2;
   float x[4][8];
   float a = 0.f, m = 0.f;
@@ -2242,7 +2248,9 @@ hipError_t launch_append_quant(int dtype, const void* k_new, const void* v_new,
                                int kv_heads, int head_dim, int block_size, int64_t num_slots,
                                hipStream_t stream) {
   // rows in groups of 16 (quant_append_item); the padding rows' threads return
+  if (batch <= 0) return hipSuccess;
   const long threads = (long)((batch + 15) / 16) * 16 * kv_heads * 2 * (head_dim / 32);
+  if (threads > 0xffffff00L) return hipErrorInvalidValue;  // 32-bit thread indices
   const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
   const char* kn = static_cast<const char*>(k_new);
   const char* vn = static_cast<const char*>(v_new);
