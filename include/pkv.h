@@ -253,9 +253,10 @@ int pkv_copy_blocks(pkv_pool* pool, const int32_t* host_pairs, int n, uintptr_t 
  * passes one row and one slot (from pkv_prepare_write) per token; the slots
  * must be distinct. Device slots are not checked on the host; a slot outside
  * [0, num_blocks * block_size) is skipped by the kernel (nothing is written
- * for that row). The kernels index their work items with 32-bit integers: a
- * call whose batch * kv_heads * 2 * head_dim exceeds about 2^35 elements (far
- * beyond any pool) returns PKV_EHIP without writing.
+ * for that row). The kernels index their work items with 32-bit integers:
+ * batch * kv_heads * 2 * head_dim may reach 2^37 elements for q8_0 / q4_0 and
+ * 2^43 / (element bytes) otherwise; a larger call returns PKV_EHIP without
+ * writing.
  */
 int pkv_kv_append(pkv_pool* pool, int layer, const void* k_new, const void* v_new,
                   const int64_t* dev_slots, int batch, uintptr_t stream);
